@@ -1,0 +1,144 @@
+"""Seeded synthetic inputs for the nearest-centroid assignment / Lloyd update.
+
+This module only draws input arrays. It holds none of the method's arithmetic
+(no distance, argmin, sum or mean), so both the GPU path and the float64 CPU
+oracle may take their inputs from it without sharing any computation.
+
+The pages ("Three shapes that fit an eager Gram assignment", section Shapes;
+"Fusion probe", section Probe shape; "004 - tile sizes, a Cython Lloyd step,
+and k-means++", sections Gram tiles on feature-heavy and Same arrays as the
+Cython iteration) fix the float32 shapes but never state how X and C were drawn.
+The recipe used here is Gaussian blobs:
+
+  1. blob centres (kb, d) = sigma_c * N(0, 1), float32;
+  2. membership = a seeded permutation of arange(n) % kb (balanced blobs);
+  3. X = centres[membership] + sigma * N(0, 1), float32;
+  4. C = X[rows], rows drawn without replacement (k distinct rows of X).
+
+The sample-heavy shape draws X i.i.d. N(0, 1) instead of blobs.  Every array is
+drawn from ``numpy.random.default_rng(seed)`` in exactly that order, so a seed
+names the bytes.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = [
+    "Config",
+    "CONFIGS",
+    "make",
+    "make_blobs",
+    "make_integer",
+    "with_far_centroid",
+]
+
+
+@dataclass(frozen=True)
+class Config:
+    """A workload: n samples, k centroids, d features (all float32)."""
+
+    name: str
+    n: int
+    k: int
+    d: int
+    kb: int | None  # number of Gaussian blobs; None = i.i.d. N(0, sigma^2)
+    sigma_c: float  # standard deviation of the blob centres
+    sigma: float  # per-feature noise around a blob centre
+
+    @property
+    def flops(self) -> float:
+        """Algorithmic work of one assignment: the Gram product, 2*n*k*d."""
+        return 2.0 * self.n * self.k * self.d
+
+
+# The five workloads. Shapes: Tiny = the n=512, k=17, d=64 label check of the
+# fusion probe; Probe = the fusion probe shape; Mid = the shape shared with the
+# Cython Lloyd iteration; sample-heavy and feature-heavy = two of the three
+# large shapes of the resized-shapes page (the Gram tile grid and the Lloyd
+# step of the tile-tradeoff page use feature-heavy).
+CONFIGS: dict[str, Config] = {
+    c.name: c
+    for c in (
+        Config("tiny", 512, 17, 64, kb=17, sigma_c=4.0, sigma=1.0),
+        Config("probe", 4096, 256, 512, kb=256, sigma_c=1.0, sigma=0.5),
+        Config("mid", 65536, 1024, 2048, kb=1024, sigma_c=1.0, sigma=0.5),
+        Config("sample_heavy", 131072, 8192, 8192, kb=None, sigma_c=0.0, sigma=1.0),
+        Config("feature_heavy", 65536, 4096, 16384, kb=4096, sigma_c=1.0, sigma=1.0),
+    )
+}
+
+
+def _fill_normal(rng: np.random.Generator, out: np.ndarray, chunk_rows: int = 4096) -> None:
+    """Fill a (rows, d) float32 array with N(0, 1) draws, row-chunk by row-chunk.
+
+    Chunking bounds the temporary memory; the draw order is row-major, so the
+    bytes equal those of one ``rng.standard_normal(out.shape, dtype=float32)``
+    call.
+    """
+    rows = out.shape[0]
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        rng.standard_normal(out[r0:r1].shape, dtype=np.float32, out=out[r0:r1])
+
+
+def make_blobs(n: int, k: int, d: int, kb: int | None, sigma_c: float, sigma: float,
+               seed: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """Draw (X, C) following the blob recipe in this module's docstring.
+
+    Returns X (n, d) and C (k, d), both C-contiguous float32. Requires k <= n.
+    """
+    if not (1 <= k <= n) or d < 1:
+        raise ValueError(f"need 1 <= k <= n and d >= 1, got n={n} k={k} d={d}")
+    rng = np.random.default_rng(seed)
+    X = np.empty((n, d), dtype=np.float32)
+    if kb is None:
+        _fill_normal(rng, X)
+        if sigma != 1.0:
+            X *= np.float32(sigma)
+    else:
+        centres = np.empty((kb, d), dtype=np.float32)
+        _fill_normal(rng, centres)
+        centres *= np.float32(sigma_c)
+        membership = rng.permutation(np.arange(n) % kb)
+        _fill_normal(rng, X)
+        X *= np.float32(sigma)
+        step = 4096
+        for r0 in range(0, n, step):
+            r1 = min(n, r0 + step)
+            X[r0:r1] += centres[membership[r0:r1]]
+    rows = rng.choice(n, size=k, replace=False)
+    C = np.ascontiguousarray(X[rows])
+    return X, C
+
+
+def make(config: str | Config, seed: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """Draw (X, C) for a named workload (a key of ``CONFIGS``)."""
+    cfg = CONFIGS[config] if isinstance(config, str) else config
+    return make_blobs(cfg.n, cfg.k, cfg.d, cfg.kb, cfg.sigma_c, cfg.sigma, seed)
+
+
+def make_integer(n: int, k: int, d: int, lo: int = -8, hi: int = 8,
+                 seed: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """Integer-valued float32 X (n, d) and C (k, d), entries uniform in [lo, hi].
+
+    With |entries| <= 8 and d <= 256 every product and partial sum of the
+    distance is an integer below 2**24, so float32 arithmetic on them is exact
+    and exact ties between centroids are frequent.
+    """
+    rng = np.random.default_rng(seed)
+    X = rng.integers(lo, hi + 1, size=(n, d)).astype(np.float32)
+    C = rng.integers(lo, hi + 1, size=(k, d)).astype(np.float32)
+    return X, C
+
+
+def with_far_centroid(X: np.ndarray, C: np.ndarray, position: int, offset: float = 1.0e3
+                      ) -> np.ndarray:
+    """Return a copy of C where row ``position`` is moved far from every sample.
+
+    That centroid then wins no sample, which forces an empty cluster.
+    """
+    C2 = np.array(C, dtype=np.float32, copy=True)
+    C2[position] = np.float32(offset) + np.abs(X).max(axis=0)
+    return C2

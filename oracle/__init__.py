@@ -1,0 +1,182 @@
+"""float64 brute-force CPU oracle (test infrastructure only).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of the
+benchmark may import this package. It shares no code with the GPU path; the GPU
+path must never call it.
+
+The arithmetic lives in ``oracle.c`` (plain C, OpenMP over the outer loop,
+float64, difference form). This module only builds and loads that library,
+marshals numpy arrays, and derives the near-tie mask from the oracle's best and
+second-best distances.
+
+Functions and the passages they follow:
+
+* ``assign``  - squared distance in the explicit difference form and the
+  lowest-index argmin ("Fusion probe", section PyTorch, naive argmin;
+  "Three shapes that fit an eager Gram assignment", section Running argmin).
+* ``update``  - per-cluster counts, sums and means ("Three shapes ...", section
+  Full Lloyd step; "004 - tile sizes ...", section Cython reference). Empty
+  clusters keep their old centre.
+* ``lloyd_step`` - ``assign`` with the old centres, then ``update`` with those
+  labels ("004 - tile sizes ...", section Cython reference: the assignment
+  precedes the scatter into centre sums).
+* ``near_ties`` - rows whose best-to-second-best gap is within
+  ``rtol * (||x||^2 + ||c_label||^2)``; on these rows two correct float32
+  implementations may pick different labels ("004 - tile sizes ...", section
+  Same arrays as the Cython iteration, where two implementations disagree on
+  one row of 65536).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "oracle.c")
+
+_lock = threading.Lock()
+_lib = None
+
+_f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+_f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+_i64p = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
+
+
+def build(verbose: bool = False, src: str = SRC_PATH, out: str = LIB_PATH) -> str:
+    """Compile ``oracle.c`` (or ``src``) into a shared library with gcc and OpenMP."""
+    cmd = ["gcc", "-O3", "-march=x86-64-v3", "-fopenmp", "-fPIC", "-shared",
+           "-std=c11", "-Wall", "-Wextra", "-o", out + ".tmp", src, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _f32(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.float32:
+        raise TypeError(f"expected float32, got {a.dtype}")
+    return a
+
+
+class Oracle:
+    """The oracle bound to one compiled library (the default one unless a test
+    loads a build with a planted mistake to show the pins catch it)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_assign.restype = None
+        lib.oracle_assign.argtypes = [_f32p, _f32p, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int64, _i64p, _f64p, _f64p]
+        lib.oracle_update.restype = ctypes.c_int
+        lib.oracle_update.argtypes = [_f32p, _i64p, _f32p, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int64, _f32p, _i64p, _f64p]
+        self.lib = lib
+        self.path = path
+
+    def num_threads(self) -> int:
+        """Threads the oracle's OpenMP loops use."""
+        return int(self.lib.oracle_num_threads())
+
+    def assign(self, X, C):
+        """Nearest centroid of every row of X.
+
+        Returns ``(labels, best, second)``: int64 labels (lowest index on exact
+        ties), float64 D_i,label and float64 second-smallest distance over the
+        other centroids (+inf if k = 1).
+        """
+        X, C = _f32(X), _f32(C)
+        n, d = X.shape
+        k, d2 = C.shape
+        if d != d2:
+            raise ValueError("X and C disagree on d")
+        labels = np.empty(n, dtype=np.int64)
+        best = np.empty(n, dtype=np.float64)
+        second = np.empty(n, dtype=np.float64)
+        if n:
+            self.lib.oracle_assign(X, C, n, k, d, labels, best, second)
+        return labels, best, second
+
+    def update(self, X, labels, C_old):
+        """Lloyd centroid update for fixed labels.
+
+        Returns ``(C_new, counts, sums)``: float32 (k, d) means (old centre kept
+        for an empty cluster), int64 counts, float64 (k, d) per-cluster sums.
+        """
+        X, C_old = _f32(X), _f32(C_old)
+        labels = np.ascontiguousarray(labels, dtype=np.int64)
+        n, d = X.shape
+        k = C_old.shape[0]
+        if labels.shape != (n,):
+            raise ValueError("labels must have shape (n,)")
+        C_new = np.empty((k, d), dtype=np.float32)
+        counts = np.empty(k, dtype=np.int64)
+        sums = np.empty((k, d), dtype=np.float64)
+        rc = self.lib.oracle_update(X, labels, C_old, n, k, d, C_new, counts, sums)
+        if rc != 0:
+            raise ValueError("a label lies outside [0, k)")
+        return C_new, counts, sums
+
+    def lloyd_step(self, X, C_old):
+        """One Lloyd iteration: labels against C_old, then the mean update.
+
+        Returns ``(labels, best, second, C_new, counts)``.
+        """
+        labels, best, second = self.assign(X, C_old)
+        C_new, counts, _ = self.update(X, labels, C_old)
+        return labels, best, second, C_new, counts
+
+
+def default() -> Oracle:
+    """The oracle built from ``oracle.c`` (built on first use if missing)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                build()
+            _lib = Oracle(LIB_PATH)
+        return _lib
+
+
+def num_threads() -> int:
+    return default().num_threads()
+
+
+def assign(X, C):
+    return default().assign(X, C)
+
+
+def update(X, labels, C_old):
+    return default().update(X, labels, C_old)
+
+
+def lloyd_step(X, C_old):
+    return default().lloyd_step(X, C_old)
+
+
+def sq_norms(A) -> np.ndarray:
+    """Row squared norms in float64."""
+    A64 = np.asarray(A, dtype=np.float64)
+    return np.einsum("ij,ij->i", A64, A64)
+
+
+def near_ties(X, C, labels, best, second, rtol: float = 1e-5) -> np.ndarray:
+    """Boolean mask of rows whose best-to-second gap is within the tie band.
+
+    The band is ``rtol * (||x_i||^2 + ||c_label_i||^2)`` with norms in float64.
+    """
+    scale = sq_norms(X) + sq_norms(C)[np.asarray(labels)]
+    return (np.asarray(second) - np.asarray(best)) <= rtol * scale
+
+
+for _name in ("num_threads", "assign", "update", "lloyd_step"):
+    globals()[_name].__doc__ = getattr(Oracle, _name).__doc__
+del _name
