@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of the Lloyd k-means hot path on one MI355X.
+
+A step is one Lloyd iteration (``kmeans_lloyd_step``: centroid norms, sample
+norms, fused MFMA assignment with the argmin in the register epilogue,
+finalize, counts, stable grouping by label, segmented float64 sums and the
+mean) over the whole workload, inputs resident in HBM. Default workload: the
+feature-heavy shape, n = 65536 samples, k = 4096 centroids, d = 16384 features,
+float32, seeded synthetic Gaussian blobs.
+
+Prints one JSON line:
+  value        2*n*k*d / (Lloyd step time), TFLOP/s (whole step, update included)
+  ms_per_step  Lloyd iteration time in ms
+  assign_*     the fused assignment alone (kmeans_assign without min_dist)
+  roofline     the fused assignment kernel against the MI355X fp32 MFMA peak
+  cpu_baseline the float64 oracle on a bounded sample of rows, host cores
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused assign TFLOP/s (2nkd/t) + Lloyd iteration ms, 65536×4096×16384 fp32"
+MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak (published)
+PAGES_LLOYD_MS = 1700.0        # the pages' feature-heavy Lloyd iteration (NVIDIA L4), context
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "assign_tile_feature_heavy_traffic.json")
+ASSIGN_SOURCE = os.path.join(ROOT, "nearest_centroid_assignment_amd", "csrc", "assign.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="feature_heavy",
+                    help="workload name (tiny, probe, mid, sample_heavy, feature_heavy)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target duration of the oracle CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    with open(ASSIGN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_record(cfg):
+    """HBM bytes per launch of the assignment kernel from committed rocprofv3
+    counter runs (FETCH_SIZE and WRITE_SIZE, scaled by the factor a plain copy
+    kernel of known size gives), or None when absent or when the kernel source
+    has changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("assign_source_sha256") != source_digest() or rec.get("workload") != cfg.name:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(X, C, target_s: float):
+    """Time the float64 oracle's assignment on a seeded sample of rows against
+    all centroids; scale to TFLOP/s of the same 2*rows*k*d work."""
+    import numpy as np
+
+    import oracle
+
+    k, d = C.shape
+    rng = np.random.default_rng(7)
+    probe_rows = 16
+    rows = rng.choice(len(X), probe_rows, replace=False)
+    t0 = time.perf_counter()
+    oracle.assign(X[rows], C)
+    t_probe = time.perf_counter() - t0
+    m = int(min(len(X), max(probe_rows, probe_rows * target_s / max(t_probe, 1e-6))))
+    rows = np.sort(rng.choice(len(X), m, replace=False))
+    Xs = np.ascontiguousarray(X[rows])
+    t0 = time.perf_counter()
+    oracle.assign(Xs, C)
+    t = time.perf_counter() - t0
+    return {
+        "value": 2.0 * m * k * d / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{m} seeded rows x all {k} centroids x {d} features "
+                  f"(float64 difference-form assignment, {t:.1f} s)",
+    }
+
+
+def main() -> int:
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the per-GPU shard would run the same kernels; see the sharding design).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from nearest_centroid_assignment_amd import binding, datagen
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    cfg = datagen.CONFIGS[args.config]
+    n, k, d = cfg.n, cfg.k, cfg.d
+    dev = torch.device("cuda:0")
+
+    log(f"generating {cfg.name} {n}x{k}x{d}")
+    X, C = datagen.make(cfg)
+    Xg = torch.from_numpy(X).to(dev)
+    Cg = torch.from_numpy(C).to(dev)
+    labels = torch.empty(n, dtype=torch.int64, device=dev)
+    md = torch.empty(n, dtype=torch.float32, device=dev)
+    C_new = torch.empty_like(Cg)
+    counts = torch.empty(k, dtype=torch.int64, device=dev)
+    ws_bytes = binding.kmeans_workspace_bytes(n, k, d, binding.KM_OP_LLOYD)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+
+    def lloyd():
+        binding.kmeans_lloyd_step(Xg, Cg, labels, md, C_new, counts, workspace=ws, stream=stream)
+
+    def assign_only():
+        binding.kmeans_assign(Xg, Cg, labels, None, workspace=ws, stream=stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        lloyd()
+    torch.cuda.synchronize()
+
+    # Timed Lloyd steps: events on the stream the kernels run on, bracketed by
+    # device synchronisation; the wall clock is kept beside the events.
+    torch.cuda.reset_peak_memory_stats(dev)
+    base_alloc = torch.cuda.memory_allocated(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} Lloyd steps")
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        lloyd()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3 / args.steps
+    lloyd_ms = ev0.elapsed_time(ev1) / args.steps
+    peak_extra = torch.cuda.max_memory_allocated(dev) - base_alloc
+
+    # The fused assignment alone, one event pair per call, for the roofline of
+    # its dominant kernel (the three tiny kernels around it are included, so
+    # the kernel's own rate is slightly higher than reported).
+    log(f"timing {args.steps} assignments")
+    assign_only()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        assign_only()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(a.elapsed_time(b) for a, b in evs)
+    assign_ms = sum(per_call) / len(per_call)
+    flops = cfg.flops
+    assign_tflops = flops / (assign_ms * 1e-3) / 1e12
+
+    traffic = traffic_record(cfg)
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(assign_tflops, 3),
+        "peak": MFMA_FP32_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(assign_tflops / MFMA_FP32_PEAK_TFLOPS, 4),
+        "traffic": traffic,
+        "kernel": "assign_tile_kernel",
+        "algorithmic_per_launch": f"2*n*k*d = {flops:.4e} flop",
+    }
+
+    result = {
+        "metric": METRIC,
+        "value": round(flops / (lloyd_ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(lloyd_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(PAGES_LLOYD_MS / lloyd_ms, 2) if cfg.name == "feature_heavy" else None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} n={n} k={k} d={d} float32 Gaussian blobs, seed 0",
+                   "n": n, "k": k, "d": d},
+        "lloyd_ms": round(lloyd_ms, 3),
+        "lloyd_wall_ms": round(wall_ms, 3),
+        "assign_ms": round(assign_ms, 3),
+        "assign_ms_min": round(per_call[0], 3),
+        "assign_tflops": round(assign_tflops, 3),
+        "workspace_bytes": ws_bytes,
+        "peak_extra_bytes_during_step": int(peak_extra),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle CPU baseline")
+        result["cpu_baseline"] = cpu_baseline(X, C, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

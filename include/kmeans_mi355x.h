@@ -1,0 +1,125 @@
+/*
+ * kmeans_mi355x.h - C ABI of the MI355X (gfx950) nearest-centroid assignment
+ * and Lloyd centroid update.
+ *
+ * Operations (pages: "Three shapes that fit an eager Gram assignment",
+ * "Fusion probe", "004 - tile sizes, a Cython Lloyd step, and k-means++"):
+ *
+ *   assign  labels[i] = argmin_j ||x_i - c_j||^2, computed in Gram form as the
+ *           argmin of ||c_j||^2 - 2 x_i.c_j (the Gram identity of "Three
+ *           shapes ...", section Gram assignment, with ||x||^2 dropped inside
+ *           the tile as in "004 ...", section Schedules added). Exact ties go
+ *           to the lowest index. min_dist[i] = max(0, ||x_i||^2 + that
+ *           minimum) is the full squared distance, the running winning
+ *           distance of "Three shapes ...", section Running argmin.
+ *   update  counts[j] = #{i : labels[i] = j}; C_new[j] = mean of those x_i;
+ *           a cluster with no sample keeps C_old[j] ("Three shapes ...",
+ *           section Full Lloyd step; "004 ...", section Lloyd step).
+ *   lloyd   assign against C_old, then update with those labels: one Lloyd
+ *           iteration ("004 ...", sections Lloyd step and Cython reference).
+ *
+ * Common conventions
+ *   - Every array pointer is a DEVICE pointer owned by the caller. Matrices are
+ *     row-major and dense: X is (n, d) float32, C / C_old / C_new are (k, d)
+ *     float32, labels is (n,) int64, counts is (k,) int64, min_dist is (n,)
+ *     float32. The library never allocates, frees or keeps device memory.
+ *   - workspace is a caller-owned device buffer of at least
+ *     kmeans_workspace_bytes(n, k, d, op) bytes, any alignment. Its contents
+ *     on entry do not matter; it is clobbered. Two calls that may run at the
+ *     same time need two workspaces.
+ *   - stream is a hipStream_t (NULL = the default stream). Every call only
+ *     enqueues kernels on it and returns: no host synchronisation. Results are
+ *     ready when the stream has reached that point. A fault inside a kernel
+ *     surfaces at the caller's next synchronisation, not as a return value.
+ *   - Shapes: 0 <= n < 2^31, 1 <= k < 2^31, 1 <= d < 2^31. With n = 0 nothing
+ *     is read from X, labels or min_dist (they may be NULL). k > n is allowed.
+ *   - Inputs must be finite; NaN or Inf inputs give unspecified labels.
+ *   - Outputs must not overlap any input, any other output or the workspace,
+ *     with one exception: C_new may equal C_old exactly (in-place update).
+ *   - Arguments are validated on the host before any HIP call; an invalid
+ *     call returns a negative km_status and enqueues nothing.
+ *   - Arithmetic: float32 MFMA products with float32 accumulation for the
+ *     assignment; per-cluster sums accumulated in float64 in increasing
+ *     sample order, then divided in float64 and rounded once to float32.
+ *     Results are deterministic: the same inputs give the same bits.
+ */
+#ifndef KMEANS_MI355X_H
+#define KMEANS_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+typedef enum {
+    KM_OK = 0,
+    KM_ERR_NULL = -1,      /* a required pointer is NULL                          */
+    KM_ERR_SHAPE = -2,     /* n, k or d outside the documented range              */
+    KM_ERR_ALIGN = -3,     /* a pointer is not aligned to its element size        */
+    KM_ERR_WORKSPACE = -4, /* workspace_bytes < kmeans_workspace_bytes(...)       */
+    KM_ERR_ALIAS = -5,     /* an output overlaps an input, output or workspace    */
+    KM_ERR_HIP = -6,       /* a kernel launch was rejected by the HIP runtime     */
+    KM_ERR_OP = -7         /* unknown op code                                     */
+} km_status;
+
+/* Op codes for kmeans_workspace_bytes. */
+enum { KM_OP_ASSIGN = 0, KM_OP_UPDATE = 1, KM_OP_LLOYD = 2 };
+
+/*
+ * Workspace bytes needed by one call of the given op at shape (n, k, d).
+ * The size is O(k + n + k * ceil(n / 1024)) 4-byte words, far below the
+ * (n, k) distance matrix and the (n, d) sample matrix. Returns 0 when the
+ * shape or op is invalid (a valid shape never needs 0 bytes).
+ */
+size_t kmeans_workspace_bytes(int64_t n, int64_t k, int64_t d, int op);
+
+/*
+ * Nearest-centroid assignment ("Three shapes ...", section Gram assignment).
+ *   X         (n, d) float32 samples, read only.
+ *   C         (k, d) float32 centroids, read only.
+ *   labels    (n,) int64 output: the lowest j minimising ||x_i - c_j||^2
+ *             (Gram form, float32). Also used as scratch during the call.
+ *   min_dist  (n,) float32 output, or NULL to skip it: the squared distance to
+ *             the chosen centroid, clamped at 0.
+ * Neither an (n, k) distance matrix nor an (n, d) temporary is ever written.
+ */
+int kmeans_assign(const float *X, const float *C, int64_t n, int64_t k, int64_t d,
+                  int64_t *labels, float *min_dist,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Centroid update for fixed labels ("Three shapes ...", section Full Lloyd
+ * step; "004 ...", section Lloyd step).
+ *   X       (n, d) float32 samples, read only.
+ *   labels  (n,) int64, read only. A row whose label lies outside [0, k) is
+ *           ignored: it is counted nowhere and added to no sum.
+ *   C_old   (k, d) float32, read only: the centre kept by an empty cluster.
+ *   C_new   (k, d) float32 output (may be the same pointer as C_old).
+ *   counts  (k,) int64 output.
+ */
+int kmeans_update(const float *X, const int64_t *labels, const float *C_old,
+                  int64_t n, int64_t k, int64_t d,
+                  float *C_new, int64_t *counts,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One Lloyd iteration: kmeans_assign against C_old, then kmeans_update with
+ * the labels just computed ("004 ...", sections Lloyd step and Cython
+ * reference). Arguments as in those two calls; labels are with respect to
+ * C_old. C_new may be the same pointer as C_old.
+ */
+int kmeans_lloyd_step(const float *X, const float *C_old, int64_t n, int64_t k, int64_t d,
+                      int64_t *labels, float *min_dist, float *C_new, int64_t *counts,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static, NUL-terminated description of a km_status value (never NULL). */
+const char *kmeans_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KMEANS_MI355X_H */

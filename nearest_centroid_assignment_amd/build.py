@@ -1,0 +1,64 @@
+"""Build ``libkmeans_mi355x.so`` (the C-ABI HIP library) in-tree for gfx950.
+
+Usage: ``python -m nearest_centroid_assignment_amd.build [--save-temps]``.
+hipcc cross-compiles without a GPU, so this runs on any host with ROCm.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB_NAME = "libkmeans_mi355x.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+SOURCES = ["api.hip", "assign.hip", "update.hip"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-Wall",
+    # No packed-FP32 instructions in generated code.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def build(verbose: bool = False, save_temps: bool = False) -> str:
+    """Compile every HIP source into the shared library; returns its path."""
+    out_tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", out_tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
+    cwd = None
+    if save_temps:
+        tmpdir = os.path.join(HERE, "..", "_build")
+        os.makedirs(tmpdir, exist_ok=True)
+        cmd.insert(1, "-save-temps")
+        cwd = tmpdir
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, cwd=cwd, capture_output=True, text=True)
+    # The host pass warns that it does not know the packed-fp32 feature; that
+    # warning is expected. Anything else is shown.
+    noise = "'-packed-fp32-ops' is not a recognized feature for this target"
+    msgs = [l for l in (proc.stdout + proc.stderr).splitlines() if noise not in l and l.strip()]
+    if msgs and (verbose or proc.returncode):
+        print("\n".join(msgs), file=sys.stderr)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
+    os.replace(out_tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    build(verbose=True, save_temps="--save-temps" in sys.argv)

@@ -1,0 +1,209 @@
+// api.hip - the C ABI declared in include/kmeans_mi355x.h.
+//
+// Every entry point validates its arguments on the host before the first HIP
+// call, carves its sections out of the caller's workspace, and enqueues the
+// kernels on the caller's stream. Nothing here allocates, frees or
+// synchronises, and there is no global state.
+#include "../../include/kmeans_mi355x.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = 2147483647;  // n, k, d < 2^31
+constexpr size_t kAlign = 256;           // section alignment inside the workspace
+constexpr int64_t kMaxGridThreads = 4294967295LL;  // one dispatch dimension, in work-items
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Layout {
+    size_t cn = 0, tile_hist = 0, cnt = 0, seg_start = 0, perm = 0, total = 0;
+};
+
+// Offsets from the first 256-byte boundary at or after the workspace start;
+// total includes that much slack so any base alignment works.
+Layout layout(int64_t n, int64_t k, int op) {
+    Layout L;
+    size_t off = 0;
+    if (op == KM_OP_ASSIGN || op == KM_OP_LLOYD) {
+        L.cn = off;
+        off += round_up((size_t)k * sizeof(float));
+    }
+    if (op == KM_OP_UPDATE || op == KM_OP_LLOYD) {
+        const int64_t n_tiles = cdiv(n, km::kSortTileRows);
+        L.tile_hist = off;
+        off += round_up((size_t)k * (size_t)n_tiles * sizeof(int));
+        L.cnt = off;
+        off += round_up((size_t)k * sizeof(int));
+        L.seg_start = off;
+        off += round_up((size_t)k * sizeof(int));
+        L.perm = off;
+        off += round_up((size_t)n * sizeof(int));
+    }
+    L.total = off + kAlign;
+    return L;
+}
+
+bool shape_ok(int64_t n, int64_t k, int64_t d) {
+    return n >= 0 && n <= kMaxDim && k >= 1 && k <= kMaxDim && d >= 1 && d <= kMaxDim;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi); empty when lo == hi
+};
+
+Range range(const void *p, int64_t count, size_t elem) {
+    const uintptr_t lo = (uintptr_t)p;
+    return Range{lo, p ? lo + (uintptr_t)count * elem : lo};
+}
+
+bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+char *ws_base(void *workspace) {
+    const uintptr_t p = (uintptr_t)workspace;
+    return (char *)((p + kAlign - 1) / kAlign * kAlign);
+}
+
+bool grid_ok(int64_t n, int64_t k, int64_t d) {
+    return km::assign_grid_blocks(n, k) * 256 <= kMaxGridThreads &&
+           km::update_grid_blocks(n, k, d) * 256 <= kMaxGridThreads;
+}
+
+// An array argument: pointer, element count, element size.
+struct Out {
+    const void *p;
+    int64_t count;
+    size_t elem;
+};
+
+// Output `inplace_out` may coincide exactly with input `inplace_in` (C_new and
+// C_old); -1 disables the exception.
+int check_alias(const Out *outs, int n_outs, const Out *ins, int n_ins, int inplace_out,
+                int inplace_in) {
+    for (int i = 0; i < n_outs; ++i) {
+        const Range ri = range(outs[i].p, outs[i].count, outs[i].elem);
+        for (int j = 0; j < n_ins; ++j) {
+            if (i == inplace_out && j == inplace_in && outs[i].p == ins[j].p) continue;
+            if (overlap(ri, range(ins[j].p, ins[j].count, ins[j].elem))) return KM_ERR_ALIAS;
+        }
+        for (int j = i + 1; j < n_outs; ++j)
+            if (overlap(ri, range(outs[j].p, outs[j].count, outs[j].elem))) return KM_ERR_ALIAS;
+    }
+    return KM_OK;
+}
+
+int run_assign(const float *X, const float *C, int64_t n, int64_t k, int64_t d, int64_t *labels,
+               float *min_dist, float *cn, hipStream_t s) {
+    hipError_t e = km::launch_row_sqnorms(C, k, d, cn, s);
+    if (e == hipSuccess) e = km::launch_fill_keys((unsigned long long *)labels, n, s);
+    if (e == hipSuccess && min_dist) e = km::launch_row_sqnorms(X, n, d, min_dist, s);
+    if (e == hipSuccess)
+        e = km::launch_assign_tiles(X, C, cn, n, k, d, (unsigned long long *)labels, s);
+    if (e == hipSuccess) e = km::launch_finalize((unsigned long long *)labels, min_dist, n, s);
+    return e == hipSuccess ? KM_OK : KM_ERR_HIP;
+}
+
+km::UpdateScratch update_scratch(char *base, const Layout &L, int64_t n) {
+    km::UpdateScratch ws;
+    ws.tile_hist = (int *)(base + L.tile_hist);
+    ws.cnt = (int *)(base + L.cnt);
+    ws.seg_start = (int *)(base + L.seg_start);
+    ws.perm = (int *)(base + L.perm);
+    ws.n_tiles = cdiv(n, km::kSortTileRows);
+    return ws;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kmeans_workspace_bytes(int64_t n, int64_t k, int64_t d, int op) {
+    if (!shape_ok(n, k, d)) return 0;
+    if (op != KM_OP_ASSIGN && op != KM_OP_UPDATE && op != KM_OP_LLOYD) return 0;
+    return layout(n, k, op).total;
+}
+
+const char *kmeans_status_string(int status) {
+    switch (status) {
+        case KM_OK: return "ok";
+        case KM_ERR_NULL: return "a required pointer is NULL";
+        case KM_ERR_SHAPE: return "n, k or d outside the supported range";
+        case KM_ERR_ALIGN: return "a pointer is not aligned to its element size";
+        case KM_ERR_WORKSPACE: return "workspace smaller than kmeans_workspace_bytes()";
+        case KM_ERR_ALIAS: return "an output overlaps an input, another output or the workspace";
+        case KM_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+        case KM_ERR_OP: return "unknown op code";
+        default: return "unknown status";
+    }
+}
+
+int kmeans_assign(const float *X, const float *C, int64_t n, int64_t k, int64_t d,
+                  int64_t *labels, float *min_dist, void *workspace, size_t workspace_bytes,
+                  void *stream) {
+    if (!shape_ok(n, k, d) || !grid_ok(n, k, d)) return KM_ERR_SHAPE;
+    if (!C || !workspace || (n > 0 && (!X || !labels))) return KM_ERR_NULL;
+    if (!aligned(X, 4) || !aligned(C, 4) || !aligned(labels, 8) || !aligned(min_dist, 4))
+        return KM_ERR_ALIGN;
+    const Layout L = layout(n, k, KM_OP_ASSIGN);
+    if (workspace_bytes < L.total) return KM_ERR_WORKSPACE;
+    const Out outs[] = {{labels, n, 8}, {min_dist, n, 4}, {workspace, (int64_t)workspace_bytes, 1}};
+    const Out ins[] = {{X, n * d, 4}, {C, k * d, 4}};
+    if (int rc = check_alias(outs, 3, ins, 2, -1, -1)) return rc;
+    if (n == 0) return KM_OK;
+    char *base = ws_base(workspace);
+    return run_assign(X, C, n, k, d, labels, min_dist, (float *)(base + L.cn), (hipStream_t)stream);
+}
+
+int kmeans_update(const float *X, const int64_t *labels, const float *C_old, int64_t n, int64_t k,
+                  int64_t d, float *C_new, int64_t *counts, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    if (!shape_ok(n, k, d) || !grid_ok(n, k, d)) return KM_ERR_SHAPE;
+    if (!C_old || !C_new || !counts || !workspace || (n > 0 && (!X || !labels)))
+        return KM_ERR_NULL;
+    if (!aligned(X, 4) || !aligned(labels, 8) || !aligned(C_old, 4) || !aligned(C_new, 4) ||
+        !aligned(counts, 8))
+        return KM_ERR_ALIGN;
+    const Layout L = layout(n, k, KM_OP_UPDATE);
+    if (workspace_bytes < L.total) return KM_ERR_WORKSPACE;
+    const Out outs[] = {{C_new, k * d, 4}, {counts, k, 8}, {workspace, (int64_t)workspace_bytes, 1}};
+    const Out ins[] = {{X, n * d, 4}, {labels, n, 8}, {C_old, k * d, 4}};
+    if (int rc = check_alias(outs, 3, ins, 3, /*C_new*/ 0, /*C_old*/ 2)) return rc;
+    char *base = ws_base(workspace);
+    const hipError_t e = km::launch_update(X, labels, C_old, n, k, d, C_new, counts,
+                                           update_scratch(base, L, n), (hipStream_t)stream);
+    return e == hipSuccess ? KM_OK : KM_ERR_HIP;
+}
+
+int kmeans_lloyd_step(const float *X, const float *C_old, int64_t n, int64_t k, int64_t d,
+                      int64_t *labels, float *min_dist, float *C_new, int64_t *counts,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    if (!shape_ok(n, k, d) || !grid_ok(n, k, d)) return KM_ERR_SHAPE;
+    if (!C_old || !C_new || !counts || !workspace || (n > 0 && (!X || !labels)))
+        return KM_ERR_NULL;
+    if (!aligned(X, 4) || !aligned(C_old, 4) || !aligned(labels, 8) || !aligned(min_dist, 4) ||
+        !aligned(C_new, 4) || !aligned(counts, 8))
+        return KM_ERR_ALIGN;
+    const Layout L = layout(n, k, KM_OP_LLOYD);
+    if (workspace_bytes < L.total) return KM_ERR_WORKSPACE;
+    const Out outs[] = {{labels, n, 8},
+                        {min_dist, n, 4},
+                        {C_new, k * d, 4},
+                        {counts, k, 8},
+                        {workspace, (int64_t)workspace_bytes, 1}};
+    const Out ins[] = {{X, n * d, 4}, {C_old, k * d, 4}};
+    if (int rc = check_alias(outs, 5, ins, 2, /*C_new*/ 2, /*C_old*/ 1)) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    char *base = ws_base(workspace);
+    if (n > 0) {
+        const int rc = run_assign(X, C_old, n, k, d, labels, min_dist, (float *)(base + L.cn), s);
+        if (rc != KM_OK) return rc;
+    }
+    const hipError_t e = km::launch_update(X, labels, C_old, n, k, d, C_new, counts,
+                                           update_scratch(base, L, n), s);
+    return e == hipSuccess ? KM_OK : KM_ERR_HIP;
+}
+
+}  // extern "C"

@@ -15,12 +15,19 @@ The recipe used here is Gaussian blobs:
   3. X = centres[membership] + sigma * N(0, 1), float32;
   4. C = X[rows], rows drawn without replacement (k distinct rows of X).
 
-The sample-heavy shape draws X i.i.d. N(0, 1) instead of blobs.  Every array is
-drawn from ``numpy.random.default_rng(seed)`` in exactly that order, so a seed
-names the bytes.
+The sample-heavy shape draws X i.i.d. N(0, 1) instead of blobs.
+
+Streams: the membership permutation and the rows of C come from
+``numpy.random.default_rng(seed)`` in that order. The normal draws of the
+centres and of the noise are split into blocks of 4096 rows; block b of stream
+s is drawn from ``numpy.random.default_rng([seed, s, b])`` (s = 1 for the
+centres, 2 for the noise), so blocks can be filled by parallel threads and a
+seed still names the bytes, whatever the thread count.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
@@ -70,17 +77,31 @@ CONFIGS: dict[str, Config] = {
 }
 
 
-def _fill_normal(rng: np.random.Generator, out: np.ndarray, chunk_rows: int = 4096) -> None:
-    """Fill a (rows, d) float32 array with N(0, 1) draws, row-chunk by row-chunk.
+BLOCK_ROWS = 4096
 
-    Chunking bounds the temporary memory; the draw order is row-major, so the
-    bytes equal those of one ``rng.standard_normal(out.shape, dtype=float32)``
-    call.
+
+def _fill_normal(seed: int, stream: int, out: np.ndarray, block_rows: int = BLOCK_ROWS) -> None:
+    """Fill a (rows, d) float32 array with N(0, 1) draws, block by block.
+
+    Block b (rows [b * block_rows, (b + 1) * block_rows)) is drawn from
+    ``default_rng([seed, stream, b])``; blocks are filled by a thread pool.
     """
     rows = out.shape[0]
-    for r0 in range(0, rows, chunk_rows):
-        r1 = min(rows, r0 + chunk_rows)
-        rng.standard_normal(out[r0:r1].shape, dtype=np.float32, out=out[r0:r1])
+    starts = list(range(0, rows, block_rows))
+
+    def work(b: int) -> None:
+        r0 = starts[b]
+        r1 = min(rows, r0 + block_rows)
+        np.random.default_rng([seed, stream, b]).standard_normal(
+            out[r0:r1].shape, dtype=np.float32, out=out[r0:r1])
+
+    workers = max(1, min(16, os.cpu_count() or 1, len(starts)))
+    if workers == 1:
+        for b in range(len(starts)):
+            work(b)
+    else:
+        with ThreadPoolExecutor(max_workers=workers) as pool:
+            list(pool.map(work, range(len(starts))))
 
 
 def make_blobs(n: int, k: int, d: int, kb: int | None, sigma_c: float, sigma: float,
@@ -94,19 +115,18 @@ def make_blobs(n: int, k: int, d: int, kb: int | None, sigma_c: float, sigma: fl
     rng = np.random.default_rng(seed)
     X = np.empty((n, d), dtype=np.float32)
     if kb is None:
-        _fill_normal(rng, X)
+        _fill_normal(seed, 2, X)
         if sigma != 1.0:
             X *= np.float32(sigma)
     else:
         centres = np.empty((kb, d), dtype=np.float32)
-        _fill_normal(rng, centres)
+        _fill_normal(seed, 1, centres)
         centres *= np.float32(sigma_c)
         membership = rng.permutation(np.arange(n) % kb)
-        _fill_normal(rng, X)
+        _fill_normal(seed, 2, X)
         X *= np.float32(sigma)
-        step = 4096
-        for r0 in range(0, n, step):
-            r1 = min(n, r0 + step)
+        for r0 in range(0, n, BLOCK_ROWS):
+            r1 = min(n, r0 + BLOCK_ROWS)
             X[r0:r1] += centres[membership[r0:r1]]
     rows = rng.choice(n, size=k, replace=False)
     C = np.ascontiguousarray(X[rows])

@@ -1,0 +1,140 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+compare it with the float64 oracle under the parity rules.
+
+Parity rules (all checked, none relaxed):
+
+* labels  - equal to the oracle's, except on rows whose oracle gap between the
+  best and second-best distance is <= 1e-5 * (||x||^2 + ||c_label||^2) (a
+  near tie). Every mismatch must be such a row, and the GPU's centroid must be
+  within that band of the oracle's best distance.
+* counts  - bit-exact against the oracle's update applied to the GPU's labels;
+  against the oracle's own labels they may differ only by the moved rows.
+* centroids - the oracle's update on the GPU's labels: per row,
+  max |dC| <= 1e-4 * max |C_ref| (and, by construction of the float64 sum in
+  increasing sample order, bit-exact; that is asserted too).
+* min_dist - |dD| <= 1e-4 * D_ref or |dD| <= 1e-5 * (||x||^2 + ||c||^2), D_ref
+  the float64 distance to the GPU's chosen centroid.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+
+TIE_RTOL = 1e-5
+REL_TOL = 1e-4
+
+
+def announce(msg: str) -> None:
+    """Print a progress line that bypasses pytest's capture (flushed now)."""
+    sys.__stderr__.write(f"[gpu-test] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def to_gpu(a):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def gpu_lloyd(X, C, min_dist=True):
+    """One Lloyd iteration on the GPU; returns numpy (labels, md, C_new, counts)."""
+    import torch
+
+    from nearest_centroid_assignment_amd import binding
+
+    Xg, Cg = to_gpu(X), to_gpu(C)
+    labels, md, C_new, counts = binding.lloyd_step(Xg, Cg, min_dist=min_dist)
+    torch.cuda.synchronize()
+    return (labels.cpu().numpy(), None if md is None else md.cpu().numpy(),
+            C_new.cpu().numpy(), counts.cpu().numpy())
+
+
+def gpu_assign(X, C, min_dist=True):
+    import torch
+
+    from nearest_centroid_assignment_amd import binding
+
+    labels, md = binding.assign(to_gpu(X), to_gpu(C), min_dist=min_dist)
+    torch.cuda.synchronize()
+    return labels.cpu().numpy(), None if md is None else md.cpu().numpy()
+
+
+def sq_norms(A):
+    A64 = np.asarray(A, dtype=np.float64)
+    return np.einsum("ij,ij->i", A64, A64)
+
+
+def exact_dist(X, C, rows, cols):
+    """float64 difference-form distance of X[rows[i]] to C[cols[i]]."""
+    diff = X[rows].astype(np.float64) - C[cols].astype(np.float64)
+    return np.einsum("ij,ij->i", diff, diff)
+
+
+def check_labels(X, C, g_labels, o_labels, best, second, rows=None):
+    """Labels rule; returns the number of near-tie rows and of mismatches.
+
+    ``rows`` maps the oracle's rows to rows of X (sampled parity); X and C are
+    the full arrays.
+    """
+    if rows is None:
+        rows = np.arange(len(o_labels))
+    g = g_labels[rows]
+    assert g.min() >= 0 and g.max() < len(C)
+    xn = sq_norms(X[rows])
+    cn = sq_norms(C)
+    band = TIE_RTOL * (xn + cn[o_labels])
+    ties = (second - best) <= band
+    mism = np.nonzero(g != o_labels)[0]
+    assert np.all(ties[mism]), (
+        f"{len(mism)} label mismatches, {int((~ties[mism]).sum())} outside the near-tie band; "
+        f"first rows {rows[mism[~ties[mism]]][:5]}")
+    if len(mism):
+        dg = exact_dist(X, C, rows[mism], g[mism])
+        assert np.all(dg - best[mism] <= band[mism])
+    return int(ties.sum()), int(len(mism))
+
+
+def check_min_dist(X, C, g_labels, g_md, rows=None):
+    if rows is None:
+        rows = np.arange(len(X))
+    g = g_labels[rows]
+    ref = exact_dist(X, C, rows, g)
+    scale = sq_norms(X[rows]) + sq_norms(C)[g]
+    err = np.abs(g_md[rows].astype(np.float64) - ref)
+    ok = (err <= REL_TOL * ref) | (err <= TIE_RTOL * scale)
+    assert np.all(ok), f"min_dist off on {int((~ok).sum())} rows, worst {err[~ok].max()}"
+    assert np.all(g_md[rows] >= 0)
+
+
+def check_update(X, g_labels, C_old, g_Cnew, g_counts):
+    """Update rules against the oracle's update on the GPU's labels."""
+    C_ref, cnt_ref, _ = oracle.update(X, g_labels, C_old)
+    assert np.array_equal(g_counts, cnt_ref), "counts differ"
+    scale = np.abs(C_ref).max(axis=1, keepdims=True)
+    err = np.abs(g_Cnew.astype(np.float64) - C_ref)
+    assert np.all(err <= REL_TOL * scale), f"centroids off, worst {err.max()}"
+    assert np.array_equal(g_Cnew.view(np.uint32), C_ref.view(np.uint32)), \
+        "centroids not bit-exact against the float64 in-order mean"
+
+
+def check_counts_vs_oracle_labels(g_counts, o_labels, k, n_mismatch):
+    o_counts = np.bincount(o_labels, minlength=k)
+    diff = np.abs(g_counts - o_counts).sum()
+    assert diff <= 2 * n_mismatch
+    if n_mismatch == 0:
+        assert np.array_equal(g_counts, o_counts)
+
+
+def full_parity(X, C, min_dist=True):
+    """The whole Lloyd step on the GPU against the oracle on every row."""
+    g_labels, g_md, g_Cnew, g_counts = gpu_lloyd(X, C, min_dist=min_dist)
+    o_labels, best, second = oracle.assign(X, C)
+    ties, mism = check_labels(X, C, g_labels, o_labels, best, second)
+    if min_dist:
+        check_min_dist(X, C, g_labels, g_md)
+    check_update(X, g_labels, C, g_Cnew, g_counts)
+    check_counts_vs_oracle_labels(g_counts, o_labels, len(C), mism)
+    return {"near_ties": ties, "mismatches": mism, "labels": g_labels}

@@ -1,0 +1,163 @@
+"""The C-ABI library loads, exports what include/kmeans_mi355x.h declares, and
+rejects invalid arguments on the host (no GPU: no call here reaches a kernel
+launch, every one fails validation first or has n = 0)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from nearest_centroid_assignment_amd import binding
+from nearest_centroid_assignment_amd.datagen import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kmeans_mi355x.h")
+
+OK, NULL, SHAPE, ALIGN, WORKSPACE, ALIAS, HIP, OP = 0, -1, -2, -3, -4, -5, -6, -7
+
+# Fake, far-apart device addresses: validation never dereferences them. These
+# tests only run where no GPU is present, so a validation bug that let such a
+# call through could never reach a real device.
+no_gpu = pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                            reason="fake-pointer validation tests run only without a GPU")
+GIB = 1 << 30
+X_P, C_P, LAB_P, MD_P, CN_P, CNT_P, WS_P = (GIB * (16 << i) for i in range(7))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.lib()
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kmeans_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == {"kmeans_workspace_bytes", "kmeans_assign", "kmeans_update",
+                          "kmeans_lloyd_step", "kmeans_status_string"}
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in (OK, NULL, SHAPE, ALIGN, WORKSPACE, ALIAS, HIP, OP):
+        s = binding.kmeans_status_string(code)
+        assert s and s != "unknown status"
+    assert binding.kmeans_status_string(12345) == "unknown status"
+
+
+def test_workspace_bytes_rules(lib):
+    ws = binding.kmeans_workspace_bytes
+    assert ws(10, 0, 4, 0) == 0 and ws(10, 3, 0, 0) == 0 and ws(-1, 3, 4, 0) == 0
+    assert ws(10, 3, 4, 9) == 0
+    assert ws(2**31, 3, 4, 0) == 0
+    assert ws(0, 1, 1, 0) > 0 and ws(0, 1, 1, 1) > 0
+    for cfg in CONFIGS.values():
+        a, u, l = (ws(cfg.n, cfg.k, cfg.d, op) for op in (0, 1, 2))
+        assert l >= max(a, u) and l <= a + u
+        # The assignment needs only the centroid norms (k floats + alignment).
+        assert a <= cfg.k * 4 + 512
+        # The update: k x ceil(n/1024) tile counters, 2k words, n words.
+        n_tiles = -(-cfg.n // 1024)
+        assert u <= 4 * (cfg.k * n_tiles + 2 * cfg.k + cfg.n) + 5 * 256
+        # Far below the (n, k) distance matrix and the (n, d) sample matrix.
+        if cfg.n >= 4096:
+            assert l < cfg.n * cfg.k * 4 / 64 and l < cfg.n * cfg.d * 4 / 64
+
+
+def _assign(lib, X=X_P, C=C_P, n=100, k=10, d=8, labels=LAB_P, md=MD_P, ws=WS_P, wsb=None):
+    if wsb is None:
+        wsb = binding.kmeans_workspace_bytes(max(n, 0), max(k, 1), max(d, 1), 0)
+    return lib.kmeans_assign(X, C, n, k, d, labels, md, ws, wsb, None)
+
+
+@no_gpu
+def test_assign_validation(lib):
+    assert _assign(lib, C=None) == NULL
+    assert _assign(lib, X=None) == NULL
+    assert _assign(lib, labels=None) == NULL
+    assert _assign(lib, ws=None) == NULL
+    assert _assign(lib, k=0) == SHAPE
+    assert _assign(lib, d=0) == SHAPE
+    assert _assign(lib, n=-1) == SHAPE
+    assert _assign(lib, n=2**31) == SHAPE
+    assert _assign(lib, labels=LAB_P + 4) == ALIGN
+    assert _assign(lib, X=X_P + 2) == ALIGN
+    assert _assign(lib, md=MD_P + 1) == ALIGN
+    assert _assign(lib, wsb=16) == WORKSPACE
+    assert _assign(lib, labels=X_P + 64) == ALIAS
+    assert _assign(lib, md=LAB_P + 8) == ALIAS
+    assert _assign(lib, ws=C_P) == ALIAS
+    # n = 0: nothing to do, X / labels may be NULL, and nothing is launched.
+    assert _assign(lib, n=0, X=None, labels=None, md=None) == OK
+
+
+def _update(lib, X=X_P, labels=LAB_P, C_old=C_P, C_new=CN_P, counts=CNT_P, n=100, k=10, d=8,
+            ws=WS_P, wsb=None):
+    if wsb is None:
+        wsb = binding.kmeans_workspace_bytes(max(n, 0), max(k, 1), max(d, 1), 1)
+    return lib.kmeans_update(X, labels, C_old, n, k, d, C_new, counts, ws, wsb, None)
+
+
+@no_gpu
+def test_update_validation(lib):
+    assert _update(lib, C_old=None) == NULL
+    assert _update(lib, C_new=None) == NULL
+    assert _update(lib, counts=None) == NULL
+    assert _update(lib, labels=None) == NULL
+    assert _update(lib, k=0) == SHAPE
+    assert _update(lib, counts=CNT_P + 4) == ALIGN
+    assert _update(lib, wsb=100) == WORKSPACE
+    assert _update(lib, C_new=C_P + 4) == ALIAS          # partial overlap with C_old
+    assert _update(lib, C_new=X_P, C_old=X_P) == ALIAS   # in place, but on top of X
+    assert _update(lib, counts=LAB_P) == ALIAS
+    assert _update(lib, ws=CN_P + 8) == ALIAS
+
+
+@no_gpu
+def test_lloyd_validation(lib):
+    n, k, d = 100, 10, 8
+    wsb = binding.kmeans_workspace_bytes(n, k, d, 2)
+
+    def call(**kw):
+        a = dict(X=X_P, C_old=C_P, labels=LAB_P, md=MD_P, C_new=CN_P, counts=CNT_P, ws=WS_P,
+                 wsb=wsb)
+        a.update(kw)
+        return lib.kmeans_lloyd_step(a["X"], a["C_old"], n, k, d, a["labels"], a["md"],
+                                     a["C_new"], a["counts"], a["ws"], a["wsb"], None)
+
+    assert call(C_new=None) == NULL
+    assert call(labels=LAB_P + 2) == ALIGN
+    assert call(wsb=wsb - 1) == WORKSPACE
+    assert call(counts=LAB_P + 16) == ALIAS
+    assert call(md=CN_P) == ALIAS
+    assert call(C_new=C_P + 4) == ALIAS
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    X = torch.zeros(4, 3)
+    with pytest.raises(ValueError):
+        binding.assign(X, X[:2].clone())
+
+
+def test_library_imports_no_allocation_or_sync():
+    """The library neither allocates device memory nor synchronises: none of
+    those HIP entry points is even imported."""
+    import shutil
+    import subprocess
+
+    nm = shutil.which("nm") or "/opt/rocm/llvm/bin/llvm-nm"
+    out = subprocess.run([nm, "-D", "--undefined-only", binding.LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    imported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    forbidden = [s for s in imported
+                 if re.match(r"hip(Malloc|Free|HostAlloc|HostMalloc|ExtMalloc|MallocAsync|"
+                             r"DeviceSynchronize|StreamSynchronize|EventSynchronize|"
+                             r"HostRegister|Memcpy)", s)]
+    assert not forbidden, forbidden

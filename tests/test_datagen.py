@@ -32,13 +32,16 @@ def test_blob_statistics():
     assert abs(X.std() - np.sqrt(cfg.sigma_c**2 + cfg.sigma**2)) < 0.3
 
 
-def test_chunked_normal_matches_single_draw():
-    rng1 = np.random.default_rng(5)
-    rng2 = np.random.default_rng(5)
-    out = np.empty((10000, 3), dtype=np.float32)
-    datagen._fill_normal(rng1, out, chunk_rows=777)
-    ref = rng2.standard_normal((10000, 3), dtype=np.float32)
-    assert np.array_equal(out, ref)
+def test_block_streams_independent_of_threads(monkeypatch):
+    """The parallel block fill gives the same bytes as a serial fill."""
+    out1 = np.empty((10000, 3), dtype=np.float32)
+    datagen._fill_normal(5, 2, out1, block_rows=777)
+    monkeypatch.setattr(datagen.os, "cpu_count", lambda: 1)
+    out2 = np.empty((10000, 3), dtype=np.float32)
+    datagen._fill_normal(5, 2, out2, block_rows=777)
+    assert np.array_equal(out1, out2)
+    ref = np.random.default_rng([5, 2, 1]).standard_normal((777, 3), dtype=np.float32)
+    assert np.array_equal(out1[777:1554], ref)
 
 
 def test_integer_and_far_centroid():

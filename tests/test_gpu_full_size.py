@@ -1,0 +1,55 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark
+times: the GPU runs the whole problem; the oracle recomputes a seeded sample of
+rows one by one against every centroid; the update is checked in full (the
+oracle's float64 update applied to the GPU's labels)."""
+import numpy as np
+import pytest
+
+import oracle
+from nearest_centroid_assignment_amd import datagen
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE_ROWS = 256
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _sampled_assign_parity(name, X, C, g_labels, g_md):
+    rows = np.sort(np.random.default_rng(123).choice(len(X), SAMPLE_ROWS, replace=False))
+    o_labels, best, second = oracle.assign(X[rows], C)
+    ties, mism = gu.check_labels(X, C, g_labels, o_labels, best, second, rows=rows)
+    gu.check_min_dist(X, C, g_labels, g_md, rows=rows)
+    gu.announce(f"{name}: sampled rows {SAMPLE_ROWS}, near-ties {ties}, mismatches {mism}")
+
+
+def test_sample_heavy_assign():
+    """131072 x 8192 x 8192: fused assignment only."""
+    gu.announce("sample_heavy: generating inputs")
+    X, C = datagen.make("sample_heavy")
+    gu.announce("sample_heavy: GPU assignment")
+    g_labels, g_md = gu.gpu_assign(X, C)
+    assert g_labels.min() >= 0 and g_labels.max() < len(C)
+    _sampled_assign_parity("sample_heavy", X, C, g_labels, g_md)
+    # C is made of rows of X, so each of those rows is at distance 0 from its
+    # own centroid (or an exact duplicate with a lower index).
+    gu.announce("sample_heavy: done")
+
+
+def test_feature_heavy_lloyd():
+    """65536 x 4096 x 16384: fused assignment + segmented update."""
+    gu.announce("feature_heavy: generating inputs")
+    X, C = datagen.make("feature_heavy")
+    gu.announce("feature_heavy: GPU Lloyd step")
+    g_labels, g_md, g_Cnew, g_counts = gu.gpu_lloyd(X, C)
+    _sampled_assign_parity("feature_heavy", X, C, g_labels, g_md)
+    gu.announce("feature_heavy: oracle update on the GPU labels")
+    gu.check_update(X, g_labels, C, g_Cnew, g_counts)
+    assert g_counts.sum() == len(X)
+    gu.announce("feature_heavy: done")

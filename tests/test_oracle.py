@@ -34,16 +34,18 @@ def test_near_tie_band(oracle_mod):
 
 def test_second_formulation_small_configs(oracle_mod):
     """numpy float64 Gram + first-occurrence argmin agrees with the oracle on
-    the Tiny and Probe workloads, which have no float64 near ties."""
+    the Tiny and Probe workloads on every row outside the near-tie band (Tiny
+    has none; Probe has one)."""
     from nearest_centroid_assignment_amd import datagen
 
-    for name in ("tiny", "probe"):
+    for name, max_ties in (("tiny", 0), ("probe", 1)):
         X, C = datagen.make(name)
         labels, best, second = oracle_mod.assign(X, C)
         X64, C64 = X.astype(np.float64), C.astype(np.float64)
         G = (C64 * C64).sum(1)[None, :] - 2.0 * X64 @ C64.T
-        assert np.array_equal(np.argmin(G, axis=1), labels)
-        assert not oracle_mod.near_ties(X, C, labels, best, second).any()
+        ties = oracle_mod.near_ties(X, C, labels, best, second)
+        assert ties.sum() <= max_ties
+        assert np.array_equal(np.argmin(G, axis=1)[~ties], labels[~ties])
 
 
 def test_thread_count_independent(oracle_mod, monkeypatch):
