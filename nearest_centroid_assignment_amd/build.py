@@ -15,6 +15,10 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libkmeans_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["api.hip", "assign.hip", "update.hip"]
+# Calibration kernels for the measurements (copy, MFMA loop): a separate library.
+CALIB_NAME = "libkm_calib.so"
+CALIB_PATH = os.path.join(HERE, CALIB_NAME)
+CALIB_SOURCES = ["calib.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -35,10 +39,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def build(verbose: bool = False, save_temps: bool = False) -> str:
-    """Compile every HIP source into the shared library; returns its path."""
-    out_tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", out_tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
+def _compile(sources, out_path, verbose: bool, save_temps: bool) -> str:
+    out_tmp = out_path + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", out_tmp, *[os.path.join(CSRC, s) for s in sources]]
     cwd = None
     if save_temps:
         tmpdir = os.path.join(HERE, "..", "_build")
@@ -56,8 +59,15 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
         print("\n".join(msgs), file=sys.stderr)
     if proc.returncode != 0:
         raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
-    os.replace(out_tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(out_tmp, out_path)
+    return out_path
+
+
+def build(verbose: bool = False, save_temps: bool = False) -> str:
+    """Compile the k-means library and the calibration library; returns the
+    path of the k-means library."""
+    _compile(CALIB_SOURCES, CALIB_PATH, verbose, save_temps)
+    return _compile(SOURCES, LIB_PATH, verbose, save_temps)
 
 
 if __name__ == "__main__":

@@ -1,0 +1,123 @@
+"""Driver and summarizer for the rocprofv3 hardware-counter runs.
+
+run (default):
+    python3 -m nearest_centroid_assignment_amd.profile_run [--workload feature_heavy]
+  launches, in order and each once: a 1 GiB streaming copy (calibration), then
+  one ``kmeans_assign`` (no min_dist) on the workload's seeded inputs. Meant to
+  be run under ``rocprofv3 --pmc FETCH_SIZE`` and, separately, under
+  ``rocprofv3 --pmc WRITE_SIZE`` (csv output).
+
+summarize:
+    python3 -m nearest_centroid_assignment_amd.profile_run summarize \
+        --fetch <dir of the FETCH_SIZE run> --write <dir of the WRITE_SIZE run> \
+        --out profiles/assign_tile_feature_heavy_traffic.json
+  reads the counter_collection csv files, scales each counter of the
+  assignment kernel by (known copy bytes / what the same counter read for the
+  copy kernel), and records the HBM bytes per launch together with the
+  SHA-256 of csrc/assign.hip, so that a later change to the kernel voids it.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ASSIGN_SOURCE = os.path.join(HERE, "csrc", "assign.hip")
+COPY_BYTES = 1 << 30
+COPY_KERNEL = "copy_kernel"
+ASSIGN_KERNEL = "assign_tile_kernel"
+
+
+def run(workload: str) -> None:
+    import torch
+
+    from . import binding, calib, datagen
+
+    dev = torch.device("cuda:0")
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    print(f"[profile_run] copy {COPY_BYTES} bytes", flush=True)
+    calib.copy_once(dst, src, COPY_BYTES)
+    torch.cuda.synchronize()
+    del src, dst
+    cfg = datagen.CONFIGS[workload]
+    X, C = datagen.make(cfg)
+    Xg, Cg = torch.from_numpy(X).to(dev), torch.from_numpy(C).to(dev)
+    labels = torch.empty(cfg.n, dtype=torch.int64, device=dev)
+    torch.cuda.synchronize()
+    print(f"[profile_run] kmeans_assign {cfg.name} {cfg.n}x{cfg.k}x{cfg.d}", flush=True)
+    binding.kmeans_assign(Xg, Cg, labels, None)
+    torch.cuda.synchronize()
+    print("[profile_run] done", flush=True)
+
+
+def _counter_rows(run_dir: str, counter: str):
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") == counter:
+                    rows.append(r)
+    return rows
+
+
+def _per_kernel(rows, name_part: str):
+    vals = [float(r["Counter_Value"]) for r in rows if name_part in r.get("Kernel_Name", "")]
+    if not vals:
+        raise ValueError(f"no dispatch of a kernel named *{name_part}* in the counter rows")
+    return vals
+
+
+def summarize(fetch_dir: str, write_dir: str, out: str, workload: str) -> dict:
+    from .datagen import CONFIGS
+
+    cfg = CONFIGS[workload]
+    rec = {"workload": workload, "copy_bytes": COPY_BYTES}
+    total = 0.0
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, counter)
+        copy_kib = _per_kernel(rows, COPY_KERNEL)[0]
+        assign_kib = _per_kernel(rows, ASSIGN_KERNEL)
+        scale = (COPY_BYTES / 1024.0) / copy_kib
+        per_launch = sum(assign_kib) / len(assign_kib) * scale * 1024.0
+        rec[counter] = {"copy_kib": copy_kib, "assign_kib_per_launch": assign_kib,
+                        "scale": scale, "assign_bytes_per_launch": per_launch}
+        total += per_launch
+    alg = 4.0 * (cfg.n * cfg.d + cfg.k * cfg.d) + 8.0 * cfg.n
+    rec["hbm_bytes_per_launch"] = total
+    rec["algorithmic_min_bytes"] = alg
+    rec["traffic_over_min"] = total / alg
+    with open(ASSIGN_SOURCE, "rb") as f:
+        rec["assign_source_sha256"] = hashlib.sha256(f.read()).hexdigest()
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("mode", nargs="?", default="run", choices=["run", "summarize"])
+    ap.add_argument("--workload", default="feature_heavy")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--out")
+    a = ap.parse_args(argv)
+    if a.mode == "run":
+        run(a.workload)
+    else:
+        print(json.dumps(summarize(a.fetch, a.write, a.out, a.workload), indent=1))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
