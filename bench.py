@@ -18,7 +18,6 @@ Prints one JSON line:
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -31,7 +30,6 @@ METRIC = "fused assign TFLOP/s (2nkd/t) + Lloyd iteration ms, 65536×4096×16384
 MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak (published)
 PAGES_LLOYD_MS = 1700.0        # the pages' feature-heavy Lloyd iteration (NVIDIA L4), context
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "assign_tile_feature_heavy_traffic.json")
-ASSIGN_SOURCE = os.path.join(ROOT, "nearest_centroid_assignment_amd", "csrc", "assign.hip")
 
 
 def log(msg: str) -> None:
@@ -51,11 +49,6 @@ def parse_args():
     return ap.parse_args()
 
 
-def source_digest() -> str:
-    with open(ASSIGN_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
-
-
 def traffic_record(cfg):
     """HBM bytes per launch of the assignment kernel from committed rocprofv3
     counter runs (FETCH_SIZE and WRITE_SIZE, scaled by the factor a plain copy
@@ -66,31 +59,33 @@ def traffic_record(cfg):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("assign_source_sha256") != source_digest() or rec.get("workload") != cfg.name:
+    from nearest_centroid_assignment_amd.profile_run import kernel_digest
+
+    if rec.get("assign_kernel_sha256") != kernel_digest() or rec.get("workload") != cfg.name:
         return None
     return rec.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(X, C, target_s: float):
     """Time the float64 oracle's assignment on a seeded sample of rows against
-    all centroids; scale to TFLOP/s of the same 2*rows*k*d work."""
+    all centroids; scale to TFLOP/s of the same 2*rows*k*d work. The sample
+    grows until one timed batch takes at least half of ``target_s``."""
     import numpy as np
 
     import oracle
 
     k, d = C.shape
     rng = np.random.default_rng(7)
-    probe_rows = 16
-    rows = rng.choice(len(X), probe_rows, replace=False)
-    t0 = time.perf_counter()
-    oracle.assign(X[rows], C)
-    t_probe = time.perf_counter() - t0
-    m = int(min(len(X), max(probe_rows, probe_rows * target_s / max(t_probe, 1e-6))))
-    rows = np.sort(rng.choice(len(X), m, replace=False))
-    Xs = np.ascontiguousarray(X[rows])
-    t0 = time.perf_counter()
-    oracle.assign(Xs, C)
-    t = time.perf_counter() - t0
+    order = rng.permutation(len(X))
+    m = min(len(X), 64)
+    while True:
+        Xs = np.ascontiguousarray(X[np.sort(order[:m])])
+        t0 = time.perf_counter()
+        oracle.assign(Xs, C)
+        t = time.perf_counter() - t0
+        if t >= 0.5 * target_s or m == len(X):
+            break
+        m = int(min(len(X), max(2 * m, m * target_s / max(t, 1e-3))))
     return {
         "value": 2.0 * m * k * d / t / 1e12,
         "unit": "TFLOP/s",

@@ -20,6 +20,12 @@ CALIB_NAME = "libkm_calib.so"
 CALIB_PATH = os.path.join(HERE, CALIB_NAME)
 CALIB_SOURCES = ["calib.hip"]
 
+# Per-source additional flags. The assignment kernel is scheduled for
+# instruction-level parallelism (measured: +1-2 % on the large shapes).
+EXTRA_FLAGS: dict[str, list[str]] = {
+    "assign.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
@@ -39,15 +45,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def _compile(sources, out_path, verbose: bool, save_temps: bool) -> str:
-    out_tmp = out_path + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", out_tmp, *[os.path.join(CSRC, s) for s in sources]]
-    cwd = None
-    if save_temps:
-        tmpdir = os.path.join(HERE, "..", "_build")
-        os.makedirs(tmpdir, exist_ok=True)
-        cmd.insert(1, "-save-temps")
-        cwd = tmpdir
+def _run(cmd, cwd=None, verbose=False):
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, cwd=cwd, capture_output=True, text=True)
@@ -58,7 +56,35 @@ def _compile(sources, out_path, verbose: bool, save_temps: bool) -> str:
     if msgs and (verbose or proc.returncode):
         print("\n".join(msgs), file=sys.stderr)
     if proc.returncode != 0:
-        raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
+        raise RuntimeError(f"hipcc failed with exit code {proc.returncode}: {' '.join(cmd)}")
+
+
+def _compile(sources, out_path, verbose: bool, save_temps: bool, extra_flags=None) -> str:
+    """Compile each source to an object (in parallel), then link the library.
+
+    ``extra_flags`` maps a source name to additional hipcc flags for it.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
+    extra_flags = extra_flags or {}
+    objdir = os.path.join(HERE, "..", "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+
+    def one(src):
+        obj = os.path.join(objdir, os.path.basename(out_path) + "." + src + ".o")
+        cmd = [hipcc(), *compile_flags, *extra_flags.get(src, []), "-c", "-o", obj,
+               os.path.join(CSRC, src)]
+        if save_temps:
+            cmd.insert(1, "-save-temps")
+        _run(cmd, cwd=objdir, verbose=verbose)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=len(sources)) as pool:
+        objs = list(pool.map(one, sources))
+    out_tmp = out_path + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out_tmp, *objs],
+         verbose=verbose)
     os.replace(out_tmp, out_path)
     return out_path
 
@@ -67,7 +93,7 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     """Compile the k-means library and the calibration library; returns the
     path of the k-means library."""
     _compile(CALIB_SOURCES, CALIB_PATH, verbose, save_temps)
-    return _compile(SOURCES, LIB_PATH, verbose, save_temps)
+    return _compile(SOURCES, LIB_PATH, verbose, save_temps, EXTRA_FLAGS)
 
 
 if __name__ == "__main__":

@@ -14,6 +14,9 @@
 //                       centroid tiles done on the accumulators: the (n, k)
 //                       distance matrix never exists in memory
 //   finalize_kernel     packed key -> int64 label, full squared distance
+#include <stdlib.h>
+#include <string.h>
+
 #include "kernels.h"
 
 namespace km {
@@ -80,12 +83,12 @@ __global__ __launch_bounds__(256) void fill_keys_kernel(unsigned long long *__re
 
 // ----------------------------------------------------- fused assignment
 //
-// Tile: kBM centroids x kBN samples, full depth d, 256 threads = 4 waves in a
-// 2 x 2 arrangement, each wave owning 64 centroids x 64 samples = 2 x 2 MFMA
-// blocks of 32 x 32 (v_mfma_f32_32x32x2_f32).
+// Tile: BM centroids x BN samples, full depth d. The block has WM x WN waves;
+// each wave owns MB x NB blocks of 32 x 32 results computed with
+// v_mfma_f32_32x32x2_f32 (BM = WM * MB * 32, BN = WN * NB * 32).
 //
 // Operand placement: the MFMA A operand (rows M) holds centroids and the B
-// operand (columns N) holds samples. In the 32 x 32 result a lane owns one
+// operand (columns N) holds samples. In a 32 x 32 result a lane owns one
 // column, i.e. one sample, and 16 centroid rows, so most of the argmin is a
 // scan of the lane's own accumulators; one exchange with the lane 32 apart
 // (which holds the other rows of the same column) completes it.
@@ -94,140 +97,199 @@ __global__ __launch_bounds__(256) void fill_keys_kernel(unsigned long long *__re
 // feeds them to 4 successive MFMAs; lanes 0-31 and 32-63 read features 0-3 and
 // 4-7 of each group of 8. A and B use the same feature permutation, so the
 // product is the same dot product summed in a different order.
-constexpr int kBM = 128;
-constexpr int kBN = 128;
-constexpr int kBK = 32;
-constexpr int kLDK = kBK + 4;   // padded LDS row: 16-byte reads of 32 lanes hit distinct banks
-constexpr int kGroupM = 8;      // centroid tiles per rasterisation group
+//
+// Pipeline: features advance in stages of BK through two LDS buffers. At the
+// start of stage s each thread writes its registers (stage s + 1, loaded one
+// stage earlier) into the free LDS buffer and issues the global loads of
+// stage s + 2; the LDS writes and the loads then overlap the MFMAs of stage s.
+// Inside a stage the fragments of the next group of 8 features are read from
+// LDS while the current group's MFMAs run. One barrier per stage.
+constexpr int kGroupM = 8;  // centroid tiles per rasterisation group
 
-template <bool kVec>
+template <int WM_, int WN_, int MB_, int NB_, int BK_>
+struct TileCfg {
+    static constexpr int WM = WM_, WN = WN_, MB = MB_, NB = NB_;
+    static constexpr int BM = WM * MB * 32;  // centroids per tile
+    static constexpr int BN = WN * NB * 32;  // samples per tile
+    static constexpr int BK = BK_;           // features per stage
+    // Padded LDS row: the 16-byte reads of 16 consecutive rows hit distinct banks.
+    static constexpr int LDK = BK + 4;
+    static constexpr int kThreads = WM * WN * 64;
+    static constexpr int kChunks = BK / 4;               // 16-byte chunks per row and stage
+    static constexpr int kRows = BM + BN;                // LDS rows per stage
+    static constexpr int kRowStep = kThreads / kChunks;  // rows covered by one pass of loads
+    static constexpr int Q = kRows / kRowStep;           // 16-byte loads per thread per stage
+    static_assert(BK % 8 == 0 && kThreads % kChunks == 0, "bad stage depth");
+    static_assert(kRows % kRowStep == 0, "tile rows must be a multiple of threads / chunks");
+};
+
+// Loading mode: kFull = every tile is full (n % BN == 0, k % BM == 0,
+// d % BK == 0) and 16-byte aligned, no bounds checks; kVec = 16-byte loads
+// with row / column checks; otherwise scalar loads with checks.
+enum LoadMode { kScalar = 0, kVec = 1, kFull = 2 };
+
+template <class Cfg, int Mode>
 __device__ __forceinline__ void load_stage(const float *__restrict__ X,
                                            const float *__restrict__ C, int64_t n, int64_t k,
                                            int64_t d, int64_t m0, int64_t n0, int64_t kbase,
-                                           int tid, f32x4 (&r)[8]) {
-    const int c4 = (tid & 7) * 4;
+                                           int tid, f32x4 (&r)[Cfg::Q]) {
+    const int c4 = (tid % Cfg::kChunks) * 4;
     const int64_t col = kbase + c4;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int row = (tid >> 3) + 32 * (q & 3);
-        const int64_t g = (q < 4 ? m0 : n0) + row;
-        const bool valid = g < (q < 4 ? k : n);
-        const float *base = (q < 4 ? C : X) + (valid ? g : 0) * d;
-        if (kVec) {
-            if (valid && col < d)
-                r[q] = *reinterpret_cast<const f32x4 *>(base + col);
-            else
-                r[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < Cfg::Q; ++q) {
+        const int row = tid / Cfg::kChunks + Cfg::kRowStep * q;
+        const bool is_c = row < Cfg::BM;
+        const int64_t g = is_c ? m0 + row : n0 + (row - Cfg::BM);
+        if (Mode == kFull) {
+            r[q] = *reinterpret_cast<const f32x4 *>((is_c ? C : X) + g * d + col);
         } else {
+            const bool valid = g < (is_c ? k : n);
+            const float *base = (is_c ? C : X) + (valid ? g : 0) * d;
+            if (Mode == kVec) {
+                if (valid && col < d)
+                    r[q] = *reinterpret_cast<const f32x4 *>(base + col);
+                else
+                    r[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) r[q][e] = (valid && col + e < d) ? base[col + e] : 0.f;
+                for (int e = 0; e < 4; ++e)
+                    r[q][e] = (valid && col + e < d) ? base[col + e] : 0.f;
+            }
         }
     }
 }
 
-__device__ __forceinline__ void store_stage(float (*lds)[kLDK], int tid, const f32x4 (&r)[8]) {
-    const int c4 = (tid & 7) * 4;
+template <class Cfg>
+__device__ __forceinline__ void store_stage(float (*lds)[Cfg::LDK], int tid,
+                                            const f32x4 (&r)[Cfg::Q]) {
+    const int c4 = (tid % Cfg::kChunks) * 4;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int row = (tid >> 3) + 32 * (q & 3) + (q < 4 ? 0 : kBM);
+    for (int q = 0; q < Cfg::Q; ++q) {
+        const int row = tid / Cfg::kChunks + Cfg::kRowStep * q;
         *reinterpret_cast<f32x4 *>(&lds[row][c4]) = r[q];
     }
 }
 
-template <bool kVec>
-__global__ __launch_bounds__(256, 2) void assign_tile_kernel(
+// One stage of MFMAs: for each group of 8 features, every (mb, nb) block
+// takes 4 MFMAs. The LDS->register fragments of the next group are read while
+// the MFMAs of the current group run.
+template <class Cfg>
+__device__ __forceinline__ void mma_stage(float (*lds)[Cfg::LDK], int lane, int wm, int wn,
+                                                    f32x16 (&acc)[Cfg::MB][Cfg::NB]) {
+    const int a_row = wm * Cfg::MB * 32 + (lane & 31);
+    const int b_row = Cfg::BM + wn * Cfg::NB * 32 + (lane & 31);
+    const int kofs = (lane >> 5) * 4;
+    f32x4 a[2][Cfg::MB], b[2][Cfg::NB];
+#pragma unroll
+    for (int mb = 0; mb < Cfg::MB; ++mb)
+        a[0][mb] = *reinterpret_cast<const f32x4 *>(&lds[a_row + 32 * mb][kofs]);
+#pragma unroll
+    for (int nb = 0; nb < Cfg::NB; ++nb)
+        b[0][nb] = *reinterpret_cast<const f32x4 *>(&lds[b_row + 32 * nb][kofs]);
+#pragma unroll
+    for (int g = 0; g < Cfg::BK / 8; ++g) {
+        const int cur = g & 1;
+        if (g + 1 < Cfg::BK / 8) {
+#pragma unroll
+            for (int mb = 0; mb < Cfg::MB; ++mb)
+                a[cur ^ 1][mb] =
+                    *reinterpret_cast<const f32x4 *>(&lds[a_row + 32 * mb][8 * (g + 1) + kofs]);
+#pragma unroll
+            for (int nb = 0; nb < Cfg::NB; ++nb)
+                b[cur ^ 1][nb] =
+                    *reinterpret_cast<const f32x4 *>(&lds[b_row + 32 * nb][8 * (g + 1) + kofs]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int mb = 0; mb < Cfg::MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < Cfg::NB; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                        a[cur][mb][e], b[cur][nb][e], acc[mb][nb], 0, 0, 0);
+    }
+}
+
+template <class Cfg, int Mode, int MinWaves>
+__global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
     const float *__restrict__ X, const float *__restrict__ C, const float *__restrict__ cn,
     int64_t n, int64_t k, int64_t d, int tiles_m, int tiles_n,
     unsigned long long *__restrict__ keys) {
-    __shared__ float lds[2][kBM + kBN][kLDK];
+    __shared__ float lds[2][Cfg::kRows][Cfg::LDK];
 
     // Blocks are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8).
     // Renumber so that each XCD gets one contiguous range of tiles, then walk
     // that range in groups of kGroupM centroid tiles so that the tiles resident
     // on one XCD at a time share centroid and sample rows in its L2.
-    const int nb = gridDim.x;
+    const int nblk = gridDim.x;
     const int bid = blockIdx.x;
-    const int per = nb / 8, rem = nb % 8, xcd = bid % 8, local = bid / 8;
+    const int per = nblk / 8, rem = nblk % 8, xcd = bid % 8, local = bid / 8;
     const int linear = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
     const int group_span = kGroupM * tiles_n;
     const int first_m = (linear / group_span) * kGroupM;
     const int gsize = min(tiles_m - first_m, kGroupM);
     const int tm = first_m + (linear % group_span) % gsize;
     const int tn = (linear % group_span) / gsize;
-    const int64_t m0 = (int64_t)tm * kBM;
-    const int64_t n0 = (int64_t)tn * kBN;
+    const int64_t m0 = (int64_t)tm * Cfg::BM;
+    const int64_t n0 = (int64_t)tn * Cfg::BN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave & 1;   // which 64 centroids of the tile
-    const int wn = wave >> 1;  // which 64 samples of the tile
+    const int wm = wave % Cfg::WM;  // which centroid rows of the tile
+    const int wn = wave / Cfg::WM;  // which sample columns of the tile
 
-    f32x16 acc[2][2];
+    f32x16 acc[Cfg::MB][Cfg::NB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < Cfg::MB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < Cfg::NB; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+    constexpr int kBK = Cfg::BK;
     const int64_t nk = (d + kBK - 1) / kBK;
-    f32x4 r[8];
-    load_stage<kVec>(X, C, n, k, d, m0, n0, 0, tid, r);
-    store_stage(lds[0], tid, r);
+    f32x4 r[Cfg::Q];
+    load_stage<Cfg, Mode>(X, C, n, k, d, m0, n0, 0, tid, r);
+    store_stage<Cfg>(lds[0], tid, r);
+    if (nk > 1) load_stage<Cfg, Mode>(X, C, n, k, d, m0, n0, kBK, tid, r);
     __syncthreads();
-
-    const int a_row = wm * 64 + (lane & 31);
-    const int b_row = kBM + wn * 64 + (lane & 31);
-    const int kofs = (lane >> 5) * 4;
-
+    // At the top of iteration it: lds[it % 2] holds stage it, r holds (or is
+    // receiving) stage it + 1, and lds[(it + 1) % 2] is free (its previous
+    // stage was finished by every wave before the last barrier).
     for (int64_t it = 0; it < nk; ++it) {
         const int cur = (int)(it & 1);
-        if (it + 1 < nk) load_stage<kVec>(X, C, n, k, d, m0, n0, (it + 1) * kBK, tid, r);
-#pragma unroll
-        for (int kk = 0; kk < kBK; kk += 8) {
-            f32x4 a[2], b[2];
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-                a[mb] = *reinterpret_cast<const f32x4 *>(&lds[cur][a_row + 32 * mb][kk + kofs]);
-#pragma unroll
-            for (int nb2 = 0; nb2 < 2; ++nb2)
-                b[nb2] = *reinterpret_cast<const f32x4 *>(&lds[cur][b_row + 32 * nb2][kk + kofs]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                    for (int nb2 = 0; nb2 < 2; ++nb2)
-                        acc[mb][nb2] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                            a[mb][e], b[nb2][e], acc[mb][nb2], 0, 0, 0);
+        if (it + 1 < nk) {
+            store_stage<Cfg>(lds[cur ^ 1], tid, r);
+            if (it + 2 < nk) load_stage<Cfg, Mode>(X, C, n, k, d, m0, n0, (it + 2) * kBK, tid, r);
         }
-        if (it + 1 < nk) store_stage(lds[cur ^ 1], tid, r);
+        mma_stage<Cfg>(lds[cur], lane, wm, wn, acc);
         __syncthreads();
     }
 
     // Epilogue. Accumulator element e of a 32 x 32 block sits at row
     // 8 * (e / 4) + 4 * (lane / 32) + e % 4 and column lane % 32.
-    float cnv[2][16];
+    float cnv[Cfg::MB][16];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < Cfg::MB; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int64_t m = m0 + wm * 64 + mb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            const int64_t m = m0 + (wm * Cfg::MB + mb) * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
             cnv[mb][e] = m < k ? cn[m] : __builtin_inff();
         }
 #pragma unroll
-    for (int nb2 = 0; nb2 < 2; ++nb2) {
+    for (int nb = 0; nb < Cfg::NB; ++nb) {
         // Rows are visited in increasing centroid index and only a strictly
         // smaller distance replaces the winner: lowest index on ties.
         float best = __builtin_inff();
         uint32_t bidx = 0xffffffffu;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < Cfg::MB; ++mb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t m = m0 + wm * 64 + mb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                const float v = cnv[mb][e] - 2.0f * acc[mb][nb2][e];
+                const int64_t m =
+                    m0 + (wm * Cfg::MB + mb) * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const float v = cnv[mb][e] - 2.0f * acc[mb][nb][e];
                 if (m < k && v < best) {
                     best = v;
                     bidx = (uint32_t)m;
@@ -236,10 +298,15 @@ __global__ __launch_bounds__(256, 2) void assign_tile_kernel(
         unsigned long long key = pack_key(best, bidx);
         const unsigned long long other = __shfl_xor(key, 32);
         key = other < key ? other : key;
-        const int64_t s = n0 + wn * 64 + nb2 * 32 + (lane & 31);
+        const int64_t s = n0 + (wn * Cfg::NB + nb) * 32 + (lane & 31);
         if (lane < 32 && s < n) atomicMin(keys + s, key);
     }
 }
+
+// Tile shapes (the launcher picks one by problem shape).
+using Tile256x128 = TileCfg<4, 2, 2, 2, 32>;  // 512 threads, 108 KiB LDS, 1 block per CU
+using Tile128x128 = TileCfg<2, 2, 2, 2, 16>;  // 256 threads, 40 KiB LDS, 3 blocks per CU
+using Tile64x64 = TileCfg<2, 2, 1, 1, 32>;    // 256 threads, 36 KiB LDS, small problems
 
 __global__ __launch_bounds__(256) void finalize_kernel(unsigned long long *__restrict__ keys,
                                                        float *__restrict__ min_dist, int64_t n) {
@@ -269,7 +336,9 @@ inline unsigned grid_stride_blocks(int64_t n) {
 
 }  // namespace
 
-int64_t assign_grid_blocks(int64_t n, int64_t k) { return cdiv(n, kBN) * cdiv(k, kBM); }
+int64_t assign_grid_blocks(int64_t n, int64_t k) {
+    return cdiv(n, Tile64x64::BN) * cdiv(k, Tile64x64::BM);  // the most blocks of any tile
+}
 
 hipError_t launch_row_sqnorms(const float *A, int64_t rows, int64_t d, float *out,
                               hipStream_t stream) {
@@ -288,20 +357,59 @@ hipError_t launch_fill_keys(unsigned long long *keys, int64_t n, hipStream_t str
     return hipGetLastError();
 }
 
+namespace {
+
+template <class Cfg, int MinWaves>
+hipError_t launch_tiles_cfg(const float *X, const float *C, const float *cn, int64_t n, int64_t k,
+                            int64_t d, unsigned long long *keys, hipStream_t stream) {
+    const int tiles_m = (int)cdiv(k, Cfg::BM);
+    const int tiles_n = (int)cdiv(n, Cfg::BN);
+    const unsigned blocks = (unsigned)((int64_t)tiles_m * tiles_n);
+    const bool vec = vec_ok(X, d) && vec_ok(C, d);
+    const bool full = vec && n % Cfg::BN == 0 && k % Cfg::BM == 0 && d % Cfg::BK == 0;
+    if (full)
+        assign_tile_kernel<Cfg, kFull, MinWaves><<<blocks, Cfg::kThreads, 0, stream>>>(
+            X, C, cn, n, k, d, tiles_m, tiles_n, keys);
+    else if (vec)
+        assign_tile_kernel<Cfg, kVec, MinWaves><<<blocks, Cfg::kThreads, 0, stream>>>(
+            X, C, cn, n, k, d, tiles_m, tiles_n, keys);
+    else
+        assign_tile_kernel<Cfg, kScalar, MinWaves><<<blocks, Cfg::kThreads, 0, stream>>>(
+            X, C, cn, n, k, d, tiles_m, tiles_n, keys);
+    return hipGetLastError();
+}
+
+template <class Cfg>
+int64_t tile_blocks(int64_t n, int64_t k) {
+    return cdiv(n, Cfg::BN) * cdiv(k, Cfg::BM);
+}
+
+}  // namespace
+
+static const char *assign_tile_name(int64_t n, int64_t k, int64_t d) {
+    // KMEANS_ASSIGN_TILE=256x128 | 128x128 | 64x64 forces a tile (tuning).
+    const char *forced = getenv("KMEANS_ASSIGN_TILE");
+    if (forced && (!strcmp(forced, "256x128") || !strcmp(forced, "128x128") ||
+                   !strcmp(forced, "64x64")))
+        return forced;
+    // Long feature loops: the largest tile (fewest operand bytes per flop).
+    // Otherwise 128 x 128 with short stages (3 blocks per CU), unless that
+    // leaves CUs idle, then 64 x 64.
+    if (d >= 4096 && tile_blocks<Tile256x128>(n, k) >= 512) return "256x128";
+    if (tile_blocks<Tile128x128>(n, k) >= 256) return "128x128";
+    return "64x64";
+}
+
 hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, int64_t n,
                                int64_t k, int64_t d, unsigned long long *keys,
                                hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    const int tiles_m = (int)cdiv(k, kBM);
-    const int tiles_n = (int)cdiv(n, kBN);
-    const unsigned blocks = (unsigned)((int64_t)tiles_m * tiles_n);
-    if (vec_ok(X, d) && vec_ok(C, d))
-        assign_tile_kernel<true><<<blocks, 256, 0, stream>>>(X, C, cn, n, k, d, tiles_m,
-                                                             tiles_n, keys);
-    else
-        assign_tile_kernel<false><<<blocks, 256, 0, stream>>>(X, C, cn, n, k, d, tiles_m,
-                                                              tiles_n, keys);
-    return hipGetLastError();
+    const char *tile = assign_tile_name(n, k, d);
+    if (!strcmp(tile, "256x128"))
+        return launch_tiles_cfg<Tile256x128, 2>(X, C, cn, n, k, d, keys, stream);
+    if (!strcmp(tile, "128x128"))
+        return launch_tiles_cfg<Tile128x128, 3>(X, C, cn, n, k, d, keys, stream);
+    return launch_tiles_cfg<Tile64x64, 4>(X, C, cn, n, k, d, keys, stream);
 }
 
 hipError_t launch_finalize(unsigned long long *keys, float *min_dist, int64_t n,

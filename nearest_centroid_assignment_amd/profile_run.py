@@ -13,8 +13,9 @@ summarize:
         --out profiles/assign_tile_feature_heavy_traffic.json
   reads the counter_collection csv files, scales each counter of the
   assignment kernel by (known copy bytes / what the same counter read for the
-  copy kernel), and records the HBM bytes per launch together with the
-  SHA-256 of csrc/assign.hip, so that a later change to the kernel voids it.
+  copy kernel), and records the HBM bytes per launch together with a SHA-256
+  of csrc/assign.hip and its compile flags, so that a later change to the
+  kernel voids it.
 """
 from __future__ import annotations
 
@@ -31,6 +32,18 @@ ASSIGN_SOURCE = os.path.join(HERE, "csrc", "assign.hip")
 COPY_BYTES = 1 << 30
 COPY_KERNEL = "copy_kernel"
 ASSIGN_KERNEL = "assign_tile_kernel"
+
+
+def kernel_digest() -> str:
+    """SHA-256 of what defines the assignment kernel's code: its source file
+    and the hipcc flags it is compiled with."""
+    from . import build
+
+    h = hashlib.sha256()
+    with open(ASSIGN_SOURCE, "rb") as f:
+        h.update(f.read())
+    h.update(json.dumps([build.HIPCC_FLAGS, build.EXTRA_FLAGS.get("assign.hip", [])]).encode())
+    return h.hexdigest()
 
 
 def run(workload: str) -> None:
@@ -97,8 +110,7 @@ def summarize(fetch_dir: str, write_dir: str, out: str, workload: str) -> dict:
     rec["hbm_bytes_per_launch"] = total
     rec["algorithmic_min_bytes"] = alg
     rec["traffic_over_min"] = total / alg
-    with open(ASSIGN_SOURCE, "rb") as f:
-        rec["assign_source_sha256"] = hashlib.sha256(f.read()).hexdigest()
+    rec["assign_kernel_sha256"] = kernel_digest()
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
     return rec

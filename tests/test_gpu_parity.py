@@ -213,3 +213,22 @@ def test_library_allocates_nothing():
     assert torch.cuda.max_memory_allocated() == base
     assert torch.cuda.mem_get_info()[0] >= free_before - (64 << 20)
     assert wsb < n * k * 4 / 64 and wsb < n * d * 4 / 64
+
+
+@pytest.mark.parametrize("tile", ["256x128", "128x128", "64x64"])
+@pytest.mark.parametrize("n,k,d", [(1000, 300, 1028), (130, 129, 33), (2048, 512, 256),
+                                   (777, 260, 64), (512, 256, 48)])
+def test_tile_variants(monkeypatch, tile, n, k, d):
+    """Every tile shape the launcher can select, on full, ragged and scalar
+    paths (integer data: bit-exact labels, ties included)."""
+    monkeypatch.setenv("KMEANS_ASSIGN_TILE", tile)
+    gu.announce(f"tile {tile} {n}x{k}x{d}")
+    X, C = datagen.make_integer(n, k, d, seed=n + d)
+    C[k - 1] = C[2]
+    if d > 64:
+        X = X / np.float32(4.0)  # still exact: quarter-integers, small sums
+        C = C / np.float32(4.0)
+    g_labels, g_md = gu.gpu_assign(X, C)
+    o_labels, best, _ = oracle.assign(X, C)
+    assert np.array_equal(g_labels, o_labels)
+    assert np.array_equal(g_md.astype(np.float64), best)
