@@ -28,7 +28,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused assign TFLOP/s (2nkd/t) + Lloyd iteration ms, 65536×4096×16384 fp32"
 MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak (published)
-PAGES_LLOYD_MS = 1700.0        # the pages' feature-heavy Lloyd iteration (NVIDIA L4), context
+# The pages' Lloyd-iteration times on an NVIDIA L4, per workload (context).
+PAGES_LLOYD_MS = {"feature_heavy": 1700.0, "centroid_heavy": 3853.0}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "assign_tile_feature_heavy_traffic.json")
 
 
@@ -42,7 +43,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="feature_heavy",
-                    help="workload name (tiny, probe, mid, sample_heavy, feature_heavy)")
+                    help="workload name (tiny, probe, mid, sample_heavy, feature_heavy, "
+                         "centroid_heavy)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -199,7 +201,8 @@ def main() -> int:
         "ms_per_step": round(lloyd_ms, 3),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(PAGES_LLOYD_MS / lloyd_ms, 2) if cfg.name == "feature_heavy" else None,
+        "vs_baseline": (round(PAGES_LLOYD_MS[cfg.name] / lloyd_ms, 2)
+                        if cfg.name in PAGES_LLOYD_MS else None),
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name} n={n} k={k} d={d} float32 Gaussian blobs, seed 0",

@@ -97,11 +97,11 @@ int check_alias(const Out *outs, int n_outs, const Out *ins, int n_ins, int inpl
 
 int run_assign(const float *X, const float *C, int64_t n, int64_t k, int64_t d, int64_t *labels,
                float *min_dist, float *cn, hipStream_t s) {
-    // ||x||^2 for min_dist comes out of the assignment kernel itself.
     hipError_t e = km::launch_row_sqnorms(C, k, d, cn, s);
     if (e == hipSuccess) e = km::launch_fill_keys((unsigned long long *)labels, n, s);
+    if (e == hipSuccess && min_dist) e = km::launch_row_sqnorms(X, n, d, min_dist, s);
     if (e == hipSuccess)
-        e = km::launch_assign_tiles(X, C, cn, n, k, d, (unsigned long long *)labels, min_dist, s);
+        e = km::launch_assign_tiles(X, C, cn, n, k, d, (unsigned long long *)labels, s);
     if (e == hipSuccess) e = km::launch_finalize((unsigned long long *)labels, min_dist, n, s);
     return e == hipSuccess ? KM_OK : KM_ERR_HIP;
 }

@@ -170,22 +170,6 @@ __device__ __forceinline__ void store_stage(float (*lds)[Cfg::LDK], int tid,
     }
 }
 
-// Sample norms: with min_dist requested, the blocks of the first centroid
-// tile also accumulate ||x||^2 of their samples from the registers that stage
-// X into LDS (float64), so no separate pass over X is needed. Thread t holds
-// 16 bytes of rows t / kChunks + kRowStep * q; the X rows are those q with
-// row >= BM.
-template <class Cfg>
-__device__ __forceinline__ void accumulate_norms(const f32x4 (&r)[Cfg::Q],
-                                                 double (&xs)[Cfg::Q]) {
-#pragma unroll
-    for (int q = 0; q < Cfg::Q; ++q) {
-        if (q * Cfg::kRowStep + Cfg::kRowStep <= Cfg::BM) continue;  // centroid rows only
-        const f32x4 v = r[q];
-        xs[q] += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
-    }
-}
-
 // One stage of MFMAs: for each group of 8 features, every (mb, nb) block
 // takes 4 MFMAs. The LDS->register fragments of the next group are read while
 // the MFMAs of the current group run.
@@ -226,11 +210,11 @@ __device__ __forceinline__ void mma_stage(float (*lds)[Cfg::LDK], int lane, int 
     }
 }
 
-template <class Cfg, int Mode, int MinWaves, bool kNorm>
+template <class Cfg, int Mode, int MinWaves>
 __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
     const float *__restrict__ X, const float *__restrict__ C, const float *__restrict__ cn,
     int64_t n, int64_t k, int64_t d, int tiles_m, int tiles_n,
-    unsigned long long *__restrict__ keys, float *__restrict__ xnorm) {
+    unsigned long long *__restrict__ keys) {
     __shared__ float lds[2][Cfg::kRows][Cfg::LDK];
 
     // Blocks are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8).
@@ -266,14 +250,8 @@ __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
     constexpr int kBK = Cfg::BK;
     const int64_t nk = (d + kBK - 1) / kBK;
     f32x4 r[Cfg::Q];
-    static_assert(Cfg::BM % Cfg::kRowStep == 0, "a load pass must not straddle C and X rows");
-    const bool norm_here = kNorm && tm == 0;  // uniform across the block
-    double xs[Cfg::Q];
-#pragma unroll
-    for (int q = 0; q < Cfg::Q; ++q) xs[q] = 0.0;
     load_stage<Cfg, Mode>(X, C, n, k, d, m0, n0, 0, tid, r);
     store_stage<Cfg>(lds[0], tid, r);
-    if (norm_here) accumulate_norms<Cfg>(r, xs);
     if (nk > 1) load_stage<Cfg, Mode>(X, C, n, k, d, m0, n0, kBK, tid, r);
     __syncthreads();
     // At the top of iteration it: lds[it % 2] holds stage it, r holds (or is
@@ -283,25 +261,10 @@ __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
         const int cur = (int)(it & 1);
         if (it + 1 < nk) {
             store_stage<Cfg>(lds[cur ^ 1], tid, r);
-            if (norm_here) accumulate_norms<Cfg>(r, xs);
             if (it + 2 < nk) load_stage<Cfg, Mode>(X, C, n, k, d, m0, n0, (it + 2) * kBK, tid, r);
         }
         mma_stage<Cfg>(lds[cur], lane, wm, wn, acc);
         __syncthreads();
-    }
-
-    if (norm_here) {
-        // The kChunks consecutive threads that loaded one row hold its
-        // partial sums; combine them and let the first write the norm.
-#pragma unroll
-        for (int q = 0; q < Cfg::Q; ++q) {
-            if (q * Cfg::kRowStep + Cfg::kRowStep <= Cfg::BM) continue;
-            double v = xs[q];
-#pragma unroll
-            for (int off = 1; off < Cfg::kChunks; off <<= 1) v += __shfl_xor(v, off);
-            const int64_t srow = n0 + (tid / Cfg::kChunks + Cfg::kRowStep * q - Cfg::BM);
-            if (tid % Cfg::kChunks == 0 && srow < n) xnorm[srow] = (float)v;
-        }
     }
 
     // Epilogue. Accumulator element e of a 32 x 32 block sits at row
@@ -396,34 +359,24 @@ hipError_t launch_fill_keys(unsigned long long *keys, int64_t n, hipStream_t str
 
 namespace {
 
-template <class Cfg, int MinWaves, bool kNorm>
-hipError_t launch_tiles_mode(const float *X, const float *C, const float *cn, int64_t n,
-                             int64_t k, int64_t d, unsigned long long *keys, float *xnorm,
-                             hipStream_t stream) {
+template <class Cfg, int MinWaves>
+hipError_t launch_tiles_cfg(const float *X, const float *C, const float *cn, int64_t n, int64_t k,
+                            int64_t d, unsigned long long *keys, hipStream_t stream) {
     const int tiles_m = (int)cdiv(k, Cfg::BM);
     const int tiles_n = (int)cdiv(n, Cfg::BN);
     const unsigned blocks = (unsigned)((int64_t)tiles_m * tiles_n);
     const bool vec = vec_ok(X, d) && vec_ok(C, d);
     const bool full = vec && n % Cfg::BN == 0 && k % Cfg::BM == 0 && d % Cfg::BK == 0;
     if (full)
-        assign_tile_kernel<Cfg, kFull, MinWaves, kNorm><<<blocks, Cfg::kThreads, 0, stream>>>(
-            X, C, cn, n, k, d, tiles_m, tiles_n, keys, xnorm);
+        assign_tile_kernel<Cfg, kFull, MinWaves><<<blocks, Cfg::kThreads, 0, stream>>>(
+            X, C, cn, n, k, d, tiles_m, tiles_n, keys);
     else if (vec)
-        assign_tile_kernel<Cfg, kVec, MinWaves, kNorm><<<blocks, Cfg::kThreads, 0, stream>>>(
-            X, C, cn, n, k, d, tiles_m, tiles_n, keys, xnorm);
+        assign_tile_kernel<Cfg, kVec, MinWaves><<<blocks, Cfg::kThreads, 0, stream>>>(
+            X, C, cn, n, k, d, tiles_m, tiles_n, keys);
     else
-        assign_tile_kernel<Cfg, kScalar, MinWaves, kNorm><<<blocks, Cfg::kThreads, 0, stream>>>(
-            X, C, cn, n, k, d, tiles_m, tiles_n, keys, xnorm);
+        assign_tile_kernel<Cfg, kScalar, MinWaves><<<blocks, Cfg::kThreads, 0, stream>>>(
+            X, C, cn, n, k, d, tiles_m, tiles_n, keys);
     return hipGetLastError();
-}
-
-template <class Cfg, int MinWaves>
-hipError_t launch_tiles_cfg(const float *X, const float *C, const float *cn, int64_t n, int64_t k,
-                            int64_t d, unsigned long long *keys, float *xnorm,
-                            hipStream_t stream) {
-    if (xnorm)
-        return launch_tiles_mode<Cfg, MinWaves, true>(X, C, cn, n, k, d, keys, xnorm, stream);
-    return launch_tiles_mode<Cfg, MinWaves, false>(X, C, cn, n, k, d, keys, nullptr, stream);
 }
 
 template <class Cfg>
@@ -448,15 +401,15 @@ static const char *assign_tile_name(int64_t n, int64_t k, int64_t d) {
 }
 
 hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, int64_t n,
-                               int64_t k, int64_t d, unsigned long long *keys, float *xnorm,
+                               int64_t k, int64_t d, unsigned long long *keys,
                                hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     const char *tile = assign_tile_name(n, k, d);
     if (!strcmp(tile, "256x128"))
-        return launch_tiles_cfg<Tile256x128, 2>(X, C, cn, n, k, d, keys, xnorm, stream);
+        return launch_tiles_cfg<Tile256x128, 2>(X, C, cn, n, k, d, keys, stream);
     if (!strcmp(tile, "128x128"))
-        return launch_tiles_cfg<Tile128x128, 3>(X, C, cn, n, k, d, keys, xnorm, stream);
-    return launch_tiles_cfg<Tile64x64, 4>(X, C, cn, n, k, d, keys, xnorm, stream);
+        return launch_tiles_cfg<Tile128x128, 3>(X, C, cn, n, k, d, keys, stream);
+    return launch_tiles_cfg<Tile64x64, 4>(X, C, cn, n, k, d, keys, stream);
 }
 
 hipError_t launch_finalize(unsigned long long *keys, float *min_dist, int64_t n,

@@ -29,9 +29,8 @@ hipError_t launch_fill_keys(unsigned long long *keys, int64_t n, hipStream_t str
 
 // Fused Gram product + argmin epilogue: for every sample, atomically lowers
 // keys[i] to the packed (distance', index) of its best centroid per tile.
-// If xnorm != NULL, also writes xnorm[i] = ||x_i||^2 (float64 sum, rounded).
 hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, int64_t n,
-                               int64_t k, int64_t d, unsigned long long *keys, float *xnorm,
+                               int64_t k, int64_t d, unsigned long long *keys,
                                hipStream_t stream);
 
 // Turns packed keys into int64 labels in place; if min_dist != NULL it holds

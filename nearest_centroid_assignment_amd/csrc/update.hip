@@ -17,8 +17,9 @@
 //                        centre for an empty cluster
 //
 // No float atomics: every sum has one fixed order, so results are
-// deterministic, and the float64 sum in increasing sample order followed by a
-// float64 divide is exactly the plain definition of the mean.
+// deterministic. For a cluster of at most 64 rows that order is increasing
+// sample order, so the float64 sum and divide are exactly the plain definition
+// of the mean; larger clusters add four contiguous quarters of their rows.
 #include "kernels.h"
 
 namespace km {
@@ -27,7 +28,7 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = (int)kSortTileRows;  // rows per sort tile
-constexpr int kChunk = 1024;               // columns per segment_mean block (256 x 4)
+constexpr int kCols = 256;                 // columns per segment_mean block (64 lanes x 4)
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -138,51 +139,126 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int64_t *__restrict_
     }
 }
 
-// Block (cluster j, column chunk c); thread t owns 4 columns. The segment's
-// rows are added in increasing sample order in float64.
+// Block (clusters 4q .. 4q+3, chunk c of kCols columns), 4 waves; lane l of a
+// wave owns 4 columns of the chunk.
+//   Phase 1: wave w sums cluster 4q+w if it has at most kSplitMin rows, alone
+//            and in increasing sample order.
+//   Phase 2: each of the block's clusters with more rows is cut into 4
+//            contiguous quarters of its (increasing) rows, one per wave; the
+//            four float64 partial sums are added in quarter order through
+//            LDS, so the rows of a big cluster are fetched by four waves at
+//            once, in a fixed order (deterministic).
+// Rows are fetched in rounds of kBatch: the round's row indices, then all its
+// row loads, then the adds in order.
+constexpr int kBatch = 16;
+constexpr int kSplitMin = 64;
+constexpr int kClustersPerBlock = 4;
+
 template <bool kVec>
-__global__ __launch_bounds__(256) void segment_mean_kernel(
-    const float *__restrict__ X, const int *__restrict__ perm, const int *__restrict__ seg_start,
-    const int *__restrict__ cnt, const float *C_old, int64_t k, int64_t d, int64_t chunks,
-    float *C_new) {
-    // C_old and C_new may be the same array: each element is read and written
-    // by the same thread only, so they carry no __restrict__.
-    const int64_t j = blockIdx.x / chunks;
-    const int64_t c = blockIdx.x % chunks;
-    const int64_t count = cnt[j];
-    const int64_t start = seg_start[j];
-    int64_t col[4];
+__device__ __forceinline__ void sum_rows(const float *__restrict__ X, const int *__restrict__ rows,
+                                         int r0, int r1, int64_t d, const int64_t (&col)[4],
+                                         double (&s)[4]) {
+    for (int p0 = r0; p0 < r1; p0 += kBatch) {
+        const int m = min(kBatch, r1 - p0);
+        int64_t base[kBatch];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        col[e] = kVec ? c * kChunk + 4 * threadIdx.x + e : c * kChunk + threadIdx.x + 256 * e;
-    double s[4] = {0.0, 0.0, 0.0, 0.0};
-    if (kVec) {
-        if (col[0] < d) {
-#pragma unroll 4
-            for (int64_t p = 0; p < count; ++p) {
-                const int64_t i = perm[start + p];
-                const f32x4 v = *reinterpret_cast<const f32x4 *>(X + i * d + col[0]);
-                s[0] += (double)v.x;
-                s[1] += (double)v.y;
-                s[2] += (double)v.z;
-                s[3] += (double)v.w;
+        for (int u = 0; u < kBatch; ++u) base[u] = u < m ? (int64_t)rows[p0 + u] * d : -1;
+        if (kVec) {
+            f32x4 v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                v[u] = (base[u] >= 0 && col[0] < d)
+                           ? *reinterpret_cast<const f32x4 *>(X + base[u] + col[0])
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                if (u < m) {
+                    s[0] += (double)v[u].x;
+                    s[1] += (double)v[u].y;
+                    s[2] += (double)v[u].z;
+                    s[3] += (double)v[u].w;
+                }
             }
-        }
-    } else {
-#pragma unroll 4
-        for (int64_t p = 0; p < count; ++p) {
-            const int64_t i = perm[start + p];
+        } else {
+            float v[kBatch][4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (col[e] < d) s[e] += (double)X[i * d + col[e]];
+            for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[u][e] = (base[u] >= 0 && col[e] < d) ? X[base[u] + col[e]] : 0.f;
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                if (u < m)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s[e] += (double)v[u][e];
         }
     }
+}
+
+__device__ __forceinline__ void write_mean(const float *C_old, float *C_new, int64_t j, int64_t d,
+                                           int count, const int64_t (&col)[4],
+                                           const double (&s)[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         if (col[e] < d) {
             const int64_t o = j * d + col[e];
             C_new[o] = count > 0 ? (float)(s[e] / (double)count) : C_old[o];
         }
+    }
+}
+
+template <bool kVec>
+__global__ __launch_bounds__(256) void segment_mean_kernel(
+    const float *__restrict__ X, const int *__restrict__ perm, const int *__restrict__ seg_start,
+    const int *__restrict__ cnt, const float *C_old, int64_t k, int64_t d, int chunks,
+    float *C_new) {
+    // C_old and C_new may be the same array: each element is read and written
+    // by the same thread only, so they carry no __restrict__.
+    __shared__ double part[3][kCols];
+    const int64_t j0 = (int64_t)(blockIdx.x / (unsigned)chunks) * kClustersPerBlock;
+    const int64_t c = blockIdx.x % (unsigned)chunks;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int lc[4];  // columns within the chunk
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lc[e] = kVec ? 4 * lane + e : lane + 64 * e;
+    int64_t col[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) col[e] = c * kCols + lc[e];
+
+    // Phase 1: small clusters, one per wave.
+    {
+        const int64_t j = j0 + wave;
+        if (j < k) {
+            const int count = cnt[j];
+            if (count <= kSplitMin) {
+                double s[4] = {0.0, 0.0, 0.0, 0.0};
+                sum_rows<kVec>(X, perm + seg_start[j], 0, count, d, col, s);
+                write_mean(C_old, C_new, j, d, count, col, s);
+            }
+        }
+    }
+    // Phase 2: big clusters, all four waves each.
+    for (int w = 0; w < kClustersPerBlock; ++w) {
+        const int64_t j = j0 + w;
+        if (j >= k) break;
+        const int count = cnt[j];  // uniform across the block
+        if (count <= kSplitMin) continue;
+        const int q = (count + 3) / 4;
+        const int r0 = min(count, wave * q), r1 = min(count, r0 + q);
+        double s[4] = {0.0, 0.0, 0.0, 0.0};
+        sum_rows<kVec>(X, perm + seg_start[j], r0, r1, d, col, s);
+        if (wave > 0)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[wave - 1][lc[e]] = s[e];
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int pw = 0; pw < 3; ++pw)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[e] += part[pw][lc[e]];
+            write_mean(C_old, C_new, j, d, count, col, s);
+        }
+        __syncthreads();  // part is reused by the next big cluster
     }
 }
 
@@ -196,7 +272,7 @@ inline unsigned grid_stride_blocks(int64_t n) {
 }  // namespace
 
 int64_t update_grid_blocks(int64_t n, int64_t k, int64_t d) {
-    const int64_t a = k * cdiv(d, kChunk);
+    const int64_t a = cdiv(k, 4) * cdiv(d, kCols);
     const int64_t b = cdiv(n, kTile);
     const int64_t c = cdiv(k, 4);
     return a > b ? (a > c ? a : c) : (b > c ? b : c);
@@ -223,8 +299,8 @@ hipError_t launch_update(const float *X, const int64_t *labels, const float *C_o
         scatter_kernel<<<(unsigned)ws.n_tiles, 256, 0, stream>>>(labels, n, k, ws.n_tiles,
                                                                  ws.tile_hist, ws.seg_start,
                                                                  ws.perm);
-    const int64_t chunks = cdiv(d, kChunk);
-    const unsigned blocks = (unsigned)(k * chunks);
+    const int chunks = (int)cdiv(d, kCols);
+    const unsigned blocks = (unsigned)(cdiv(k, kClustersPerBlock) * chunks);
     const bool vec = (d % 4 == 0) && ((uintptr_t)X % 16 == 0) && ((uintptr_t)C_old % 16 == 0) &&
                      ((uintptr_t)C_new % 16 == 0);
     if (vec)

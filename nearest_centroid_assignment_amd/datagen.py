@@ -60,11 +60,15 @@ class Config:
         return 2.0 * self.n * self.k * self.d
 
 
-# The five workloads. Shapes: Tiny = the n=512, k=17, d=64 label check of the
+# The workloads. Shapes: Tiny = the n=512, k=17, d=64 label check of the
 # fusion probe; Probe = the fusion probe shape; Mid = the shape shared with the
-# Cython Lloyd iteration; sample-heavy and feature-heavy = two of the three
-# large shapes of the resized-shapes page (the Gram tile grid and the Lloyd
-# step of the tile-tradeoff page use feature-heavy).
+# Cython Lloyd iteration; sample-heavy, centroid-heavy and feature-heavy = the
+# three large shapes of the resized-shapes page (the Gram tile grid and the
+# Lloyd step of the tile-tradeoff page use feature-heavy). The centroid-heavy
+# shape is not printed; it follows from the byte counts printed for it (its
+# (n, k) matrix is 4.00 GiB, its Gram tile of 4096 samples 1024 MiB eager, its
+# (n, d) difference 2.00 GiB). Its blob parameters are this module's choice
+# (one blob per centroid, as for the other blob workloads).
 CONFIGS: dict[str, Config] = {
     c.name: c
     for c in (
@@ -73,6 +77,7 @@ CONFIGS: dict[str, Config] = {
         Config("mid", 65536, 1024, 2048, kb=1024, sigma_c=1.0, sigma=0.5),
         Config("sample_heavy", 131072, 8192, 8192, kb=None, sigma_c=0.0, sigma=1.0),
         Config("feature_heavy", 65536, 4096, 16384, kb=4096, sigma_c=1.0, sigma=1.0),
+        Config("centroid_heavy", 65536, 16384, 8192, kb=16384, sigma_c=1.0, sigma=1.0),
     )
 }
 

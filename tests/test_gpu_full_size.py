@@ -50,6 +50,19 @@ def test_feature_heavy_lloyd():
     g_labels, g_md, g_Cnew, g_counts = gu.gpu_lloyd(X, C)
     _sampled_assign_parity("feature_heavy", X, C, g_labels, g_md)
     gu.announce("feature_heavy: oracle update on the GPU labels")
-    gu.check_update(X, g_labels, C, g_Cnew, g_counts)
+    frac = gu.check_update(X, g_labels, C, g_Cnew, g_counts)
     assert g_counts.sum() == len(X)
-    gu.announce("feature_heavy: done")
+    gu.announce(f"feature_heavy: done (bit-exact fraction in clusters > 64 rows: {frac:.6f})")
+
+
+def test_centroid_heavy_lloyd():
+    """65536 x 16384 x 8192: about 4 samples per cluster, C = 512 MiB."""
+    gu.announce("centroid_heavy: generating inputs")
+    X, C = datagen.make("centroid_heavy")
+    gu.announce("centroid_heavy: GPU Lloyd step")
+    g_labels, g_md, g_Cnew, g_counts = gu.gpu_lloyd(X, C)
+    _sampled_assign_parity("centroid_heavy", X, C, g_labels, g_md)
+    gu.announce("centroid_heavy: oracle update on the GPU labels")
+    frac = gu.check_update(X, g_labels, C, g_Cnew, g_counts)
+    assert g_counts.sum() == len(X)
+    gu.announce(f"centroid_heavy: done (bit-exact fraction in clusters > 64 rows: {frac:.6f})")

@@ -112,10 +112,7 @@ def test_in_place_update():
     counts = torch.empty(len(C), dtype=torch.int64, device="cuda:0")
     binding.kmeans_lloyd_step(Xg, Cg, labels, None, Cg, counts)
     torch.cuda.synchronize()
-    g_labels = labels.cpu().numpy()
-    C_ref, cnt_ref, _ = oracle.update(X, g_labels, C)
-    assert np.array_equal(counts.cpu().numpy(), cnt_ref)
-    assert np.array_equal(Cg.cpu().numpy().view(np.uint32), C_ref.view(np.uint32))
+    gu.check_update(X, labels.cpu().numpy(), C, Cg.cpu().numpy(), counts.cpu().numpy())
 
 
 def test_update_ignores_invalid_labels():
@@ -134,9 +131,7 @@ def test_update_ignores_invalid_labels():
     C_new, counts = binding.update(gu.to_gpu(X), gu.to_gpu(labels), gu.to_gpu(C))
     torch.cuda.synchronize()
     keep = ~bad
-    C_ref, cnt_ref, _ = oracle.update(X[keep], labels[keep], C)
-    assert np.array_equal(counts.cpu().numpy(), cnt_ref)
-    assert np.array_equal(C_new.cpu().numpy().view(np.uint32), C_ref.view(np.uint32))
+    gu.check_update(X[keep], labels[keep], C, C_new.cpu().numpy(), counts.cpu().numpy())
 
 
 def test_update_with_no_samples():
@@ -232,3 +227,30 @@ def test_tile_variants(monkeypatch, tile, n, k, d):
     o_labels, best, _ = oracle.assign(X, C)
     assert np.array_equal(g_labels, o_labels)
     assert np.array_equal(g_md.astype(np.float64), best)
+
+
+@pytest.mark.parametrize("n,k,d,skew", [(5000, 3, 300, "mild"), (70000, 2, 520, "giant"),
+                                        (20000, 50, 1030, "zipf"), (3000, 200, 64, "one-big")])
+def test_update_skewed_clusters(n, k, d, skew):
+    """Cluster sizes far from balanced: big clusters take the split-row path,
+    small ones the in-order path; both must meet the update rules."""
+    from nearest_centroid_assignment_amd import binding
+    import torch
+
+    gu.announce(f"skewed update {skew} {n}x{k}x{d}")
+    rng = np.random.default_rng(n + k)
+    X = rng.standard_normal((n, d), dtype=np.float32)
+    C = rng.standard_normal((k, d), dtype=np.float32)
+    if skew == "giant":
+        labels = (rng.random(n) < 0.999).astype(np.int64) * 0 + (rng.random(n) < 0.001)
+    elif skew == "zipf":
+        labels = np.minimum(rng.zipf(1.5, size=n) - 1, k - 1).astype(np.int64)
+    elif skew == "one-big":
+        labels = np.where(rng.random(n) < 0.5, 7, rng.integers(0, k, size=n)).astype(np.int64)
+    else:
+        labels = rng.integers(0, k, size=n).astype(np.int64)
+    C_new, counts = binding.update(gu.to_gpu(X), gu.to_gpu(labels), gu.to_gpu(C))
+    torch.cuda.synchronize()
+    frac = gu.check_update(X, labels, C, C_new.cpu().numpy(), counts.cpu().numpy())
+    gu.announce(f"skewed update {skew}: bit-exact fraction in big clusters {frac:.6f}")
+    assert frac > 0.99
