@@ -303,7 +303,8 @@ __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
     }
 }
 
-// Tile shapes (the launcher picks one by problem shape).
+// Tile shapes (centroids x samples; the launcher picks one by problem shape).
+using Tile128x256 = TileCfg<2, 4, 2, 2, 32>;  // 512 threads, 108 KiB LDS, 1 block per CU
 using Tile256x128 = TileCfg<4, 2, 2, 2, 32>;  // 512 threads, 108 KiB LDS, 1 block per CU
 using Tile128x128 = TileCfg<2, 2, 2, 2, 16>;  // 256 threads, 40 KiB LDS, 3 blocks per CU
 using Tile64x64 = TileCfg<2, 2, 1, 1, 32>;    // 256 threads, 36 KiB LDS, small problems
@@ -387,15 +388,15 @@ int64_t tile_blocks(int64_t n, int64_t k) {
 }  // namespace
 
 static const char *assign_tile_name(int64_t n, int64_t k, int64_t d) {
-    // KMEANS_ASSIGN_TILE=256x128 | 128x128 | 64x64 forces a tile (tuning).
+    // KMEANS_ASSIGN_TILE=128x256 | 256x128 | 128x128 | 64x64 forces a tile (tuning).
     const char *forced = getenv("KMEANS_ASSIGN_TILE");
     if (forced && (!strcmp(forced, "256x128") || !strcmp(forced, "128x128") ||
-                   !strcmp(forced, "64x64")))
+                   !strcmp(forced, "64x64") || !strcmp(forced, "128x256")))
         return forced;
-    // Long feature loops: the largest tile (fewest operand bytes per flop).
-    // Otherwise 128 x 128 with short stages (3 blocks per CU), unless that
-    // leaves CUs idle, then 64 x 64.
-    if (d >= 4096 && tile_blocks<Tile256x128>(n, k) >= 512) return "256x128";
+    // The largest tile (fewest operand bytes per flop) when it gives at least
+    // two blocks per CU; otherwise 128 x 128 with short stages (3 blocks per
+    // CU), unless that leaves CUs idle, then 64 x 64.
+    if (tile_blocks<Tile128x256>(n, k) >= 512) return "128x256";
     if (tile_blocks<Tile128x128>(n, k) >= 256) return "128x128";
     return "64x64";
 }
@@ -409,6 +410,8 @@ hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, 
         return launch_tiles_cfg<Tile256x128, 2>(X, C, cn, n, k, d, keys, stream);
     if (!strcmp(tile, "128x128"))
         return launch_tiles_cfg<Tile128x128, 3>(X, C, cn, n, k, d, keys, stream);
+    if (!strcmp(tile, "128x256"))
+        return launch_tiles_cfg<Tile128x256, 2>(X, C, cn, n, k, d, keys, stream);
     return launch_tiles_cfg<Tile64x64, 4>(X, C, cn, n, k, d, keys, stream);
 }
 

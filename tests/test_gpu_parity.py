@@ -210,7 +210,7 @@ def test_library_allocates_nothing():
     assert wsb < n * k * 4 / 64 and wsb < n * d * 4 / 64
 
 
-@pytest.mark.parametrize("tile", ["256x128", "128x128", "64x64"])
+@pytest.mark.parametrize("tile", ["128x256", "256x128", "128x128", "64x64"])
 @pytest.mark.parametrize("n,k,d", [(1000, 300, 1028), (130, 129, 33), (2048, 512, 256),
                                    (777, 260, 64), (512, 256, 48)])
 def test_tile_variants(monkeypatch, tile, n, k, d):
