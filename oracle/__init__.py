@@ -180,3 +180,75 @@ def near_ties(X, C, labels, best, second, rtol: float = 1e-5) -> np.ndarray:
 for _name in ("num_threads", "assign", "update", "lloyd_step"):
     globals()[_name].__doc__ = getattr(Oracle, _name).__doc__
 del _name
+
+
+# --------------------------------------------------------------------------
+# Lloyd driver with empty-cluster relocation ("004 - tile sizes ...", section
+# Cython timing: the Lloyd call updates the centres and relocates empty
+# clusters). The pages do not give the relocation rule; the reading used here:
+#
+#   after the assignment against the old centres, let E be the empty clusters
+#   in increasing index and m = min(|E|, n). The m samples farthest from their
+#   assigned old centre (float64 difference-form distance, larger first, lower
+#   sample index first on equal distances) are moved, the r-th of them becoming
+#   the only member of cluster E[r]. The update then runs on the new labels; a
+#   cluster emptied by a move keeps its old centre.
+#
+# The driver repeats assignment (+ relocation) + update from C_init until the
+# centre shift sum_j ||C_new_j - C_old_j||^2 (float64) is <= tol or max_iter
+# iterations ran, then assigns once more against the final centres; inertia is
+# the sum of those final squared distances.
+
+
+def relocate(labels, best, k):
+    """Apply the relocation rule above; returns (new_labels, moves) where
+    moves is a list of (sample, new_cluster) pairs in order."""
+    labels = np.array(labels, dtype=np.int64, copy=True)
+    n = len(labels)
+    counts = np.bincount(labels, minlength=k)
+    empty = np.nonzero(counts == 0)[0]
+    m = min(len(empty), n)
+    if m == 0:
+        return labels, []
+    order = np.lexsort((np.arange(n), -np.asarray(best, dtype=np.float64)))
+    moves = [(int(order[r]), int(empty[r])) for r in range(m)]
+    for i, j in moves:
+        labels[i] = j
+    return labels, moves
+
+
+def centre_shift(C_new, C_old) -> float:
+    """sum_j ||C_new_j - C_old_j||^2 in float64."""
+    diff = np.asarray(C_new, dtype=np.float64) - np.asarray(C_old, dtype=np.float64)
+    return float(np.sum(diff * diff))
+
+
+def fit(X, C_init, max_iter: int, tol: float, relocate_empty: bool):
+    """Lloyd iterations from C_init (see the rule above).
+
+    Returns a dict: labels, best (final squared distances), centres, counts,
+    n_iter, inertia, shift (the last iteration's centre shift), history (the
+    centre shift of every iteration).
+    """
+    orc = default()
+    C = np.array(C_init, dtype=np.float32, copy=True)
+    k = C.shape[0]
+    history = []
+    n_iter = 0
+    shift = 0.0
+    for it in range(max_iter):
+        labels, best, _ = orc.assign(X, C)
+        if relocate_empty:
+            labels, _ = relocate(labels, best, k)
+        C_new, _, _ = orc.update(X, labels, C)
+        shift = centre_shift(C_new, C)
+        history.append(shift)
+        C = C_new
+        n_iter = it + 1
+        if shift <= tol:
+            break
+    labels, best, _ = orc.assign(X, C)
+    counts = np.bincount(labels, minlength=k).astype(np.int64)
+    return {"labels": labels, "best": best, "centres": C, "counts": counts,
+            "n_iter": n_iter, "inertia": float(np.sum(best)), "shift": shift,
+            "history": history}
