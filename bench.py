@@ -48,6 +48,9 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["lloyd", "fit"], default="lloyd",
+                    help="lloyd: one Lloyd step per timed step (default); fit: kmeans_fit "
+                         "with relocation running exactly --steps iterations")
     return ap.parse_args()
 
 
@@ -98,6 +101,74 @@ def cpu_baseline(X, C, target_s: float):
     }
 
 
+def bench_fit(args, cfg, Xg, Cg, labels, md, counts, stream) -> int:
+    """kmeans_fit with empty-cluster relocation, forced to run exactly
+    --steps iterations (tol = -1), against --steps separate Lloyd steps."""
+    import torch
+
+    from nearest_centroid_assignment_amd import binding
+
+    n, k, d = cfg.n, cfg.k, cfg.d
+    dev = Xg.device
+    C_out = torch.empty_like(Cg)
+    info = torch.empty(3, dtype=torch.float64, device=dev)
+    wsb = binding.kmeans_workspace_bytes(n, k, d, binding.KM_OP_FIT)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def fit(iters):
+        binding.kmeans_fit(Xg, Cg, iters, -1.0, binding.KM_FIT_RELOCATE_EMPTY, C_out, labels,
+                           md, counts, info, workspace=ws, stream=stream)
+
+    log(f"fit warmup ({args.warmup} iterations)")
+    fit(max(1, args.warmup))
+    torch.cuda.synchronize()
+    log(f"timing fit with {args.steps} iterations")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    fit(args.steps)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3
+    total_ms = ev0.elapsed_time(ev1)
+    n_iter = int(info[0].item())
+    # The call ends with one more assignment against the final centres; time
+    # that assignment alone to report the cost of an iteration without it.
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    binding.kmeans_assign(Xg, C_out, labels, md, stream=stream)
+    a1.record(stream)
+    torch.cuda.synchronize()
+    final_assign_ms = a0.elapsed_time(a1)
+    per_iter = (total_ms - final_assign_ms) / max(n_iter, 1)
+    result = {
+        "metric": "kmeans_fit ms (iterations of assignment + relocation + update + convergence "
+                  "check, then a final assignment)",
+        "value": round(total_ms, 3),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(per_iter, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} n={n} k={k} d={d} float32 Gaussian blobs, seed 0",
+                   "n": n, "k": k, "d": d, "iterations": n_iter},
+        "fit_wall_ms": round(wall_ms, 3),
+        "final_assign_ms": round(final_assign_ms, 3),
+        "ms_per_iteration": round(per_iter, 3),
+        "inertia": info[1].item(),
+        "tflops_per_iter": round(cfg.flops / (per_iter * 1e-3) / 1e12, 3),
+        "workspace_bytes": wsb,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -134,6 +205,9 @@ def main() -> int:
 
     def lloyd():
         binding.kmeans_lloyd_step(Xg, Cg, labels, md, C_new, counts, workspace=ws, stream=stream)
+
+    if args.mode == "fit":
+        return bench_fit(args, cfg, Xg, Cg, labels, md, counts, stream)
 
     def assign_only():
         binding.kmeans_assign(Xg, Cg, labels, None, workspace=ws, stream=stream)

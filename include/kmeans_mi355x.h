@@ -27,10 +27,11 @@
  *     kmeans_workspace_bytes(n, k, d, op) bytes, any alignment. Its contents
  *     on entry do not matter; it is clobbered. Two calls that may run at the
  *     same time need two workspaces.
- *   - stream is a hipStream_t (NULL = the default stream). Every call only
- *     enqueues kernels on it and returns: no host synchronisation. Results are
- *     ready when the stream has reached that point. A fault inside a kernel
- *     surfaces at the caller's next synchronisation, not as a return value.
+ *   - stream is a hipStream_t (NULL = the default stream). Every call except
+ *     kmeans_fit only enqueues kernels on it and returns: no host
+ *     synchronisation. Results are ready when the stream has reached that
+ *     point. A fault inside a kernel surfaces at the caller's next
+ *     synchronisation, not as a return value.
  *   - Shapes: 0 <= n < 2^31, 1 <= k < 2^31, 1 <= d < 2^31. With n = 0 nothing
  *     is read from X, labels or min_dist (they may be NULL). k > n is allowed.
  *   - Inputs must be finite; NaN or Inf inputs give unspecified labels.
@@ -39,9 +40,11 @@
  *   - Arguments are validated on the host before any HIP call; an invalid
  *     call returns a negative km_status and enqueues nothing.
  *   - Arithmetic: float32 MFMA products with float32 accumulation for the
- *     assignment; per-cluster sums accumulated in float64 in increasing
- *     sample order, then divided in float64 and rounded once to float32.
- *     Results are deterministic: the same inputs give the same bits.
+ *     assignment; per-cluster sums accumulated in float64 (in increasing
+ *     sample order for a cluster of at most 64 samples; as four contiguous
+ *     quarters of its samples, added in order, for a larger one), divided in
+ *     float64 and rounded once to float32. Every reduction has a fixed
+ *     order: the same inputs give the same bits.
  */
 #ifndef KMEANS_MI355X_H
 #define KMEANS_MI355X_H
@@ -62,17 +65,21 @@ typedef enum {
     KM_ERR_WORKSPACE = -4, /* workspace_bytes < kmeans_workspace_bytes(...)       */
     KM_ERR_ALIAS = -5,     /* an output overlaps an input, output or workspace    */
     KM_ERR_HIP = -6,       /* a kernel launch was rejected by the HIP runtime     */
-    KM_ERR_OP = -7         /* unknown op code                                     */
+    KM_ERR_OP = -7         /* unknown op code or flag                             */
 } km_status;
 
 /* Op codes for kmeans_workspace_bytes. */
-enum { KM_OP_ASSIGN = 0, KM_OP_UPDATE = 1, KM_OP_LLOYD = 2 };
+enum { KM_OP_ASSIGN = 0, KM_OP_UPDATE = 1, KM_OP_LLOYD = 2, KM_OP_FIT = 3 };
+
+/* Flags for kmeans_fit. */
+enum { KM_FIT_RELOCATE_EMPTY = 1 };
 
 /*
  * Workspace bytes needed by one call of the given op at shape (n, k, d).
- * The size is O(k + n + k * ceil(n / 1024)) 4-byte words, far below the
- * (n, k) distance matrix and the (n, d) sample matrix. Returns 0 when the
- * shape or op is invalid (a valid shape never needs 0 bytes).
+ * The size is O(k + n + k * ceil(n / 1024)) 4-byte words (plus about
+ * k * d / 1024 doubles for kmeans_fit), far below the (n, k) distance matrix
+ * and the (n, d) sample matrix. Returns 0 when the shape or op is invalid (a
+ * valid shape never needs 0 bytes).
  */
 size_t kmeans_workspace_bytes(int64_t n, int64_t k, int64_t d, int op);
 
@@ -114,6 +121,37 @@ int kmeans_update(const float *X, const int64_t *labels, const float *C_old,
 int kmeans_lloyd_step(const float *X, const float *C_old, int64_t n, int64_t k, int64_t d,
                       int64_t *labels, float *min_dist, float *C_new, int64_t *counts,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Lloyd iterations from C_init: assignment, optional empty-cluster
+ * relocation, update, repeated until the centre shift
+ * sum_j ||C_new_j - C_old_j||^2 (float64) is <= tol or max_iter iterations
+ * ran; then one more assignment against the final centres ("004 ...",
+ * sections Lloyd step and Cython timing, whose Lloyd call updates the
+ * centres and relocates empty clusters).
+ *   max_iter  >= 1.
+ *   tol       convergence threshold on the centre shift (not NaN).
+ *   flags     0, or KM_FIT_RELOCATE_EMPTY: after each assignment, the
+ *             min(#empty, n) samples farthest from their assigned centre
+ *             (float64 distance; lower index first on ties) each become the
+ *             only member of the next empty cluster in increasing index.
+ *             Without it (and for a cluster a move empties) an empty
+ *             cluster keeps its centre.
+ *   C_out     (k, d) float32 output: the final centres. May equal C_init.
+ *   labels    (n,) int64 output: assignment against the final centres.
+ *   min_dist  (n,) float32 output or NULL: squared distances of that
+ *             assignment (as in kmeans_assign).
+ *   counts    (k,) int64 output: cluster sizes of those labels.
+ *   info      device array of 3 doubles, output: iterations run, inertia
+ *             (sum of the final squared distances, float64), and the centre
+ *             shift of the last iteration.
+ * Synchronisation: waits on `stream` once per iteration to read a 4-byte
+ * convergence flag back to the host; it is the only entry point that does.
+ */
+int kmeans_fit(const float *X, const float *C_init, int64_t n, int64_t k, int64_t d,
+               int64_t max_iter, double tol, int flags,
+               float *C_out, int64_t *labels, float *min_dist, int64_t *counts, double *info,
+               void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, NUL-terminated description of a km_status value (never NULL). */
 const char *kmeans_status_string(int status);

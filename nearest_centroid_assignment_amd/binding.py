@@ -6,9 +6,9 @@ step of the computation runs in the library's HIP kernels. There is no CPU
 fallback: if the library is missing, loading fails with an error.
 
 The functions ``kmeans_assign``, ``kmeans_update``, ``kmeans_lloyd_step``,
-``kmeans_workspace_bytes`` and ``kmeans_status_string`` mirror the C entry
-points of the same names; ``assign``, ``update`` and ``lloyd_step`` also
-allocate the outputs.
+``kmeans_fit``, ``kmeans_workspace_bytes`` and ``kmeans_status_string`` mirror
+the C entry points of the same names; ``assign``, ``update``, ``lloyd_step``
+and ``fit`` also allocate the outputs.
 """
 from __future__ import annotations
 
@@ -20,7 +20,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkmeans_mi355x.so")
 
 KM_OK = 0
-KM_OP_ASSIGN, KM_OP_UPDATE, KM_OP_LLOYD = 0, 1, 2
+KM_OP_ASSIGN, KM_OP_UPDATE, KM_OP_LLOYD, KM_OP_FIT = 0, 1, 2, 3
+KM_FIT_RELOCATE_EMPTY = 1
 STATUS_NAMES = {
     0: "KM_OK",
     -1: "KM_ERR_NULL",
@@ -67,6 +68,9 @@ def lib() -> ctypes.CDLL:
         L.kmeans_update.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
         L.kmeans_lloyd_step.restype = ctypes.c_int
         L.kmeans_lloyd_step.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+        L.kmeans_fit.restype = ctypes.c_int
+        L.kmeans_fit.argtypes = [vp, vp, i64, i64, i64, i64, ctypes.c_double, ctypes.c_int,
+                                 vp, vp, vp, vp, vp, vp, sz, vp]
         _lib = L
         return L
 
@@ -170,6 +174,23 @@ def kmeans_lloyd_step(X, C_old, labels, min_dist, C_new, counts, workspace=None,
     _check(rc, "kmeans_lloyd_step")
 
 
+def kmeans_fit(X, C_init, max_iter, tol, flags, C_out, labels, min_dist, counts, info,
+               workspace=None, stream=None):
+    """Run Lloyd iterations (waits on the stream once per iteration)."""
+    torch = _torch()
+    n, d = X.shape
+    k = C_init.shape[0]
+    args = (_ptr(X, torch.float32, (n, d), "X"), _ptr(C_init, torch.float32, (k, d), "C_init"),
+            n, k, d, int(max_iter), float(tol), int(flags),
+            _ptr(C_out, torch.float32, (k, d), "C_out"), _ptr(labels, torch.int64, (n,), "labels"),
+            _ptr(min_dist, torch.float32, (n,), "min_dist"),
+            _ptr(counts, torch.int64, (k,), "counts"), _ptr(info, torch.float64, (3,), "info"))
+    workspace = _workspace(workspace, kmeans_workspace_bytes(n, k, d, KM_OP_FIT), X.device)
+    rc = lib().kmeans_fit(*args, workspace.data_ptr(), workspace.numel(),
+                          _stream(stream, X.device))
+    _check(rc, "kmeans_fit")
+
+
 # ------------------------------------------------------ allocating wrappers
 
 
@@ -203,3 +224,21 @@ def lloyd_step(X, C_old, min_dist: bool = True, stream=None):
     counts = torch.empty(k, dtype=torch.int64, device=X.device)
     kmeans_lloyd_step(X, C_old, labels, md, C_new, counts, stream=stream)
     return labels, md, C_new, counts
+
+
+def fit(X, C_init, max_iter: int = 300, tol: float = 0.0, relocate_empty: bool = True,
+        stream=None):
+    """Lloyd iterations from C_init. Returns a dict of GPU tensors and numbers:
+    centres, labels, min_dist, counts, n_iter, inertia, shift."""
+    torch = _torch()
+    n, k = X.shape[0], C_init.shape[0]
+    C_out = torch.empty_like(C_init)
+    labels = torch.empty(n, dtype=torch.int64, device=X.device)
+    md = torch.empty(n, dtype=torch.float32, device=X.device)
+    counts = torch.empty(k, dtype=torch.int64, device=X.device)
+    info = torch.empty(3, dtype=torch.float64, device=X.device)
+    kmeans_fit(X, C_init, max_iter, tol, KM_FIT_RELOCATE_EMPTY if relocate_empty else 0,
+               C_out, labels, md, counts, info, stream=stream)
+    n_iter, inertia, shift = info.cpu().tolist()
+    return {"centres": C_out, "labels": labels, "min_dist": md, "counts": counts,
+            "n_iter": int(n_iter), "inertia": inertia, "shift": shift}

@@ -18,19 +18,23 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Layout {
-    size_t cn = 0, tile_hist = 0, cnt = 0, seg_start = 0, perm = 0, total = 0;
+    size_t cn = 0, tile_hist = 0, cnt = 0, seg_start = 0, perm = 0;
+    // kmeans_fit only
+    size_t md = 0, dist = 0, empty = 0, sort_key = 0, sort_idx = 0, moves_src = 0, moves_dst = 0,
+           shift_partial = 0, scalars = 0;
+    size_t total = 0;
 };
 
 // Offsets from the first 256-byte boundary at or after the workspace start;
 // total includes that much slack so any base alignment works.
-Layout layout(int64_t n, int64_t k, int op) {
+Layout layout(int64_t n, int64_t k, int64_t d, int op) {
     Layout L;
     size_t off = 0;
-    if (op == KM_OP_ASSIGN || op == KM_OP_LLOYD) {
+    if (op == KM_OP_ASSIGN || op == KM_OP_LLOYD || op == KM_OP_FIT) {
         L.cn = off;
         off += round_up((size_t)k * sizeof(float));
     }
-    if (op == KM_OP_UPDATE || op == KM_OP_LLOYD) {
+    if (op == KM_OP_UPDATE || op == KM_OP_LLOYD || op == KM_OP_FIT) {
         const int64_t n_tiles = cdiv(n, km::kSortTileRows);
         L.tile_hist = off;
         off += round_up((size_t)k * (size_t)n_tiles * sizeof(int));
@@ -40,6 +44,28 @@ Layout layout(int64_t n, int64_t k, int op) {
         off += round_up((size_t)k * sizeof(int));
         L.perm = off;
         off += round_up((size_t)n * sizeof(int));
+    }
+    if (op == KM_OP_FIT) {
+        const int64_t nk = n < k ? n : k;
+        const int64_t cap = km::reloc_sort_cap(n, k);
+        L.md = off;
+        off += round_up((size_t)n * sizeof(float));
+        L.dist = off;
+        off += round_up((size_t)n * sizeof(double));
+        L.empty = off;
+        off += round_up((size_t)k * sizeof(int));
+        L.sort_key = off;
+        off += round_up((size_t)cap * sizeof(unsigned long long));
+        L.sort_idx = off;
+        off += round_up((size_t)cap * sizeof(int));
+        L.moves_src = off;
+        off += round_up((size_t)nk * sizeof(int));
+        L.moves_dst = off;
+        off += round_up((size_t)nk * sizeof(int));
+        L.shift_partial = off;
+        off += round_up((size_t)km::mean_blocks(k, d) * sizeof(double));
+        L.scalars = off;  // num_empty, n_moves, converged
+        off += round_up(4 * sizeof(int));
     }
     L.total = off + kAlign;
     return L;
@@ -122,8 +148,9 @@ extern "C" {
 
 size_t kmeans_workspace_bytes(int64_t n, int64_t k, int64_t d, int op) {
     if (!shape_ok(n, k, d)) return 0;
-    if (op != KM_OP_ASSIGN && op != KM_OP_UPDATE && op != KM_OP_LLOYD) return 0;
-    return layout(n, k, op).total;
+    if (op != KM_OP_ASSIGN && op != KM_OP_UPDATE && op != KM_OP_LLOYD && op != KM_OP_FIT)
+        return 0;
+    return layout(n, k, d, op).total;
 }
 
 const char *kmeans_status_string(int status) {
@@ -135,7 +162,7 @@ const char *kmeans_status_string(int status) {
         case KM_ERR_WORKSPACE: return "workspace smaller than kmeans_workspace_bytes()";
         case KM_ERR_ALIAS: return "an output overlaps an input, another output or the workspace";
         case KM_ERR_HIP: return "the HIP runtime rejected a kernel launch";
-        case KM_ERR_OP: return "unknown op code";
+        case KM_ERR_OP: return "unknown op code or flag";
         default: return "unknown status";
     }
 }
@@ -147,7 +174,7 @@ int kmeans_assign(const float *X, const float *C, int64_t n, int64_t k, int64_t 
     if (!C || !workspace || (n > 0 && (!X || !labels))) return KM_ERR_NULL;
     if (!aligned(X, 4) || !aligned(C, 4) || !aligned(labels, 8) || !aligned(min_dist, 4))
         return KM_ERR_ALIGN;
-    const Layout L = layout(n, k, KM_OP_ASSIGN);
+    const Layout L = layout(n, k, d, KM_OP_ASSIGN);
     if (workspace_bytes < L.total) return KM_ERR_WORKSPACE;
     const Out outs[] = {{labels, n, 8}, {min_dist, n, 4}, {workspace, (int64_t)workspace_bytes, 1}};
     const Out ins[] = {{X, n * d, 4}, {C, k * d, 4}};
@@ -166,7 +193,7 @@ int kmeans_update(const float *X, const int64_t *labels, const float *C_old, int
     if (!aligned(X, 4) || !aligned(labels, 8) || !aligned(C_old, 4) || !aligned(C_new, 4) ||
         !aligned(counts, 8))
         return KM_ERR_ALIGN;
-    const Layout L = layout(n, k, KM_OP_UPDATE);
+    const Layout L = layout(n, k, d, KM_OP_UPDATE);
     if (workspace_bytes < L.total) return KM_ERR_WORKSPACE;
     const Out outs[] = {{C_new, k * d, 4}, {counts, k, 8}, {workspace, (int64_t)workspace_bytes, 1}};
     const Out ins[] = {{X, n * d, 4}, {labels, n, 8}, {C_old, k * d, 4}};
@@ -186,7 +213,7 @@ int kmeans_lloyd_step(const float *X, const float *C_old, int64_t n, int64_t k, 
     if (!aligned(X, 4) || !aligned(C_old, 4) || !aligned(labels, 8) || !aligned(min_dist, 4) ||
         !aligned(C_new, 4) || !aligned(counts, 8))
         return KM_ERR_ALIGN;
-    const Layout L = layout(n, k, KM_OP_LLOYD);
+    const Layout L = layout(n, k, d, KM_OP_LLOYD);
     if (workspace_bytes < L.total) return KM_ERR_WORKSPACE;
     const Out outs[] = {{labels, n, 8},
                         {min_dist, n, 4},
@@ -203,6 +230,73 @@ int kmeans_lloyd_step(const float *X, const float *C_old, int64_t n, int64_t k, 
     }
     const hipError_t e = km::launch_update(X, labels, C_old, n, k, d, C_new, counts,
                                            update_scratch(base, L, n), s);
+    return e == hipSuccess ? KM_OK : KM_ERR_HIP;
+}
+
+int kmeans_fit(const float *X, const float *C_init, int64_t n, int64_t k, int64_t d,
+               int64_t max_iter, double tol, int flags, float *C_out, int64_t *labels,
+               float *min_dist, int64_t *counts, double *info, void *workspace,
+               size_t workspace_bytes, void *stream) {
+    if (!shape_ok(n, k, d) || !grid_ok(n, k, d) || max_iter < 1 || tol != tol)
+        return KM_ERR_SHAPE;
+    if (flags & ~KM_FIT_RELOCATE_EMPTY) return KM_ERR_OP;
+    if (!C_init || !C_out || !counts || !info || !workspace || (n > 0 && (!X || !labels)))
+        return KM_ERR_NULL;
+    if (!aligned(X, 4) || !aligned(C_init, 4) || !aligned(C_out, 4) || !aligned(labels, 8) ||
+        !aligned(min_dist, 4) || !aligned(counts, 8) || !aligned(info, 8))
+        return KM_ERR_ALIGN;
+    const Layout L = layout(n, k, d, KM_OP_FIT);
+    if (workspace_bytes < L.total) return KM_ERR_WORKSPACE;
+    const Out outs[] = {{C_out, k * d, 4},   {labels, n, 8}, {min_dist, n, 4},
+                        {counts, k, 8},      {info, 3, 8},   {workspace, (int64_t)workspace_bytes, 1}};
+    const Out ins[] = {{X, n * d, 4}, {C_init, k * d, 4}};
+    if (int rc = check_alias(outs, 6, ins, 2, /*C_out*/ 0, /*C_init*/ 1)) return rc;
+
+    hipStream_t s = (hipStream_t)stream;
+    char *base = ws_base(workspace);
+    const km::UpdateScratch ws = update_scratch(base, L, n);
+    float *cn = (float *)(base + L.cn);
+    float *md = min_dist ? min_dist : (float *)(base + L.md);
+    int *scalars = (int *)(base + L.scalars);
+    km::RelocScratch rs;
+    rs.dist = (double *)(base + L.dist);
+    rs.empty = (int *)(base + L.empty);
+    rs.sort_key = (unsigned long long *)(base + L.sort_key);
+    rs.sort_idx = (int *)(base + L.sort_idx);
+    rs.moves_src = (int *)(base + L.moves_src);
+    rs.moves_dst = (int *)(base + L.moves_dst);
+    rs.num_empty = scalars;
+    rs.n_moves = scalars + 1;
+    int *converged = scalars + 2;
+    double *shift_partial = (double *)(base + L.shift_partial);
+    const bool relocate = (flags & KM_FIT_RELOCATE_EMPTY) != 0;
+
+    hipError_t e = km::launch_copy_f32(C_out, C_init, k * d, s);
+    int64_t n_iter = 0;
+    for (int64_t it = 0; it < max_iter && e == hipSuccess; ++it) {
+        if (n > 0 && run_assign(X, C_out, n, k, d, labels, nullptr, cn, s) != KM_OK)
+            return KM_ERR_HIP;
+        e = km::launch_count(labels, n, k, counts, relocate ? rs.num_empty : nullptr, ws, s);
+        if (e == hipSuccess && relocate) {
+            e = km::launch_relocate(X, C_out, labels, n, k, d, rs, ws, s);
+            if (e == hipSuccess) e = km::launch_count(labels, n, k, counts, nullptr, ws, s);
+        }
+        if (e == hipSuccess)
+            e = km::launch_group_and_mean(X, labels, C_out, n, k, d, C_out, shift_partial, ws, s);
+        if (e == hipSuccess)
+            e = km::launch_shift(shift_partial, km::mean_blocks(k, d), tol, info + 2, converged, s);
+        int host_converged = 0;
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(&host_converged, converged, sizeof(int), hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        n_iter = it + 1;
+        if (host_converged) break;
+    }
+    if (e == hipSuccess && n > 0 && run_assign(X, C_out, n, k, d, labels, md, cn, s) != KM_OK)
+        return KM_ERR_HIP;
+    if (e == hipSuccess) e = km::launch_count(labels, n, k, counts, nullptr, ws, s);
+    if (e == hipSuccess) e = km::launch_inertia(md, n, info + 1, s);
+    if (e == hipSuccess) e = km::launch_store_f64(info, (double)n_iter, s);
     return e == hipSuccess ? KM_OK : KM_ERR_HIP;
 }
 

@@ -38,11 +38,57 @@ hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, 
 hipError_t launch_finalize(unsigned long long *keys, float *min_dist, int64_t n,
                            hipStream_t stream);
 
+// Counting phase of the update: per-cluster sizes (ws.cnt, counts) and the
+// segment starts; num_empty (nullable) receives the number of empty clusters.
+hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t *counts,
+                        int *num_empty, const UpdateScratch &ws, hipStream_t stream);
+
+// Second phase: stable grouping of rows by label and the float64 segmented
+// sums and means (old centre kept for an empty cluster). If shift_partial is
+// not NULL, mean_blocks(k, d) partial sums of (new - old)^2 are written there.
+hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const float *C_old,
+                                 int64_t n, int64_t k, int64_t d, float *C_new,
+                                 double *shift_partial, const UpdateScratch &ws,
+                                 hipStream_t stream);
+int64_t mean_blocks(int64_t k, int64_t d);
+
 // The whole update: counts, stable grouping of rows by label, segmented sums
 // in float64 and the mean (old centre kept for empty clusters).
 hipError_t launch_update(const float *X, const int64_t *labels, const float *C_old, int64_t n,
                          int64_t k, int64_t d, float *C_new, int64_t *counts,
                          const UpdateScratch &ws, hipStream_t stream);
+
+// Workspace sections of the empty-cluster relocation (device pointers).
+struct RelocScratch {
+    double *dist;                  // n: float64 distance of each sample to its centre
+    int *empty;                    // k: empty clusters in increasing index
+    unsigned long long *sort_key;  // reloc_sort_cap(n, k)
+    int *sort_idx;                 // reloc_sort_cap(n, k)
+    int *moves_src;                // min(n, k): moved samples
+    int *moves_dst;                // min(n, k): their new clusters
+    int *num_empty;                // 1: empty clusters after the assignment
+    int *n_moves;                  // 1: relocations made
+};
+
+// Size of the relocation sort buffers: the power of two >= min(n, k).
+int64_t reloc_sort_cap(int64_t n, int64_t k);
+
+// Relocation of the clusters left empty by the assignment (counts already
+// taken into ws.cnt with num_empty set): relabels the moved samples.
+hipError_t launch_relocate(const float *X, const float *C_old, int64_t *labels, int64_t n,
+                           int64_t k, int64_t d, const RelocScratch &rs, const UpdateScratch &ws,
+                           hipStream_t stream);
+
+// shift_out = sum of the first `blocks` partials (fixed order); converged =
+// (shift_out <= tol).
+hipError_t launch_shift(const double *partial, int64_t blocks, double tol, double *shift_out,
+                        int *converged, hipStream_t stream);
+
+// out = sum of min_dist[0 .. n) in float64 (fixed order).
+hipError_t launch_inertia(const float *min_dist, int64_t n, double *out, hipStream_t stream);
+
+hipError_t launch_copy_f32(float *dst, const float *src, int64_t count, hipStream_t stream);
+hipError_t launch_store_f64(double *dst, double v, hipStream_t stream);
 
 // Upper limits of the launch grids (blocks); checked by the C-ABI layer.
 int64_t assign_grid_blocks(int64_t n, int64_t k);

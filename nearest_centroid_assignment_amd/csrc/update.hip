@@ -76,15 +76,19 @@ __global__ __launch_bounds__(256) void tile_scan_kernel(int *__restrict__ tile_h
 }
 
 // A single block of 1024 threads: exclusive scan over the k cluster sizes.
+// If num_empty != NULL it receives the number of clusters of size 0.
 __global__ __launch_bounds__(1024) void cluster_scan_kernel(const int *__restrict__ cnt, int64_t k,
                                                             int *__restrict__ seg_start,
-                                                            int64_t *__restrict__ counts) {
+                                                            int64_t *__restrict__ counts,
+                                                            int *__restrict__ num_empty) {
     __shared__ int wave_tot[16];
+    __shared__ int wave_empty[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int carry = 0;
+    int carry = 0, empties = 0;
     for (int64_t base = 0; base < k; base += 1024) {
         const int64_t j = base + tid;
         const int v = j < k ? cnt[j] : 0;
+        empties += (j < k && v == 0);
         int incl = v;
         for (int off = 1; off < 64; off <<= 1) {
             const int up = __shfl_up(incl, off);
@@ -104,6 +108,16 @@ __global__ __launch_bounds__(1024) void cluster_scan_kernel(const int *__restric
         }
         carry += total;
         __syncthreads();  // wave_tot is rewritten by the next chunk
+    }
+    if (num_empty) {
+        for (int off = 32; off > 0; off >>= 1) empties += __shfl_xor(empties, off);
+        if (lane == 0) wave_empty[wave] = empties;
+        __syncthreads();
+        if (tid == 0) {
+            int t = 0;
+            for (int w = 0; w < 16; ++w) t += wave_empty[w];
+            *num_empty = t;
+        }
     }
 }
 
@@ -195,26 +209,36 @@ __device__ __forceinline__ void sum_rows(const float *__restrict__ X, const int 
     }
 }
 
+// Writes the new centre elements of this thread and adds their squared move
+// (new - old)^2 to `shift` (the old value is read before the new one is
+// written, so C_new may be C_old).
 __device__ __forceinline__ void write_mean(const float *C_old, float *C_new, int64_t j, int64_t d,
                                            int count, const int64_t (&col)[4],
-                                           const double (&s)[4]) {
+                                           const double (&s)[4], double &shift) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         if (col[e] < d) {
             const int64_t o = j * d + col[e];
-            C_new[o] = count > 0 ? (float)(s[e] / (double)count) : C_old[o];
+            const float old = C_old[o];
+            const float v = count > 0 ? (float)(s[e] / (double)count) : old;
+            C_new[o] = v;
+            const double diff = (double)v - (double)old;
+            shift += diff * diff;
         }
     }
 }
 
+// If shift_partial != NULL, block b also writes the sum over its elements of
+// (new - old)^2 to shift_partial[b] (fixed summation order).
 template <bool kVec>
 __global__ __launch_bounds__(256) void segment_mean_kernel(
     const float *__restrict__ X, const int *__restrict__ perm, const int *__restrict__ seg_start,
     const int *__restrict__ cnt, const float *C_old, int64_t k, int64_t d, int chunks,
-    float *C_new) {
+    float *C_new, double *__restrict__ shift_partial) {
     // C_old and C_new may be the same array: each element is read and written
     // by the same thread only, so they carry no __restrict__.
     __shared__ double part[3][kCols];
+    double shift = 0.0;
     const int64_t j0 = (int64_t)(blockIdx.x / (unsigned)chunks) * kClustersPerBlock;
     const int64_t c = blockIdx.x % (unsigned)chunks;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -233,7 +257,7 @@ __global__ __launch_bounds__(256) void segment_mean_kernel(
             if (count <= kSplitMin) {
                 double s[4] = {0.0, 0.0, 0.0, 0.0};
                 sum_rows<kVec>(X, perm + seg_start[j], 0, count, d, col, s);
-                write_mean(C_old, C_new, j, d, count, col, s);
+                write_mean(C_old, C_new, j, d, count, col, s, shift);
             }
         }
     }
@@ -256,9 +280,16 @@ __global__ __launch_bounds__(256) void segment_mean_kernel(
             for (int pw = 0; pw < 3; ++pw)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) s[e] += part[pw][lc[e]];
-            write_mean(C_old, C_new, j, d, count, col, s);
+            write_mean(C_old, C_new, j, d, count, col, s, shift);
         }
         __syncthreads();  // part is reused by the next big cluster
+    }
+    if (shift_partial) {
+        for (int off = 32; off > 0; off >>= 1) shift += __shfl_xor(shift, off);
+        if (lane == 0) part[0][wave] = shift;
+        __syncthreads();
+        if (threadIdx.x == 0)
+            shift_partial[blockIdx.x] = ((part[0][0] + part[0][1]) + part[0][2]) + part[0][3];
     }
 }
 
@@ -278,9 +309,8 @@ int64_t update_grid_blocks(int64_t n, int64_t k, int64_t d) {
     return a > b ? (a > c ? a : c) : (b > c ? b : c);
 }
 
-hipError_t launch_update(const float *X, const int64_t *labels, const float *C_old, int64_t n,
-                         int64_t k, int64_t d, float *C_new, int64_t *counts,
-                         const UpdateScratch &ws, hipStream_t stream) {
+hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t *counts,
+                        int *num_empty, const UpdateScratch &ws, hipStream_t stream) {
     const int64_t hist_words = k * ws.n_tiles;
     if (hist_words > 0) {
         fill_i32_kernel<<<grid_stride_blocks(hist_words), 256, 0, stream>>>(ws.tile_hist,
@@ -294,22 +324,39 @@ hipError_t launch_update(const float *X, const int64_t *labels, const float *C_o
         // n == 0: every cluster is empty.
         fill_i32_kernel<<<grid_stride_blocks(k), 256, 0, stream>>>(ws.cnt, k);
     }
-    cluster_scan_kernel<<<1, 1024, 0, stream>>>(ws.cnt, k, ws.seg_start, counts);
+    cluster_scan_kernel<<<1, 1024, 0, stream>>>(ws.cnt, k, ws.seg_start, counts, num_empty);
+    return hipGetLastError();
+}
+
+int64_t mean_blocks(int64_t k, int64_t d) { return cdiv(k, kClustersPerBlock) * cdiv(d, kCols); }
+
+hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const float *C_old,
+                                 int64_t n, int64_t k, int64_t d, float *C_new,
+                                 double *shift_partial, const UpdateScratch &ws,
+                                 hipStream_t stream) {
     if (n > 0)
         scatter_kernel<<<(unsigned)ws.n_tiles, 256, 0, stream>>>(labels, n, k, ws.n_tiles,
                                                                  ws.tile_hist, ws.seg_start,
                                                                  ws.perm);
     const int chunks = (int)cdiv(d, kCols);
-    const unsigned blocks = (unsigned)(cdiv(k, kClustersPerBlock) * chunks);
+    const unsigned blocks = (unsigned)mean_blocks(k, d);
     const bool vec = (d % 4 == 0) && ((uintptr_t)X % 16 == 0) && ((uintptr_t)C_old % 16 == 0) &&
                      ((uintptr_t)C_new % 16 == 0);
     if (vec)
-        segment_mean_kernel<true><<<blocks, 256, 0, stream>>>(X, ws.perm, ws.seg_start, ws.cnt,
-                                                              C_old, k, d, chunks, C_new);
+        segment_mean_kernel<true><<<blocks, 256, 0, stream>>>(
+            X, ws.perm, ws.seg_start, ws.cnt, C_old, k, d, chunks, C_new, shift_partial);
     else
-        segment_mean_kernel<false><<<blocks, 256, 0, stream>>>(X, ws.perm, ws.seg_start, ws.cnt,
-                                                               C_old, k, d, chunks, C_new);
+        segment_mean_kernel<false><<<blocks, 256, 0, stream>>>(
+            X, ws.perm, ws.seg_start, ws.cnt, C_old, k, d, chunks, C_new, shift_partial);
     return hipGetLastError();
+}
+
+hipError_t launch_update(const float *X, const int64_t *labels, const float *C_old, int64_t n,
+                         int64_t k, int64_t d, float *C_new, int64_t *counts,
+                         const UpdateScratch &ws, hipStream_t stream) {
+    hipError_t e = launch_count(labels, n, k, counts, nullptr, ws, stream);
+    if (e != hipSuccess) return e;
+    return launch_group_and_mean(X, labels, C_old, n, k, d, C_new, nullptr, ws, stream);
 }
 
 }  // namespace km

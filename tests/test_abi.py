@@ -39,7 +39,7 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"kmeans_workspace_bytes", "kmeans_assign", "kmeans_update",
-                          "kmeans_lloyd_step", "kmeans_status_string"}
+                          "kmeans_lloyd_step", "kmeans_fit", "kmeans_status_string"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -55,6 +55,7 @@ def test_workspace_bytes_rules(lib):
     ws = binding.kmeans_workspace_bytes
     assert ws(10, 0, 4, 0) == 0 and ws(10, 3, 0, 0) == 0 and ws(-1, 3, 4, 0) == 0
     assert ws(10, 3, 4, 9) == 0
+    assert ws(100, 10, 8, 3) >= ws(100, 10, 8, 2)
     assert ws(2**31, 3, 4, 0) == 0
     assert ws(0, 1, 1, 0) > 0 and ws(0, 1, 1, 1) > 0
     for cfg in CONFIGS.values():
@@ -146,9 +147,10 @@ def test_binding_rejects_cpu_tensors():
         binding.assign(X, X[:2].clone())
 
 
-def test_library_imports_no_allocation_or_sync():
-    """The library neither allocates device memory nor synchronises: none of
-    those HIP entry points is even imported."""
+def test_library_imports_no_allocation():
+    """The library never allocates or frees memory and never waits for the
+    whole device: none of those HIP entry points is even imported. (Only
+    kmeans_fit waits for its own stream, once per iteration.)"""
     import shutil
     import subprocess
 
@@ -158,6 +160,32 @@ def test_library_imports_no_allocation_or_sync():
     imported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     forbidden = [s for s in imported
                  if re.match(r"hip(Malloc|Free|HostAlloc|HostMalloc|ExtMalloc|MallocAsync|"
-                             r"DeviceSynchronize|StreamSynchronize|EventSynchronize|"
-                             r"HostRegister|Memcpy)", s)]
+                             r"DeviceSynchronize|HostRegister|Memset)", s)]
     assert not forbidden, forbidden
+
+
+
+@no_gpu
+def test_fit_validation(lib):
+    n, k, d = 100, 10, 8
+    wsb = binding.kmeans_workspace_bytes(n, k, d, 3)
+    INFO_P = GIB * (16 << 8)
+
+    def call(**kw):
+        a = dict(X=X_P, C=C_P, max_iter=10, tol=0.0, flags=1, C_out=CN_P, labels=LAB_P, md=MD_P,
+                 counts=CNT_P, info=INFO_P, ws=WS_P, wsb=wsb)
+        a.update(kw)
+        return lib.kmeans_fit(a["X"], a["C"], n, k, d, a["max_iter"], a["tol"], a["flags"],
+                              a["C_out"], a["labels"], a["md"], a["counts"], a["info"], a["ws"],
+                              a["wsb"], None)
+
+    assert call(max_iter=0) == SHAPE
+    assert call(tol=float("nan")) == SHAPE
+    assert call(flags=2) == OP
+    assert call(info=None) == NULL
+    assert call(C_out=None) == NULL
+    assert call(info=INFO_P + 4) == ALIGN
+    assert call(wsb=wsb - 1) == WORKSPACE
+    assert call(info=LAB_P) == ALIAS
+    assert call(C_out=C_P + 4) == ALIAS
+    assert call(C_out=X_P, C=X_P) == ALIAS  # in place, but on top of X
