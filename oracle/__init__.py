@@ -79,6 +79,10 @@ class Oracle:
         lib.oracle_update.restype = ctypes.c_int
         lib.oracle_update.argtypes = [_f32p, _i64p, _f32p, ctypes.c_int64, ctypes.c_int64,
                                       ctypes.c_int64, _f32p, _i64p, _f64p]
+        i64 = ctypes.c_int64
+        lib.oracle_kmeanspp.restype = None
+        lib.oracle_kmeanspp.argtypes = [_f32p, i64, i64, i64, i64, i64, _f64p, _i64p, _f64p,
+                                        _f64p, _i64p, _f64p]
         self.lib = lib
         self.path = path
 
@@ -125,6 +129,28 @@ class Oracle:
             raise ValueError("a label lies outside [0, k)")
         return C_new, counts, sums
 
+    def kmeanspp(self, X, k, first, trials, rand):
+        """Greedy k-means++ seeding with the given draws (see oracle.c).
+
+        rand: (k - 1, trials) uniforms in [0, 1). Returns (chosen indices,
+        final potential is not returned; centres = X[chosen]).
+        """
+        X = _f32(X)
+        n, d = X.shape
+        rand = np.ascontiguousarray(rand, dtype=np.float64).reshape(-1)
+        if not (1 <= k <= n) or trials < 1 or rand.size < (k - 1) * trials:
+            raise ValueError("bad k-means++ arguments")
+        chosen = np.empty(k, dtype=np.int64)
+        closest = np.empty(n, dtype=np.float64)
+        cand_d = np.empty(max(trials * n, 1), dtype=np.float64)
+        cand = np.empty(trials, dtype=np.int64)
+        pots = np.empty(trials, dtype=np.float64)
+        if rand.size == 0:
+            rand = np.zeros(1, dtype=np.float64)
+        self.lib.oracle_kmeanspp(X, n, d, k, int(first), trials, rand, chosen, closest, cand_d,
+                                 cand, pots)
+        return chosen
+
     def lloyd_step(self, X, C_old):
         """One Lloyd iteration: labels against C_old, then the mean update.
 
@@ -162,6 +188,17 @@ def lloyd_step(X, C_old):
     return default().lloyd_step(X, C_old)
 
 
+def kmeanspp(X, k, first, trials, rand):
+    return default().kmeanspp(X, k, first, trials, rand)
+
+
+def default_trials(k: int) -> int:
+    """The pages' trial count, 2 + log(k) (natural log, truncated)."""
+    import math
+
+    return 2 + int(math.log(k)) if k > 0 else 2
+
+
 def sq_norms(A) -> np.ndarray:
     """Row squared norms in float64."""
     A64 = np.asarray(A, dtype=np.float64)
@@ -177,7 +214,7 @@ def near_ties(X, C, labels, best, second, rtol: float = 1e-5) -> np.ndarray:
     return (np.asarray(second) - np.asarray(best)) <= rtol * scale
 
 
-for _name in ("num_threads", "assign", "update", "lloyd_step"):
+for _name in ("num_threads", "assign", "update", "lloyd_step", "kmeanspp"):
     globals()[_name].__doc__ = getattr(Oracle, _name).__doc__
 del _name
 

@@ -128,3 +128,75 @@ int oracle_update(const float *X, const int64_t *labels, const float *C_old,
     }
     return 0;
 }
+
+/* Squared distance between rows a and b of X in float64, difference form. */
+static double row_dist(const float *X, int64_t d, int64_t a, int64_t b) {
+    const float *x = X + a * d, *y = X + b * d;
+    double s = 0.0;
+#pragma omp simd reduction(+ : s)
+    for (int64_t t = 0; t < d; ++t) {
+        double diff = (double)x[t] - (double)y[t];
+        s += diff * diff;
+    }
+    return s;
+}
+
+/*
+ * oracle_kmeanspp: greedy k-means++ seeding ("004 - tile sizes ...", section
+ * k-means++: 2 + log(k) trials per centre, sample norms computed once in the
+ * pages' version; here the plain difference form is used).
+ *
+ *   chosen[0] = first. D(i) = squared distance of sample i to its nearest
+ *   chosen centre; pot = sum_i D(i). For every further centre c, each trial t
+ *   draws u = rand[(c-1)*trials + t] in [0, 1) and takes the first sample i
+ *   whose running sum D(0) + ... + D(i) reaches u * pot (the last sample if
+ *   none does). For each candidate, the potential sum_i min(D(i), dist(i,
+ *   candidate)) is computed; the candidate of smallest potential (lowest t on
+ *   ties) becomes centre c, and D and pot are updated to it.
+ *
+ * Scratch: closest (n doubles), cand_d (trials * n doubles), cand (trials),
+ * pots (trials). All sums are sequential in sample order.
+ */
+void oracle_kmeanspp(const float *X, int64_t n, int64_t d, int64_t k, int64_t first,
+                     int64_t trials, const double *rand, int64_t *chosen, double *closest,
+                     double *cand_d, int64_t *cand, double *pots) {
+    chosen[0] = first;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) closest[i] = row_dist(X, d, i, first);
+    double pot = 0.0;
+    for (int64_t i = 0; i < n; ++i) pot += closest[i];
+
+    for (int64_t c = 1; c < k; ++c) {
+        for (int64_t t = 0; t < trials; ++t) {
+            const double target = rand[(c - 1) * trials + t] * pot;
+            double acc = 0.0;
+            int64_t idx = n - 1;
+            for (int64_t i = 0; i < n; ++i) {
+                acc += closest[i];
+                if (acc >= target) {
+                    idx = i;
+                    break;
+                }
+            }
+            cand[t] = idx;
+        }
+        for (int64_t t = 0; t < trials; ++t) {
+            double *dt = cand_d + t * n;
+#pragma omp parallel for schedule(static)
+            for (int64_t i = 0; i < n; ++i) {
+                const double di = row_dist(X, d, i, cand[t]);
+                dt[i] = di < closest[i] ? di : closest[i];
+            }
+            double p = 0.0;
+            for (int64_t i = 0; i < n; ++i) p += dt[i];
+            pots[t] = p;
+        }
+        int64_t best = 0;
+        for (int64_t t = 1; t < trials; ++t)
+            if (pots[t] < pots[best]) best = t;
+        chosen[c] = cand[best];
+        pot = pots[best];
+        const double *db = cand_d + best * n;
+        for (int64_t i = 0; i < n; ++i) closest[i] = db[i];
+    }
+}

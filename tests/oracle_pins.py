@@ -26,6 +26,11 @@ What pins what:
   sizes ...", section Schedules added) leaves the argmin unchanged.
 * ``pin_invariants``        - translation invariance, centroid permutation,
   k = 1, C = X, duplicate centroids, Lloyd monotonicity.
+* ``pin_kmeanspp_*``        - k-means++ seeding ("004 - tile sizes ...", section
+  k-means++): a hand-worked draw; with one trial, over evenly spaced draws each
+  sample is taken for a fraction D(i)/pot of them (D^2 sampling); each centre
+  is the trial candidate of least potential (recomputed with numpy) and the
+  potential never rises.
 """
 from __future__ import annotations
 
@@ -221,3 +226,67 @@ def pin_invariants(orc, seed: int = 4):
 
 ALL_PINS = [pin_exhaustive_small, pin_exhaustive_grid, pin_update_exact,
             pin_gram_identity, pin_invariants]
+
+
+# ------------------------------------------------------------------ k-means++
+
+
+def _dist64(X, a, b):
+    diff = X[a].astype(np.float64) - X[b].astype(np.float64)
+    return float(diff @ diff)
+
+
+def pin_kmeanspp_hand(orc):
+    """1-D samples 0, 1, 3 with the first centre at 0: D = 0, 1, 9, pot = 10.
+    u = 0.05 -> target 0.5 -> sample 1 (running sums 0, 1, 10); u = 0.5 ->
+    target 5 -> sample 2. Worked by hand from the definition."""
+    X = np.array([[0], [1], [3]], dtype=np.float32)
+    assert orc.kmeanspp(X, 2, 0, 1, np.array([[0.05]])).tolist() == [0, 1]
+    assert orc.kmeanspp(X, 2, 0, 1, np.array([[0.5]])).tolist() == [0, 2]
+    # Two trials: candidates 1 and 2; potentials min(D, d(., 1)) = 0+0+4 = 4 and
+    # min(D, d(., 2)) = 0+1+0 = 1, so the second wins.
+    assert orc.kmeanspp(X, 2, 0, 2, np.array([[0.05, 0.5]])).tolist() == [0, 2]
+
+
+def pin_kmeanspp_d2_quadrature(orc, seed: int = 6):
+    """With one trial, D^2 sampling: over u = (j + 1/2) / N the second centre is
+    sample i for a fraction D(i) / pot of the draws (to within 1/N each)."""
+    rng = np.random.default_rng(seed)
+    X = rng.integers(-5, 6, size=(9, 2)).astype(np.float32)
+    first = 4
+    D = np.array([_dist64(X, i, first) for i in range(len(X))])
+    N = 2000
+    hits = np.zeros(len(X))
+    for j in range(N):
+        c = orc.kmeanspp(X, 2, first, 1, np.array([[(j + 0.5) / N]]))
+        hits[c[1]] += 1
+    assert np.all(np.abs(hits / N - D / D.sum()) <= 1.0 / N + 1e-12)
+
+
+def pin_kmeanspp_greedy(orc, seed: int = 7):
+    """Each chosen centre is, among its trials' candidates (recomputed here
+    from the same draws with numpy), the one of smallest potential, and the
+    potential never rises."""
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((300, 5)).astype(np.float32)
+    k, trials = 12, 4
+    u = rng.random((k - 1, trials))
+    chosen = orc.kmeanspp(X, k, 17, trials, u)
+    X64 = X.astype(np.float64)
+    D = ((X64 - X64[17]) ** 2).sum(1)
+    assert chosen[0] == 17
+    prev_pot = D.sum()
+    for c in range(1, k):
+        cum = np.cumsum(D)
+        cands = [min(int(np.searchsorted(cum, u[c - 1, t] * D.sum(), side="left")), len(X) - 1)
+                 for t in range(trials)]
+        pots = [np.minimum(D, ((X64 - X64[i]) ** 2).sum(1)).sum() for i in cands]
+        best = int(np.argmin(pots))
+        assert chosen[c] == cands[best]
+        D = np.minimum(D, ((X64 - X64[chosen[c]]) ** 2).sum(1))
+        assert D.sum() <= prev_pot
+        prev_pot = D.sum()
+    assert len(set(chosen.tolist())) == k  # distinct points give distinct centres
+
+
+ALL_PINS += [pin_kmeanspp_hand, pin_kmeanspp_d2_quadrature, pin_kmeanspp_greedy]

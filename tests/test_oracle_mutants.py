@@ -15,7 +15,8 @@ from tests import oracle_pins as pins
 MUTANTS = [
     ("tie_to_highest_index", "if (s < b1) {", "if (s <= b1) {"),
     ("wrong_sign", "(double)x[t] - (double)c[t]", "(double)x[t] + (double)c[t]"),
-    ("dropped_square", "s += diff * diff;", "s += diff;"),
+    ("dropped_square", "double diff = (double)x[t] - (double)c[t];\n                s += diff * diff;",
+     "double diff = (double)x[t] - (double)c[t];\n                s += diff;"),
     ("centroid_row_index", "const float *c = C + j * d;", "const float *c = C + j;"),
     ("sample_row_index", "const float *x = X + i * d;\n        double b1", "const float *x = X + i;\n        double b1"),
     ("dropped_last_term", "for (int64_t t = 0; t < d; ++t) {\n                double diff",
@@ -27,6 +28,11 @@ MUTANTS = [
     ("empty_cluster_zeroed", "C_new[j * d + t] = C_old[j * d + t];", "C_new[j * d + t] = 0.0f;"),
     ("update_transposed", "const float *x = X + i * d;\n            double *s", "const float *x = X + i;\n            double *s"),
     ("sum_in_float", "s[t] += (double)x[t];", "s[t] = (float)(s[t] + x[t]);"),
+    ("pp_search_strict", "if (acc >= target) {", "if (acc > target + 1.0) {"),
+    ("pp_highest_potential", "if (pots[t] < pots[best]) best = t;", "if (pots[t] > pots[best]) best = t;"),
+    ("pp_no_min", "dt[i] = di < closest[i] ? di : closest[i];", "dt[i] = di;"),
+    ("pp_stale_pot", "pot = pots[best];", "pot = pot;"),
+    ("pp_wrong_row", "const float *x = X + a * d, *y = X + b * d;", "const float *x = X + a * d, *y = X + b;"),
 ]
 
 
