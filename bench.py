@@ -28,6 +28,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused assign TFLOP/s (2nkd/t) + Lloyd iteration ms, 65536×4096×16384 fp32"
 MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak (published)
+# The pages' k-means++ time on an NVIDIA L4 at 65536 x 1024 x 8192 (context).
+PAGES_KMEANSPP_MS = 10300.0
 # The pages' Lloyd-iteration times on an NVIDIA L4, per workload (context).
 PAGES_LLOYD_MS = {"feature_heavy": 1700.0, "centroid_heavy": 3853.0}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "assign_tile_feature_heavy_traffic.json")
@@ -48,9 +50,11 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["lloyd", "fit"], default="lloyd",
+    ap.add_argument("--mode", choices=["lloyd", "fit", "kmeanspp"], default="lloyd",
                     help="lloyd: one Lloyd step per timed step (default); fit: kmeans_fit "
-                         "with relocation running exactly --steps iterations")
+                         "with relocation running exactly --steps iterations; kmeanspp: greedy "
+                         "k-means++ seeding of k centres (use --config kmeanspp for the pages' "
+                         "65536 x 1024 x 8192 shape)")
     return ap.parse_args()
 
 
@@ -169,6 +173,64 @@ def bench_fit(args, cfg, Xg, Cg, labels, md, counts, stream) -> int:
     return 0
 
 
+def bench_kmeanspp(args, cfg, X, Xg, stream) -> int:
+    """Greedy k-means++ seeding of cfg.k centres (2 + log(k) trials) with
+    seeded draws; --steps timed runs after --warmup."""
+    import torch
+
+    import oracle
+    from nearest_centroid_assignment_amd import binding, datagen
+
+    n, k, d = cfg.n, cfg.k, cfg.d
+    trials = oracle.default_trials(k)
+    first, rand = datagen.make_seeding_draws(n, k, trials)
+    rg = torch.from_numpy(rand.reshape(-1).copy()).to(Xg.device)
+    centres = torch.empty((k, d), dtype=torch.float32, device=Xg.device)
+    chosen = torch.empty(k, dtype=torch.int64, device=Xg.device)
+    wsb = binding.kmeans_workspace_bytes(n, k, d, binding.KM_OP_KMEANSPP)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=Xg.device)
+
+    def run():
+        binding.kmeans_plusplus(Xg, k, first, trials, rg, centres, chosen, workspace=ws,
+                                stream=stream)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = sorted(times)[len(times) // 2]
+    # Bytes the distance kernels must read: X once per centre.
+    x_bytes = 4.0 * n * d * k
+    result = {
+        "metric": "k-means++ seeding ms (greedy, 2 + log(k) trials)",
+        "value": round(ms, 3),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": (round(PAGES_KMEANSPP_MS / ms, 2)
+                        if (n, k, d) == (65536, 1024, 8192) else None),
+        "dtype": "f64 distances on f32 samples",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} n={n} k={k} d={d} float32 Gaussian blobs, seed 0",
+                   "n": n, "k": k, "d": d, "trials": trials},
+        "x_read_gbps": round(x_bytes / (ms * 1e-3) / 1e9, 1),
+        "workspace_bytes": wsb,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -208,6 +270,8 @@ def main() -> int:
 
     if args.mode == "fit":
         return bench_fit(args, cfg, Xg, Cg, labels, md, counts, stream)
+    if args.mode == "kmeanspp":
+        return bench_kmeanspp(args, cfg, X, Xg, stream)
 
     def assign_only():
         binding.kmeans_assign(Xg, Cg, labels, None, workspace=ws, stream=stream)

@@ -69,7 +69,7 @@ typedef enum {
 } km_status;
 
 /* Op codes for kmeans_workspace_bytes. */
-enum { KM_OP_ASSIGN = 0, KM_OP_UPDATE = 1, KM_OP_LLOYD = 2, KM_OP_FIT = 3 };
+enum { KM_OP_ASSIGN = 0, KM_OP_UPDATE = 1, KM_OP_LLOYD = 2, KM_OP_FIT = 3, KM_OP_KMEANSPP = 4 };
 
 /* Flags for kmeans_fit. */
 enum { KM_FIT_RELOCATE_EMPTY = 1 };
@@ -152,6 +152,30 @@ int kmeans_fit(const float *X, const float *C_init, int64_t n, int64_t k, int64_
                int64_t max_iter, double tol, int flags,
                float *C_out, int64_t *labels, float *min_dist, int64_t *counts, double *info,
                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Greedy k-means++ seeding ("004 ...", section k-means++: 2 + log(k) trials
+ * per centre). chosen[0] = first. With D(i) the squared distance of sample i
+ * to its nearest chosen centre and pot = sum_i D(i), each further centre c
+ * draws `trials` candidates: trial t takes the first sample whose running
+ * sum of D reaches rand[(c - 1) * trials + t] * pot (the last sample if none
+ * does); the candidate with the smallest potential sum_i min(D(i),
+ * |x_i - x_cand|^2) (lowest trial on ties) becomes centre c. Distances are
+ * float64 in difference form. The random draws are an input so that a run
+ * is reproducible.
+ *   X        (n, d) float32 samples.
+ *   k        number of centres, 1 <= k <= n.
+ *   first    index of the first centre, 0 <= first < n.
+ *   trials   candidates per centre, 1 <= trials <= 16.
+ *   rand     device array of (k - 1) * trials float64 uniforms in [0, 1)
+ *            (may be NULL when k == 1).
+ *   centres  (k, d) float32 output: the chosen rows of X.
+ *   chosen   (k,) int64 output: their indices.
+ * Asynchronous like kmeans_assign; 2 kernel launches per centre.
+ */
+int kmeans_plusplus(const float *X, int64_t n, int64_t d, int64_t k, int64_t first,
+                    int64_t trials, const double *rand, float *centres, int64_t *chosen,
+                    void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, NUL-terminated description of a km_status value (never NULL). */
 const char *kmeans_status_string(int status);

@@ -6,9 +6,10 @@ step of the computation runs in the library's HIP kernels. There is no CPU
 fallback: if the library is missing, loading fails with an error.
 
 The functions ``kmeans_assign``, ``kmeans_update``, ``kmeans_lloyd_step``,
-``kmeans_fit``, ``kmeans_workspace_bytes`` and ``kmeans_status_string`` mirror
-the C entry points of the same names; ``assign``, ``update``, ``lloyd_step``
-and ``fit`` also allocate the outputs.
+``kmeans_fit``, ``kmeans_plusplus``, ``kmeans_workspace_bytes`` and
+``kmeans_status_string`` mirror the C entry points of the same names;
+``assign``, ``update``, ``lloyd_step``, ``fit`` and ``plusplus`` also allocate
+the outputs.
 """
 from __future__ import annotations
 
@@ -20,7 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkmeans_mi355x.so")
 
 KM_OK = 0
-KM_OP_ASSIGN, KM_OP_UPDATE, KM_OP_LLOYD, KM_OP_FIT = 0, 1, 2, 3
+KM_OP_ASSIGN, KM_OP_UPDATE, KM_OP_LLOYD, KM_OP_FIT, KM_OP_KMEANSPP = 0, 1, 2, 3, 4
 KM_FIT_RELOCATE_EMPTY = 1
 STATUS_NAMES = {
     0: "KM_OK",
@@ -68,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.kmeans_update.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
         L.kmeans_lloyd_step.restype = ctypes.c_int
         L.kmeans_lloyd_step.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+        L.kmeans_plusplus.restype = ctypes.c_int
+        L.kmeans_plusplus.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, sz, vp]
         L.kmeans_fit.restype = ctypes.c_int
         L.kmeans_fit.argtypes = [vp, vp, i64, i64, i64, i64, ctypes.c_double, ctypes.c_int,
                                  vp, vp, vp, vp, vp, vp, sz, vp]
@@ -191,6 +194,19 @@ def kmeans_fit(X, C_init, max_iter, tol, flags, C_out, labels, min_dist, counts,
     _check(rc, "kmeans_fit")
 
 
+def kmeans_plusplus(X, k, first, trials, rand, centres, chosen, workspace=None, stream=None):
+    """Enqueue greedy k-means++ seeding with the given uniforms."""
+    torch = _torch()
+    n, d = X.shape
+    args = (_ptr(X, torch.float32, (n, d), "X"), n, d, int(k), int(first), int(trials),
+            _ptr(rand, torch.float64, (max(k - 1, 0) * trials,), "rand") if k > 1 else None,
+            _ptr(centres, torch.float32, (k, d), "centres"), _ptr(chosen, torch.int64, (k,), "chosen"))
+    workspace = _workspace(workspace, kmeans_workspace_bytes(n, k, d, KM_OP_KMEANSPP), X.device)
+    rc = lib().kmeans_plusplus(*args, workspace.data_ptr(), workspace.numel(),
+                               _stream(stream, X.device))
+    _check(rc, "kmeans_plusplus")
+
+
 # ------------------------------------------------------ allocating wrappers
 
 
@@ -242,3 +258,15 @@ def fit(X, C_init, max_iter: int = 300, tol: float = 0.0, relocate_empty: bool =
     n_iter, inertia, shift = info.cpu().tolist()
     return {"centres": C_out, "labels": labels, "min_dist": md, "counts": counts,
             "n_iter": int(n_iter), "inertia": inertia, "shift": shift}
+
+
+def plusplus(X, k, first, trials, rand, stream=None):
+    """Returns (centres, chosen) of greedy k-means++ seeding as GPU tensors;
+    rand is a (k - 1, trials) or flat float64 GPU tensor of uniforms."""
+    torch = _torch()
+    d = X.shape[1]
+    centres = torch.empty((k, d), dtype=torch.float32, device=X.device)
+    chosen = torch.empty(k, dtype=torch.int64, device=X.device)
+    r = rand.reshape(-1) if rand is not None and k > 1 else None
+    kmeans_plusplus(X, k, first, trials, r, centres, chosen, stream=stream)
+    return centres, chosen

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libkmeans_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["api.hip", "assign.hip", "update.hip", "fit.hip"]
+SOURCES = ["api.hip", "assign.hip", "update.hip", "fit.hip", "kmeanspp.hip"]
 # Calibration kernels for the measurements (copy, MFMA loop): a separate library.
 CALIB_NAME = "libkm_calib.so"
 CALIB_PATH = os.path.join(HERE, CALIB_NAME)

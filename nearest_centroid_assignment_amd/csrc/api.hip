@@ -22,6 +22,9 @@ struct Layout {
     // kmeans_fit only
     size_t md = 0, dist = 0, empty = 0, sort_key = 0, sort_idx = 0, moves_src = 0, moves_dst = 0,
            shift_partial = 0, scalars = 0;
+    // kmeans_plusplus only
+    size_t pp_buf_a = 0, pp_buf_b = 0, pp_parts_a = 0, pp_parts_b = 0, pp_cand_a = 0,
+           pp_cand_b = 0, pp_state = 0;
     size_t total = 0;
 };
 
@@ -66,6 +69,24 @@ Layout layout(int64_t n, int64_t k, int64_t d, int op) {
         off += round_up((size_t)km::mean_blocks(k, d) * sizeof(double));
         L.scalars = off;  // num_empty, n_moves, converged
         off += round_up(4 * sizeof(int));
+    }
+    if (op == KM_OP_KMEANSPP) {
+        const size_t t = (size_t)km::pp_max_trials();
+        const size_t nb = (size_t)km::pp_blocks(n);
+        L.pp_buf_a = off;
+        off += round_up(t * (size_t)n * sizeof(double));
+        L.pp_buf_b = off;
+        off += round_up(t * (size_t)n * sizeof(double));
+        L.pp_parts_a = off;
+        off += round_up(t * nb * sizeof(double));
+        L.pp_parts_b = off;
+        off += round_up(t * nb * sizeof(double));
+        L.pp_cand_a = off;
+        off += round_up(t * sizeof(int64_t));
+        L.pp_cand_b = off;
+        off += round_up(t * sizeof(int64_t));
+        L.pp_state = off;
+        off += round_up(km::pp_state_bytes());
     }
     L.total = off + kAlign;
     return L;
@@ -148,8 +169,7 @@ extern "C" {
 
 size_t kmeans_workspace_bytes(int64_t n, int64_t k, int64_t d, int op) {
     if (!shape_ok(n, k, d)) return 0;
-    if (op != KM_OP_ASSIGN && op != KM_OP_UPDATE && op != KM_OP_LLOYD && op != KM_OP_FIT)
-        return 0;
+    if (op < KM_OP_ASSIGN || op > KM_OP_KMEANSPP) return 0;
     return layout(n, k, d, op).total;
 }
 
@@ -297,6 +317,34 @@ int kmeans_fit(const float *X, const float *C_init, int64_t n, int64_t k, int64_
     if (e == hipSuccess) e = km::launch_count(labels, n, k, counts, nullptr, ws, s);
     if (e == hipSuccess) e = km::launch_inertia(md, n, info + 1, s);
     if (e == hipSuccess) e = km::launch_store_f64(info, (double)n_iter, s);
+    return e == hipSuccess ? KM_OK : KM_ERR_HIP;
+}
+
+int kmeans_plusplus(const float *X, int64_t n, int64_t d, int64_t k, int64_t first,
+                    int64_t trials, const double *rand, float *centres, int64_t *chosen,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    if (!shape_ok(n, k, d) || n < 1 || k > n || first < 0 || first >= n || trials < 1 ||
+        trials > km::pp_max_trials() || km::pp_blocks(n) * 1024 > kMaxGridThreads)
+        return KM_ERR_SHAPE;
+    if (!X || !centres || !chosen || !workspace || (k > 1 && !rand)) return KM_ERR_NULL;
+    if (!aligned(X, 4) || !aligned(rand, 8) || !aligned(centres, 4) || !aligned(chosen, 8))
+        return KM_ERR_ALIGN;
+    const Layout L = layout(n, k, d, KM_OP_KMEANSPP);
+    if (workspace_bytes < L.total) return KM_ERR_WORKSPACE;
+    const Out outs[] = {{centres, k * d, 4}, {chosen, k, 8}, {workspace, (int64_t)workspace_bytes, 1}};
+    const Out ins[] = {{X, n * d, 4}, {rand, k > 1 ? (k - 1) * trials : 0, 8}};
+    if (int rc = check_alias(outs, 3, ins, 2, -1, -1)) return rc;
+    char *base = ws_base(workspace);
+    km::PPScratch ws;
+    ws.buf_a = (double *)(base + L.pp_buf_a);
+    ws.buf_b = (double *)(base + L.pp_buf_b);
+    ws.parts_a = (double *)(base + L.pp_parts_a);
+    ws.parts_b = (double *)(base + L.pp_parts_b);
+    ws.cand_a = (int64_t *)(base + L.pp_cand_a);
+    ws.cand_b = (int64_t *)(base + L.pp_cand_b);
+    ws.state = base + L.pp_state;
+    const hipError_t e = km::launch_kmeanspp(X, n, d, k, first, (int)trials, rand, centres, chosen,
+                                             ws, (hipStream_t)stream);
     return e == hipSuccess ? KM_OK : KM_ERR_HIP;
 }
 

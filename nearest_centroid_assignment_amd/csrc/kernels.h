@@ -90,6 +90,23 @@ hipError_t launch_inertia(const float *min_dist, int64_t n, double *out, hipStre
 hipError_t launch_copy_f32(float *dst, const float *src, int64_t count, hipStream_t stream);
 hipError_t launch_store_f64(double *dst, double v, hipStream_t stream);
 
+// Workspace sections of the k-means++ seeding (device pointers).
+struct PPScratch {
+    double *buf_a, *buf_b;      // trials * n: D of each candidate (alternating)
+    double *parts_a, *parts_b;  // trials * pp_blocks(n): per-block sums of those
+    int64_t *cand_a, *cand_b;   // trials: candidate sample indices (alternating)
+    void *state;                // pp_state_bytes(): winner and its potential
+};
+int64_t pp_blocks(int64_t n);
+int pp_max_trials();
+size_t pp_state_bytes();
+
+// Greedy k-means++ seeding: chosen[0] = first, then k - 1 centres drawn with
+// rand ((k - 1) * trials uniforms); centres[c] = X[chosen[c]].
+hipError_t launch_kmeanspp(const float *X, int64_t n, int64_t d, int64_t k, int64_t first,
+                           int trials, const double *rand, float *centres, int64_t *chosen,
+                           const PPScratch &ws, hipStream_t stream);
+
 // Upper limits of the launch grids (blocks); checked by the C-ABI layer.
 int64_t assign_grid_blocks(int64_t n, int64_t k);
 int64_t update_grid_blocks(int64_t n, int64_t k, int64_t d);

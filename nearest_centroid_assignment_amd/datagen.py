@@ -38,6 +38,7 @@ __all__ = [
     "make",
     "make_blobs",
     "make_integer",
+    "make_seeding_draws",
     "with_far_centroid",
 ]
 
@@ -78,6 +79,8 @@ CONFIGS: dict[str, Config] = {
         Config("sample_heavy", 131072, 8192, 8192, kb=None, sigma_c=0.0, sigma=1.0),
         Config("feature_heavy", 65536, 4096, 16384, kb=4096, sigma_c=1.0, sigma=1.0),
         Config("centroid_heavy", 65536, 16384, 8192, kb=16384, sigma_c=1.0, sigma=1.0),
+        # The k-means++ timing shape of the tile-tradeoff page (k = centres to seed).
+        Config("kmeanspp", 65536, 1024, 8192, kb=1024, sigma_c=1.0, sigma=1.0),
     )
 }
 
@@ -142,6 +145,15 @@ def make(config: str | Config, seed: int = 0) -> tuple[np.ndarray, np.ndarray]:
     """Draw (X, C) for a named workload (a key of ``CONFIGS``)."""
     cfg = CONFIGS[config] if isinstance(config, str) else config
     return make_blobs(cfg.n, cfg.k, cfg.d, cfg.kb, cfg.sigma_c, cfg.sigma, seed)
+
+
+def make_seeding_draws(n: int, k: int, trials: int, seed: int = 0) -> tuple[int, np.ndarray]:
+    """Random draws consumed by k-means++ seeding: the first centre's index
+    (uniform in [0, n)) and (k - 1, trials) float64 uniforms in [0, 1), from
+    ``default_rng([seed, 3])`` in that order."""
+    rng = np.random.default_rng([seed, 3])
+    first = int(rng.integers(0, n))
+    return first, rng.random((max(k - 1, 0), trials))
 
 
 def make_integer(n: int, k: int, d: int, lo: int = -8, hi: int = 8,

@@ -39,7 +39,8 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"kmeans_workspace_bytes", "kmeans_assign", "kmeans_update",
-                          "kmeans_lloyd_step", "kmeans_fit", "kmeans_status_string"}
+                          "kmeans_lloyd_step", "kmeans_fit", "kmeans_plusplus",
+                          "kmeans_status_string"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -189,3 +190,28 @@ def test_fit_validation(lib):
     assert call(info=LAB_P) == ALIAS
     assert call(C_out=C_P + 4) == ALIAS
     assert call(C_out=X_P, C=X_P) == ALIAS  # in place, but on top of X
+
+
+
+@no_gpu
+def test_plusplus_validation(lib):
+    n, k, d, T = 100, 10, 8, 4
+    wsb = binding.kmeans_workspace_bytes(n, k, d, 4)
+    R_P = GIB * (16 << 9)
+
+    def call(**kw):
+        a = dict(X=X_P, n=n, k=k, first=3, trials=T, rand=R_P, centres=CN_P, chosen=LAB_P,
+                 ws=WS_P, wsb=wsb)
+        a.update(kw)
+        return lib.kmeans_plusplus(a["X"], a["n"], d, a["k"], a["first"], a["trials"], a["rand"],
+                                   a["centres"], a["chosen"], a["ws"], a["wsb"], None)
+
+    assert call(k=n + 1) == SHAPE
+    assert call(first=n) == SHAPE and call(first=-1) == SHAPE
+    assert call(trials=0) == SHAPE and call(trials=17) == SHAPE
+    assert call(rand=None) == NULL
+    assert call(rand=R_P + 4) == ALIGN
+    assert call(wsb=wsb - 1) == WORKSPACE
+    assert call(chosen=X_P + 8) == ALIAS
+    assert call(centres=R_P) == ALIAS
+    assert binding.kmeans_workspace_bytes(n, k, d, 5) == 0

@@ -1,0 +1,86 @@
+"""GPU k-means++ seeding against the float64 oracle with the same draws.
+
+Integer-valued samples make every distance, running sum and potential an
+exact integer, so the GPU must then pick exactly the oracle's centres. On
+real-valued data both sides compute float64 sums in different orders, which
+can only matter if a draw lands within ~1e-15 of a boundary; the chosen
+indices are compared exactly there too.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from nearest_centroid_assignment_amd import datagen
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def gpu_pp(X, k, first, trials, rand):
+    import torch
+
+    from nearest_centroid_assignment_amd import binding
+
+    r = gu.to_gpu(np.ascontiguousarray(rand, dtype=np.float64)) if k > 1 else None
+    centres, chosen = binding.plusplus(gu.to_gpu(X), k, first, trials, r)
+    torch.cuda.synchronize()
+    return centres.cpu().numpy(), chosen.cpu().numpy()
+
+
+def test_pp_hand_example():
+    gu.announce("kmeans++ hand example")
+    X = np.array([[0], [1], [3]], dtype=np.float32)
+    for u, want in ((0.05, 1), (0.5, 2)):
+        C, ch = gpu_pp(X, 2, 0, 1, np.array([[u]]))
+        assert ch.tolist() == [0, want] and C.ravel().tolist() == [0.0, float(X[want, 0])]
+    _, ch = gpu_pp(X, 2, 0, 2, np.array([[0.05, 0.5]]))
+    assert ch.tolist() == [0, 2]
+
+
+@pytest.mark.parametrize("n,k,d,trials", [(500, 40, 7, 5), (3000, 64, 33, 6), (257, 257, 3, 1),
+                                          (2048, 100, 1030, 16), (70, 1, 5, 3)])
+def test_pp_integer_exact(n, k, d, trials):
+    gu.announce(f"kmeans++ integer {n}x{k}x{d} trials {trials}")
+    X, _ = datagen.make_integer(n, 1, d, seed=n + d)
+    first, rand = datagen.make_seeding_draws(n, k, trials, seed=k)
+    C, ch = gpu_pp(X, k, first, trials, rand)
+    want = oracle.kmeanspp(X, k, first, trials, rand)
+    assert np.array_equal(ch, want)
+    assert np.array_equal(C, X[want])
+
+
+@pytest.mark.parametrize("name", ["tiny", "probe"])
+def test_pp_blobs(name):
+    gu.announce(f"kmeans++ blobs {name}")
+    cfg = datagen.CONFIGS[name]
+    X, _ = datagen.make(name)
+    trials = oracle.default_trials(cfg.k)
+    first, rand = datagen.make_seeding_draws(cfg.n, cfg.k, trials)
+    C, ch = gpu_pp(X, cfg.k, first, trials, rand)
+    want = oracle.kmeanspp(X, cfg.k, first, trials, rand)
+    assert np.array_equal(ch, want)
+
+
+def test_pp_pages_shape_prefix():
+    """65536 x 1024 x 8192 (the pages' k-means++ timing shape): the GPU seeds
+    all 1024 centres; seeding is sequential, so its first 12 centres must be
+    the oracle's 12 centres from the same draws."""
+    gu.announce("kmeans++ 65536x1024x8192: generating")
+    cfg = datagen.CONFIGS["kmeanspp"]
+    X, _ = datagen.make(cfg)
+    trials = oracle.default_trials(cfg.k)
+    first, rand = datagen.make_seeding_draws(cfg.n, cfg.k, trials)
+    gu.announce("kmeans++ 65536x1024x8192: GPU seeding")
+    C, ch = gpu_pp(X, cfg.k, first, trials, rand)
+    assert len(set(ch.tolist())) == cfg.k
+    gu.announce("kmeans++ 65536x1024x8192: oracle prefix of 12 centres")
+    want = oracle.kmeanspp(X, 12, first, trials, rand[:11])
+    assert np.array_equal(ch[:12], want)
+    assert np.array_equal(C[:12], X[want])
