@@ -324,7 +324,7 @@ int kmeans_plusplus(const float *X, int64_t n, int64_t d, int64_t k, int64_t fir
                     int64_t trials, const double *rand, float *centres, int64_t *chosen,
                     void *workspace, size_t workspace_bytes, void *stream) {
     if (!shape_ok(n, k, d) || n < 1 || k > n || first < 0 || first >= n || trials < 1 ||
-        trials > km::pp_max_trials() || km::pp_blocks(n) * 1024 > kMaxGridThreads)
+        trials > km::pp_max_trials() || km::pp_blocks(n) * km::pp_block_threads() > kMaxGridThreads)
         return KM_ERR_SHAPE;
     if (!X || !centres || !chosen || !workspace || (k > 1 && !rand)) return KM_ERR_NULL;
     if (!aligned(X, 4) || !aligned(rand, 8) || !aligned(centres, 4) || !aligned(chosen, 8))

@@ -99,6 +99,7 @@ struct PPScratch {
 };
 int64_t pp_blocks(int64_t n);
 int pp_max_trials();
+int pp_block_threads();  // threads per block of the distance kernel
 size_t pp_state_bytes();
 
 // Greedy k-means++ seeding: chosen[0] = first, then k - 1 centres drawn with

@@ -19,10 +19,10 @@
 //                     block each draw falls in, one wave per draw walks its
 //                     rows
 //   pp_dist_kernel    every sample against all candidates: candidate rows
-//                     staged in LDS 1024 features at a time (double buffered,
+//                     staged in LDS 256 features at a time (double buffered,
 //                     the next stage's loads in flight during the current
-//                     one), one wave per sample, float64 sums; min with D;
-//                     per-block partials
+//                     one), a wave on 1, 2 or 4 samples at once, float64
+//                     sums; min with D; per-block partials
 // Buffers of D and partials alternate between centres (A <-> B).
 #include "kernels.h"
 
@@ -30,7 +30,7 @@ namespace km {
 namespace {
 
 constexpr int kPPMaxTrials = 16;
-constexpr int kPPChunk = 1024;      // features per LDS stage
+constexpr int kPPChunk = 256;       // features per LDS stage: 4 per lane
 constexpr int kPPRowsPerBlock = 64; // samples per block of pp_dist_kernel
 
 struct PPState {
@@ -38,115 +38,212 @@ struct PPState {
     int best;    // its trial index
 };
 
-// Samples [b * kPPRowsPerBlock, ...) against the `trials` candidate rows.
-// closest_prev = D of the previous centre set (NULL: +inf, the first centre).
+// X[i, f .. f+3] with zeros for i >= n or features >= d. kVec: X is 16-byte
+// aligned and d % 4 == 0, so the four values are one 16-byte load.
+template <bool kVec>
+__device__ __forceinline__ float4 load_row4(const float *__restrict__ X, int64_t n, int64_t d,
+                                            int64_t i, int64_t f) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i >= n) return v;
+    const float *p = X + i * d + f;
+    if (kVec) {
+        if (f < d) v = *(const float4 *)p;
+    } else {
+        if (f < d) v.x = p[0];
+        if (f + 1 < d) v.y = p[1];
+        if (f + 2 < d) v.z = p[2];
+        if (f + 3 < d) v.w = p[3];
+    }
+    return v;
+}
+
+// Sums over the 64 lanes of a wave of M values per lane, M = 2^m <= 64: at
+// each halving step a lane keeps one half of its values and adds the
+// partner's copy of that half, sending the other half (M - 1 shuffles
+// instead of M * 6). On return v[0] of lane l holds the total of value
+// l >> (6 - m). The order of the additions is fixed.
+template <int M>
+__device__ __forceinline__ void wave_sum_transpose(double (&v)[M], int lane) {
+    static_assert(M >= 1 && M <= 64 && (M & (M - 1)) == 0, "M must be a power of two");
+    constexpr int kSteps = M == 1 ? 0 : M == 2 ? 1 : M == 4 ? 2 : M == 8 ? 3 : M == 16 ? 4 : M == 32 ? 5 : 6;
+#pragma unroll
+    for (int step = 0; step < kSteps; ++step) {
+        const int half = M >> (step + 1), bit = 5 - step;
+        const bool hi = (lane >> bit) & 1;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            // Opaque copies: without them the compiler turns the two selects
+            // below into a lane-dependent index into v, which it can only
+            // lower as a compare chain over the whole array.
+            double lo = v[i], up = v[i + half];
+            asm volatile("" : "+v"(lo), "+v"(up));
+            const double send = hi ? lo : up;
+            const double keep = hi ? up : lo;
+            v[i] = keep + __shfl_xor(send, 1 << bit);
+        }
+    }
+#pragma unroll
+    for (int bit = 5 - kSteps; bit >= 0; --bit) v[0] += __shfl_xor(v[0], 1 << bit);
+}
+
+constexpr int pow2_at_least(int x) { return x <= 1 ? 1 : 2 * pow2_at_least((x + 1) / 2); }
+
+constexpr int kPPWaves = 8;  // waves per block of pp_dist_kernel (512 threads)
+
+// Samples [b * 64, b * 64 + 64) against the T candidate rows cand[0..T).
+// prev_buf + best * n holds D of the previous centre set (prev_buf NULL: the
+// first centre, D = +inf).
 //
-// 16 waves; wave w handles samples b*64 + w, +16, +32, +48 (4 row groups).
-// The work is a sequence of stages (row group g, feature chunk c); at every
-// stage each lane holds 16 features of its wave's sample in registers and the
-// block holds the candidates' values of chunk c in LDS. The loads of stage
-// s + 1 (sample values into registers, candidate values into registers, then
-// into the other LDS buffer) are issued before stage s is computed, so memory
-// latency overlaps the float64 arithmetic. One barrier per stage.
-__global__ __launch_bounds__(1024) void pp_dist_kernel(
-    const float *__restrict__ X, int64_t n, int64_t d, int trials,
-    const long long *__restrict__ cand, const PPState *__restrict__ st,
-    const double *__restrict__ prev_buf, double *__restrict__ out_buf,
-    double *__restrict__ out_parts, int64_t nb) {
-    __shared__ float cs[2][kPPMaxTrials * kPPChunk];  // 2 x 64 KiB
-    __shared__ double wave_part[16][kPPMaxTrials];
+// 8 waves; a wave works on R samples at once, so every candidate value read
+// from LDS and widened to float64 serves R samples (R = 1, 2 or 4). Wave w's
+// samples are b*64 + w + 8 m for m = p*R + r (pass p, slot r), 8/R passes.
+// The work is a sequence of stages (pass, chunk of 256 features): lane l
+// holds features 4l .. 4l+3 of the chunk for its R samples in registers; the
+// block holds the chunk of every candidate in LDS, stored [t][q][lane] so
+// that the reads of one (t, q) are 64 consecutive words. The loads of stage
+// s + 1 are in flight while stage s is computed (double-buffered LDS, one
+// barrier per stage); at most 128 registers (4 waves per SIMD) let two blocks
+// share a CU, so one computes while the other waits.
+template <int T, int R, bool kVec>
+__global__ __launch_bounds__(kPPWaves * 64, 4) void pp_dist_kernel(
+    const float *__restrict__ X, int64_t n, int64_t d, const long long *__restrict__ cand,
+    const PPState *__restrict__ st, const double *__restrict__ prev_buf,
+    double *__restrict__ out_buf, double *__restrict__ out_parts, int64_t nb) {
+    constexpr int kPasses = kPPRowsPerBlock / (kPPWaves * R);
+    constexpr int kCandPerWave = (T + kPPWaves - 1) / kPPWaves;
+    constexpr int kM = pow2_at_least(R * T);          // values per lane to reduce
+    constexpr int kGroup = 64 / kM;                   // lanes holding one total
+    __shared__ float cs[2][T][4][64];
+    __shared__ double wave_part[kPPWaves][R][T];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t b = blockIdx.x;
     const double *closest = prev_buf ? prev_buf + (int64_t)st->best * n : nullptr;
     const int64_t chunks = (d + kPPChunk - 1) / kPPChunk;
-    const int64_t stages = 4 * chunks;
-    constexpr int kPerLane = kPPChunk / 64;  // 16 features per lane and stage
-
-    if (lane < kPPMaxTrials) wave_part[wave][lane] = 0.0;
-
-    // Stage s: row group s / chunks, chunk s % chunks.
-    auto load_x = [&](int64_t s, float (&xr)[kPerLane]) {
-        const int64_t i = b * kPPRowsPerBlock + (s / chunks) * 16 + wave;
-        const int64_t c0 = (s % chunks) * kPPChunk;
+    const int64_t stages = kPasses * chunks;
+    // Wave w stages candidates w, w + 8 (those below T).
+    int64_t my_cand[kCandPerWave];
 #pragma unroll
-        for (int j = 0; j < kPerLane; ++j) {
-            const int64_t f = c0 + lane + 64 * j;
-            xr[j] = (i < n && f < d) ? X[i * d + f] : 0.f;
+    for (int j = 0; j < kCandPerWave; ++j) {
+        const int t = wave + kPPWaves * j;
+        my_cand[j] = t < T ? (int64_t)cand[t] : 0;
+    }
+
+    auto row = [&](int64_t p, int r) {
+        return b * kPPRowsPerBlock + (p * R + r) * kPPWaves + wave;
+    };
+    auto load_stage = [&](int64_t s, float4 (&xr)[R], float4 (&cv)[kCandPerWave]) {
+        const int64_t p = s / chunks, f = (s % chunks) * kPPChunk + 4 * lane;
+#pragma unroll
+        for (int r = 0; r < R; ++r) xr[r] = load_row4<kVec>(X, n, d, row(p, r), f);
+#pragma unroll
+        for (int j = 0; j < kCandPerWave; ++j)
+            if (wave + kPPWaves * j < T) cv[j] = load_row4<kVec>(X, n, d, my_cand[j], f);
+    };
+    auto store_cand = [&](int buf, const float4 (&cv)[kCandPerWave]) {
+#pragma unroll
+        for (int j = 0; j < kCandPerWave; ++j) {
+            const int t = wave + kPPWaves * j;
+            if (t < T) {
+                cs[buf][t][0][lane] = cv[j].x;
+                cs[buf][t][1][lane] = cv[j].y;
+                cs[buf][t][2][lane] = cv[j].z;
+                cs[buf][t][3][lane] = cv[j].w;
+            }
         }
     };
-    auto load_c = [&](int64_t s, float (&cv)[kPPMaxTrials]) {
-        const int64_t f = (s % chunks) * kPPChunk + tid;
-#pragma unroll
-        for (int t = 0; t < kPPMaxTrials; ++t)
-            cv[t] = (t < trials && f < d) ? X[(int64_t)cand[t] * d + f] : 0.f;
-    };
-    auto store_c = [&](int buf, const float (&cv)[kPPMaxTrials]) {
-#pragma unroll
-        for (int t = 0; t < kPPMaxTrials; ++t)
-            if (t < trials) cs[buf][t * kPPChunk + tid] = cv[t];
-    };
 
-    float xr[kPerLane], xn[kPerLane], cv[kPPMaxTrials];
-    load_x(0, xr);
-    load_c(0, cv);
-    store_c(0, cv);
+    float4 xr[R], xn[R], cv[kCandPerWave];
+    load_stage(0, xr, cv);
+    store_cand(0, cv);
     __syncthreads();
 
-    double acc[kPPMaxTrials];
+    // acc[r * T + t]: this lane's part of |x - c_t|^2 for slot r; the
+    // entries from R * T up to kM stay 0 and only pad the reduction.
+    double acc[kM];
 #pragma unroll
-    for (int t = 0; t < kPPMaxTrials; ++t) acc[t] = 0.0;
+    for (int j = 0; j < kM; ++j) acc[j] = 0.0;
+    // This lane's running sum of the final D over its passes, for the value
+    // (r, t) it receives from the reduction.
+    const int my_idx = lane / kGroup;
+    double my_part = 0.0;
+
     for (int64_t s = 0; s < stages; ++s) {
         const int cur = (int)(s & 1);
-        if (s + 1 < stages) {
-            load_x(s + 1, xn);
-            load_c(s + 1, cv);
-        }
-        // Features of this stage beyond d were loaded as 0 for the sample and
-        // every candidate, so they add 0.
+        if (s + 1 < stages) load_stage(s + 1, xn, cv);
+        // Features beyond d were loaded as 0 for samples and candidates alike,
+        // so they add 0.
 #pragma unroll
-        for (int j = 0; j < kPerLane; ++j) {
-            const double xv = (double)xr[j];
-            const int f = lane + 64 * j;
+        for (int q = 0; q < 4; ++q) {
+            double xd[R];
 #pragma unroll
-            for (int t = 0; t < kPPMaxTrials; ++t) {
-                if (t < trials) {
-                    const double diff = xv - (double)cs[cur][t * kPPChunk + f];
-                    acc[t] += diff * diff;
+            for (int r = 0; r < R; ++r)
+                xd[r] = (double)(q == 0 ? xr[r].x : q == 1 ? xr[r].y : q == 2 ? xr[r].z : xr[r].w);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const double c = (double)cs[cur][t][q][lane];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const double diff = xd[r] - c;
+                    acc[r * T + t] += diff * diff;
                 }
             }
         }
         if (s % chunks == chunks - 1) {
-            // The wave's sample of this row group is complete.
-            const int64_t i = b * kPPRowsPerBlock + (s / chunks) * 16 + wave;
-            if (i < n) {
+            // The R samples of this pass are complete.
+            wave_sum_transpose<kM>(acc, lane);
+            const int64_t i = row(s / chunks, my_idx / T);
+            if (lane % kGroup == 0 && my_idx < R * T && i < n) {
                 const double cur_d = closest ? closest[i] : __builtin_inf();
-#pragma unroll
-                for (int t = 0; t < kPPMaxTrials; ++t) {
-                    if (t < trials) {
-                        double v = acc[t];
-                        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-                        const double nd = v < cur_d ? v : cur_d;
-                        if (lane == 0) {
-                            out_buf[(int64_t)t * n + i] = nd;
-                            wave_part[wave][t] += nd;  // this wave's rows, in order
-                        }
-                    }
-                }
+                const double nd = acc[0] < cur_d ? acc[0] : cur_d;
+                out_buf[(int64_t)(my_idx % T) * n + i] = nd;
+                my_part += nd;
             }
 #pragma unroll
-            for (int t = 0; t < kPPMaxTrials; ++t) acc[t] = 0.0;
+            for (int j = 0; j < kM; ++j) acc[j] = 0.0;
         }
         if (s + 1 < stages) {
-            store_c(cur ^ 1, cv);
+            store_cand(cur ^ 1, cv);
 #pragma unroll
-            for (int j = 0; j < kPerLane; ++j) xr[j] = xn[j];
+            for (int r = 0; r < R; ++r) xr[r] = xn[r];
         }
         __syncthreads();
     }
-    if (tid < trials) {
+    if (lane % kGroup == 0 && my_idx < R * T) wave_part[wave][my_idx / T][my_idx % T] = my_part;
+    __syncthreads();
+    if (tid < T) {
         double sum = 0.0;
-        for (int w = 0; w < 16; ++w) sum += wave_part[w][tid];
+        for (int w = 0; w < kPPWaves; ++w)
+            for (int r = 0; r < R; ++r) sum += wave_part[w][r][tid];
         out_parts[(int64_t)tid * nb + b] = sum;
+    }
+}
+
+// Launch of pp_dist_kernel for a run-time trial count. A wave takes R
+// samples at once with R * T <= 16, so that the float64 accumulators fit in
+// 32 registers and two blocks fit on a CU without spilling.
+template <int T>
+void launch_dist_t(bool vec, unsigned nb, hipStream_t stream, const float *X, int64_t n,
+                   int64_t d, const long long *cand, const PPState *st, const double *prev,
+                   double *out, double *parts) {
+    constexpr int R = T <= 4 ? 4 : T <= 8 ? 2 : 1;
+    if (vec)
+        pp_dist_kernel<T, R, true><<<nb, kPPWaves * 64, 0, stream>>>(X, n, d, cand, st, prev, out, parts, nb);
+    else
+        pp_dist_kernel<T, R, false><<<nb, kPPWaves * 64, 0, stream>>>(X, n, d, cand, st, prev, out, parts, nb);
+}
+
+void launch_dist(int trials, bool vec, unsigned nb, hipStream_t stream, const float *X,
+                 int64_t n, int64_t d, const long long *cand, const PPState *st,
+                 const double *prev, double *out, double *parts) {
+    switch (trials) {
+#define KM_PP_CASE(T) \
+    case T: launch_dist_t<T>(vec, nb, stream, X, n, d, cand, st, prev, out, parts); break;
+        KM_PP_CASE(1) KM_PP_CASE(2) KM_PP_CASE(3) KM_PP_CASE(4)
+        KM_PP_CASE(5) KM_PP_CASE(6) KM_PP_CASE(7) KM_PP_CASE(8)
+        KM_PP_CASE(9) KM_PP_CASE(10) KM_PP_CASE(11) KM_PP_CASE(12)
+        KM_PP_CASE(13) KM_PP_CASE(14) KM_PP_CASE(15) KM_PP_CASE(16)
+#undef KM_PP_CASE
+        default: break;  // trials is validated to 1 .. kPPMaxTrials by the caller
     }
 }
 
@@ -284,6 +381,7 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int64_t pp_blocks(int64_t n) { return cdiv(n, kPPRowsPerBlock); }
 int pp_max_trials() { return kPPMaxTrials; }
+int pp_block_threads() { return kPPWaves * 64; }
 size_t pp_state_bytes() { return sizeof(PPState); }
 
 hipError_t launch_kmeanspp(const float *X, int64_t n, int64_t d, int64_t k, int64_t first,
@@ -296,8 +394,8 @@ hipError_t launch_kmeanspp(const float *X, int64_t n, int64_t d, int64_t k, int6
     long long *cand[2] = {(long long *)ws.cand_a, (long long *)ws.cand_b};
     pp_init_kernel<<<1, 1, 0, stream>>>(cand[0], first);
     // D of the first centre alone (one "trial": the given sample).
-    pp_dist_kernel<<<(unsigned)nb, 1024, 0, stream>>>(X, n, d, 1, cand[0], st, nullptr, buf[0],
-                                                      parts[0], nb);
+    const bool vec = d % 4 == 0 && reinterpret_cast<uintptr_t>(X) % 16 == 0;
+    launch_dist(1, vec, (unsigned)nb, stream, X, n, d, cand[0], st, nullptr, buf[0], parts[0]);
     int cur = 0, trials_prev = 1;
     for (int64_t c = 1; c <= k; ++c) {
         const bool more = c < k;
@@ -306,9 +404,8 @@ hipError_t launch_kmeanspp(const float *X, int64_t n, int64_t d, int64_t k, int6
             (long long *)chosen, centres, more ? rand + (c - 1) * trials : nullptr, trials,
             cand[cur ^ 1]);
         if (!more) break;
-        pp_dist_kernel<<<(unsigned)nb, 1024, 0, stream>>>(X, n, d, trials, cand[cur ^ 1], st,
-                                                          buf[cur], buf[cur ^ 1],
-                                                          parts[cur ^ 1], nb);
+        launch_dist(trials, vec, (unsigned)nb, stream, X, n, d, cand[cur ^ 1], st, buf[cur],
+                    buf[cur ^ 1], parts[cur ^ 1]);
         cur ^= 1;
         trials_prev = trials;
     }
