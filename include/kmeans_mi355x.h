@@ -161,8 +161,10 @@ int kmeans_fit(const float *X, const float *C_init, int64_t n, int64_t k, int64_
  * sum of D reaches rand[(c - 1) * trials + t] * pot (the last sample if none
  * does); the candidate with the smallest potential sum_i min(D(i),
  * |x_i - x_cand|^2) (lowest trial on ties) becomes centre c. Distances are
- * float64 in difference form. The random draws are an input so that a run
- * is reproducible.
+ * float64 in Gram form, |x|^2 + |c|^2 - 2 x.c clamped at 0, with the sample
+ * norms computed once per call (the pages' faster version); the float32
+ * products are exact in float64 and a sample's distance to itself is exactly
+ * 0. The random draws are an input so that a run is reproducible.
  *   X        (n, d) float32 samples.
  *   k        number of centres, 1 <= k <= n.
  *   first    index of the first centre, 0 <= first < n.
@@ -172,6 +174,8 @@ int kmeans_fit(const float *X, const float *C_init, int64_t n, int64_t k, int64_
  *   centres  (k, d) float32 output: the chosen rows of X.
  *   chosen   (k,) int64 output: their indices.
  * Asynchronous like kmeans_assign; 2 kernel launches per centre.
+ * Workspace: about (2 * 16 + 1) * n doubles (kmeans_workspace_bytes with
+ * KM_OP_KMEANSPP).
  */
 int kmeans_plusplus(const float *X, int64_t n, int64_t d, int64_t k, int64_t first,
                     int64_t trials, const double *rand, float *centres, int64_t *chosen,

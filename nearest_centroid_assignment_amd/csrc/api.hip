@@ -24,7 +24,7 @@ struct Layout {
            shift_partial = 0, scalars = 0;
     // kmeans_plusplus only
     size_t pp_buf_a = 0, pp_buf_b = 0, pp_parts_a = 0, pp_parts_b = 0, pp_cand_a = 0,
-           pp_cand_b = 0, pp_state = 0;
+           pp_cand_b = 0, pp_state = 0, pp_xnorm = 0;
     size_t total = 0;
 };
 
@@ -87,6 +87,8 @@ Layout layout(int64_t n, int64_t k, int64_t d, int op) {
         off += round_up(t * sizeof(int64_t));
         L.pp_state = off;
         off += round_up(km::pp_state_bytes());
+        L.pp_xnorm = off;
+        off += round_up((size_t)n * sizeof(double));
     }
     L.total = off + kAlign;
     return L;
@@ -343,6 +345,7 @@ int kmeans_plusplus(const float *X, int64_t n, int64_t d, int64_t k, int64_t fir
     ws.cand_a = (int64_t *)(base + L.pp_cand_a);
     ws.cand_b = (int64_t *)(base + L.pp_cand_b);
     ws.state = base + L.pp_state;
+    ws.xnorm = (double *)(base + L.pp_xnorm);
     const hipError_t e = km::launch_kmeanspp(X, n, d, k, first, (int)trials, rand, centres, chosen,
                                              ws, (hipStream_t)stream);
     return e == hipSuccess ? KM_OK : KM_ERR_HIP;

@@ -96,6 +96,7 @@ struct PPScratch {
     double *parts_a, *parts_b;  // trials * pp_blocks(n): per-block sums of those
     int64_t *cand_a, *cand_b;   // trials: candidate sample indices (alternating)
     void *state;                // pp_state_bytes(): winner and its potential
+    double *xnorm;              // n: |x_i|^2 in float64
 };
 int64_t pp_blocks(int64_t n);
 int pp_max_trials();

@@ -9,9 +9,17 @@
 // trials + t] and takes the first sample whose running sum of D reaches
 // u * pot (the last sample if none does); the candidate whose potential
 // sum_i min(D(i), |x_i - x_cand|^2) is smallest (lowest trial on ties) is
-// kept, and D becomes those minima. Distances are float64 in difference form.
+// kept, and D becomes those minima.
 //
-// Per centre, two launches and nothing on the host:
+// Distances are float64 in Gram form, |x|^2 + |c|^2 - 2 x.c clamped at 0,
+// with the sample norms computed once per call as the pages' faster version
+// does. A float32 x float32 product is exact in float64, so the only
+// roundings are those of the float64 sums; the norms use the same per-lane
+// order and reduction tree as the dot products, so a sample's distance to
+// itself is exactly 0.
+//
+// Per call, pp_norm_kernel computes |x_i|^2 once. Per centre, two launches
+// and nothing on the host:
 //   pp_select_kernel  one block: potentials of the previous trials from the
 //                     per-block partials (fixed-order block reduction), the
 //                     winner, its row copied out as a centre, then the next
@@ -19,10 +27,10 @@
 //                     block each draw falls in, one wave per draw walks its
 //                     rows
 //   pp_dist_kernel    every sample against all candidates: candidate rows
-//                     staged in LDS 256 features at a time (double buffered,
-//                     the next stage's loads in flight during the current
-//                     one), a wave on 1, 2 or 4 samples at once, float64
-//                     sums; min with D; per-block partials
+//                     staged in LDS 256 or 512 features at a time (double
+//                     buffered, the next stage's loads in flight during the
+//                     current one), a wave on 1, 2 or 4 samples at once,
+//                     float64 dot products; min with D; per-block partials
 // Buffers of D and partials alternate between centres (A <-> B).
 #include "kernels.h"
 
@@ -30,7 +38,7 @@ namespace km {
 namespace {
 
 constexpr int kPPMaxTrials = 16;
-constexpr int kPPChunk = 256;       // features per LDS stage: 4 per lane
+constexpr int kPPChunk = 256;       // features per lane-slice of a stage: 4 per lane
 constexpr int kPPRowsPerBlock = 64; // samples per block of pp_dist_kernel
 
 struct PPState {
@@ -97,28 +105,62 @@ constexpr int kPPWaves = 8;  // waves per block of pp_dist_kernel (512 threads)
 // 8 waves; a wave works on R samples at once, so every candidate value read
 // from LDS and widened to float64 serves R samples (R = 1, 2 or 4). Wave w's
 // samples are b*64 + w + 8 m for m = p*R + r (pass p, slot r), 8/R passes.
-// The work is a sequence of stages (pass, chunk of 256 features): lane l
-// holds features 4l .. 4l+3 of the chunk for its R samples in registers; the
-// block holds the chunk of every candidate in LDS, stored [t][q][lane] so
-// that the reads of one (t, q) are 64 consecutive words. The loads of stage
-// s + 1 are in flight while stage s is computed (double-buffered LDS, one
-// barrier per stage); at most 128 registers (4 waves per SIMD) let two blocks
-// share a CU, so one computes while the other waits.
-template <int T, int R, bool kVec>
+// The work is a sequence of stages (pass, chunk of 256 V features); lane l
+// loads features 256 v + 4 l .. +3 (v < V) of its R samples and of the
+// candidates it stages. Everything a stage reads sits in LDS: the wave's own
+// sample values in xs (each wave overwrites only its own slice, after its
+// own reads, so one buffer suffices) and the candidates in cs, double
+// buffered and stored [t][4 v + q][lane] so that the reads of one (t, v, q)
+// are 64 consecutive words. The registers only carry the next stage's loads,
+// issued before the current stage is computed; one barrier per stage. At
+// most 128 registers (4 waves per SIMD) let two blocks share a CU, so one
+// computes while the other waits.
+// |x_i|^2 in float64, one wave per sample, 4 samples per 256-thread block.
+// Lane l adds x_f^2 for f = 256 s' + 4 l + q in the order of slices s' and
+// then q, and the lanes are combined by the butterfly of wave_sum_transpose:
+// the same order as the dot products of pp_dist_kernel, so |x_i|^2 equals
+// x_i . x_i there bit for bit.
+__global__ __launch_bounds__(256) void pp_norm_kernel(const float *__restrict__ X, int64_t n,
+                                                     int64_t d, double *__restrict__ xnorm) {
+    const int lane = threadIdx.x & 63;
+    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (i >= n) return;  // whole wave
+    const float *x = X + i * d;
+    double acc[1] = {0.0};
+    for (int64_t f0 = 4 * lane; f0 < d; f0 += kPPChunk) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const double v = f0 + q < d ? (double)x[f0 + q] : 0.0;
+            acc[0] = __builtin_fma(v, v, acc[0]);
+        }
+    }
+    wave_sum_transpose<1>(acc, lane);
+    if (lane == 0) xnorm[i] = acc[0];
+}
+
+// LDS of one pp_dist_kernel block: xs, cs and wave_part below.
+constexpr int pp_dist_lds_bytes(int T, int R, int V) {
+    return kPPWaves * R * V * 64 * 16 + 2 * T * 4 * V * 64 * 4 + kPPWaves * R * T * 8;
+}
+
+template <int T, int R, int V, bool kVec>
 __global__ __launch_bounds__(kPPWaves * 64, 4) void pp_dist_kernel(
-    const float *__restrict__ X, int64_t n, int64_t d, const long long *__restrict__ cand,
-    const PPState *__restrict__ st, const double *__restrict__ prev_buf,
-    double *__restrict__ out_buf, double *__restrict__ out_parts, int64_t nb) {
+    const float *__restrict__ X, const double *__restrict__ xnorm, int64_t n, int64_t d,
+    const long long *__restrict__ cand, const PPState *__restrict__ st,
+    const double *__restrict__ prev_buf, double *__restrict__ out_buf,
+    double *__restrict__ out_parts, int64_t nb) {
+    constexpr int kChunk = kPPChunk * V;
     constexpr int kPasses = kPPRowsPerBlock / (kPPWaves * R);
     constexpr int kCandPerWave = (T + kPPWaves - 1) / kPPWaves;
     constexpr int kM = pow2_at_least(R * T);          // values per lane to reduce
     constexpr int kGroup = 64 / kM;                   // lanes holding one total
-    __shared__ float cs[2][T][4][64];
+    __shared__ float4 xs[kPPWaves][R][V][64];
+    __shared__ float cs[2][T][4 * V][64];
     __shared__ double wave_part[kPPWaves][R][T];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t b = blockIdx.x;
     const double *closest = prev_buf ? prev_buf + (int64_t)st->best * n : nullptr;
-    const int64_t chunks = (d + kPPChunk - 1) / kPPChunk;
+    const int64_t chunks = (d + kChunk - 1) / kChunk;
     const int64_t stages = kPasses * chunks;
     // Wave w stages candidates w, w + 8 (those below T).
     int64_t my_cand[kCandPerWave];
@@ -127,38 +169,53 @@ __global__ __launch_bounds__(kPPWaves * 64, 4) void pp_dist_kernel(
         const int t = wave + kPPWaves * j;
         my_cand[j] = t < T ? (int64_t)cand[t] : 0;
     }
+    __shared__ double cand_norm[T];
+    if (tid < T) cand_norm[tid] = xnorm[cand[tid]];
 
     auto row = [&](int64_t p, int r) {
         return b * kPPRowsPerBlock + (p * R + r) * kPPWaves + wave;
     };
-    auto load_stage = [&](int64_t s, float4 (&xr)[R], float4 (&cv)[kCandPerWave]) {
-        const int64_t p = s / chunks, f = (s % chunks) * kPPChunk + 4 * lane;
+    auto load_stage = [&](int64_t s, float4 (&xr)[R][V], float4 (&cv)[kCandPerWave][V]) {
+        const int64_t p = s / chunks, f = (s % chunks) * kChunk + 4 * lane;
 #pragma unroll
-        for (int r = 0; r < R; ++r) xr[r] = load_row4<kVec>(X, n, d, row(p, r), f);
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+                xr[r][v] = load_row4<kVec>(X, n, d, row(p, r), f + kPPChunk * v);
 #pragma unroll
         for (int j = 0; j < kCandPerWave; ++j)
-            if (wave + kPPWaves * j < T) cv[j] = load_row4<kVec>(X, n, d, my_cand[j], f);
+            if (wave + kPPWaves * j < T)
+#pragma unroll
+                for (int v = 0; v < V; ++v)
+                    cv[j][v] = load_row4<kVec>(X, n, d, my_cand[j], f + kPPChunk * v);
     };
-    auto store_cand = [&](int buf, const float4 (&cv)[kCandPerWave]) {
+    auto store_stage = [&](int buf, const float4 (&xr)[R][V], const float4 (&cv)[kCandPerWave][V]) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int v = 0; v < V; ++v) xs[wave][r][v][lane] = xr[r][v];
 #pragma unroll
         for (int j = 0; j < kCandPerWave; ++j) {
             const int t = wave + kPPWaves * j;
             if (t < T) {
-                cs[buf][t][0][lane] = cv[j].x;
-                cs[buf][t][1][lane] = cv[j].y;
-                cs[buf][t][2][lane] = cv[j].z;
-                cs[buf][t][3][lane] = cv[j].w;
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    cs[buf][t][4 * v + 0][lane] = cv[j][v].x;
+                    cs[buf][t][4 * v + 1][lane] = cv[j][v].y;
+                    cs[buf][t][4 * v + 2][lane] = cv[j][v].z;
+                    cs[buf][t][4 * v + 3][lane] = cv[j][v].w;
+                }
             }
         }
     };
 
-    float4 xr[R], xn[R], cv[kCandPerWave];
-    load_stage(0, xr, cv);
-    store_cand(0, cv);
+    float4 xn[R][V], cv[kCandPerWave][V];
+    load_stage(0, xn, cv);
+    store_stage(0, xn, cv);
     __syncthreads();
 
-    // acc[r * T + t]: this lane's part of |x - c_t|^2 for slot r; the
-    // entries from R * T up to kM stay 0 and only pad the reduction.
+    // acc[r * T + t]: this lane's part of x . c_t for slot r; the entries
+    // from R * T up to kM stay 0 and only pad the reduction.
     double acc[kM];
 #pragma unroll
     for (int j = 0; j < kM; ++j) acc[j] = 0.0;
@@ -171,20 +228,26 @@ __global__ __launch_bounds__(kPPWaves * 64, 4) void pp_dist_kernel(
         const int cur = (int)(s & 1);
         if (s + 1 < stages) load_stage(s + 1, xn, cv);
         // Features beyond d were loaded as 0 for samples and candidates alike,
-        // so they add 0.
+        // so they add 0. Per lane the features come in the order 256 s' + 4
+        // lane + q over slices s' and then q, as in pp_norm_kernel. (Not
+        // unrolled over v: the compiler would hoist the
+        // LDS reads of every slice and run out of registers.)
+#pragma unroll 1
+        for (int v = 0; v < V; ++v) {
+            float4 xf[R];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            double xd[R];
+            for (int r = 0; r < R; ++r) xf[r] = xs[wave][r][v][lane];
 #pragma unroll
-            for (int r = 0; r < R; ++r)
-                xd[r] = (double)(q == 0 ? xr[r].x : q == 1 ? xr[r].y : q == 2 ? xr[r].z : xr[r].w);
+            for (int q = 0; q < 4; ++q) {
+                double xd[R];
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const double c = (double)cs[cur][t][q][lane];
+                for (int r = 0; r < R; ++r)
+                    xd[r] = (double)(q == 0 ? xf[r].x : q == 1 ? xf[r].y : q == 2 ? xf[r].z : xf[r].w);
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const double diff = xd[r] - c;
-                    acc[r * T + t] += diff * diff;
+                for (int t = 0; t < T; ++t) {
+                    const double c = (double)cs[cur][t][4 * v + q][lane];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) acc[r * T + t] = __builtin_fma(xd[r], c, acc[r * T + t]);
                 }
             }
         }
@@ -193,19 +256,18 @@ __global__ __launch_bounds__(kPPWaves * 64, 4) void pp_dist_kernel(
             wave_sum_transpose<kM>(acc, lane);
             const int64_t i = row(s / chunks, my_idx / T);
             if (lane % kGroup == 0 && my_idx < R * T && i < n) {
+                const int t = my_idx % T;
                 const double cur_d = closest ? closest[i] : __builtin_inf();
-                const double nd = acc[0] < cur_d ? acc[0] : cur_d;
-                out_buf[(int64_t)(my_idx % T) * n + i] = nd;
+                const double dist = __builtin_fma(-2.0, acc[0], xnorm[i] + cand_norm[t]);
+                const double pos = dist > 0.0 ? dist : 0.0;
+                const double nd = pos < cur_d ? pos : cur_d;
+                out_buf[(int64_t)t * n + i] = nd;
                 my_part += nd;
             }
 #pragma unroll
             for (int j = 0; j < kM; ++j) acc[j] = 0.0;
         }
-        if (s + 1 < stages) {
-            store_cand(cur ^ 1, cv);
-#pragma unroll
-            for (int r = 0; r < R; ++r) xr[r] = xn[r];
-        }
+        if (s + 1 < stages) store_stage(cur ^ 1, xn, cv);
         __syncthreads();
     }
     if (lane % kGroup == 0 && my_idx < R * T) wave_part[wave][my_idx / T][my_idx % T] = my_part;
@@ -222,22 +284,27 @@ __global__ __launch_bounds__(kPPWaves * 64, 4) void pp_dist_kernel(
 // samples at once with R * T <= 16, so that the float64 accumulators fit in
 // 32 registers and two blocks fit on a CU without spilling.
 template <int T>
-void launch_dist_t(bool vec, unsigned nb, hipStream_t stream, const float *X, int64_t n,
-                   int64_t d, const long long *cand, const PPState *st, const double *prev,
-                   double *out, double *parts) {
+void launch_dist_t(bool vec, unsigned nb, hipStream_t stream, const float *X,
+                   const double *xnorm, int64_t n, int64_t d, const long long *cand,
+                   const PPState *st, const double *prev, double *out, double *parts) {
     constexpr int R = T <= 4 ? 4 : T <= 8 ? 2 : 1;
+    // Two 256-feature slices per stage where the LDS of two blocks still fits
+    // in a CU's 160 KiB, else one.
+    constexpr int V = 2 * pp_dist_lds_bytes(T, R, 2) <= 160 * 1024 ? 2 : 1;
     if (vec)
-        pp_dist_kernel<T, R, true><<<nb, kPPWaves * 64, 0, stream>>>(X, n, d, cand, st, prev, out, parts, nb);
+        pp_dist_kernel<T, R, V, true><<<nb, kPPWaves * 64, 0, stream>>>(X, xnorm, n, d, cand, st,
+                                                                        prev, out, parts, nb);
     else
-        pp_dist_kernel<T, R, false><<<nb, kPPWaves * 64, 0, stream>>>(X, n, d, cand, st, prev, out, parts, nb);
+        pp_dist_kernel<T, R, V, false><<<nb, kPPWaves * 64, 0, stream>>>(X, xnorm, n, d, cand, st,
+                                                                         prev, out, parts, nb);
 }
 
 void launch_dist(int trials, bool vec, unsigned nb, hipStream_t stream, const float *X,
-                 int64_t n, int64_t d, const long long *cand, const PPState *st,
-                 const double *prev, double *out, double *parts) {
+                 const double *xnorm, int64_t n, int64_t d, const long long *cand,
+                 const PPState *st, const double *prev, double *out, double *parts) {
     switch (trials) {
 #define KM_PP_CASE(T) \
-    case T: launch_dist_t<T>(vec, nb, stream, X, n, d, cand, st, prev, out, parts); break;
+    case T: launch_dist_t<T>(vec, nb, stream, X, xnorm, n, d, cand, st, prev, out, parts); break;
         KM_PP_CASE(1) KM_PP_CASE(2) KM_PP_CASE(3) KM_PP_CASE(4)
         KM_PP_CASE(5) KM_PP_CASE(6) KM_PP_CASE(7) KM_PP_CASE(8)
         KM_PP_CASE(9) KM_PP_CASE(10) KM_PP_CASE(11) KM_PP_CASE(12)
@@ -395,7 +462,9 @@ hipError_t launch_kmeanspp(const float *X, int64_t n, int64_t d, int64_t k, int6
     pp_init_kernel<<<1, 1, 0, stream>>>(cand[0], first);
     // D of the first centre alone (one "trial": the given sample).
     const bool vec = d % 4 == 0 && reinterpret_cast<uintptr_t>(X) % 16 == 0;
-    launch_dist(1, vec, (unsigned)nb, stream, X, n, d, cand[0], st, nullptr, buf[0], parts[0]);
+    pp_norm_kernel<<<(unsigned)cdiv(n, 4), 256, 0, stream>>>(X, n, d, ws.xnorm);
+    launch_dist(1, vec, (unsigned)nb, stream, X, ws.xnorm, n, d, cand[0], st, nullptr, buf[0],
+                parts[0]);
     int cur = 0, trials_prev = 1;
     for (int64_t c = 1; c <= k; ++c) {
         const bool more = c < k;
@@ -404,8 +473,8 @@ hipError_t launch_kmeanspp(const float *X, int64_t n, int64_t d, int64_t k, int6
             (long long *)chosen, centres, more ? rand + (c - 1) * trials : nullptr, trials,
             cand[cur ^ 1]);
         if (!more) break;
-        launch_dist(trials, vec, (unsigned)nb, stream, X, n, d, cand[cur ^ 1], st, buf[cur],
-                    buf[cur ^ 1], parts[cur ^ 1]);
+        launch_dist(trials, vec, (unsigned)nb, stream, X, ws.xnorm, n, d, cand[cur ^ 1], st,
+                    buf[cur], buf[cur ^ 1], parts[cur ^ 1]);
         cur ^= 1;
         trials_prev = trials;
     }
