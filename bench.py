@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused assign TFLOP/s (2nkd/t) + Lloyd iteration ms, 65536×4096×16384 fp32"
 MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak (published)
+HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E bandwidth (published)
 # The pages' k-means++ time on an NVIDIA L4 at 65536 x 1024 x 8192 (context).
 PAGES_KMEANSPP_MS = 10300.0
 # The pages' Lloyd-iteration times on an NVIDIA L4, per workload (context).
@@ -102,6 +103,32 @@ def cpu_baseline(X, C, target_s: float):
         "kind": "oracle",
         "sample": f"{m} seeded rows x all {k} centroids x {d} features "
                   f"(float64 difference-form assignment, {t:.1f} s)",
+    }
+
+
+def cpu_baseline_kmeanspp(X, k, first, trials, rand, target_s: float):
+    """Time the float64 oracle's seeding of the first m centres (same draws),
+    m growing until one run takes at least half of ``target_s``; every centre
+    after the first costs the same, so the full seeding is estimated as
+    t(m) * (k - 1) / (m - 1) ms."""
+    import oracle
+
+    m = min(k, 3)
+    while True:
+        t0 = time.perf_counter()
+        oracle.kmeanspp(X, m, first, trials, rand[: m - 1])
+        t = time.perf_counter() - t0
+        if t >= 0.5 * target_s or m == k:
+            break
+        m = int(min(k, max(m + 1, 1 + (m - 1) * target_s / max(t, 1e-3))))
+    scale = (k - 1) / (m - 1) if m > 1 else 1.0
+    return {
+        "value": round(t * 1e3 * scale, 1),
+        "unit": "ms",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"first {m} of {k} centres of the same seeding (float64 difference form, "
+                  f"{t:.1f} s), scaled by (k - 1) / (m - 1)",
     }
 
 
@@ -208,6 +235,21 @@ def bench_kmeanspp(args, cfg, X, Xg, stream) -> int:
     ms = sorted(times)[len(times) // 2]
     # Bytes the distance kernels must read: X once per centre.
     x_bytes = 4.0 * n * d * k
+    # Algorithmic bytes of the distance launches: per launch X (4nd), the
+    # previous D (8n), the new D of every trial (8n per trial) and the
+    # candidate rows (4d per trial); the first launch has one trial and no
+    # previous D. Attributed to the whole seeding time (which also holds the
+    # selection launches and the sample norms), so this underestimates the
+    # distance kernel's own rate.
+    dist_bytes = (4.0 * n * d + 8.0 * n + 4.0 * d) + (k - 1) * (
+        4.0 * n * d + 8.0 * n + trials * (8.0 * n + 4.0 * d))
+    achieved = dist_bytes / (ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle k-means++ on a prefix of the centres")
+        cpu = cpu_baseline_kmeanspp(X, k, first, trials, rand, args.cpu_seconds)
     result = {
         "metric": "k-means++ seeding ms (greedy, 2 + log(k) trials)",
         "value": round(ms, 3),
@@ -226,6 +268,8 @@ def bench_kmeanspp(args, cfg, X, Xg, stream) -> int:
                    "n": n, "k": k, "d": d, "trials": trials},
         "x_read_gbps": round(x_bytes / (ms * 1e-3) / 1e9, 1),
         "workspace_bytes": wsb,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
     return 0

@@ -20,6 +20,13 @@ Functions and the passages they follow:
 * ``lloyd_step`` - ``assign`` with the old centres, then ``update`` with those
   labels ("004 - tile sizes ...", section Cython reference: the assignment
   precedes the scatter into centre sums).
+* ``kmeanspp`` - greedy k-means++ seeding with the random draws passed in
+  ("004 - tile sizes ...", section k-means++: 2 + log(k) candidate trials per
+  centre); the steps are written out in ``oracle.c``. ``default_trials`` is
+  that trial count.
+* ``relocate``, ``fit`` - the Lloyd driver with empty-cluster relocation
+  ("004 - tile sizes ...", section Cython timing); the relocation rule is a
+  reading, stated above ``relocate``.
 * ``near_ties`` - rows whose best-to-second-best gap is within
   ``rtol * (||x||^2 + ||c_label||^2)``; on these rows two correct float32
   implementations may pick different labels ("004 - tile sizes ...", section
