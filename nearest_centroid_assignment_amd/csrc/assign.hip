@@ -173,19 +173,33 @@ __device__ __forceinline__ void store_stage(float (*lds)[Cfg::LDK], int tid,
 // One stage of MFMAs: for each group of 8 features, every (mb, nb) block
 // takes 4 MFMAs. The LDS->register fragments of the next group are read while
 // the MFMAs of the current group run.
+// Fragments of the first group of 8 features of a stage.
+template <class Cfg>
+__device__ __forceinline__ void first_frags(float (*lds)[Cfg::LDK], int lane, int wm, int wn,
+                                            f32x4 (&a0)[Cfg::MB], f32x4 (&b0)[Cfg::NB]) {
+    const int a_row = wm * Cfg::MB * 32 + (lane & 31);
+    const int b_row = Cfg::BM + wn * Cfg::NB * 32 + (lane & 31);
+    const int kofs = (lane >> 5) * 4;
+#pragma unroll
+    for (int mb = 0; mb < Cfg::MB; ++mb)
+        a0[mb] = *reinterpret_cast<const f32x4 *>(&lds[a_row + 32 * mb][kofs]);
+#pragma unroll
+    for (int nb = 0; nb < Cfg::NB; ++nb)
+        b0[nb] = *reinterpret_cast<const f32x4 *>(&lds[b_row + 32 * nb][kofs]);
+}
+
 template <class Cfg>
 __device__ __forceinline__ void mma_stage(float (*lds)[Cfg::LDK], int lane, int wm, int wn,
-                                                    f32x16 (&acc)[Cfg::MB][Cfg::NB]) {
+                                          const f32x4 (&a0)[Cfg::MB], const f32x4 (&b0)[Cfg::NB],
+                                          f32x16 (&acc)[Cfg::MB][Cfg::NB]) {
     const int a_row = wm * Cfg::MB * 32 + (lane & 31);
     const int b_row = Cfg::BM + wn * Cfg::NB * 32 + (lane & 31);
     const int kofs = (lane >> 5) * 4;
     f32x4 a[2][Cfg::MB], b[2][Cfg::NB];
 #pragma unroll
-    for (int mb = 0; mb < Cfg::MB; ++mb)
-        a[0][mb] = *reinterpret_cast<const f32x4 *>(&lds[a_row + 32 * mb][kofs]);
+    for (int mb = 0; mb < Cfg::MB; ++mb) a[0][mb] = a0[mb];
 #pragma unroll
-    for (int nb = 0; nb < Cfg::NB; ++nb)
-        b[0][nb] = *reinterpret_cast<const f32x4 *>(&lds[b_row + 32 * nb][kofs]);
+    for (int nb = 0; nb < Cfg::NB; ++nb) b[0][nb] = b0[nb];
 #pragma unroll
     for (int g = 0; g < Cfg::BK / 8; ++g) {
         const int cur = g & 1;
@@ -257,14 +271,38 @@ __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
     // At the top of iteration it: lds[it % 2] holds stage it, r holds (or is
     // receiving) stage it + 1, and lds[(it + 1) % 2] is free (its previous
     // stage was finished by every wave before the last barrier).
-    for (int64_t it = 0; it < nk; ++it) {
+    // The first fragments of a stage are read before its LDS writes are
+    // issued, so the first MFMAs do not wait behind those writes. The last
+    // two stages are peeled off so that the main loop has no branch between
+    // those reads and the MFMAs (a branch there makes the compiler wait for
+    // every LDS operation, writes included).
+    int64_t it = 0;
+    for (; it + 2 < nk; ++it) {
         const int cur = (int)(it & 1);
-        if (it + 1 < nk) {
-            store_stage<Cfg>(lds[cur ^ 1], tid, r);
-            if (it + 2 < nk) load_stage<Cfg, Mode>(X, C, n, k, d, m0, n0, (it + 2) * kBK, tid, r);
-        }
-        mma_stage<Cfg>(lds[cur], lane, wm, wn, acc);
+        f32x4 a0[Cfg::MB], b0[Cfg::NB];
+        first_frags<Cfg>(lds[cur], lane, wm, wn, a0, b0);
+        store_stage<Cfg>(lds[cur ^ 1], tid, r);
+        load_stage<Cfg, Mode>(X, C, n, k, d, m0, n0, (it + 2) * kBK, tid, r);
+        // Keep the global loads here, a whole stage ahead of their use: left
+        // alone, the scheduler sinks them below the MFMAs to reuse registers.
+        __builtin_amdgcn_sched_barrier(0);
+        mma_stage<Cfg>(lds[cur], lane, wm, wn, a0, b0, acc);
         __syncthreads();
+    }
+    if (it + 1 < nk) {
+        const int cur = (int)(it & 1);
+        f32x4 a0[Cfg::MB], b0[Cfg::NB];
+        first_frags<Cfg>(lds[cur], lane, wm, wn, a0, b0);
+        store_stage<Cfg>(lds[cur ^ 1], tid, r);
+        mma_stage<Cfg>(lds[cur], lane, wm, wn, a0, b0, acc);
+        __syncthreads();
+        ++it;
+    }
+    if (it < nk) {
+        const int cur = (int)(it & 1);
+        f32x4 a0[Cfg::MB], b0[Cfg::NB];
+        first_frags<Cfg>(lds[cur], lane, wm, wn, a0, b0);
+        mma_stage<Cfg>(lds[cur], lane, wm, wn, a0, b0, acc);
     }
 
     // Epilogue. Accumulator element e of a 32 x 32 block sits at row
@@ -308,6 +346,7 @@ using Tile128x256 = TileCfg<2, 4, 2, 2, 32>;  // 512 threads, 108 KiB LDS, 1 blo
 using Tile256x128 = TileCfg<4, 2, 2, 2, 32>;  // 512 threads, 108 KiB LDS, 1 block per CU
 using Tile128x128 = TileCfg<2, 2, 2, 2, 16>;  // 256 threads, 40 KiB LDS, 3 blocks per CU
 using Tile64x64 = TileCfg<2, 2, 1, 1, 32>;    // 256 threads, 36 KiB LDS, small problems
+using Tile128x256s = TileCfg<2, 4, 2, 2, 16>; // 512 threads, 60 KiB LDS, 2 blocks per CU
 
 __global__ __launch_bounds__(256) void finalize_kernel(unsigned long long *__restrict__ keys,
                                                        float *__restrict__ min_dist, int64_t n) {
@@ -391,7 +430,8 @@ static const char *assign_tile_name(int64_t n, int64_t k, int64_t d) {
     // KMEANS_ASSIGN_TILE=128x256 | 256x128 | 128x128 | 64x64 forces a tile (tuning).
     const char *forced = getenv("KMEANS_ASSIGN_TILE");
     if (forced && (!strcmp(forced, "256x128") || !strcmp(forced, "128x128") ||
-                   !strcmp(forced, "64x64") || !strcmp(forced, "128x256")))
+                   !strcmp(forced, "64x64") || !strcmp(forced, "128x256") ||
+                   !strcmp(forced, "128x256s")))
         return forced;
     // The largest tile (fewest operand bytes per flop) when it gives at least
     // two blocks per CU; otherwise 128 x 128 with short stages (3 blocks per
@@ -412,6 +452,8 @@ hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, 
         return launch_tiles_cfg<Tile128x128, 3>(X, C, cn, n, k, d, keys, stream);
     if (!strcmp(tile, "128x256"))
         return launch_tiles_cfg<Tile128x256, 2>(X, C, cn, n, k, d, keys, stream);
+    if (!strcmp(tile, "128x256s"))
+        return launch_tiles_cfg<Tile128x256s, 4>(X, C, cn, n, k, d, keys, stream);
     return launch_tiles_cfg<Tile64x64, 4>(X, C, cn, n, k, d, keys, stream);
 }
 
