@@ -99,11 +99,13 @@ __global__ __launch_bounds__(256) void fill_keys_kernel(unsigned long long *__re
 // product is the same dot product summed in a different order.
 //
 // Pipeline: features advance in stages of BK through two LDS buffers. At the
-// start of stage s each thread writes its registers (stage s + 1, loaded one
-// stage earlier) into the free LDS buffer and issues the global loads of
-// stage s + 2; the LDS writes and the loads then overlap the MFMAs of stage s.
-// Inside a stage the fragments of the next group of 8 features are read from
-// LDS while the current group's MFMAs run. One barrier per stage.
+// start of stage s each thread reads the stage's first fragments, writes its
+// registers (stage s + 1, loaded one stage earlier) into the free LDS buffer
+// and issues the global loads of stage s + 2; the LDS writes and the loads
+// then overlap the MFMAs of stage s. Inside a stage the fragments of the next
+// group of 8 features are read from LDS while the current group's MFMAs run;
+// the last group's MFMAs are deferred past the stage's barrier. One barrier
+// per stage.
 constexpr int kGroupM = 8;  // centroid tiles per rasterisation group
 
 template <int WM_, int WN_, int MB_, int NB_, int BK_>
@@ -188,10 +190,30 @@ __device__ __forceinline__ void first_frags(float (*lds)[Cfg::LDK], int lane, in
         b0[nb] = *reinterpret_cast<const f32x4 *>(&lds[b_row + 32 * nb][kofs]);
 }
 
+// The MFMAs of one group of 8 features for every (mb, nb) block.
 template <class Cfg>
-__device__ __forceinline__ void mma_stage(float (*lds)[Cfg::LDK], int lane, int wm, int wn,
-                                          const f32x4 (&a0)[Cfg::MB], const f32x4 (&b0)[Cfg::NB],
+__device__ __forceinline__ void mma_group(const f32x4 (&a)[Cfg::MB], const f32x4 (&b)[Cfg::NB],
                                           f32x16 (&acc)[Cfg::MB][Cfg::NB]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int mb = 0; mb < Cfg::MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < Cfg::NB; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[mb][e], b[nb][e],
+                                                                  acc[mb][nb], 0, 0, 0);
+}
+
+// Every group of a stage but the last: the fragments of the next group are
+// read while the current group's MFMAs run. The last group's fragments are
+// returned in aL / bL; its MFMAs run after the stage's barrier (mma_group),
+// once the next stage's first reads have been issued.
+template <class Cfg>
+__device__ __forceinline__ void mma_head(float (*lds)[Cfg::LDK], int lane, int wm, int wn,
+                                         const f32x4 (&a0)[Cfg::MB], const f32x4 (&b0)[Cfg::NB],
+                                         f32x16 (&acc)[Cfg::MB][Cfg::NB], f32x4 (&aL)[Cfg::MB],
+                                         f32x4 (&bL)[Cfg::NB]) {
+    constexpr int G = Cfg::BK / 8;
     const int a_row = wm * Cfg::MB * 32 + (lane & 31);
     const int b_row = Cfg::BM + wn * Cfg::NB * 32 + (lane & 31);
     const int kofs = (lane >> 5) * 4;
@@ -201,27 +223,22 @@ __device__ __forceinline__ void mma_stage(float (*lds)[Cfg::LDK], int lane, int 
 #pragma unroll
     for (int nb = 0; nb < Cfg::NB; ++nb) b[0][nb] = b0[nb];
 #pragma unroll
-    for (int g = 0; g < Cfg::BK / 8; ++g) {
+    for (int g = 0; g + 1 < G; ++g) {
         const int cur = g & 1;
-        if (g + 1 < Cfg::BK / 8) {
 #pragma unroll
-            for (int mb = 0; mb < Cfg::MB; ++mb)
-                a[cur ^ 1][mb] =
-                    *reinterpret_cast<const f32x4 *>(&lds[a_row + 32 * mb][8 * (g + 1) + kofs]);
+        for (int mb = 0; mb < Cfg::MB; ++mb)
+            a[cur ^ 1][mb] =
+                *reinterpret_cast<const f32x4 *>(&lds[a_row + 32 * mb][8 * (g + 1) + kofs]);
 #pragma unroll
-            for (int nb = 0; nb < Cfg::NB; ++nb)
-                b[cur ^ 1][nb] =
-                    *reinterpret_cast<const f32x4 *>(&lds[b_row + 32 * nb][8 * (g + 1) + kofs]);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int mb = 0; mb < Cfg::MB; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < Cfg::NB; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                        a[cur][mb][e], b[cur][nb][e], acc[mb][nb], 0, 0, 0);
+        for (int nb = 0; nb < Cfg::NB; ++nb)
+            b[cur ^ 1][nb] =
+                *reinterpret_cast<const f32x4 *>(&lds[b_row + 32 * nb][8 * (g + 1) + kofs]);
+        mma_group<Cfg>(a[cur], b[cur], acc);
     }
+#pragma unroll
+    for (int mb = 0; mb < Cfg::MB; ++mb) aL[mb] = a[(G - 1) & 1][mb];
+#pragma unroll
+    for (int nb = 0; nb < Cfg::NB; ++nb) bL[nb] = b[(G - 1) & 1][nb];
 }
 
 template <class Cfg, int Mode, int MinWaves>
@@ -271,30 +288,41 @@ __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
     // At the top of iteration it: lds[it % 2] holds stage it, r holds (or is
     // receiving) stage it + 1, and lds[(it + 1) % 2] is free (its previous
     // stage was finished by every wave before the last barrier).
-    // The first fragments of a stage are read before its LDS writes are
-    // issued, so the first MFMAs do not wait behind those writes. The last
-    // two stages are peeled off so that the main loop has no branch between
-    // those reads and the MFMAs (a branch there makes the compiler wait for
-    // every LDS operation, writes included).
+    // Each stage's last group of MFMAs is deferred past the barrier into the
+    // next iteration, where it keeps the matrix cores busy while the next
+    // stage's first fragments are read. Those reads are issued before the
+    // stage's LDS writes, so the first MFMAs do not wait behind the writes.
+    // The last two stages are peeled off so that the main loop has no branch
+    // between those reads and the MFMAs (a branch there makes the compiler
+    // wait for every LDS operation, writes included). Before the first stage
+    // the pending group is zeros: those MFMAs add exact zeros to the zero
+    // accumulators, and every accumulator still sees its features in order.
+    f32x4 aL[Cfg::MB], bL[Cfg::NB];
+#pragma unroll
+    for (int mb = 0; mb < Cfg::MB; ++mb) aL[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nb = 0; nb < Cfg::NB; ++nb) bL[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     int64_t it = 0;
     for (; it + 2 < nk; ++it) {
         const int cur = (int)(it & 1);
         f32x4 a0[Cfg::MB], b0[Cfg::NB];
         first_frags<Cfg>(lds[cur], lane, wm, wn, a0, b0);
+        mma_group<Cfg>(aL, bL, acc);
         store_stage<Cfg>(lds[cur ^ 1], tid, r);
         load_stage<Cfg, Mode>(X, C, n, k, d, m0, n0, (it + 2) * kBK, tid, r);
         // Keep the global loads here, a whole stage ahead of their use: left
         // alone, the scheduler sinks them below the MFMAs to reuse registers.
         __builtin_amdgcn_sched_barrier(0);
-        mma_stage<Cfg>(lds[cur], lane, wm, wn, a0, b0, acc);
+        mma_head<Cfg>(lds[cur], lane, wm, wn, a0, b0, acc, aL, bL);
         __syncthreads();
     }
     if (it + 1 < nk) {
         const int cur = (int)(it & 1);
         f32x4 a0[Cfg::MB], b0[Cfg::NB];
         first_frags<Cfg>(lds[cur], lane, wm, wn, a0, b0);
+        mma_group<Cfg>(aL, bL, acc);
         store_stage<Cfg>(lds[cur ^ 1], tid, r);
-        mma_stage<Cfg>(lds[cur], lane, wm, wn, a0, b0, acc);
+        mma_head<Cfg>(lds[cur], lane, wm, wn, a0, b0, acc, aL, bL);
         __syncthreads();
         ++it;
     }
@@ -302,8 +330,10 @@ __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
         const int cur = (int)(it & 1);
         f32x4 a0[Cfg::MB], b0[Cfg::NB];
         first_frags<Cfg>(lds[cur], lane, wm, wn, a0, b0);
-        mma_stage<Cfg>(lds[cur], lane, wm, wn, a0, b0, acc);
+        mma_group<Cfg>(aL, bL, acc);
+        mma_head<Cfg>(lds[cur], lane, wm, wn, a0, b0, acc, aL, bL);
     }
+    mma_group<Cfg>(aL, bL, acc);
 
     // Epilogue. Accumulator element e of a 32 x 32 block sits at row
     // 8 * (e / 4) + 4 * (lane / 32) + e % 4 and column lane % 32.
