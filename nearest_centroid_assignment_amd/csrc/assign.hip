@@ -376,7 +376,6 @@ using Tile128x256 = TileCfg<2, 4, 2, 2, 32>;  // 512 threads, 108 KiB LDS, 1 blo
 using Tile256x128 = TileCfg<4, 2, 2, 2, 32>;  // 512 threads, 108 KiB LDS, 1 block per CU
 using Tile128x128 = TileCfg<2, 2, 2, 2, 16>;  // 256 threads, 40 KiB LDS, 3 blocks per CU
 using Tile64x64 = TileCfg<2, 2, 1, 1, 32>;    // 256 threads, 36 KiB LDS, small problems
-using Tile128x256s = TileCfg<2, 4, 2, 2, 16>; // 512 threads, 60 KiB LDS, 2 blocks per CU
 
 __global__ __launch_bounds__(256) void finalize_kernel(unsigned long long *__restrict__ keys,
                                                        float *__restrict__ min_dist, int64_t n) {
@@ -460,8 +459,7 @@ static const char *assign_tile_name(int64_t n, int64_t k, int64_t d) {
     // KMEANS_ASSIGN_TILE=128x256 | 256x128 | 128x128 | 64x64 forces a tile (tuning).
     const char *forced = getenv("KMEANS_ASSIGN_TILE");
     if (forced && (!strcmp(forced, "256x128") || !strcmp(forced, "128x128") ||
-                   !strcmp(forced, "64x64") || !strcmp(forced, "128x256") ||
-                   !strcmp(forced, "128x256s")))
+                   !strcmp(forced, "64x64") || !strcmp(forced, "128x256")))
         return forced;
     // The largest tile (fewest operand bytes per flop) when it gives at least
     // two blocks per CU; otherwise 128 x 128 with short stages (3 blocks per
@@ -482,8 +480,6 @@ hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, 
         return launch_tiles_cfg<Tile128x128, 3>(X, C, cn, n, k, d, keys, stream);
     if (!strcmp(tile, "128x256"))
         return launch_tiles_cfg<Tile128x256, 2>(X, C, cn, n, k, d, keys, stream);
-    if (!strcmp(tile, "128x256s"))
-        return launch_tiles_cfg<Tile128x256s, 4>(X, C, cn, n, k, d, keys, stream);
     return launch_tiles_cfg<Tile64x64, 4>(X, C, cn, n, k, d, keys, stream);
 }
 
