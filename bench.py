@@ -12,6 +12,7 @@ Prints one JSON line:
   value        2*n*k*d / (Lloyd step time), TFLOP/s (whole step, update included)
   ms_per_step  Lloyd iteration time in ms
   assign_*     the fused assignment alone (kmeans_assign without min_dist)
+  update_*     the centroid update alone (kmeans_update) and its HBM rate
   roofline     the fused assignment kernel against the MI355X fp32 MFMA peak
   cpu_baseline the float64 oracle on a bounded sample of rows, host cores
 """
@@ -361,6 +362,20 @@ def main() -> int:
     flops = cfg.flops
     assign_tflops = flops / (assign_ms * 1e-3) / 1e12
 
+    # The update alone (labels from the assignments just timed), for its HBM
+    # rate: algorithmic bytes = X once (4nd), the labels once (8n) and the new
+    # centres (4kd).
+    log(f"timing {args.steps} updates")
+    uevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
+    for a, b in uevs:
+        a.record(stream)
+        binding.kmeans_update(Xg, labels, Cg, C_new, counts, workspace=ws, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    update_ms = sum(a.elapsed_time(b) for a, b in uevs) / len(uevs)
+    update_gbps = (4.0 * n * d + 8.0 * n + 4.0 * k * d) / (update_ms * 1e-3) / 1e9
+
     traffic = traffic_record(cfg)
     roofline = {
         "bound": "mfma",
@@ -394,6 +409,9 @@ def main() -> int:
         "assign_ms": round(assign_ms, 3),
         "assign_ms_min": round(per_call[0], 3),
         "assign_tflops": round(assign_tflops, 3),
+        "update_ms": round(update_ms, 3),
+        "update_hbm_gbps": round(update_gbps, 1),
+        "update_frac_of_hbm_peak": round(update_gbps / HBM_PEAK_GBPS, 4),
         "workspace_bytes": ws_bytes,
         "peak_extra_bytes_during_step": int(peak_extra),
         "roofline": roofline,
