@@ -20,7 +20,7 @@
 //
 // Per call, pp_norm_kernel computes |x_i|^2 once. Per centre, two launches
 // and nothing on the host:
-//   pp_select_kernel  one block: potentials of the previous trials from the
+//   pp_select_kernel  one 1024-thread block: potentials of the previous trials from the
 //                     per-block partials (fixed-order block reduction), the
 //                     winner, its row copied out as a centre, then the next
 //                     candidates: a scan over the block sums of D finds the
@@ -314,41 +314,58 @@ void launch_dist(int trials, bool vec, unsigned nb, hipStream_t stream, const fl
     }
 }
 
-// Sum over the 256 threads of the block in a fixed order.
-__device__ double block_sum256(double v, double *lds4) {
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    if ((threadIdx.x & 63) == 0) lds4[threadIdx.x >> 6] = v;
-    __syncthreads();
-    const double t = ((lds4[0] + lds4[1]) + lds4[2]) + lds4[3];
-    __syncthreads();
-    return t;
-}
+constexpr int kSelWaves = 16;  // pp_select_kernel: one 1024-thread block
 
 // Winner of the previous trials, recorded as centre c_rec; then, if rand_row
-// is not NULL, the next candidates. One block of 256 threads.
-__global__ __launch_bounds__(256) void pp_select_kernel(
+// is not NULL, the next candidates. One block of 1024 threads; every sum has
+// a fixed order.
+__global__ __launch_bounds__(kSelWaves * 64) void pp_select_kernel(
     const float *__restrict__ X, int64_t n, int64_t d, const double *__restrict__ prev_buf,
     const double *__restrict__ prev_parts, int64_t nb, int trials_prev,
     const long long *__restrict__ cand_prev, PPState *st, int64_t c_rec,
     long long *__restrict__ chosen, float *__restrict__ centres,
     const double *__restrict__ rand_row, int trials_next, long long *__restrict__ cand_next) {
-    __shared__ double lds4[4];
+    constexpr int kThreads = kSelWaves * 64;
+    __shared__ double wsum[kPPMaxTrials][kSelWaves];
     __shared__ double pots[kPPMaxTrials];
-    __shared__ double scan_tot[4];
+    __shared__ double scan_tot[kSelWaves];
+    __shared__ double chunk_excl[kThreads];
+    __shared__ int wave_first[kPPMaxTrials][kSelWaves];
     __shared__ int found_block[kPPMaxTrials];
     __shared__ double found_before[kPPMaxTrials];
-    __shared__ int wave_first[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    // Potentials: thread j adds the partials b = j, j + 256, ... in order,
-    // then a fixed tree over the threads.
-    for (int t = 0; t < trials_prev; ++t) {
-        double s = 0.0;
-        for (int64_t b = tid; b < nb; b += 256) s += prev_parts[(int64_t)t * nb + b];
-        const double tot = block_sum256(s, lds4);
-        if (tid == 0) pots[t] = tot;
+    // Potentials: thread j adds the partials b = j, j + 1024, ... in order;
+    // the threads are combined by a butterfly within each wave, then the
+    // waves in order. All trials' loads are issued together.
+    {
+        double s[kPPMaxTrials];
+#pragma unroll
+        for (int t = 0; t < kPPMaxTrials; ++t) s[t] = 0.0;
+        for (int64_t b = tid; b < nb; b += kThreads) {
+            double v[kPPMaxTrials];
+#pragma unroll
+            for (int t = 0; t < kPPMaxTrials; ++t)
+                v[t] = t < trials_prev ? prev_parts[(int64_t)t * nb + b] : 0.0;
+#pragma unroll
+            for (int t = 0; t < kPPMaxTrials; ++t) s[t] += v[t];
+        }
+#pragma unroll
+        for (int t = 0; t < kPPMaxTrials; ++t) {
+            if (t < trials_prev) {
+                double v = s[t];
+                for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+                if (lane == 0) wsum[t][wave] = v;
+            }
+        }
+        __syncthreads();
+        if (tid < trials_prev) {
+            double tot = 0.0;
+            for (int w = 0; w < kSelWaves; ++w) tot += wsum[tid][w];
+            pots[tid] = tot;
+        }
+        __syncthreads();
     }
-    __syncthreads();
     int best = 0;
     for (int t = 1; t < trials_prev; ++t)
         if (pots[t] < pots[best]) best = t;
@@ -359,7 +376,7 @@ __global__ __launch_bounds__(256) void pp_select_kernel(
         st->pot = pot;
         chosen[c_rec] = row;
     }
-    for (int64_t f = tid; f < d; f += 256) centres[c_rec * d + f] = X[row * d + f];
+    for (int64_t f = tid; f < d; f += kThreads) centres[c_rec * d + f] = X[row * d + f];
     if (!rand_row) return;
 
     // Candidate draws: the first sample whose running sum of D reaches
@@ -372,9 +389,8 @@ __global__ __launch_bounds__(256) void pp_select_kernel(
         found_block[tid] = -1;
         found_before[tid] = 0.0;
     }
-    __syncthreads();
     double carry = 0.0;
-    for (int64_t b0 = 0; b0 < nb; b0 += 256) {
+    for (int64_t b0 = 0; b0 < nb; b0 += kThreads) {
         const int64_t b = b0 + tid;
         const double v = b < nb ? parts[b] : 0.0;
         double incl = v;
@@ -385,37 +401,39 @@ __global__ __launch_bounds__(256) void pp_select_kernel(
         double excl = __shfl_up(incl, 1);
         if (lane == 0) excl = 0.0;
         if (lane == 63) scan_tot[wave] = incl;
-        __syncthreads();
-        double before_wave = 0.0;
-        for (int w = 0; w < wave; ++w) before_wave += scan_tot[w];
-        const double chunk_tot = ((scan_tot[0] + scan_tot[1]) + scan_tot[2]) + scan_tot[3];
+        __syncthreads();  // also publishes found_block from the previous chunk
+        double before_wave = 0.0, chunk_tot = 0.0;
+        for (int w = 0; w < kSelWaves; ++w) {
+            before_wave += w < wave ? scan_tot[w] : 0.0;
+            chunk_tot += scan_tot[w];
+        }
         const double run_incl = carry + (before_wave + incl);
-        const double run_excl = carry + (before_wave + excl);
-        // For each trial still open: the lowest block of this chunk whose
-        // inclusive running sum reaches its target.
+        chunk_excl[tid] = carry + (before_wave + excl);
+        // For each trial still open: this wave's lowest block whose inclusive
+        // running sum reaches the trial's target.
         for (int t = 0; t < trials_next; ++t) {
-            const bool open = found_block[t] < 0;  // uniform
-            const bool hit = open && b < nb && run_incl >= rand_row[t] * pot;
+            const bool hit = found_block[t] < 0 && b < nb && run_incl >= rand_row[t] * pot;
             const unsigned long long m = __ballot(hit);
-            if (lane == 0) wave_first[wave] = m ? (int)(b0 + wave * 64 + __ffsll((long long)m) - 1) : -1;
-            __syncthreads();
-            if (tid == 0 && open) {
-                for (int w = 0; w < 4; ++w)
-                    if (wave_first[w] >= 0) {
-                        found_block[t] = wave_first[w];
-                        break;
-                    }
-            }
-            __syncthreads();
-            if (open && b == found_block[t]) found_before[t] = run_excl;
-            __syncthreads();
+            if (lane == 0) wave_first[t][wave] = m ? (int)(b0 + wave * 64 + __ffsll((long long)m) - 1) : -1;
+        }
+        __syncthreads();
+        bool all_found = true;
+        if (tid < trials_next && found_block[tid] < 0) {
+            for (int w = 0; w < kSelWaves; ++w)
+                if (wave_first[tid][w] >= 0) {
+                    found_block[tid] = wave_first[tid][w];
+                    found_before[tid] = chunk_excl[wave_first[tid][w] - b0];
+                    break;
+                }
         }
         carry += chunk_tot;
-        __syncthreads();  // scan_tot is rewritten by the next chunk
+        __syncthreads();  // found_block, found_before published; scan_tot, chunk_excl reusable
+        for (int t = 0; t < trials_next; ++t) all_found = all_found && found_block[t] >= 0;
+        if (all_found) break;  // uniform: every thread reads the same LDS values
     }
     // One wave per trial: walk the rows from the block found (64 rows = one
     // wave), continuing into later blocks if the target lies beyond it.
-    for (int t = wave; t < trials_next; t += 4) {
+    for (int t = wave; t < trials_next; t += kSelWaves) {
         const double target = rand_row[t] * pot;
         int64_t idx = n - 1;
         if (found_block[t] >= 0) {
@@ -468,7 +486,7 @@ hipError_t launch_kmeanspp(const float *X, int64_t n, int64_t d, int64_t k, int6
     int cur = 0, trials_prev = 1;
     for (int64_t c = 1; c <= k; ++c) {
         const bool more = c < k;
-        pp_select_kernel<<<1, 256, 0, stream>>>(
+        pp_select_kernel<<<1, kSelWaves * 64, 0, stream>>>(
             X, n, d, buf[cur], parts[cur], nb, trials_prev, cand[cur], st, c - 1,
             (long long *)chosen, centres, more ? rand + (c - 1) * trials : nullptr, trials,
             cand[cur ^ 1]);
