@@ -1,0 +1,60 @@
+"""Host-side logic of bench.py (no GPU needed)."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from nearest_centroid_assignment_amd import datagen  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""  # no JSON line for a configuration that was not measured
+
+
+def test_traffic_record_requires_matching_kernel(tmp_path, monkeypatch):
+    from nearest_centroid_assignment_amd.profile_run import kernel_digest
+
+    cfg = datagen.CONFIGS["feature_heavy"]
+    rec = {"workload": "feature_heavy", "hbm_bytes_per_launch": 123.0,
+           "assign_kernel_sha256": kernel_digest()}
+    f = tmp_path / "t.json"
+    f.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.traffic_record(cfg) == 123.0
+    # Another workload, or a kernel changed since the counters were taken.
+    assert bench.traffic_record(datagen.CONFIGS["mid"]) is None
+    rec["assign_kernel_sha256"] = "0" * 64
+    f.write_text(json.dumps(rec))
+    assert bench.traffic_record(cfg) is None
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
+    assert bench.traffic_record(cfg) is None
+
+
+def test_cpu_baselines_report_their_sample():
+    X, C = datagen.make("tiny")
+    b = bench.cpu_baseline(X, C, 0.05)
+    assert b["kind"] == "oracle" and b["unit"] == "TFLOP/s" and b["value"] > 0
+    assert b["cores"] >= 1 and "rows" in b["sample"]
+    k, trials = 17, 4
+    first, rand = datagen.make_seeding_draws(len(X), k, trials)
+    p = bench.cpu_baseline_kmeanspp(X, k, first, trials, rand, 0.05)
+    assert p["kind"] == "oracle" and p["unit"] == "ms" and p["value"] > 0
+    assert "of 17 centres" in p["sample"]
+
+
+def test_bench_workloads_exist():
+    for name in ("feature_heavy", "centroid_heavy", "kmeanspp", "mid"):
+        cfg = datagen.CONFIGS[name]
+        assert cfg.flops == 2.0 * cfg.n * cfg.k * cfg.d or np.isclose(
+            cfg.flops, 2.0 * cfg.n * cfg.k * cfg.d)
+    assert set(bench.PAGES_LLOYD_MS) <= set(datagen.CONFIGS)
