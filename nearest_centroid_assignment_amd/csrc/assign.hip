@@ -280,58 +280,86 @@ __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
 
     constexpr int kBK = Cfg::BK;
     const int64_t nk = (d + kBK - 1) / kBK;
-    f32x4 r[Cfg::Q];
-    load_stage<Cfg, Mode>(X, C, n, k, d, m0, n0, 0, tid, r);
-    store_stage<Cfg>(lds[0], tid, r);
-    if (nk > 1) load_stage<Cfg, Mode>(X, C, n, k, d, m0, n0, kBK, tid, r);
+    // Two register sets carry the global loads: rA the odd stages, rB the
+    // even ones (from stage 2 on), so each load has two stages to arrive.
+    f32x4 rA[Cfg::Q], rB[Cfg::Q];
+    load_stage<Cfg, Mode>(X, C, n, k, d, m0, n0, 0, tid, rA);
+    store_stage<Cfg>(lds[0], tid, rA);
+    if (nk > 1) load_stage<Cfg, Mode>(X, C, n, k, d, m0, n0, kBK, tid, rA);
+    if (nk > 2) load_stage<Cfg, Mode>(X, C, n, k, d, m0, n0, 2 * kBK, tid, rB);
     __syncthreads();
-    // At the top of iteration it: lds[it % 2] holds stage it, r holds (or is
-    // receiving) stage it + 1, and lds[(it + 1) % 2] is free (its previous
-    // stage was finished by every wave before the last barrier).
     // Each stage's last group of MFMAs is deferred past the barrier into the
-    // next iteration, where it keeps the matrix cores busy while the next
-    // stage's first fragments are read. Those reads are issued before the
-    // stage's LDS writes, so the first MFMAs do not wait behind the writes.
-    // The last two stages are peeled off so that the main loop has no branch
-    // between those reads and the MFMAs (a branch there makes the compiler
-    // wait for every LDS operation, writes included). Before the first stage
-    // the pending group is zeros: those MFMAs add exact zeros to the zero
-    // accumulators, and every accumulator still sees its features in order.
+    // next stage, where it keeps the matrix cores busy while the next stage's
+    // first fragments are read. Those reads are issued before the stage's LDS
+    // writes, so the first MFMAs do not wait behind the writes. The main loop
+    // takes two stages at a time (stage it even: lds[0] holds it, rA holds
+    // it + 1, rB holds it + 2) and runs while both of its loads exist, so it
+    // has no branch between those reads and the MFMAs (a branch there makes
+    // the compiler wait for every LDS operation, writes included); the last
+    // one to four stages follow. Before the first stage the pending group is
+    // zeros: those MFMAs add exact zeros to the zero accumulators, and every
+    // accumulator still sees its features in order.
     f32x4 aL[Cfg::MB], bL[Cfg::NB];
 #pragma unroll
     for (int mb = 0; mb < Cfg::MB; ++mb) aL[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nb = 0; nb < Cfg::NB; ++nb) bL[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     int64_t it = 0;
-    for (; it + 2 < nk; ++it) {
-        const int cur = (int)(it & 1);
+    for (; it + 4 < nk; it += 2) {
+        {
+            f32x4 a0[Cfg::MB], b0[Cfg::NB];
+            first_frags<Cfg>(lds[0], lane, wm, wn, a0, b0);
+            mma_group<Cfg>(aL, bL, acc);
+            store_stage<Cfg>(lds[1], tid, rA);
+            load_stage<Cfg, Mode>(X, C, n, k, d, m0, n0, (it + 3) * kBK, tid, rA);
+            // Keep the global loads here, ahead of the MFMAs: left alone, the
+            // scheduler sinks them below the MFMAs to reuse registers.
+            __builtin_amdgcn_sched_barrier(0);
+            mma_head<Cfg>(lds[0], lane, wm, wn, a0, b0, acc, aL, bL);
+            __syncthreads();
+        }
+        {
+            f32x4 a0[Cfg::MB], b0[Cfg::NB];
+            first_frags<Cfg>(lds[1], lane, wm, wn, a0, b0);
+            mma_group<Cfg>(aL, bL, acc);
+            store_stage<Cfg>(lds[0], tid, rB);
+            load_stage<Cfg, Mode>(X, C, n, k, d, m0, n0, (it + 4) * kBK, tid, rB);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_head<Cfg>(lds[1], lane, wm, wn, a0, b0, acc, aL, bL);
+            __syncthreads();
+        }
+    }
+    // The last 1 to 4 stages: it, it + 1, it + 2, it + 3 (it is even).
+    {
         f32x4 a0[Cfg::MB], b0[Cfg::NB];
-        first_frags<Cfg>(lds[cur], lane, wm, wn, a0, b0);
+        first_frags<Cfg>(lds[0], lane, wm, wn, a0, b0);
         mma_group<Cfg>(aL, bL, acc);
-        store_stage<Cfg>(lds[cur ^ 1], tid, r);
-        load_stage<Cfg, Mode>(X, C, n, k, d, m0, n0, (it + 2) * kBK, tid, r);
-        // Keep the global loads here, a whole stage ahead of their use: left
-        // alone, the scheduler sinks them below the MFMAs to reuse registers.
-        __builtin_amdgcn_sched_barrier(0);
-        mma_head<Cfg>(lds[cur], lane, wm, wn, a0, b0, acc, aL, bL);
-        __syncthreads();
+        if (it + 1 < nk) store_stage<Cfg>(lds[1], tid, rA);
+        if (it + 3 < nk) load_stage<Cfg, Mode>(X, C, n, k, d, m0, n0, (it + 3) * kBK, tid, rA);
+        mma_head<Cfg>(lds[0], lane, wm, wn, a0, b0, acc, aL, bL);
+        if (it + 1 < nk) __syncthreads();
     }
     if (it + 1 < nk) {
-        const int cur = (int)(it & 1);
         f32x4 a0[Cfg::MB], b0[Cfg::NB];
-        first_frags<Cfg>(lds[cur], lane, wm, wn, a0, b0);
+        first_frags<Cfg>(lds[1], lane, wm, wn, a0, b0);
         mma_group<Cfg>(aL, bL, acc);
-        store_stage<Cfg>(lds[cur ^ 1], tid, r);
-        mma_head<Cfg>(lds[cur], lane, wm, wn, a0, b0, acc, aL, bL);
-        __syncthreads();
-        ++it;
+        if (it + 2 < nk) store_stage<Cfg>(lds[0], tid, rB);
+        mma_head<Cfg>(lds[1], lane, wm, wn, a0, b0, acc, aL, bL);
+        if (it + 2 < nk) __syncthreads();
     }
-    if (it < nk) {
-        const int cur = (int)(it & 1);
+    if (it + 2 < nk) {
         f32x4 a0[Cfg::MB], b0[Cfg::NB];
-        first_frags<Cfg>(lds[cur], lane, wm, wn, a0, b0);
+        first_frags<Cfg>(lds[0], lane, wm, wn, a0, b0);
         mma_group<Cfg>(aL, bL, acc);
-        mma_head<Cfg>(lds[cur], lane, wm, wn, a0, b0, acc, aL, bL);
+        if (it + 3 < nk) store_stage<Cfg>(lds[1], tid, rA);
+        mma_head<Cfg>(lds[0], lane, wm, wn, a0, b0, acc, aL, bL);
+        if (it + 3 < nk) __syncthreads();
+    }
+    if (it + 3 < nk) {
+        f32x4 a0[Cfg::MB], b0[Cfg::NB];
+        first_frags<Cfg>(lds[1], lane, wm, wn, a0, b0);
+        mma_group<Cfg>(aL, bL, acc);
+        mma_head<Cfg>(lds[1], lane, wm, wn, a0, b0, acc, aL, bL);
     }
     mma_group<Cfg>(aL, bL, acc);
 

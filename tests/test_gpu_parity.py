@@ -212,10 +212,13 @@ def test_library_allocates_nothing():
 
 @pytest.mark.parametrize("tile", ["128x256", "256x128", "128x128", "64x64"])
 @pytest.mark.parametrize("n,k,d", [(1000, 300, 1028), (130, 129, 33), (2048, 512, 256),
-                                   (777, 260, 64), (512, 256, 48)])
+                                   (777, 260, 64), (512, 256, 48), (300, 260, 150),
+                                   (257, 130, 100), (260, 257, 16)])
 def test_tile_variants(monkeypatch, tile, n, k, d):
     """Every tile shape the launcher can select, on full, ragged and scalar
-    paths (integer data: bit-exact labels, ties included)."""
+    paths (integer data: bit-exact labels, ties included). The feature counts
+    give 1 to 65 stages, so the main loop runs zero, one or many times and
+    every length of the pipeline's tail (1 to 4 stages) occurs."""
     monkeypatch.setenv("KMEANS_ASSIGN_TILE", tile)
     gu.announce(f"tile {tile} {n}x{k}x{d}")
     X, C = datagen.make_integer(n, k, d, seed=n + d)
