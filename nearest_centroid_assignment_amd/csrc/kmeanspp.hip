@@ -14,23 +14,22 @@
 // Distances are float64 in Gram form, |x|^2 + |c|^2 - 2 x.c clamped at 0,
 // with the sample norms computed once per call as the pages' faster version
 // does. A float32 x float32 product is exact in float64, so the only
-// roundings are those of the float64 sums; the norms use the same per-lane
-// order and reduction tree as the dot products, so a sample's distance to
-// itself is exactly 0.
+// roundings are those of the float64 sums; a sample's distance to itself is
+// set to exactly 0.
 //
 // Per call, pp_norm_kernel computes |x_i|^2 once. Per centre, two launches
 // and nothing on the host:
-//   pp_select_kernel  one 1024-thread block: potentials of the previous trials from the
-//                     per-block partials (fixed-order block reduction), the
-//                     winner, its row copied out as a centre, then the next
-//                     candidates: a scan over the block sums of D finds the
-//                     block each draw falls in, one wave per draw walks its
-//                     rows
-//   pp_dist_kernel    every sample against all candidates: candidate rows
-//                     staged in LDS 256 or 512 features at a time (double
-//                     buffered, the next stage's loads in flight during the
-//                     current one), a wave on 1, 2 or 4 samples at once,
-//                     float64 dot products; min with D; per-block partials
+//   pp_select_kernel  one 1024-thread block: potentials of the previous
+//                     trials from the per-block partials (fixed-order
+//                     reduction), the winner, its row copied out as a centre,
+//                     then the next candidates: a scan over the block sums of
+//                     D finds the block each draw falls in, one wave per draw
+//                     walks its rows
+//   pp_dist_kernel    every sample against all candidates on the float64
+//                     matrix cores (16 samples x 16 candidate slots per wave),
+//                     samples staged through per-wave LDS slices, candidates
+//                     through shared LDS, the next stage's loads in flight
+//                     during the current one; min with D; per-block partials
 // Buffers of D and partials alternate between centres (A <-> B).
 #include "kernels.h"
 
@@ -38,7 +37,6 @@ namespace km {
 namespace {
 
 constexpr int kPPMaxTrials = 16;
-constexpr int kPPChunk = 256;       // features per lane-slice of a stage: 4 per lane
 constexpr int kPPRowsPerBlock = 64; // samples per block of pp_dist_kernel
 
 struct PPState {
@@ -65,253 +63,174 @@ __device__ __forceinline__ float4 load_row4(const float *__restrict__ X, int64_t
     return v;
 }
 
-// Sums over the 64 lanes of a wave of M values per lane, M = 2^m <= 64: at
-// each halving step a lane keeps one half of its values and adds the
-// partner's copy of that half, sending the other half (M - 1 shuffles
-// instead of M * 6). On return v[0] of lane l holds the total of value
-// l >> (6 - m). The order of the additions is fixed.
-template <int M>
-__device__ __forceinline__ void wave_sum_transpose(double (&v)[M], int lane) {
-    static_assert(M >= 1 && M <= 64 && (M & (M - 1)) == 0, "M must be a power of two");
-    constexpr int kSteps = M == 1 ? 0 : M == 2 ? 1 : M == 4 ? 2 : M == 8 ? 3 : M == 16 ? 4 : M == 32 ? 5 : 6;
-#pragma unroll
-    for (int step = 0; step < kSteps; ++step) {
-        const int half = M >> (step + 1), bit = 5 - step;
-        const bool hi = (lane >> bit) & 1;
-#pragma unroll
-        for (int i = 0; i < half; ++i) {
-            // Opaque copies: without them the compiler turns the two selects
-            // below into a lane-dependent index into v, which it can only
-            // lower as a compare chain over the whole array.
-            double lo = v[i], up = v[i + half];
-            asm volatile("" : "+v"(lo), "+v"(up));
-            const double send = hi ? lo : up;
-            const double keep = hi ? up : lo;
-            v[i] = keep + __shfl_xor(send, 1 << bit);
-        }
-    }
-#pragma unroll
-    for (int bit = 5 - kSteps; bit >= 0; --bit) v[0] += __shfl_xor(v[0], 1 << bit);
-}
-
-constexpr int pow2_at_least(int x) { return x <= 1 ? 1 : 2 * pow2_at_least((x + 1) / 2); }
-
-constexpr int kPPWaves = 8;  // waves per block of pp_dist_kernel (512 threads)
-
-// Samples [b * 64, b * 64 + 64) against the T candidate rows cand[0..T).
-// prev_buf + best * n holds D of the previous centre set (prev_buf NULL: the
-// first centre, D = +inf).
-//
-// 8 waves; a wave works on R samples at once, so every candidate value read
-// from LDS and widened to float64 serves R samples (R = 1, 2 or 4). Wave w's
-// samples are b*64 + w + 8 m for m = p*R + r (pass p, slot r), 8/R passes.
-// The work is a sequence of stages (pass, chunk of 256 V features); lane l
-// loads features 256 v + 4 l .. +3 (v < V) of its R samples and of the
-// candidates it stages. Everything a stage reads sits in LDS: the wave's own
-// sample values in xs (each wave overwrites only its own slice, after its
-// own reads, so one buffer suffices) and the candidates in cs, double
-// buffered and stored [t][4 v + q][lane] so that the reads of one (t, v, q)
-// are 64 consecutive words. The registers only carry the next stage's loads,
-// issued before the current stage is computed; one barrier per stage. At
-// most 128 registers (4 waves per SIMD) let two blocks share a CU, so one
-// computes while the other waits.
-// |x_i|^2 in float64, one wave per sample, 4 samples per 256-thread block.
-// Lane l adds x_f^2 for f = 256 s' + 4 l + q in the order of slices s' and
-// then q, and the lanes are combined by the butterfly of wave_sum_transpose:
-// the same order as the dot products of pp_dist_kernel, so |x_i|^2 equals
-// x_i . x_i there bit for bit.
+// |x_i|^2 in float64 (exact float32 squares, float64 sums in a fixed order),
+// one wave per sample, 4 samples per 256-thread block.
 __global__ __launch_bounds__(256) void pp_norm_kernel(const float *__restrict__ X, int64_t n,
                                                      int64_t d, double *__restrict__ xnorm) {
     const int lane = threadIdx.x & 63;
     const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (i >= n) return;  // whole wave
     const float *x = X + i * d;
-    double acc[1] = {0.0};
-    for (int64_t f0 = 4 * lane; f0 < d; f0 += kPPChunk) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const double v = f0 + q < d ? (double)x[f0 + q] : 0.0;
-            acc[0] = __builtin_fma(v, v, acc[0]);
-        }
+    double acc = 0.0;
+    for (int64_t f = lane; f < d; f += 64) {
+        const double v = (double)x[f];
+        acc = __builtin_fma(v, v, acc);
     }
-    wave_sum_transpose<1>(acc, lane);
-    if (lane == 0) xnorm[i] = acc[0];
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) xnorm[i] = acc;
 }
 
-// LDS of one pp_dist_kernel block: xs, cs and wave_part below.
-constexpr int pp_dist_lds_bytes(int T, int R, int V) {
-    return kPPWaves * R * V * 64 * 16 + 2 * T * 4 * V * 64 * 4 + kPPWaves * R * T * 8;
-}
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-template <int T, int R, int V, bool kVec>
-__global__ __launch_bounds__(kPPWaves * 64, 4) void pp_dist_kernel(
+// Every sample against up to 16 candidates with float64 matrix cores
+// (v_mfma_f64_16x16x4_f64: D(16 x 16) += A(16 x 4) B(4 x 16)). A block holds
+// 64 samples, 16 per wave; a wave's tile is its 16 samples x the 16 candidate
+// slots (slots >= trials are zero), so one 16 x 16 float64 accumulator (4
+// values per lane) carries whole dot products and no cross-lane sum is
+// needed. Features go in stages of kMfF; inside a stage, k-group g (lanes
+// 16g .. 16g+15) takes the contiguous features g * kMfRun .. +kMfRun, one per
+// MFMA step (the same order for samples and candidates). Samples are loaded
+// coalesced (whole 512-byte row pieces per half-wave) one stage ahead into
+// registers and turned round through the wave's own LDS slice, which needs no
+// barrier because a wave's LDS operations run in order; candidates are staged
+// in shared, double-buffered LDS. Registers carry no accumulators but the 4
+// per lane, which leaves room for the next stage's samples in flight: with
+// three blocks per CU, 96 KiB of samples per CU.
+// Output layout (probed on the chip): lane l, value i is sample (l / 16) +
+// 4 i of the wave's 16, candidate slot l % 16.
+constexpr int kMfF = 128;           // features per stage
+constexpr int kMfRun = kMfF / 4;    // contiguous features per lane per stage
+constexpr int kMfLdk = kMfF + 4;    // padded LDS row of a candidate
+
+template <bool kVec>
+__global__ __launch_bounds__(256, 3) void pp_dist_kernel(
     const float *__restrict__ X, const double *__restrict__ xnorm, int64_t n, int64_t d,
-    const long long *__restrict__ cand, const PPState *__restrict__ st,
+    int trials, const long long *__restrict__ cand, const PPState *__restrict__ st,
     const double *__restrict__ prev_buf, double *__restrict__ out_buf,
     double *__restrict__ out_parts, int64_t nb) {
-    constexpr int kChunk = kPPChunk * V;
-    constexpr int kPasses = kPPRowsPerBlock / (kPPWaves * R);
-    constexpr int kCandPerWave = (T + kPPWaves - 1) / kPPWaves;
-    constexpr int kM = pow2_at_least(R * T);          // values per lane to reduce
-    constexpr int kGroup = 64 / kM;                   // lanes holding one total
-    __shared__ float4 xs[kPPWaves][R][V][64];
-    __shared__ float cs[2][T][4 * V][64];
-    __shared__ double wave_part[kPPWaves][R][T];
+    __shared__ __attribute__((aligned(16))) float cs[2][16][kMfLdk];
+    __shared__ __attribute__((aligned(16))) float xw[4][16][kMfLdk];  // per wave
+    __shared__ double wpart[4][16];
+    __shared__ double cand_norm[16];
+    __shared__ long long cand_row[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t b = blockIdx.x;
     const double *closest = prev_buf ? prev_buf + (int64_t)st->best * n : nullptr;
-    const int64_t chunks = (d + kChunk - 1) / kChunk;
-    const int64_t stages = kPasses * chunks;
-    // Wave w stages candidates w, w + 8 (those below T).
-    int64_t my_cand[kCandPerWave];
-#pragma unroll
-    for (int j = 0; j < kCandPerWave; ++j) {
-        const int t = wave + kPPWaves * j;
-        my_cand[j] = t < T ? (int64_t)cand[t] : 0;
+    const int grp = lane >> 4;  // k-group of this lane's MFMA operands
+    const int64_t row0 = b * kPPRowsPerBlock + wave * 16;
+    const int64_t chunks = (d + kMfF - 1) / kMfF;
+    if (tid < 16) {
+        cand_row[tid] = tid < trials ? cand[tid] : -1;
+        cand_norm[tid] = tid < trials ? xnorm[cand[tid]] : 0.0;
     }
-    __shared__ double cand_norm[T];
-    if (tid < T) cand_norm[tid] = xnorm[cand[tid]];
+    // Candidate staging: thread tid moves 8 features (two 16-byte pieces) of
+    // candidate slot tid / 16 per stage.
+    const int c_slot = tid >> 4, c_off = (tid & 15) * 8;
+    const long long c_row = c_slot < trials ? cand[c_slot] : -1;
 
-    auto row = [&](int64_t p, int r) {
-        return b * kPPRowsPerBlock + (p * R + r) * kPPWaves + wave;
-    };
-    auto load_stage = [&](int64_t s, float4 (&xr)[R][V], float4 (&cv)[kCandPerWave][V]) {
-        const int64_t p = s / chunks, f = (s % chunks) * kChunk + 4 * lane;
+    // Sample staging, coalesced: piece e = lane + 64 q (q < 8) of the wave's
+    // 16 rows x kMfF features is row e / 32, features 4 (e % 32) .. +3.
+    auto load_x = [&](int64_t c, float4 (&xv)[8]) {
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int v = 0; v < V; ++v)
-                xr[r][v] = load_row4<kVec>(X, n, d, row(p, r), f + kPPChunk * v);
-#pragma unroll
-        for (int j = 0; j < kCandPerWave; ++j)
-            if (wave + kPPWaves * j < T)
-#pragma unroll
-                for (int v = 0; v < V; ++v)
-                    cv[j][v] = load_row4<kVec>(X, n, d, my_cand[j], f + kPPChunk * v);
-    };
-    auto store_stage = [&](int buf, const float4 (&xr)[R][V], const float4 (&cv)[kCandPerWave][V]) {
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int v = 0; v < V; ++v) xs[wave][r][v][lane] = xr[r][v];
-#pragma unroll
-        for (int j = 0; j < kCandPerWave; ++j) {
-            const int t = wave + kPPWaves * j;
-            if (t < T) {
-#pragma unroll
-                for (int v = 0; v < V; ++v) {
-                    cs[buf][t][4 * v + 0][lane] = cv[j][v].x;
-                    cs[buf][t][4 * v + 1][lane] = cv[j][v].y;
-                    cs[buf][t][4 * v + 2][lane] = cv[j][v].z;
-                    cs[buf][t][4 * v + 3][lane] = cv[j][v].w;
-                }
-            }
+        for (int q = 0; q < 8; ++q) {
+            const int e = lane + 64 * q;
+            xv[q] = load_row4<kVec>(X, n, d, row0 + (e >> 5), c * kMfF + 4 * (e & 31));
         }
     };
+    auto store_x = [&](const float4 (&xv)[8]) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int e = lane + 64 * q;
+            *reinterpret_cast<float4 *>(&xw[wave][e >> 5][4 * (e & 31)]) = xv[q];
+        }
+    };
+    auto load_c = [&](int64_t c, float4 (&cv)[2]) {
+        const int64_t f = c * kMfF + c_off;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            cv[q] = c_row >= 0 ? load_row4<kVec>(X, n, d, c_row, f + 4 * q)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    };
+    auto store_c = [&](int buf, const float4 (&cv)[2]) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            *reinterpret_cast<float4 *>(&cs[buf][c_slot][c_off + 4 * q]) = cv[q];
+    };
 
-    float4 xn[R][V], cv[kCandPerWave][V];
-    load_stage(0, xn, cv);
-    store_stage(0, xn, cv);
+    float4 xn[8], cv[2];
+    load_x(0, xn);
+    load_c(0, cv);
+    store_x(xn);
+    store_c(0, cv);
     __syncthreads();
 
-    // acc[r * T + t]: this lane's part of x . c_t for slot r; the entries
-    // from R * T up to kM stay 0 and only pad the reduction.
-    double acc[kM];
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+    for (int64_t c = 0; c < chunks; ++c) {
+        const int cur = (int)(c & 1);
+        // This lane's A operands of the stage (its own wave's slice: the
+        // wave's LDS operations run in order, so the slice can be rewritten
+        // below without a barrier).
+        float4 xa[kMfRun / 4];
+        const float *arow = &xw[wave][lane & 15][grp * kMfRun];
 #pragma unroll
-    for (int j = 0; j < kM; ++j) acc[j] = 0.0;
-    // This lane's running sum of the final D over its passes, for the value
-    // (r, t) it receives from the reduction.
-    const int my_idx = lane / kGroup;
-    double my_part = 0.0;
-
-    for (int64_t s = 0; s < stages; ++s) {
-        const int cur = (int)(s & 1);
-        if (s + 1 < stages) load_stage(s + 1, xn, cv);
-        // Features beyond d were loaded as 0 for samples and candidates alike,
-        // so they add 0. Per lane the features come in the order 256 s' + 4
-        // lane + q over slices s' and then q, as in pp_norm_kernel. (Not
-        // unrolled over v: the compiler would hoist the
-        // LDS reads of every slice and run out of registers.)
-#pragma unroll 1
-        for (int v = 0; v < V; ++v) {
-            float4 xf[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) xf[r] = xs[wave][r][v][lane];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                double xd[R];
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-                    xd[r] = (double)(q == 0 ? xf[r].x : q == 1 ? xf[r].y : q == 2 ? xf[r].z : xf[r].w);
-#pragma unroll
-                for (int t = 0; t < T; ++t) {
-                    const double c = (double)cs[cur][t][4 * v + q][lane];
-#pragma unroll
-                    for (int r = 0; r < R; ++r) acc[r * T + t] = __builtin_fma(xd[r], c, acc[r * T + t]);
-                }
-            }
+        for (int q = 0; q < kMfRun / 4; ++q) xa[q] = *reinterpret_cast<const float4 *>(arow + 4 * q);
+        if (c + 1 < chunks) {
+            load_x(c + 1, xn);
+            load_c(c + 1, cv);
         }
-        if (s % chunks == chunks - 1) {
-            // The R samples of this pass are complete.
-            wave_sum_transpose<kM>(acc, lane);
-            const int64_t i = row(s / chunks, my_idx / T);
-            if (lane % kGroup == 0 && my_idx < R * T && i < n) {
-                const int t = my_idx % T;
-                const double cur_d = closest ? closest[i] : __builtin_inf();
-                const double dist = __builtin_fma(-2.0, acc[0], xnorm[i] + cand_norm[t]);
-                const double pos = dist > 0.0 ? dist : 0.0;
-                const double nd = pos < cur_d ? pos : cur_d;
-                out_buf[(int64_t)t * n + i] = nd;
-                my_part += nd;
-            }
+        // Features beyond d were loaded as 0 for samples and candidates alike.
+        const float *brow = &cs[cur][lane & 15][grp * kMfRun];
 #pragma unroll
-            for (int j = 0; j < kM; ++j) acc[j] = 0.0;
+        for (int q = 0; q < kMfRun / 4; ++q) {
+            const float4 bv = *reinterpret_cast<const float4 *>(brow + 4 * q);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[q].x, (double)bv.x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[q].y, (double)bv.y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[q].z, (double)bv.z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[q].w, (double)bv.w, acc, 0, 0, 0);
         }
-        if (s + 1 < stages) store_stage(cur ^ 1, xn, cv);
+        if (c + 1 < chunks) {
+            store_x(xn);
+            store_c(cur ^ 1, cv);
+        }
         __syncthreads();
     }
-    if (lane % kGroup == 0 && my_idx < R * T) wave_part[wave][my_idx / T][my_idx % T] = my_part;
-    __syncthreads();
-    if (tid < T) {
-        double sum = 0.0;
-        for (int w = 0; w < kPPWaves; ++w)
-            for (int r = 0; r < R; ++r) sum += wave_part[w][r][tid];
-        out_parts[(int64_t)tid * nb + b] = sum;
-    }
-}
 
-// Launch of pp_dist_kernel for a run-time trial count. A wave takes R
-// samples at once with R * T <= 16, so that the float64 accumulators fit in
-// 32 registers and two blocks fit on a CU without spilling.
-template <int T>
-void launch_dist_t(bool vec, unsigned nb, hipStream_t stream, const float *X,
-                   const double *xnorm, int64_t n, int64_t d, const long long *cand,
-                   const PPState *st, const double *prev, double *out, double *parts) {
-    constexpr int R = T <= 4 ? 4 : T <= 8 ? 2 : 1;
-    // Two 256-feature slices per stage where the LDS of two blocks still fits
-    // in a CU's 160 KiB, else one.
-    constexpr int V = 2 * pp_dist_lds_bytes(T, R, 2) <= 160 * 1024 ? 2 : 1;
-    if (vec)
-        pp_dist_kernel<T, R, V, true><<<nb, kPPWaves * 64, 0, stream>>>(X, xnorm, n, d, cand, st,
-                                                                        prev, out, parts, nb);
-    else
-        pp_dist_kernel<T, R, V, false><<<nb, kPPWaves * 64, 0, stream>>>(X, xnorm, n, d, cand, st,
-                                                                         prev, out, parts, nb);
+    // D for this lane's 4 samples against candidate slot t; the sample that is
+    // the candidate itself gets exactly 0.
+    const int t = lane & 15;
+    double part = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t gi = row0 + grp + 4 * i;
+        if (t < trials && gi < n) {
+            const double dist =
+                gi == cand_row[t] ? 0.0 : __builtin_fma(-2.0, acc[i], xnorm[gi] + cand_norm[t]);
+            const double pos = dist > 0.0 ? dist : 0.0;
+            const double cur_d = closest ? closest[gi] : __builtin_inf();
+            const double nd = pos < cur_d ? pos : cur_d;
+            out_buf[(int64_t)t * n + gi] = nd;
+            part += nd;
+        }
+    }
+    // The four lanes of candidate t (t, t + 16, t + 32, t + 48), then the
+    // waves in order.
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    if (lane < 16) wpart[wave][lane] = part;
+    __syncthreads();
+    if (tid < trials)
+        out_parts[(int64_t)tid * nb + b] = ((wpart[0][tid] + wpart[1][tid]) + wpart[2][tid]) + wpart[3][tid];
 }
 
 void launch_dist(int trials, bool vec, unsigned nb, hipStream_t stream, const float *X,
                  const double *xnorm, int64_t n, int64_t d, const long long *cand,
                  const PPState *st, const double *prev, double *out, double *parts) {
-    switch (trials) {
-#define KM_PP_CASE(T) \
-    case T: launch_dist_t<T>(vec, nb, stream, X, xnorm, n, d, cand, st, prev, out, parts); break;
-        KM_PP_CASE(1) KM_PP_CASE(2) KM_PP_CASE(3) KM_PP_CASE(4)
-        KM_PP_CASE(5) KM_PP_CASE(6) KM_PP_CASE(7) KM_PP_CASE(8)
-        KM_PP_CASE(9) KM_PP_CASE(10) KM_PP_CASE(11) KM_PP_CASE(12)
-        KM_PP_CASE(13) KM_PP_CASE(14) KM_PP_CASE(15) KM_PP_CASE(16)
-#undef KM_PP_CASE
-        default: break;  // trials is validated to 1 .. kPPMaxTrials by the caller
-    }
+    if (vec)
+        pp_dist_kernel<true><<<nb, 256, 0, stream>>>(X, xnorm, n, d, trials, cand, st, prev, out,
+                                                     parts, nb);
+    else
+        pp_dist_kernel<false><<<nb, 256, 0, stream>>>(X, xnorm, n, d, trials, cand, st, prev, out,
+                                                      parts, nb);
 }
 
 constexpr int kSelWaves = 16;  // pp_select_kernel: one 1024-thread block
@@ -466,7 +385,7 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int64_t pp_blocks(int64_t n) { return cdiv(n, kPPRowsPerBlock); }
 int pp_max_trials() { return kPPMaxTrials; }
-int pp_block_threads() { return kPPWaves * 64; }
+int pp_block_threads() { return 256; }
 size_t pp_state_bytes() { return sizeof(PPState); }
 
 hipError_t launch_kmeanspp(const float *X, int64_t n, int64_t d, int64_t k, int64_t first,
