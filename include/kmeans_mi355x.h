@@ -34,6 +34,9 @@
  *     synchronisation, not as a return value.
  *   - Shapes: 0 <= n < 2^31, 1 <= k < 2^31, 1 <= d < 2^31. With n = 0 nothing
  *     is read from X, labels or min_dist (they may be NULL). k > n is allowed.
+ *     A shape whose launch grid would exceed 2^32 - 1 work-items in one
+ *     dimension (for the assignment roughly n * k > 2^38 with the tile chosen
+ *     for large problems) returns KM_ERR_SHAPE.
  *   - Inputs must be finite; NaN or Inf inputs give unspecified labels.
  *   - Outputs must not overlap any input, any other output or the workspace,
  *     with one exception: C_new may equal C_old exactly (in-place update).
@@ -78,8 +81,8 @@ enum { KM_FIT_RELOCATE_EMPTY = 1 };
  * Workspace bytes needed by one call of the given op at shape (n, k, d).
  * The size is O(k + n + k * ceil(n / 1024)) 4-byte words (plus about
  * k * d / 1024 doubles for kmeans_fit), far below the (n, k) distance matrix
- * and the (n, d) sample matrix. Returns 0 when the shape or op is invalid (a
- * valid shape never needs 0 bytes).
+ * and the (n, d) sample matrix. Returns 0 when the shape or op is invalid or
+ * the shape's launch grid does not fit (a valid shape never needs 0 bytes).
  */
 size_t kmeans_workspace_bytes(int64_t n, int64_t k, int64_t d, int op);
 

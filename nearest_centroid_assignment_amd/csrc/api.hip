@@ -117,7 +117,7 @@ char *ws_base(void *workspace) {
 }
 
 bool grid_ok(int64_t n, int64_t k, int64_t d) {
-    return km::assign_grid_blocks(n, k) * 256 <= kMaxGridThreads &&
+    return km::assign_grid_threads(n, k, d) <= kMaxGridThreads &&
            km::update_grid_blocks(n, k, d) * 256 <= kMaxGridThreads;
 }
 
@@ -172,6 +172,10 @@ extern "C" {
 size_t kmeans_workspace_bytes(int64_t n, int64_t k, int64_t d, int op) {
     if (!shape_ok(n, k, d)) return 0;
     if (op < KM_OP_ASSIGN || op > KM_OP_KMEANSPP) return 0;
+    // A shape whose launch grid does not fit is unsupported, as in the calls.
+    if (op == KM_OP_KMEANSPP ? km::pp_blocks(n) * km::pp_block_threads() > kMaxGridThreads
+                             : !grid_ok(n, k, d))
+        return 0;
     return layout(n, k, d, op).total;
 }
 

@@ -433,9 +433,6 @@ inline unsigned grid_stride_blocks(int64_t n) {
 
 }  // namespace
 
-int64_t assign_grid_blocks(int64_t n, int64_t k) {
-    return cdiv(n, Tile64x64::BN) * cdiv(k, Tile64x64::BM);  // the most blocks of any tile
-}
 
 hipError_t launch_row_sqnorms(const float *A, int64_t rows, int64_t d, float *out,
                               hipStream_t stream) {
@@ -495,6 +492,15 @@ static const char *assign_tile_name(int64_t n, int64_t k, int64_t d) {
     if (tile_blocks<Tile128x256>(n, k) >= 512) return "128x256";
     if (tile_blocks<Tile128x128>(n, k) >= 256) return "128x128";
     return "64x64";
+}
+
+int64_t assign_grid_threads(int64_t n, int64_t k, int64_t d) {
+    if (n <= 0) return 0;
+    const char *tile = assign_tile_name(n, k, d);
+    if (!strcmp(tile, "256x128")) return tile_blocks<Tile256x128>(n, k) * Tile256x128::kThreads;
+    if (!strcmp(tile, "128x128")) return tile_blocks<Tile128x128>(n, k) * Tile128x128::kThreads;
+    if (!strcmp(tile, "128x256")) return tile_blocks<Tile128x256>(n, k) * Tile128x256::kThreads;
+    return tile_blocks<Tile64x64>(n, k) * Tile64x64::kThreads;
 }
 
 hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, int64_t n,

@@ -110,7 +110,8 @@ hipError_t launch_kmeanspp(const float *X, int64_t n, int64_t d, int64_t k, int6
                            const PPScratch &ws, hipStream_t stream);
 
 // Upper limits of the launch grids (blocks); checked by the C-ABI layer.
-int64_t assign_grid_blocks(int64_t n, int64_t k);
+// Work-items of the assignment launch (the tile the launcher will choose).
+int64_t assign_grid_threads(int64_t n, int64_t k, int64_t d);
 int64_t update_grid_blocks(int64_t n, int64_t k, int64_t d);
 
 }  // namespace km

@@ -72,6 +72,21 @@ def test_workspace_bytes_rules(lib):
             assert l < cfg.n * cfg.k * 4 / 64 and l < cfg.n * cfg.d * 4 / 64
 
 
+def test_launch_grid_limit(lib, monkeypatch):
+    """The grid check follows the tile the launcher picks: a large problem is
+    accepted while the 128 x 256 tile's launch fits in 2^32 - 1 work-items,
+    and refused once it does not (or when a smaller tile is forced)."""
+    monkeypatch.delenv("KMEANS_ASSIGN_TILE", raising=False)
+    ws = binding.kmeans_workspace_bytes
+    # 2^23 x 2^14: (2^23 / 256) x (2^14 / 128) blocks x 512 threads = 2^31.
+    assert ws(2**23, 2**14, 1, 0) > 0
+    # 2^24 x 2^14: 2^32 work-items, one too many.
+    assert ws(2**24, 2**14, 1, 0) == 0
+    monkeypatch.setenv("KMEANS_ASSIGN_TILE", "64x64")  # 4x the work-items
+    assert ws(2**23, 2**14, 1, 0) == 0
+    assert ws(2**21, 2**14, 1, 0) > 0
+
+
 def _assign(lib, X=X_P, C=C_P, n=100, k=10, d=8, labels=LAB_P, md=MD_P, ws=WS_P, wsb=None):
     if wsb is None:
         wsb = binding.kmeans_workspace_bytes(max(n, 0), max(k, 1), max(d, 1), 0)
