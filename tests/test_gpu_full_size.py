@@ -11,7 +11,7 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 
-SAMPLE_ROWS = 256
+SAMPLE_ROWS = 2048  # oracle rows per full-size workload (a few seconds each on the host)
 
 
 @pytest.fixture(scope="module", autouse=True)
