@@ -30,6 +30,7 @@ def test_small_config_lloyd(name):
     X, C = datagen.make(name)
     res = gu.full_parity(X, C)
     assert res["mismatches"] <= res["near_ties"]
+    gu.announce(f"{name} near-ties {res['near_ties']} mismatches {res['mismatches']}")
 
 
 def test_mid_lloyd():
