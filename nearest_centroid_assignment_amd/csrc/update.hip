@@ -209,9 +209,11 @@ __device__ __forceinline__ void sum_rows(const float *__restrict__ X, const int 
     }
 }
 
-// Writes the new centre elements of this thread and adds their squared move
-// (new - old)^2 to `shift` (the old value is read before the new one is
-// written, so C_new may be C_old).
+// Writes the new centre elements of this thread and, if kShift, adds their
+// squared move (new - old)^2 to `shift` (the old value is read before the new
+// one is written, so C_new may be C_old). Without kShift the old centre is
+// read only for an empty cluster.
+template <bool kShift>
 __device__ __forceinline__ void write_mean(const float *C_old, float *C_new, int64_t j, int64_t d,
                                            int count, const int64_t (&col)[4],
                                            const double (&s)[4], double &shift) {
@@ -219,18 +221,22 @@ __device__ __forceinline__ void write_mean(const float *C_old, float *C_new, int
     for (int e = 0; e < 4; ++e) {
         if (col[e] < d) {
             const int64_t o = j * d + col[e];
-            const float old = C_old[o];
-            const float v = count > 0 ? (float)(s[e] / (double)count) : old;
-            C_new[o] = v;
-            const double diff = (double)v - (double)old;
-            shift += diff * diff;
+            if (kShift || count == 0) {
+                const float old = C_old[o];
+                const float v = count > 0 ? (float)(s[e] / (double)count) : old;
+                C_new[o] = v;
+                const double diff = (double)v - (double)old;
+                shift += diff * diff;
+            } else {
+                C_new[o] = (float)(s[e] / (double)count);
+            }
         }
     }
 }
 
-// If shift_partial != NULL, block b also writes the sum over its elements of
-// (new - old)^2 to shift_partial[b] (fixed summation order).
-template <bool kVec>
+// If kShift, block b also writes the sum over its elements of (new - old)^2
+// to shift_partial[b] (fixed summation order).
+template <bool kVec, bool kShift>
 __global__ __launch_bounds__(256) void segment_mean_kernel(
     const float *__restrict__ X, const int *__restrict__ perm, const int *__restrict__ seg_start,
     const int *__restrict__ cnt, const float *C_old, int64_t k, int64_t d, int chunks,
@@ -257,7 +263,7 @@ __global__ __launch_bounds__(256) void segment_mean_kernel(
             if (count <= kSplitMin) {
                 double s[4] = {0.0, 0.0, 0.0, 0.0};
                 sum_rows<kVec>(X, perm + seg_start[j], 0, count, d, col, s);
-                write_mean(C_old, C_new, j, d, count, col, s, shift);
+                write_mean<kShift>(C_old, C_new, j, d, count, col, s, shift);
             }
         }
     }
@@ -280,11 +286,11 @@ __global__ __launch_bounds__(256) void segment_mean_kernel(
             for (int pw = 0; pw < 3; ++pw)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) s[e] += part[pw][lc[e]];
-            write_mean(C_old, C_new, j, d, count, col, s, shift);
+            write_mean<kShift>(C_old, C_new, j, d, count, col, s, shift);
         }
         __syncthreads();  // part is reused by the next big cluster
     }
-    if (shift_partial) {
+    if (kShift) {
         for (int off = 32; off > 0; off >>= 1) shift += __shfl_xor(shift, off);
         if (lane == 0) part[0][wave] = shift;
         __syncthreads();
@@ -342,12 +348,18 @@ hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const fl
     const unsigned blocks = (unsigned)mean_blocks(k, d);
     const bool vec = (d % 4 == 0) && ((uintptr_t)X % 16 == 0) && ((uintptr_t)C_old % 16 == 0) &&
                      ((uintptr_t)C_new % 16 == 0);
-    if (vec)
-        segment_mean_kernel<true><<<blocks, 256, 0, stream>>>(
+    if (vec && shift_partial)
+        segment_mean_kernel<true, true><<<blocks, 256, 0, stream>>>(
+            X, ws.perm, ws.seg_start, ws.cnt, C_old, k, d, chunks, C_new, shift_partial);
+    else if (vec)
+        segment_mean_kernel<true, false><<<blocks, 256, 0, stream>>>(
+            X, ws.perm, ws.seg_start, ws.cnt, C_old, k, d, chunks, C_new, nullptr);
+    else if (shift_partial)
+        segment_mean_kernel<false, true><<<blocks, 256, 0, stream>>>(
             X, ws.perm, ws.seg_start, ws.cnt, C_old, k, d, chunks, C_new, shift_partial);
     else
-        segment_mean_kernel<false><<<blocks, 256, 0, stream>>>(
-            X, ws.perm, ws.seg_start, ws.cnt, C_old, k, d, chunks, C_new, shift_partial);
+        segment_mean_kernel<false, false><<<blocks, 256, 0, stream>>>(
+            X, ws.perm, ws.seg_start, ws.cnt, C_old, k, d, chunks, C_new, nullptr);
     return hipGetLastError();
 }
 
