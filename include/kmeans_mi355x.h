@@ -44,9 +44,9 @@
  *     call returns a negative km_status and enqueues nothing.
  *   - Arithmetic: float32 MFMA products with float32 accumulation for the
  *     assignment; per-cluster sums accumulated in float64 (in increasing
- *     sample order for a cluster of at most 64 samples; as four contiguous
- *     quarters of its samples, added in order, for a larger one), divided in
- *     float64 and rounded once to float32. Every reduction has a fixed
+ *     sample order for a cluster of at most 64 samples; as sixteen
+ *     contiguous parts of its samples, added in order, for a larger one),
+ *     divided in float64 and rounded once to float32. Every reduction has a fixed
  *     order: the same inputs give the same bits.
  */
 #ifndef KMEANS_MI355X_H

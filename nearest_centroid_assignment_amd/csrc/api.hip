@@ -18,7 +18,7 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Layout {
-    size_t cn = 0, tile_hist = 0, cnt = 0, seg_start = 0, perm = 0;
+    size_t cn = 0, tile_hist = 0, cnt = 0, seg_start = 0, perm = 0, big = 0;
     // kmeans_fit only
     size_t md = 0, dist = 0, empty = 0, sort_key = 0, sort_idx = 0, moves_src = 0, moves_dst = 0,
            shift_partial = 0, scalars = 0;
@@ -47,6 +47,8 @@ Layout layout(int64_t n, int64_t k, int64_t d, int op) {
         off += round_up((size_t)k * sizeof(int));
         L.perm = off;
         off += round_up((size_t)n * sizeof(int));
+        L.big = off;
+        off += round_up(((size_t)k + 1) * sizeof(int));
     }
     if (op == KM_OP_FIT) {
         const int64_t nk = n < k ? n : k;
@@ -161,6 +163,7 @@ km::UpdateScratch update_scratch(char *base, const Layout &L, int64_t n) {
     ws.cnt = (int *)(base + L.cnt);
     ws.seg_start = (int *)(base + L.seg_start);
     ws.perm = (int *)(base + L.perm);
+    ws.big = (int *)(base + L.big);
     ws.n_tiles = cdiv(n, km::kSortTileRows);
     return ws;
 }

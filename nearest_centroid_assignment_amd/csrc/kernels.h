@@ -17,6 +17,8 @@ struct UpdateScratch {
     int *cnt;        // k: rows per cluster
     int *seg_start;  // k: first position of each cluster in perm
     int *perm;       // n: row indices grouped by cluster, increasing within one
+    int *big;        // k + 1: the number of clusters with more than 64 rows, then
+                     // their indices in increasing order
     int64_t n_tiles; // ceil(n / kSortTileRows)
 };
 
@@ -46,6 +48,7 @@ hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t *co
 // Second phase: stable grouping of rows by label and the float64 segmented
 // sums and means (old centre kept for an empty cluster). If shift_partial is
 // not NULL, mean_blocks(k, d) partial sums of (new - old)^2 are written there.
+// mean_blocks counts the blocks of both mean kernels (small and big clusters).
 hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const float *C_old,
                                  int64_t n, int64_t k, int64_t d, float *C_new,
                                  double *shift_partial, const UpdateScratch &ws,

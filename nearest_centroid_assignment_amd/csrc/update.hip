@@ -12,14 +12,15 @@
 //   cluster_scan_kernel  exclusive prefix over clusters -> segment starts; counts
 //   scatter_kernel       perm[segment start + rows of the cluster in earlier
 //                        tiles + rank within the tile] = row   (stable)
-//   segment_mean_kernel  float64 sums over each segment, coalesced row chunks,
-//                        then the mean rounded once to float32, or the old
-//                        centre for an empty cluster
+//   segment_mean_kernel  float64 sums over each segment of at most 64 rows,
+//                        coalesced row chunks, then the mean rounded once to
+//                        float32, or the old centre for an empty cluster
+//   big_mean_kernel      the same for larger clusters, sixteen waves each
 //
 // No float atomics: every sum has one fixed order, so results are
 // deterministic. For a cluster of at most 64 rows that order is increasing
 // sample order, so the float64 sum and divide are exactly the plain definition
-// of the mean; larger clusters add four contiguous quarters of their rows.
+// of the mean; larger clusters add sixteen contiguous parts of their rows.
 #include "kernels.h"
 
 namespace km {
@@ -29,6 +30,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = (int)kSortTileRows;  // rows per sort tile
 constexpr int kCols = 256;                 // columns per segment_mean block (64 lanes x 4)
+constexpr int kSplitMin = 64;              // larger clusters go to big_mean_kernel
+constexpr int kBigWaves = 16;              // waves (parts) per big-cluster block
+constexpr int kBigBlocks = 256;            // blocks of big_mean_kernel (persistent)
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -76,15 +80,19 @@ __global__ __launch_bounds__(256) void tile_scan_kernel(int *__restrict__ tile_h
 }
 
 // A single block of 1024 threads: exclusive scan over the k cluster sizes.
-// If num_empty != NULL it receives the number of clusters of size 0.
+// If num_empty != NULL it receives the number of clusters of size 0. big[0]
+// receives the number of clusters with more than kSplitMin rows and big[1 ..]
+// their indices in increasing order.
 __global__ __launch_bounds__(1024) void cluster_scan_kernel(const int *__restrict__ cnt, int64_t k,
                                                             int *__restrict__ seg_start,
                                                             int64_t *__restrict__ counts,
-                                                            int *__restrict__ num_empty) {
+                                                            int *__restrict__ num_empty,
+                                                            int *__restrict__ big) {
     __shared__ int wave_tot[16];
+    __shared__ int wave_big[16];
     __shared__ int wave_empty[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int carry = 0, empties = 0;
+    int carry = 0, empties = 0, big_carry = 0;
     for (int64_t base = 0; base < k; base += 1024) {
         const int64_t j = base + tid;
         const int v = j < k ? cnt[j] : 0;
@@ -94,21 +102,30 @@ __global__ __launch_bounds__(1024) void cluster_scan_kernel(const int *__restric
             const int up = __shfl_up(incl, off);
             if (lane >= off) incl += up;
         }
+        const bool is_big = j < k && v > kSplitMin;
+        const unsigned long long bm = __ballot(is_big);
         if (lane == 63) wave_tot[wave] = incl;
+        if (lane == 0) wave_big[wave] = __popcll(bm);
         __syncthreads();
-        int before = 0, total = 0;
+        int before = 0, total = 0, big_before = 0, big_total = 0;
         for (int w = 0; w < 16; ++w) {
-            const int wt = wave_tot[w];
+            const int wt = wave_tot[w], wb = wave_big[w];
             before += w < wave ? wt : 0;
             total += wt;
+            big_before += w < wave ? wb : 0;
+            big_total += wb;
         }
         if (j < k) {
             seg_start[j] = carry + before + incl - v;
             counts[j] = v;
         }
+        if (is_big)
+            big[1 + big_carry + big_before + __popcll(bm & ((1ull << lane) - 1ull))] = (int)j;
         carry += total;
-        __syncthreads();  // wave_tot is rewritten by the next chunk
+        big_carry += big_total;
+        __syncthreads();  // wave_tot and wave_big are rewritten by the next chunk
     }
+    if (tid == 0) big[0] = big_carry;
     if (num_empty) {
         for (int off = 32; off > 0; off >>= 1) empties += __shfl_xor(empties, off);
         if (lane == 0) wave_empty[wave] = empties;
@@ -154,38 +171,36 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int64_t *__restrict_
 }
 
 // Block (clusters 4q .. 4q+3, chunk c of kCols columns), 4 waves; lane l of a
-// wave owns 4 columns of the chunk.
-//   Phase 1: wave w sums cluster 4q+w if it has at most kSplitMin rows, alone
-//            and in increasing sample order.
-//   Phase 2: each of the block's clusters with more rows is cut into 4
-//            contiguous quarters of its (increasing) rows, one per wave; the
-//            four float64 partial sums are added in quarter order through
-//            LDS, so the rows of a big cluster are fetched by four waves at
-//            once, in a fixed order (deterministic).
+// wave owns 4 columns of the chunk. Wave w sums cluster 4q+w if it has at
+// most kSplitMin rows, alone and in increasing sample order. Larger clusters
+// are left to big_mean_kernel, which cuts each into kBigWaves contiguous
+// parts of its (increasing) rows, one per wave, and adds the float64 partial
+// sums in part order through LDS; so the rows of a big cluster are fetched by
+// sixteen waves at once, in a fixed order (deterministic).
 // Rows are fetched in rounds of kBatch: the round's row indices, then all its
 // row loads, then the adds in order.
 constexpr int kBatch = 16;
-constexpr int kSplitMin = 64;
 constexpr int kClustersPerBlock = 4;
 
 template <bool kVec>
 __device__ __forceinline__ void sum_rows(const float *__restrict__ X, const int *__restrict__ rows,
                                          int r0, int r1, int64_t d, const int64_t (&col)[4],
                                          double (&s)[4]) {
-    for (int p0 = r0; p0 < r1; p0 += kBatch) {
-        const int m = min(kBatch, r1 - p0);
-        int64_t base[kBatch];
+    constexpr int B = kVec ? kBatch : kBatch / 2;  // rows per round (the scalar path holds 4x)
+    for (int p0 = r0; p0 < r1; p0 += B) {
+        const int m = min(B, r1 - p0);
+        int64_t base[B];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) base[u] = u < m ? (int64_t)rows[p0 + u] * d : -1;
+        for (int u = 0; u < B; ++u) base[u] = u < m ? (int64_t)rows[p0 + u] * d : -1;
         if (kVec) {
-            f32x4 v[kBatch];
+            f32x4 v[B];
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u)
+            for (int u = 0; u < B; ++u)
                 v[u] = (base[u] >= 0 && col[0] < d)
                            ? *reinterpret_cast<const f32x4 *>(X + base[u] + col[0])
                            : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
+            for (int u = 0; u < B; ++u) {
                 if (u < m) {
                     s[0] += (double)v[u].x;
                     s[1] += (double)v[u].y;
@@ -194,14 +209,14 @@ __device__ __forceinline__ void sum_rows(const float *__restrict__ X, const int 
                 }
             }
         } else {
-            float v[kBatch][4];
+            float v[B][4];
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u)
+            for (int u = 0; u < B; ++u)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     v[u][e] = (base[u] >= 0 && col[e] < d) ? X[base[u] + col[e]] : 0.f;
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u)
+            for (int u = 0; u < B; ++u)
                 if (u < m)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) s[e] += (double)v[u][e];
@@ -243,37 +258,59 @@ __global__ __launch_bounds__(256) void segment_mean_kernel(
     float *C_new, double *__restrict__ shift_partial) {
     // C_old and C_new may be the same array: each element is read and written
     // by the same thread only, so they carry no __restrict__.
-    __shared__ double part[3][kCols];
+    __shared__ double wshift[4];
     double shift = 0.0;
     const int64_t j0 = (int64_t)(blockIdx.x / (unsigned)chunks) * kClustersPerBlock;
     const int64_t c = blockIdx.x % (unsigned)chunks;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    int lc[4];  // columns within the chunk
-#pragma unroll
-    for (int e = 0; e < 4; ++e) lc[e] = kVec ? 4 * lane + e : lane + 64 * e;
     int64_t col[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) col[e] = c * kCols + lc[e];
+    for (int e = 0; e < 4; ++e) col[e] = c * kCols + (kVec ? 4 * lane + e : lane + 64 * e);
 
-    // Phase 1: small clusters, one per wave.
-    {
-        const int64_t j = j0 + wave;
-        if (j < k) {
-            const int count = cnt[j];
-            if (count <= kSplitMin) {
-                double s[4] = {0.0, 0.0, 0.0, 0.0};
-                sum_rows<kVec>(X, perm + seg_start[j], 0, count, d, col, s);
-                write_mean<kShift>(C_old, C_new, j, d, count, col, s, shift);
-            }
+    const int64_t j = j0 + wave;
+    if (j < k) {
+        const int count = cnt[j];
+        if (count <= kSplitMin) {
+            double s[4] = {0.0, 0.0, 0.0, 0.0};
+            sum_rows<kVec>(X, perm + seg_start[j], 0, count, d, col, s);
+            write_mean<kShift>(C_old, C_new, j, d, count, col, s, shift);
         }
     }
-    // Phase 2: big clusters, all four waves each.
-    for (int w = 0; w < kClustersPerBlock; ++w) {
-        const int64_t j = j0 + w;
-        if (j >= k) break;
-        const int count = cnt[j];  // uniform across the block
-        if (count <= kSplitMin) continue;
-        const int q = (count + 3) / 4;
+    if (kShift) {
+        for (int off = 32; off > 0; off >>= 1) shift += __shfl_xor(shift, off);
+        if (lane == 0) wshift[wave] = shift;
+        __syncthreads();
+        if (threadIdx.x == 0)
+            shift_partial[blockIdx.x] = ((wshift[0] + wshift[1]) + wshift[2]) + wshift[3];
+    }
+}
+
+// Clusters with more than kSplitMin rows, listed in big[1 .. big[0]]: work
+// item i is (cluster big[1 + i / chunks], chunk i % chunks); a block of
+// kBigWaves waves takes items blockIdx.x, + gridDim.x, ... Wave p sums part p
+// of the cluster's rows (kBigWaves contiguous parts), wave 0 adds the parts
+// in order and writes the mean. If kShift, block b writes the sum of its
+// items' (new - old)^2 in item order to shift_partial[b].
+template <bool kVec, bool kShift>
+__global__ __launch_bounds__(kBigWaves * 64) void big_mean_kernel(
+    const float *__restrict__ X, const int *__restrict__ perm, const int *__restrict__ seg_start,
+    const int *__restrict__ cnt, const int *__restrict__ big, const float *C_old, int64_t d,
+    int chunks, float *C_new, double *__restrict__ shift_partial) {
+    __shared__ double part[kBigWaves - 1][kCols];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int lc[4];  // columns within a chunk
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lc[e] = kVec ? 4 * lane + e : lane + 64 * e;
+    double shift = 0.0;
+    const int64_t items = (int64_t)big[0] * chunks;
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const int64_t j = big[1 + it / chunks];
+        const int64_t c = it % chunks;
+        int64_t col[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) col[e] = c * kCols + lc[e];
+        const int count = cnt[j];  // > kSplitMin
+        const int q = (count + kBigWaves - 1) / kBigWaves;
         const int r0 = min(count, wave * q), r1 = min(count, r0 + q);
         double s[4] = {0.0, 0.0, 0.0, 0.0};
         sum_rows<kVec>(X, perm + seg_start[j], r0, r1, d, col, s);
@@ -282,20 +319,17 @@ __global__ __launch_bounds__(256) void segment_mean_kernel(
             for (int e = 0; e < 4; ++e) part[wave - 1][lc[e]] = s[e];
         __syncthreads();
         if (wave == 0) {
-#pragma unroll
-            for (int pw = 0; pw < 3; ++pw)
+#pragma unroll 1
+            for (int pw = 0; pw < kBigWaves - 1; ++pw)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) s[e] += part[pw][lc[e]];
             write_mean<kShift>(C_old, C_new, j, d, count, col, s, shift);
         }
-        __syncthreads();  // part is reused by the next big cluster
+        __syncthreads();  // part is reused by the next item
     }
-    if (kShift) {
+    if (kShift && wave == 0) {
         for (int off = 32; off > 0; off >>= 1) shift += __shfl_xor(shift, off);
-        if (lane == 0) part[0][wave] = shift;
-        __syncthreads();
-        if (threadIdx.x == 0)
-            shift_partial[blockIdx.x] = ((part[0][0] + part[0][1]) + part[0][2]) + part[0][3];
+        if (lane == 0) shift_partial[blockIdx.x] = shift;
     }
 }
 
@@ -308,8 +342,12 @@ inline unsigned grid_stride_blocks(int64_t n) {
 
 }  // namespace
 
+static int64_t small_mean_blocks(int64_t k, int64_t d) {
+    return cdiv(k, kClustersPerBlock) * cdiv(d, kCols);
+}
+
 int64_t update_grid_blocks(int64_t n, int64_t k, int64_t d) {
-    const int64_t a = cdiv(k, 4) * cdiv(d, kCols);
+    const int64_t a = small_mean_blocks(k, d);
     const int64_t b = cdiv(n, kTile);
     const int64_t c = cdiv(k, 4);
     return a > b ? (a > c ? a : c) : (b > c ? b : c);
@@ -330,11 +368,12 @@ hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t *co
         // n == 0: every cluster is empty.
         fill_i32_kernel<<<grid_stride_blocks(k), 256, 0, stream>>>(ws.cnt, k);
     }
-    cluster_scan_kernel<<<1, 1024, 0, stream>>>(ws.cnt, k, ws.seg_start, counts, num_empty);
+    cluster_scan_kernel<<<1, 1024, 0, stream>>>(ws.cnt, k, ws.seg_start, counts, num_empty,
+                                                ws.big);
     return hipGetLastError();
 }
 
-int64_t mean_blocks(int64_t k, int64_t d) { return cdiv(k, kClustersPerBlock) * cdiv(d, kCols); }
+int64_t mean_blocks(int64_t k, int64_t d) { return small_mean_blocks(k, d) + kBigBlocks; }
 
 hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const float *C_old,
                                  int64_t n, int64_t k, int64_t d, float *C_new,
@@ -345,7 +384,8 @@ hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const fl
                                                                  ws.tile_hist, ws.seg_start,
                                                                  ws.perm);
     const int chunks = (int)cdiv(d, kCols);
-    const unsigned blocks = (unsigned)mean_blocks(k, d);
+    const unsigned blocks = (unsigned)small_mean_blocks(k, d);
+    double *big_shift = shift_partial ? shift_partial + blocks : nullptr;
     const bool vec = (d % 4 == 0) && ((uintptr_t)X % 16 == 0) && ((uintptr_t)C_old % 16 == 0) &&
                      ((uintptr_t)C_new % 16 == 0);
     if (vec && shift_partial)
@@ -360,6 +400,19 @@ hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const fl
     else
         segment_mean_kernel<false, false><<<blocks, 256, 0, stream>>>(
             X, ws.perm, ws.seg_start, ws.cnt, C_old, k, d, chunks, C_new, nullptr);
+    const unsigned bt = kBigWaves * 64;
+    if (vec && shift_partial)
+        big_mean_kernel<true, true><<<kBigBlocks, bt, 0, stream>>>(
+            X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, d, chunks, C_new, big_shift);
+    else if (vec)
+        big_mean_kernel<true, false><<<kBigBlocks, bt, 0, stream>>>(
+            X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, d, chunks, C_new, nullptr);
+    else if (shift_partial)
+        big_mean_kernel<false, true><<<kBigBlocks, bt, 0, stream>>>(
+            X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, d, chunks, C_new, big_shift);
+    else
+        big_mean_kernel<false, false><<<kBigBlocks, bt, 0, stream>>>(
+            X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, d, chunks, C_new, nullptr);
     return hipGetLastError();
 }
 

@@ -12,7 +12,7 @@ Parity rules (all checked, none relaxed):
 * centroids - the oracle's update on the GPU's labels: per row,
   max |dC| <= 1e-4 * max |C_ref|. Clusters of at most 64 rows are summed in
   increasing sample order in float64 on both sides, so those rows must also
-  be bit-exact; bigger clusters add four row quarters (a different order).
+  be bit-exact; bigger clusters add sixteen row parts (a different order).
 * min_dist - |dD| <= 1e-4 * D_ref or |dD| <= 1e-5 * (||x||^2 + ||c||^2), D_ref
   the float64 distance to the GPU's chosen centroid.
 """

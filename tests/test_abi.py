@@ -64,9 +64,10 @@ def test_workspace_bytes_rules(lib):
         assert l >= max(a, u) and l <= a + u
         # The assignment needs only the centroid norms (k floats + alignment).
         assert a <= cfg.k * 4 + 512
-        # The update: k x ceil(n/1024) tile counters, 2k words, n words.
+        # The update: k x ceil(n/1024) tile counters, 2k words, n words, and
+        # the list of large clusters (k + 1 words).
         n_tiles = -(-cfg.n // 1024)
-        assert u <= 4 * (cfg.k * n_tiles + 2 * cfg.k + cfg.n) + 5 * 256
+        assert u <= 4 * (cfg.k * n_tiles + 3 * cfg.k + 1 + cfg.n) + 6 * 256
         # Far below the (n, k) distance matrix and the (n, d) sample matrix.
         if cfg.n >= 4096:
             assert l < cfg.n * cfg.k * 4 / 64 and l < cfg.n * cfg.d * 4 / 64
