@@ -12,10 +12,10 @@
 //   cluster_scan_kernel  exclusive prefix over clusters -> segment starts; counts
 //   scatter_kernel       perm[segment start + rows of the cluster in earlier
 //                        tiles + rank within the tile] = row   (stable)
-//   segment_mean_kernel  float64 sums over each segment of at most 64 rows,
-//                        coalesced row chunks, then the mean rounded once to
-//                        float32, or the old centre for an empty cluster
-//   big_mean_kernel      the same for larger clusters, sixteen waves each
+//   segment_mean_kernel  float64 sums over each segment, coalesced row chunks,
+//                        then the mean rounded once to float32, or the old
+//                        centre for an empty cluster: a wave per cluster of at
+//                        most 64 rows, sixteen waves per larger one
 //
 // No float atomics: every sum has one fixed order, so results are
 // deterministic. For a cluster of at most 64 rows that order is increasing
@@ -30,9 +30,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = (int)kSortTileRows;  // rows per sort tile
 constexpr int kCols = 256;                 // columns per segment_mean block (64 lanes x 4)
-constexpr int kSplitMin = 64;              // larger clusters go to big_mean_kernel
+constexpr int kSplitMin = 64;              // larger clusters are split in kBigWaves parts
 constexpr int kBigWaves = 16;              // waves (parts) per big-cluster block
-constexpr int kBigBlocks = 256;            // blocks of big_mean_kernel (persistent)
+constexpr int kBigBlocks = 256;            // segment_mean blocks that take the large clusters
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -170,17 +170,9 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int64_t *__restrict_
     }
 }
 
-// Block (clusters 4q .. 4q+3, chunk c of kCols columns), 4 waves; lane l of a
-// wave owns 4 columns of the chunk. Wave w sums cluster 4q+w if it has at
-// most kSplitMin rows, alone and in increasing sample order. Larger clusters
-// are left to big_mean_kernel, which cuts each into kBigWaves contiguous
-// parts of its (increasing) rows, one per wave, and adds the float64 partial
-// sums in part order through LDS; so the rows of a big cluster are fetched by
-// sixteen waves at once, in a fixed order (deterministic).
 // Rows are fetched in rounds of kBatch: the round's row indices, then all its
 // row loads, then the adds in order.
 constexpr int kBatch = 16;
-constexpr int kClustersPerBlock = 4;
 
 template <bool kVec>
 __device__ __forceinline__ void sum_rows(const float *__restrict__ X, const int *__restrict__ rows,
@@ -249,87 +241,82 @@ __device__ __forceinline__ void write_mean(const float *C_old, float *C_new, int
     }
 }
 
-// If kShift, block b also writes the sum over its elements of (new - old)^2
-// to shift_partial[b] (fixed summation order).
+// One launch for both kinds of cluster, 16 waves per block. Blocks 0 ..
+// kBigBlocks-1 come first, so they run beside the others: they take the
+// clusters with more than kSplitMin rows (listed in big[1 .. big[0]]) as
+// work items (cluster big[1 + i / chunks], chunk i % chunks), blocks taking
+// items blockIdx.x, + kBigBlocks, ...; wave p sums part p of the cluster's
+// rows (kBigWaves contiguous parts) and wave 0 adds the parts in order and
+// writes the mean. Every later block covers kBigWaves clusters (one wave
+// each) x one chunk of kCols columns and sums the clusters of at most
+// kSplitMin rows alone, in increasing sample order; lane l owns 4 columns.
+// If kShift, block b writes the sum of its (new - old)^2 in a fixed order to
+// shift_partial[b].
 template <bool kVec, bool kShift>
-__global__ __launch_bounds__(256) void segment_mean_kernel(
+__global__ __launch_bounds__(kBigWaves * 64) void segment_mean_kernel(
     const float *__restrict__ X, const int *__restrict__ perm, const int *__restrict__ seg_start,
-    const int *__restrict__ cnt, const float *C_old, int64_t k, int64_t d, int chunks,
-    float *C_new, double *__restrict__ shift_partial) {
+    const int *__restrict__ cnt, const int *__restrict__ big, const float *C_old, int64_t k,
+    int64_t d, int chunks, float *C_new, double *__restrict__ shift_partial) {
     // C_old and C_new may be the same array: each element is read and written
     // by the same thread only, so they carry no __restrict__.
-    __shared__ double wshift[4];
-    double shift = 0.0;
-    const int64_t j0 = (int64_t)(blockIdx.x / (unsigned)chunks) * kClustersPerBlock;
-    const int64_t c = blockIdx.x % (unsigned)chunks;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    int64_t col[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) col[e] = c * kCols + (kVec ? 4 * lane + e : lane + 64 * e);
-
-    const int64_t j = j0 + wave;
-    if (j < k) {
-        const int count = cnt[j];
-        if (count <= kSplitMin) {
-            double s[4] = {0.0, 0.0, 0.0, 0.0};
-            sum_rows<kVec>(X, perm + seg_start[j], 0, count, d, col, s);
-            write_mean<kShift>(C_old, C_new, j, d, count, col, s, shift);
-        }
-    }
-    if (kShift) {
-        for (int off = 32; off > 0; off >>= 1) shift += __shfl_xor(shift, off);
-        if (lane == 0) wshift[wave] = shift;
-        __syncthreads();
-        if (threadIdx.x == 0)
-            shift_partial[blockIdx.x] = ((wshift[0] + wshift[1]) + wshift[2]) + wshift[3];
-    }
-}
-
-// Clusters with more than kSplitMin rows, listed in big[1 .. big[0]]: work
-// item i is (cluster big[1 + i / chunks], chunk i % chunks); a block of
-// kBigWaves waves takes items blockIdx.x, + gridDim.x, ... Wave p sums part p
-// of the cluster's rows (kBigWaves contiguous parts), wave 0 adds the parts
-// in order and writes the mean. If kShift, block b writes the sum of its
-// items' (new - old)^2 in item order to shift_partial[b].
-template <bool kVec, bool kShift>
-__global__ __launch_bounds__(kBigWaves * 64) void big_mean_kernel(
-    const float *__restrict__ X, const int *__restrict__ perm, const int *__restrict__ seg_start,
-    const int *__restrict__ cnt, const int *__restrict__ big, const float *C_old, int64_t d,
-    int chunks, float *C_new, double *__restrict__ shift_partial) {
     __shared__ double part[kBigWaves - 1][kCols];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     int lc[4];  // columns within a chunk
 #pragma unroll
     for (int e = 0; e < 4; ++e) lc[e] = kVec ? 4 * lane + e : lane + 64 * e;
     double shift = 0.0;
-    const int64_t items = (int64_t)big[0] * chunks;
-    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-        const int64_t j = big[1 + it / chunks];
-        const int64_t c = it % chunks;
+    if (blockIdx.x < kBigBlocks) {
+        const int64_t items = (int64_t)big[0] * chunks;
+        for (int64_t it = blockIdx.x; it < items; it += kBigBlocks) {
+            const int64_t j = big[1 + it / chunks];
+            const int64_t c = it % chunks;
+            int64_t col[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) col[e] = c * kCols + lc[e];
+            const int count = cnt[j];  // > kSplitMin
+            const int q = (count + kBigWaves - 1) / kBigWaves;
+            const int r0 = min(count, wave * q), r1 = min(count, r0 + q);
+            double s[4] = {0.0, 0.0, 0.0, 0.0};
+            sum_rows<kVec>(X, perm + seg_start[j], r0, r1, d, col, s);
+            if (wave > 0)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) part[wave - 1][lc[e]] = s[e];
+            __syncthreads();
+            if (wave == 0) {
+#pragma unroll 1
+                for (int pw = 0; pw < kBigWaves - 1; ++pw)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s[e] += part[pw][lc[e]];
+                write_mean<kShift>(C_old, C_new, j, d, count, col, s, shift);
+            }
+            __syncthreads();  // part is reused by the next item
+        }
+    } else {
+        const unsigned sb = blockIdx.x - kBigBlocks;
+        const int64_t j = (int64_t)(sb / (unsigned)chunks) * kBigWaves + wave;
+        const int64_t c = sb % (unsigned)chunks;
         int64_t col[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) col[e] = c * kCols + lc[e];
-        const int count = cnt[j];  // > kSplitMin
-        const int q = (count + kBigWaves - 1) / kBigWaves;
-        const int r0 = min(count, wave * q), r1 = min(count, r0 + q);
-        double s[4] = {0.0, 0.0, 0.0, 0.0};
-        sum_rows<kVec>(X, perm + seg_start[j], r0, r1, d, col, s);
-        if (wave > 0)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) part[wave - 1][lc[e]] = s[e];
-        __syncthreads();
-        if (wave == 0) {
-#pragma unroll 1
-            for (int pw = 0; pw < kBigWaves - 1; ++pw)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) s[e] += part[pw][lc[e]];
-            write_mean<kShift>(C_old, C_new, j, d, count, col, s, shift);
+        if (j < k) {
+            const int count = cnt[j];
+            if (count <= kSplitMin) {
+                double s[4] = {0.0, 0.0, 0.0, 0.0};
+                sum_rows<kVec>(X, perm + seg_start[j], 0, count, d, col, s);
+                write_mean<kShift>(C_old, C_new, j, d, count, col, s, shift);
+            }
         }
-        __syncthreads();  // part is reused by the next item
     }
-    if (kShift && wave == 0) {
+    if (kShift) {
         for (int off = 32; off > 0; off >>= 1) shift += __shfl_xor(shift, off);
-        if (lane == 0) shift_partial[blockIdx.x] = shift;
+        __syncthreads();  // part may still be read by wave 0 of the last item
+        if (lane == 0) part[0][wave] = shift;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double t = 0.0;
+            for (int w = 0; w < kBigWaves; ++w) t += part[0][w];
+            shift_partial[blockIdx.x] = t;
+        }
     }
 }
 
@@ -343,7 +330,7 @@ inline unsigned grid_stride_blocks(int64_t n) {
 }  // namespace
 
 static int64_t small_mean_blocks(int64_t k, int64_t d) {
-    return cdiv(k, kClustersPerBlock) * cdiv(d, kCols);
+    return cdiv(k, kBigWaves) * cdiv(d, kCols);
 }
 
 int64_t update_grid_blocks(int64_t n, int64_t k, int64_t d) {
@@ -384,35 +371,22 @@ hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const fl
                                                                  ws.tile_hist, ws.seg_start,
                                                                  ws.perm);
     const int chunks = (int)cdiv(d, kCols);
-    const unsigned blocks = (unsigned)small_mean_blocks(k, d);
-    double *big_shift = shift_partial ? shift_partial + blocks : nullptr;
+    const unsigned blocks = (unsigned)mean_blocks(k, d);
+    const unsigned bt = kBigWaves * 64;
     const bool vec = (d % 4 == 0) && ((uintptr_t)X % 16 == 0) && ((uintptr_t)C_old % 16 == 0) &&
                      ((uintptr_t)C_new % 16 == 0);
     if (vec && shift_partial)
-        segment_mean_kernel<true, true><<<blocks, 256, 0, stream>>>(
-            X, ws.perm, ws.seg_start, ws.cnt, C_old, k, d, chunks, C_new, shift_partial);
+        segment_mean_kernel<true, true><<<blocks, bt, 0, stream>>>(
+            X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, k, d, chunks, C_new, shift_partial);
     else if (vec)
-        segment_mean_kernel<true, false><<<blocks, 256, 0, stream>>>(
-            X, ws.perm, ws.seg_start, ws.cnt, C_old, k, d, chunks, C_new, nullptr);
+        segment_mean_kernel<true, false><<<blocks, bt, 0, stream>>>(
+            X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, k, d, chunks, C_new, nullptr);
     else if (shift_partial)
-        segment_mean_kernel<false, true><<<blocks, 256, 0, stream>>>(
-            X, ws.perm, ws.seg_start, ws.cnt, C_old, k, d, chunks, C_new, shift_partial);
+        segment_mean_kernel<false, true><<<blocks, bt, 0, stream>>>(
+            X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, k, d, chunks, C_new, shift_partial);
     else
-        segment_mean_kernel<false, false><<<blocks, 256, 0, stream>>>(
-            X, ws.perm, ws.seg_start, ws.cnt, C_old, k, d, chunks, C_new, nullptr);
-    const unsigned bt = kBigWaves * 64;
-    if (vec && shift_partial)
-        big_mean_kernel<true, true><<<kBigBlocks, bt, 0, stream>>>(
-            X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, d, chunks, C_new, big_shift);
-    else if (vec)
-        big_mean_kernel<true, false><<<kBigBlocks, bt, 0, stream>>>(
-            X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, d, chunks, C_new, nullptr);
-    else if (shift_partial)
-        big_mean_kernel<false, true><<<kBigBlocks, bt, 0, stream>>>(
-            X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, d, chunks, C_new, big_shift);
-    else
-        big_mean_kernel<false, false><<<kBigBlocks, bt, 0, stream>>>(
-            X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, d, chunks, C_new, nullptr);
+        segment_mean_kernel<false, false><<<blocks, bt, 0, stream>>>(
+            X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, k, d, chunks, C_new, nullptr);
     return hipGetLastError();
 }
 
