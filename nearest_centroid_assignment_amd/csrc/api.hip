@@ -20,7 +20,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct Layout {
     size_t cn = 0, tile_hist = 0, cnt = 0, seg_start = 0, perm = 0, big = 0;
     // kmeans_fit only
-    size_t md = 0, dist = 0, empty = 0, sort_key = 0, sort_idx = 0, moves_src = 0, moves_dst = 0,
+    size_t md = 0, dist = 0, empty = 0, sort_key = 0, sort_idx = 0,
            shift_partial = 0, scalars = 0;
     // kmeans_plusplus only
     size_t pp_buf_a = 0, pp_buf_b = 0, pp_parts_a = 0, pp_parts_b = 0, pp_cand_a = 0,
@@ -51,7 +51,6 @@ Layout layout(int64_t n, int64_t k, int64_t d, int op) {
         off += round_up(((size_t)k + 1) * sizeof(int));
     }
     if (op == KM_OP_FIT) {
-        const int64_t nk = n < k ? n : k;
         const int64_t cap = km::reloc_sort_cap(n, k);
         L.md = off;
         off += round_up((size_t)n * sizeof(float));
@@ -63,13 +62,9 @@ Layout layout(int64_t n, int64_t k, int64_t d, int op) {
         off += round_up((size_t)cap * sizeof(unsigned long long));
         L.sort_idx = off;
         off += round_up((size_t)cap * sizeof(int));
-        L.moves_src = off;
-        off += round_up((size_t)nk * sizeof(int));
-        L.moves_dst = off;
-        off += round_up((size_t)nk * sizeof(int));
         L.shift_partial = off;
         off += round_up((size_t)km::mean_blocks(k, d) * sizeof(double));
-        L.scalars = off;  // num_empty, n_moves, converged
+        L.scalars = off;  // num_empty, converged
         off += round_up(4 * sizeof(int));
     }
     if (op == KM_OP_KMEANSPP) {
@@ -120,7 +115,7 @@ char *ws_base(void *workspace) {
 
 bool grid_ok(int64_t n, int64_t k, int64_t d) {
     return km::assign_grid_threads(n, k, d) <= kMaxGridThreads &&
-           km::update_grid_blocks(n, k, d) * 256 <= kMaxGridThreads;
+           km::update_grid_threads(n, k, d) <= kMaxGridThreads;
 }
 
 // An array argument: pointer, element count, element size.
@@ -292,11 +287,8 @@ int kmeans_fit(const float *X, const float *C_init, int64_t n, int64_t k, int64_
     rs.empty = (int *)(base + L.empty);
     rs.sort_key = (unsigned long long *)(base + L.sort_key);
     rs.sort_idx = (int *)(base + L.sort_idx);
-    rs.moves_src = (int *)(base + L.moves_src);
-    rs.moves_dst = (int *)(base + L.moves_dst);
     rs.num_empty = scalars;
-    rs.n_moves = scalars + 1;
-    int *converged = scalars + 2;
+    int *converged = scalars + 1;
     double *shift_partial = (double *)(base + L.shift_partial);
     const bool relocate = (flags & KM_FIT_RELOCATE_EMPTY) != 0;
 

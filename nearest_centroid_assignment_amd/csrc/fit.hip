@@ -12,11 +12,11 @@
 //
 //   reloc_dist_kernel    exact float64 distance of every sample to its centre
 //                        (skipped, by every block, when no cluster is empty)
-//   reloc_select_kernel  one block: list E, pick the m farthest samples by a
-//                        bitwise threshold search on the distances, compact
-//                        them in sample order, sort them (bitonic) by distance
-//                        descending then index ascending, pair them with E
-//   reloc_apply_kernel   relabel the moved samples
+//   reloc_select_kernel  one block: list E, find the m-th largest distance by
+//                        a radix select (8 bits a pass, from the top), compact
+//                        the m farthest samples in sample order, sort them
+//                        (bitonic) by distance descending then index
+//                        ascending, and relabel the r-th to E[r]
 //   shift_kernel         one block: centre shift = sum of the update's
 //                        per-block partials, in block order; converged flag
 //   inertia_kernel       one block: sum of the final squared distances
@@ -34,17 +34,18 @@ __global__ __launch_bounds__(256) void reloc_dist_kernel(const float *__restrict
                                                          double *__restrict__ dist) {
     if (*num_empty == 0) return;  // uniform: nothing to relocate
     const int lane = threadIdx.x & 63;
-    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (i >= n) return;
-    const float *x = X + i * d;
-    const float *c = C + labels[i] * d;
-    double s = 0.0;
-    for (int64_t t = lane; t < d; t += 64) {
-        const double diff = (double)x[t] - (double)c[t];
-        s += diff * diff;
+    for (int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); i < n;
+         i += (int64_t)gridDim.x * 4) {
+        const float *x = X + i * d;
+        const float *c = C + labels[i] * d;
+        double s = 0.0;
+        for (int64_t t = lane; t < d; t += 64) {
+            const double diff = (double)x[t] - (double)c[t];
+            s += diff * diff;
+        }
+        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+        if (lane == 0) dist[i] = s;
     }
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (lane == 0) dist[i] = s;
 }
 
 // Exclusive prefix of a 0/1 flag over the 1024 threads of the block, in
@@ -66,17 +67,6 @@ __device__ int block_flag_scan(bool flag, int *total, int *lds16) {
     return before + in_wave;
 }
 
-// Sum of a per-thread count over the 1024 threads of the block.
-__device__ long long block_count(long long v, long long *lds16) {
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    if ((threadIdx.x & 63) == 0) lds16[threadIdx.x >> 6] = v;
-    __syncthreads();
-    long long t = 0;
-    for (int w = 0; w < 16; ++w) t += lds16[w];
-    __syncthreads();
-    return t;
-}
-
 // (key_a, idx_a) goes before (key_b, idx_b): larger distance first, then
 // lower index.
 __device__ __forceinline__ bool before(unsigned long long ka, int ia, unsigned long long kb,
@@ -84,18 +74,23 @@ __device__ __forceinline__ bool before(unsigned long long ka, int ia, unsigned l
     return ka > kb || (ka == kb && ia < ib);
 }
 
+__device__ __forceinline__ unsigned long long dist_bits(double v) {
+    return (unsigned long long)__double_as_longlong(v);
+}
+
+constexpr int kSelWaves = 16;  // reloc_select_kernel: 1024 threads
+
 __global__ __launch_bounds__(1024) void reloc_select_kernel(
     const int *__restrict__ cnt, int64_t k, int64_t n, const double *__restrict__ dist,
     const int *__restrict__ num_empty, int *__restrict__ empty, unsigned long long *sort_key,
-    int *sort_idx, int64_t sort_cap, int *__restrict__ moves_src, int *__restrict__ moves_dst,
-    int *__restrict__ n_moves) {
+    int *sort_idx, int64_t sort_cap, int64_t *__restrict__ labels) {
     __shared__ int lds16[16];
-    __shared__ long long lds16ll[16];
-    const int tid = threadIdx.x;
-    if (*num_empty == 0) {
-        if (tid == 0) *n_moves = 0;
-        return;
-    }
+    __shared__ int hist[kSelWaves][256];
+    __shared__ int bins[256];
+    __shared__ int sel_digit, sel_above;
+    __shared__ int wave_gt[kSelWaves], wave_eq[kSelWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (*num_empty == 0) return;
     // E: empty clusters in increasing index.
     int n_empty = 0;
     for (int64_t base = 0; base < k; base += 1024) {
@@ -106,43 +101,112 @@ __global__ __launch_bounds__(1024) void reloc_select_kernel(
         if (e) empty[n_empty + pos] = (int)j;
         n_empty += tot;
     }
-    const int64_t m = n_empty < n ? n_empty : n;
+    const int m = n_empty < n ? n_empty : (int)n;
 
     // Distances are >= 0, so their IEEE bit patterns order like the values.
-    // t = the largest 64-bit value with #{i : bits_i >= t} >= m, built bit by
-    // bit from the top (the count only falls as t grows).
-    unsigned long long t = 0;
-    for (int bit = 63; bit >= 0; --bit) {
-        const unsigned long long cand = t | (1ull << bit);
-        long long c = 0;
-        for (int64_t i = tid; i < n; i += 1024)
-            c += (unsigned long long)__double_as_longlong(dist[i]) >= cand;
-        if (block_count(c, lds16ll) >= m) t = cand;
-    }
-    long long g = 0;
-    for (int64_t i = tid; i < n; i += 1024)
-        g += (unsigned long long)__double_as_longlong(dist[i]) > t;
-    const long long need_ties = m - block_count(g, lds16ll);
-
-    // The m selected samples, compacted in sample order: all above t, and the
-    // need_ties lowest-indexed ones equal to t.
-    int sel = 0, ties = 0;
-    for (int64_t base = 0; base < n; base += 1024) {
-        const int64_t i = base + tid;
-        const unsigned long long b =
-            i < n ? (unsigned long long)__double_as_longlong(dist[i]) : 0ull;
-        const bool eq = i < n && b == t;
-        int eq_tot;
-        const int eq_pos = block_flag_scan(eq, &eq_tot, lds16);
-        const bool take = i < n && (b > t || (eq && ties + eq_pos < need_ties));
-        int take_tot;
-        const int pos = block_flag_scan(take, &take_tot, lds16);
-        if (take) {
-            sort_key[sel + pos] = b;
-            sort_idx[sel + pos] = (int)i;
+    // t = the m-th largest bit pattern, one byte a pass from the top: among
+    // the samples whose higher bytes equal t's, histogram the next byte (one
+    // LDS histogram per wave), and take the largest byte value whose count
+    // from the top reaches the rank still wanted. `remaining` ends as the
+    // number of samples equal to t that belong to the m farthest.
+    unsigned long long t = 0, known = 0;
+    int remaining = m;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+        for (int i = tid; i < kSelWaves * 256; i += 1024) (&hist[0][0])[i] = 0;
+        __syncthreads();
+        for (int64_t i = tid; i < n; i += 1024) {
+            const unsigned long long b = dist_bits(dist[i]);
+            if ((b & known) == t) atomicAdd(&hist[wave][(int)(b >> shift) & 255], 1);
         }
-        sel += take_tot;
-        ties += eq_tot;
+        __syncthreads();
+        if (tid < 256) {
+            int c = 0;
+            for (int w = 0; w < kSelWaves; ++w) c += hist[w][tid];
+            bins[tid] = c;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // Lane l holds bytes 4l..4l+3; S = count of bytes >= 4l.
+            const int h0 = bins[4 * lane], h1 = bins[4 * lane + 1], h2 = bins[4 * lane + 2],
+                      h3 = bins[4 * lane + 3];
+            const int own = h0 + h1 + h2 + h3;
+            int S = own;
+            for (int off = 1; off < 64; off <<= 1) {
+                const int o = __shfl_down(S, off);
+                if (lane + off < 64) S += o;
+            }
+            // S falls with the lane and lane 0 holds every candidate, so the
+            // lanes with S >= remaining are 0..L.
+            const unsigned long long ok = __ballot(S >= remaining);
+            const int L = 63 - __clzll(ok);
+            if (lane == L) {
+                int above = S - own;  // candidates with a byte above 4L + 3
+                int digit = 4 * L;
+                if (above + h3 >= remaining) {
+                    digit += 3;
+                } else {
+                    above += h3;
+                    if (above + h2 >= remaining) {
+                        digit += 2;
+                    } else {
+                        above += h2;
+                        if (above + h1 >= remaining) {
+                            digit += 1;
+                        } else {
+                            above += h1;
+                        }
+                    }
+                }
+                sel_digit = digit;
+                sel_above = above;
+            }
+        }
+        __syncthreads();
+        t |= (unsigned long long)sel_digit << shift;
+        known |= 0xffull << shift;
+        remaining -= sel_above;
+    }
+    const int need_ties = remaining;
+
+    // The m selected samples, compacted in sample order: all above t and the
+    // need_ties lowest-indexed ones equal to t. Each wave takes one contiguous
+    // range of samples; a first sweep counts, a second writes.
+    const int64_t per = (n + kSelWaves * 64 - 1) / (kSelWaves * 64) * 64;
+    const int64_t lo = wave * per, hi = lo + per < n ? lo + per : n;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int gt = 0, eq = 0;
+    for (int64_t base = lo; base < hi; base += 64) {
+        const int64_t i = base + lane;
+        const unsigned long long b = i < hi ? dist_bits(dist[i]) : 0ull;
+        gt += __popcll(__ballot(i < hi && b > t));
+        eq += __popcll(__ballot(i < hi && b == t));
+    }
+    if (lane == 0) {
+        wave_gt[wave] = gt;
+        wave_eq[wave] = eq;
+    }
+    __syncthreads();
+    int out = 0, eq_seen = 0;
+    for (int w = 0; w < wave; ++w) {
+        out += wave_gt[w];
+        eq_seen += wave_eq[w];
+    }
+    out += eq_seen < need_ties ? eq_seen : need_ties;
+    for (int64_t base = lo; base < hi; base += 64) {
+        const int64_t i = base + lane;
+        const unsigned long long b = i < hi ? dist_bits(dist[i]) : 0ull;
+        const bool is_eq = i < hi && b == t;
+        const unsigned long long eq_mask = __ballot(is_eq);
+        const bool take =
+            i < hi && (b > t || (is_eq && eq_seen + __popcll(eq_mask & below) < need_ties));
+        const unsigned long long take_mask = __ballot(take);
+        const int pos = out + __popcll(take_mask & below);
+        if (take && pos < m) {
+            sort_key[pos] = b;
+            sort_idx[pos] = (int)i;
+        }
+        out += __popcll(take_mask);
+        eq_seen += __popcll(eq_mask);
     }
     // Pad to a power of two with entries that sort last.
     int64_t p2 = 1;
@@ -173,20 +237,11 @@ __global__ __launch_bounds__(1024) void reloc_select_kernel(
             __syncthreads();
         }
     }
+    // The r-th farthest sample becomes the only member of E[r].
     for (int64_t r = tid; r < m; r += 1024) {
-        moves_src[r] = sort_idx[r];
-        moves_dst[r] = empty[r];
+        const int src = sort_idx[r];
+        if (src >= 0 && src < n) labels[src] = empty[r];
     }
-    if (tid == 0) *n_moves = (int)m;
-}
-
-__global__ __launch_bounds__(256) void reloc_apply_kernel(const int *__restrict__ n_moves,
-                                                          const int *__restrict__ moves_src,
-                                                          const int *__restrict__ moves_dst,
-                                                          int64_t *__restrict__ labels) {
-    const int m = *n_moves;
-    for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < m; r += gridDim.x * blockDim.x)
-        labels[moves_src[r]] = moves_dst[r];
 }
 
 // Sum of v over the block in a fixed order (each thread a fixed strided set,
@@ -249,15 +304,13 @@ hipError_t launch_relocate(const float *X, const float *C_old, int64_t *labels, 
                            int64_t k, int64_t d, const RelocScratch &rs, const UpdateScratch &ws,
                            hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    reloc_dist_kernel<<<(unsigned)cdiv(n, 4), 256, 0, stream>>>(X, C_old, labels, n, d,
-                                                                 rs.num_empty, rs.dist);
+    int64_t b = cdiv(n, 4);
+    if (b > 65536) b = 65536;
+    reloc_dist_kernel<<<(unsigned)b, 256, 0, stream>>>(X, C_old, labels, n, d, rs.num_empty,
+                                                       rs.dist);
     reloc_select_kernel<<<1, 1024, 0, stream>>>(ws.cnt, k, n, rs.dist, rs.num_empty, rs.empty,
                                                 rs.sort_key, rs.sort_idx, reloc_sort_cap(n, k),
-                                                rs.moves_src, rs.moves_dst, rs.n_moves);
-    int64_t b = cdiv(n < k ? n : k, 256);
-    if (b > 1024) b = 1024;
-    reloc_apply_kernel<<<(unsigned)b, 256, 0, stream>>>(rs.n_moves, rs.moves_src, rs.moves_dst,
-                                                         labels);
+                                                labels);
     return hipGetLastError();
 }
 

@@ -67,10 +67,7 @@ struct RelocScratch {
     int *empty;                    // k: empty clusters in increasing index
     unsigned long long *sort_key;  // reloc_sort_cap(n, k)
     int *sort_idx;                 // reloc_sort_cap(n, k)
-    int *moves_src;                // min(n, k): moved samples
-    int *moves_dst;                // min(n, k): their new clusters
     int *num_empty;                // 1: empty clusters after the assignment
-    int *n_moves;                  // 1: relocations made
 };
 
 // Size of the relocation sort buffers: the power of two >= min(n, k).
@@ -112,9 +109,11 @@ hipError_t launch_kmeanspp(const float *X, int64_t n, int64_t d, int64_t k, int6
                            int trials, const double *rand, float *centres, int64_t *chosen,
                            const PPScratch &ws, hipStream_t stream);
 
-// Upper limits of the launch grids (blocks); checked by the C-ABI layer.
-// Work-items of the assignment launch (the tile the launcher will choose).
+// Largest launch grids, in work-items; checked by the C-ABI layer against the
+// 2^32 - 1 limit of one dispatch dimension.
+// The assignment launch (the tile the launcher will choose).
 int64_t assign_grid_threads(int64_t n, int64_t k, int64_t d);
-int64_t update_grid_blocks(int64_t n, int64_t k, int64_t d);
+// The largest launch of the update (count, group, mean).
+int64_t update_grid_threads(int64_t n, int64_t k, int64_t d);
 
 }  // namespace km

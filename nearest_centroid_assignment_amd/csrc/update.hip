@@ -138,36 +138,42 @@ __global__ __launch_bounds__(1024) void cluster_scan_kernel(const int *__restric
     }
 }
 
-// One block per tile. The rank of a row among the rows of the same tile with
-// the same label and a smaller index is counted directly from the tile's
-// labels in LDS, which keeps the grouping stable (increasing row order inside
-// every cluster) and independent of thread timing.
-__global__ __launch_bounds__(256) void scatter_kernel(const int64_t *__restrict__ labels, int64_t n,
-                                                      int64_t k, int64_t n_tiles,
-                                                      const int *__restrict__ tile_prefix,
-                                                      const int *__restrict__ seg_start,
-                                                      int *__restrict__ perm) {
-    __shared__ int lab[kTile];
+// One block per tile, one thread per row. The rank of a row among the rows of
+// the same tile with the same label and a smaller index is counted directly
+// from the tile's labels in LDS, which keeps the grouping stable (increasing
+// row order inside every cluster) and independent of thread timing. A wave
+// first counts over the whole chunks of 64 rows before its own, four labels
+// per (broadcast) LDS read with no divergence, then over the earlier rows of
+// its own chunk.
+static_assert(kTile == 1024, "scatter_kernel runs one 1024-thread block per tile");
+__global__ __launch_bounds__(1024) void scatter_kernel(const int64_t *__restrict__ labels, int64_t n,
+                                                       int64_t k, int64_t n_tiles,
+                                                       const int *__restrict__ tile_prefix,
+                                                       const int *__restrict__ seg_start,
+                                                       int *__restrict__ perm) {
+    __shared__ __align__(16) int lab[kTile];
     const int64_t b = blockIdx.x;
     const int64_t row0 = b * kTile;
     const int rows = (int)min((int64_t)kTile, n - row0);
-    for (int r = threadIdx.x; r < kTile; r += 256) {
-        int l = -1;
-        if (r < rows) {
-            const int64_t v = labels[row0 + r];
-            l = (v >= 0 && v < k) ? (int)v : -1;
-        }
-        lab[r] = l;
+    const int r = threadIdx.x;
+    int l = -1;
+    if (r < rows) {
+        const int64_t v = labels[row0 + r];
+        l = (v >= 0 && v < k) ? (int)v : -1;
     }
+    lab[r] = l;
     __syncthreads();
-    for (int r = threadIdx.x; r < rows; r += 256) {
-        const int l = lab[r];
-        if (l < 0) continue;
-        int rank = 0;
-        for (int q = 0; q < r; ++q) rank += lab[q] == l;
-        const int64_t pos = (int64_t)seg_start[l] + tile_prefix[(int64_t)l * n_tiles + b] + rank;
-        perm[pos] = (int)(row0 + r);
+    if (l < 0) return;
+    const int chunk0 = r & ~63;
+    const int4 *lab4 = reinterpret_cast<const int4 *>(lab);
+    int rank = 0;
+    for (int q = 0; q < chunk0; q += 4) {
+        const int4 v = lab4[q >> 2];
+        rank += (v.x == l) + (v.y == l) + (v.z == l) + (v.w == l);
     }
+    for (int q = chunk0; q < r; ++q) rank += lab[q] == l;
+    const int64_t pos = (int64_t)seg_start[l] + tile_prefix[(int64_t)l * n_tiles + b] + rank;
+    perm[pos] = (int)(row0 + r);
 }
 
 // Rows are fetched in rounds of kBatch: the round's row indices, then all its
@@ -333,11 +339,12 @@ static int64_t small_mean_blocks(int64_t k, int64_t d) {
     return cdiv(k, kBigWaves) * cdiv(d, kCols);
 }
 
-int64_t update_grid_blocks(int64_t n, int64_t k, int64_t d) {
-    const int64_t a = small_mean_blocks(k, d);
-    const int64_t b = cdiv(n, kTile);
-    const int64_t c = cdiv(k, 4);
-    return a > b ? (a > c ? a : c) : (b > c ? b : c);
+int64_t update_grid_threads(int64_t n, int64_t k, int64_t d) {
+    const int64_t mean = (small_mean_blocks(k, d) + kBigBlocks) * (kBigWaves * 64);
+    const int64_t scatter = cdiv(n, kTile) * kTile;  // tile_hist uses a quarter of this
+    const int64_t scan = cdiv(k, 4) * 256;
+    const int64_t m = mean > scatter ? mean : scatter;
+    return m > scan ? m : scan;
 }
 
 hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t *counts,
@@ -367,7 +374,7 @@ hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const fl
                                  double *shift_partial, const UpdateScratch &ws,
                                  hipStream_t stream) {
     if (n > 0)
-        scatter_kernel<<<(unsigned)ws.n_tiles, 256, 0, stream>>>(labels, n, k, ws.n_tiles,
+        scatter_kernel<<<(unsigned)ws.n_tiles, kTile, 0, stream>>>(labels, n, k, ws.n_tiles,
                                                                  ws.tile_hist, ws.seg_start,
                                                                  ws.perm);
     const int chunks = (int)cdiv(d, kCols);

@@ -88,6 +88,17 @@ def test_launch_grid_limit(lib, monkeypatch):
     assert ws(2**21, 2**14, 1, 0) > 0
 
 
+def test_update_grid_limit(lib):
+    """The mean launch has one 1024-thread block per 16 clusters x 256
+    columns (plus 256 for large clusters): k = 2^20, d = 2^15 needs 2^33
+    work-items and is refused by every op that runs the update; d = 2^13
+    (about 2^31) is accepted."""
+    ws = binding.kmeans_workspace_bytes
+    for op in (1, 2, 3):  # update, Lloyd step, fit
+        assert ws(1024, 2**20, 2**15, op) == 0
+        assert ws(1024, 2**20, 2**13, op) > 0
+
+
 def _assign(lib, X=X_P, C=C_P, n=100, k=10, d=8, labels=LAB_P, md=MD_P, ws=WS_P, wsb=None):
     if wsb is None:
         wsb = binding.kmeans_workspace_bytes(max(n, 0), max(k, 1), max(d, 1), 0)

@@ -58,3 +58,10 @@ def test_bench_workloads_exist():
         assert cfg.flops == 2.0 * cfg.n * cfg.k * cfg.d or np.isclose(
             cfg.flops, 2.0 * cfg.n * cfg.k * cfg.d)
     assert set(bench.PAGES_LLOYD_MS) <= set(datagen.CONFIGS)
+
+
+def test_metric_names_the_workload_shape():
+    fh = datagen.CONFIGS["feature_heavy"]
+    assert bench.METRIC_FMT.format(n=fh.n, k=fh.k, d=fh.d) == bench.METRIC
+    mid = datagen.CONFIGS["mid"]
+    assert "65536×1024×2048" in bench.METRIC_FMT.format(n=mid.n, k=mid.k, d=mid.d)

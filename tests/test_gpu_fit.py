@@ -123,3 +123,26 @@ def test_fit_mid_valid_and_deterministic():
     gu.check_labels(X, Cf, g["labels"], o_labels, best, second, rows=rows)
     assert np.array_equal(g["counts"], np.bincount(g["labels"], minlength=len(C)))
     assert abs(g["inertia"] - float(np.sum(g["min_dist"].astype(np.float64)))) <= 1e-9 * g["inertia"]
+
+
+@pytest.mark.parametrize("n,k_near,k_far,seed", [(3000, 100, 300, 11), (5000, 100, 2000, 12)])
+def test_fit_relocates_many_empty_clusters(n, k_near, k_far, seed):
+    """k_far centres start far away and win nothing, so k_far samples are
+    moved at once: more than one 64-sample chunk and (in the second case) more
+    than one 1024-entry pass of the selection sort. Integer data makes the
+    distances exact integers with many equal values, and the threshold
+    distance is shared by more samples than are taken, so the lower-index rule
+    decides among them."""
+    gu.announce(f"fit relocating {k_far} empty clusters, n={n}")
+    X, C = datagen.make_integer(n, k_near, 16, seed=seed)
+    C = np.concatenate([C, np.full((k_far, 16), 1e4, np.float32)]).astype(np.float32)
+    labels0, _, _ = oracle.assign(X, C)
+    dist = ((X.astype(np.float64) - C[labels0].astype(np.float64)) ** 2).sum(axis=1)
+    t = np.sort(dist)[::-1][k_far - 1]
+    assert (dist == t).sum() > k_far - (dist > t).sum()  # ties straddle the cut
+    g = gpu_fit(X, C, 1, 0.0, True)
+    o = oracle.fit(X, C, 1, 0.0, True)
+    compare(g, o, X)
+    g = gpu_fit(X, C, 5, 0.0, True)
+    o = oracle.fit(X, C, 5, 0.0, True)
+    compare(g, o, X)
