@@ -177,10 +177,11 @@ __global__ __launch_bounds__(1024) void scatter_kernel(const int64_t *__restrict
 }
 
 // Rows are fetched in rounds of kBatch: the round's row indices, then all its
-// row loads, then the adds in order.
-constexpr int kBatch = 16;
-
-template <bool kVec>
+// row loads, then the adds in order. kBatch is 16, or 8 when clusters hold 32
+// rows or fewer on average: the kernel then needs about 64 registers instead
+// of about 100, so two 16-wave blocks share a CU and more short clusters are
+// in flight at once. The order of the adds does not depend on kBatch.
+template <bool kVec, int kBatch>
 __device__ __forceinline__ void sum_rows(const float *__restrict__ X, const int *__restrict__ rows,
                                          int r0, int r1, int64_t d, const int64_t (&col)[4],
                                          double (&s)[4]) {
@@ -258,7 +259,7 @@ __device__ __forceinline__ void write_mean(const float *C_old, float *C_new, int
 // kSplitMin rows alone, in increasing sample order; lane l owns 4 columns.
 // If kShift, block b writes the sum of its (new - old)^2 in a fixed order to
 // shift_partial[b].
-template <bool kVec, bool kShift>
+template <bool kVec, bool kShift, int kBatch>
 __global__ __launch_bounds__(kBigWaves * 64) void segment_mean_kernel(
     const float *__restrict__ X, const int *__restrict__ perm, const int *__restrict__ seg_start,
     const int *__restrict__ cnt, const int *__restrict__ big, const float *C_old, int64_t k,
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(kBigWaves * 64) void segment_mean_kernel(
             const int q = (count + kBigWaves - 1) / kBigWaves;
             const int r0 = min(count, wave * q), r1 = min(count, r0 + q);
             double s[4] = {0.0, 0.0, 0.0, 0.0};
-            sum_rows<kVec>(X, perm + seg_start[j], r0, r1, d, col, s);
+            sum_rows<kVec, kBatch>(X, perm + seg_start[j], r0, r1, d, col, s);
             if (wave > 0)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) part[wave - 1][lc[e]] = s[e];
@@ -308,7 +309,7 @@ __global__ __launch_bounds__(kBigWaves * 64) void segment_mean_kernel(
             const int count = cnt[j];
             if (count <= kSplitMin) {
                 double s[4] = {0.0, 0.0, 0.0, 0.0};
-                sum_rows<kVec>(X, perm + seg_start[j], 0, count, d, col, s);
+                sum_rows<kVec, kBatch>(X, perm + seg_start[j], 0, count, d, col, s);
                 write_mean<kShift>(C_old, C_new, j, d, count, col, s, shift);
             }
         }
@@ -369,6 +370,38 @@ hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t *co
 
 int64_t mean_blocks(int64_t k, int64_t d) { return small_mean_blocks(k, d) + kBigBlocks; }
 
+namespace {
+
+struct MeanArgs {
+    const float *X;
+    const int *perm, *seg_start, *cnt, *big;
+    const float *C_old;
+    int64_t k, d;
+    int chunks;
+    float *C_new;
+    double *shift_partial;  // NULL: no centre shift
+};
+
+template <int kBatch>
+void launch_mean(const MeanArgs &a, bool vec, unsigned blocks, unsigned bt, hipStream_t stream) {
+    if (vec && a.shift_partial)
+        segment_mean_kernel<true, true, kBatch><<<blocks, bt, 0, stream>>>(
+            a.X, a.perm, a.seg_start, a.cnt, a.big, a.C_old, a.k, a.d, a.chunks, a.C_new,
+            a.shift_partial);
+    else if (vec)
+        segment_mean_kernel<true, false, kBatch><<<blocks, bt, 0, stream>>>(
+            a.X, a.perm, a.seg_start, a.cnt, a.big, a.C_old, a.k, a.d, a.chunks, a.C_new, nullptr);
+    else if (a.shift_partial)
+        segment_mean_kernel<false, true, kBatch><<<blocks, bt, 0, stream>>>(
+            a.X, a.perm, a.seg_start, a.cnt, a.big, a.C_old, a.k, a.d, a.chunks, a.C_new,
+            a.shift_partial);
+    else
+        segment_mean_kernel<false, false, kBatch><<<blocks, bt, 0, stream>>>(
+            a.X, a.perm, a.seg_start, a.cnt, a.big, a.C_old, a.k, a.d, a.chunks, a.C_new, nullptr);
+}
+
+}  // namespace
+
 hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const float *C_old,
                                  int64_t n, int64_t k, int64_t d, float *C_new,
                                  double *shift_partial, const UpdateScratch &ws,
@@ -382,18 +415,12 @@ hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const fl
     const unsigned bt = kBigWaves * 64;
     const bool vec = (d % 4 == 0) && ((uintptr_t)X % 16 == 0) && ((uintptr_t)C_old % 16 == 0) &&
                      ((uintptr_t)C_new % 16 == 0);
-    if (vec && shift_partial)
-        segment_mean_kernel<true, true><<<blocks, bt, 0, stream>>>(
-            X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, k, d, chunks, C_new, shift_partial);
-    else if (vec)
-        segment_mean_kernel<true, false><<<blocks, bt, 0, stream>>>(
-            X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, k, d, chunks, C_new, nullptr);
-    else if (shift_partial)
-        segment_mean_kernel<false, true><<<blocks, bt, 0, stream>>>(
-            X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, k, d, chunks, C_new, shift_partial);
+    const MeanArgs a{X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, k, d, chunks, C_new,
+                     shift_partial};
+    if (n <= 32 * k)  // at most 32 rows per cluster on average
+        launch_mean<8>(a, vec, blocks, bt, stream);
     else
-        segment_mean_kernel<false, false><<<blocks, bt, 0, stream>>>(
-            X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, k, d, chunks, C_new, nullptr);
+        launch_mean<16>(a, vec, blocks, bt, stream);
     return hipGetLastError();
 }
 
