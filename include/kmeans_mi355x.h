@@ -29,8 +29,10 @@
  *     same time need two workspaces.
  *   - stream is a hipStream_t (NULL = the default stream). Every call except
  *     kmeans_fit only enqueues kernels on it and returns: no host
- *     synchronisation. Results are ready when the stream has reached that
- *     point. A fault inside a kernel surfaces at the caller's next
+ *     synchronisation, no memset, no copy. Results are ready when the stream
+ *     has reached that point. Such a call can also be captured into a HIP
+ *     graph and replayed; a replay reads the buffers' contents at replay
+ *     time. A fault inside a kernel surfaces at the caller's next
  *     synchronisation, not as a return value.
  *   - Shapes: 0 <= n < 2^31, 1 <= k < 2^31, 1 <= d < 2^31. With n = 0 nothing
  *     is read from X, labels or min_dist (they may be NULL). k > n is allowed.
