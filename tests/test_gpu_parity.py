@@ -63,6 +63,41 @@ def test_odd_shapes(n, k, d):
     gu.full_parity(X, C)
 
 
+def _random_shapes(count=24, seed=2024):
+    """Two in three log-uniform in n < 3000, k < 700, d < 700 (degenerate and
+    tiny edges), one in three uniform in [200, 3000) x [100, 700) x [100, 700)
+    (several tiles and stages with ragged ends)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        if i % 3 == 2:
+            out.append(tuple(int(rng.integers(lo, hi)) for lo, hi in ((200, 3000), (100, 700),
+                                                                       (100, 700))))
+        else:
+            out.append(tuple(int(np.exp(rng.uniform(0.0, np.log(hi)))) for hi in (3000, 700, 700)))
+    return out
+
+
+RANDOM_SHAPES = _random_shapes()
+
+
+@pytest.mark.parametrize("n,k,d", RANDOM_SHAPES, ids=[f"{n}x{k}x{d}" for n, k, d in RANDOM_SHAPES])
+def test_random_shapes(n, k, d):
+    """Seeded blobs with a common offset (so the Gram form cancels), centres
+    drawn from the samples when k <= n (rows at distance 0) or at random."""
+    gu.announce(f"random shape {n}x{k}x{d}")
+    rng = np.random.default_rng(n + 31 * k + 977 * d)
+    kb = max(1, min(k, 40))
+    centres = 3.0 * rng.standard_normal((kb, d))
+    offset = rng.uniform(-10.0, 10.0, d)
+    X = (centres[rng.integers(0, kb, n)] + rng.standard_normal((n, d)) + offset).astype(np.float32)
+    if k <= n and rng.random() < 0.5:
+        C = X[rng.choice(n, k, replace=False)].copy()
+    else:
+        C = (3.0 * rng.standard_normal((k, d)) + offset).astype(np.float32)
+    gu.full_parity(X, C)
+
+
 @pytest.mark.parametrize("n,k,d", [(500, 37, 64), (1500, 260, 256), (129, 130, 12)])
 def test_integer_exact(n, k, d):
     """|values| <= 8, d <= 256: every float32 product and partial sum is an
