@@ -43,11 +43,30 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def prewarm(step, ms: float) -> int:
+    """Run `step` untimed until at least `ms` of wall time has passed (at
+    least once); returns the number of runs."""
+    import torch
+
+    runs = 0
+    t0 = time.perf_counter()
+    while True:
+        step()
+        runs += 1
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= ms:
+            return runs
+
+
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--prewarm-ms", type=float, default=300.0,
+                    help="before the warmup steps, run the step untimed for at least this "
+                         "long: the GPU's clocks ramp up over the first tens of ms of "
+                         "sustained work (a short kernel runs ~15 %% slower until then)")
     ap.add_argument("--config", default="feature_heavy",
                     help="workload name (tiny, probe, mid, sample_heavy, feature_heavy, "
                          "centroid_heavy)")
@@ -153,7 +172,8 @@ def bench_fit(args, cfg, Xg, Cg, labels, md, counts, stream) -> int:
         binding.kmeans_fit(Xg, Cg, iters, -1.0, binding.KM_FIT_RELOCATE_EMPTY, C_out, labels,
                            md, counts, info, workspace=ws, stream=stream)
 
-    log(f"fit warmup ({args.warmup} iterations)")
+    pre = prewarm(lambda: fit(1), args.prewarm_ms)
+    log(f"prewarm: {pre} one-iteration fits; fit warmup ({args.warmup} iterations)")
     fit(max(1, args.warmup))
     torch.cuda.synchronize()
     log(f"timing fit with {args.steps} iterations")
@@ -184,6 +204,7 @@ def bench_fit(args, cfg, Xg, Cg, labels, md, counts, stream) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm_steps": pre,
         "ms_per_step": round(per_iter, 3),
         "higher_is_better": False,
         "scaling": "weak",
@@ -224,6 +245,7 @@ def bench_kmeanspp(args, cfg, X, Xg, stream) -> int:
         binding.kmeans_plusplus(Xg, k, first, trials, rg, centres, chosen, workspace=ws,
                                 stream=stream)
 
+    pre = prewarm(run, args.prewarm_ms)
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
@@ -260,6 +282,7 @@ def bench_kmeanspp(args, cfg, X, Xg, stream) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm_steps": pre,
         "ms_per_step": round(ms, 3),
         "higher_is_better": False,
         "scaling": "weak",
@@ -323,7 +346,8 @@ def main() -> int:
     def assign_only():
         binding.kmeans_assign(Xg, Cg, labels, None, workspace=ws, stream=stream)
 
-    log(f"warmup {args.warmup}")
+    pre = prewarm(lloyd, args.prewarm_ms)
+    log(f"prewarm {pre} steps, warmup {args.warmup}")
     for _ in range(args.warmup):
         lloyd()
     torch.cuda.synchronize()
@@ -397,6 +421,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm_steps": pre,
         "ms_per_step": round(lloyd_ms, 3),
         "higher_is_better": True,
         "scaling": "weak",
