@@ -81,10 +81,13 @@ enum { KM_FIT_RELOCATE_EMPTY = 1 };
 
 /*
  * Workspace bytes needed by one call of the given op at shape (n, k, d).
- * The size is O(k + n + k * ceil(n / 1024)) 4-byte words (plus about
- * k * d / 1024 doubles for kmeans_fit), far below the (n, k) distance matrix
- * and the (n, d) sample matrix. Returns 0 when the shape or op is invalid or
- * the shape's launch grid does not fit (a valid shape never needs 0 bytes).
+ * The size is O(k + n + k * ceil(n / 1024)) 4-byte words, plus about
+ * k * d / 1024 doubles for kmeans_fit and, when ceil(d / 256) <= k / 16,
+ * n * ceil(d / 256) floats for kmeans_lloyd_step (partial squared norms of
+ * the rows: at most 1/256 of the size of X and 1/16 of an (n, k) matrix):
+ * far below the (n, k) distance matrix and the (n, d) sample matrix.
+ * Returns 0 when the shape or op is invalid or the shape's launch grid does
+ * not fit (a valid shape never needs 0 bytes).
  */
 size_t kmeans_workspace_bytes(int64_t n, int64_t k, int64_t d, int op);
 
@@ -121,7 +124,12 @@ int kmeans_update(const float *X, const int64_t *labels, const float *C_old,
  * One Lloyd iteration: kmeans_assign against C_old, then kmeans_update with
  * the labels just computed ("004 ...", sections Lloyd step and Cython
  * reference). Arguments as in those two calls; labels are with respect to
- * C_old. C_new may be the same pointer as C_old.
+ * C_old. C_new may be the same pointer as C_old. min_dist is the same
+ * quantity as kmeans_assign's. When ceil(d / 256) <= k / 16 the squared
+ * sample norms in it are gathered by the update while it reads X (float32
+ * partial sums over 256-column chunks, combined in float64), so X is read
+ * twice per step instead of three times; otherwise a separate pass computes
+ * them as in kmeans_assign.
  */
 int kmeans_lloyd_step(const float *X, const float *C_old, int64_t n, int64_t k, int64_t d,
                       int64_t *labels, float *min_dist, float *C_new, int64_t *counts,

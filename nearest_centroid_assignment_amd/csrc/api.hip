@@ -17,8 +17,16 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Whether kmeans_lloyd_step gathers the squared sample norms inside the
+// update (n x ceil(d / 256) float32 partials in the workspace) instead of a
+// separate pass over X: only while that buffer stays below 1/16 of an (n, k)
+// float32 matrix, so the workspace never approaches the distance matrix.
+bool lloyd_fuses_norms(int64_t k, int64_t d) { return km::norm_parts(d) * 16 <= k; }
+
 struct Layout {
     size_t cn = 0, tile_hist = 0, cnt = 0, seg_start = 0, perm = 0, big = 0;
+    // kmeans_lloyd_step only
+    size_t xn_part = 0;
     // kmeans_fit only
     size_t md = 0, dist = 0, empty = 0, sort_key = 0, sort_idx = 0,
            shift_partial = 0, scalars = 0;
@@ -49,6 +57,10 @@ Layout layout(int64_t n, int64_t k, int64_t d, int op) {
         off += round_up((size_t)n * sizeof(int));
         L.big = off;
         off += round_up(((size_t)k + 1) * sizeof(int));
+    }
+    if (op == KM_OP_LLOYD && lloyd_fuses_norms(k, d)) {
+        L.xn_part = off;
+        off += round_up((size_t)n * (size_t)km::norm_parts(d) * sizeof(float));
     }
     if (op == KM_OP_FIT) {
         const int64_t cap = km::reloc_sort_cap(n, k);
@@ -141,14 +153,19 @@ int check_alias(const Out *outs, int n_outs, const Out *ins, int n_ins, int inpl
     return KM_OK;
 }
 
+// The assignment. With min_dist and add_norm, min_dist receives the full
+// squared distance (a separate pass computes ||x||^2 first); with min_dist
+// and !add_norm it receives only the best ||c||^2 - 2 x.c, and the caller
+// adds ||x||^2 later (the Lloyd step gets it from the update's reads of X).
 int run_assign(const float *X, const float *C, int64_t n, int64_t k, int64_t d, int64_t *labels,
-               float *min_dist, float *cn, hipStream_t s) {
+               float *min_dist, bool add_norm, float *cn, hipStream_t s) {
     hipError_t e = km::launch_row_sqnorms(C, k, d, cn, s);
     if (e == hipSuccess) e = km::launch_fill_keys((unsigned long long *)labels, n, s);
-    if (e == hipSuccess && min_dist) e = km::launch_row_sqnorms(X, n, d, min_dist, s);
+    if (e == hipSuccess && min_dist && add_norm) e = km::launch_row_sqnorms(X, n, d, min_dist, s);
     if (e == hipSuccess)
         e = km::launch_assign_tiles(X, C, cn, n, k, d, (unsigned long long *)labels, s);
-    if (e == hipSuccess) e = km::launch_finalize((unsigned long long *)labels, min_dist, n, s);
+    if (e == hipSuccess)
+        e = km::launch_finalize((unsigned long long *)labels, min_dist, add_norm, n, s);
     return e == hipSuccess ? KM_OK : KM_ERR_HIP;
 }
 
@@ -205,7 +222,8 @@ int kmeans_assign(const float *X, const float *C, int64_t n, int64_t k, int64_t 
     if (int rc = check_alias(outs, 3, ins, 2, -1, -1)) return rc;
     if (n == 0) return KM_OK;
     char *base = ws_base(workspace);
-    return run_assign(X, C, n, k, d, labels, min_dist, (float *)(base + L.cn), (hipStream_t)stream);
+    return run_assign(X, C, n, k, d, labels, min_dist, true, (float *)(base + L.cn),
+                      (hipStream_t)stream);
 }
 
 int kmeans_update(const float *X, const int64_t *labels, const float *C_old, int64_t n, int64_t k,
@@ -223,7 +241,7 @@ int kmeans_update(const float *X, const int64_t *labels, const float *C_old, int
     const Out ins[] = {{X, n * d, 4}, {labels, n, 8}, {C_old, k * d, 4}};
     if (int rc = check_alias(outs, 3, ins, 3, /*C_new*/ 0, /*C_old*/ 2)) return rc;
     char *base = ws_base(workspace);
-    const hipError_t e = km::launch_update(X, labels, C_old, n, k, d, C_new, counts,
+    const hipError_t e = km::launch_update(X, labels, C_old, n, k, d, C_new, counts, nullptr,
                                            update_scratch(base, L, n), (hipStream_t)stream);
     return e == hipSuccess ? KM_OK : KM_ERR_HIP;
 }
@@ -248,12 +266,20 @@ int kmeans_lloyd_step(const float *X, const float *C_old, int64_t n, int64_t k, 
     if (int rc = check_alias(outs, 5, ins, 2, /*C_new*/ 2, /*C_old*/ 1)) return rc;
     hipStream_t s = (hipStream_t)stream;
     char *base = ws_base(workspace);
+    // min_dist: the assignment leaves the best ||c||^2 - 2 x.c there; the
+    // update, which reads every row of X anyway, gathers the partial squared
+    // norms of the rows, and a last pass adds them: X is read twice per
+    // step (assignment and update), not three times.
+    float *xn_part =
+        (min_dist && lloyd_fuses_norms(k, d)) ? (float *)(base + L.xn_part) : nullptr;
     if (n > 0) {
-        const int rc = run_assign(X, C_old, n, k, d, labels, min_dist, (float *)(base + L.cn), s);
+        const int rc = run_assign(X, C_old, n, k, d, labels, min_dist, xn_part == nullptr,
+                                  (float *)(base + L.cn), s);
         if (rc != KM_OK) return rc;
     }
-    const hipError_t e = km::launch_update(X, labels, C_old, n, k, d, C_new, counts,
-                                           update_scratch(base, L, n), s);
+    const km::UpdateScratch ws = update_scratch(base, L, n);
+    hipError_t e = km::launch_update(X, labels, C_old, n, k, d, C_new, counts, xn_part, ws, s);
+    if (e == hipSuccess && xn_part) e = km::launch_add_norms(min_dist, xn_part, n, d, ws, s);
     return e == hipSuccess ? KM_OK : KM_ERR_HIP;
 }
 
@@ -295,7 +321,7 @@ int kmeans_fit(const float *X, const float *C_init, int64_t n, int64_t k, int64_
     hipError_t e = km::launch_copy_f32(C_out, C_init, k * d, s);
     int64_t n_iter = 0;
     for (int64_t it = 0; it < max_iter && e == hipSuccess; ++it) {
-        if (n > 0 && run_assign(X, C_out, n, k, d, labels, nullptr, cn, s) != KM_OK)
+        if (n > 0 && run_assign(X, C_out, n, k, d, labels, nullptr, true, cn, s) != KM_OK)
             return KM_ERR_HIP;
         e = km::launch_count(labels, n, k, counts, relocate ? rs.num_empty : nullptr, ws, s);
         if (e == hipSuccess && relocate) {
@@ -303,7 +329,8 @@ int kmeans_fit(const float *X, const float *C_init, int64_t n, int64_t k, int64_
             if (e == hipSuccess) e = km::launch_count(labels, n, k, counts, nullptr, ws, s);
         }
         if (e == hipSuccess)
-            e = km::launch_group_and_mean(X, labels, C_out, n, k, d, C_out, shift_partial, ws, s);
+            e = km::launch_group_and_mean(X, labels, C_out, n, k, d, C_out, shift_partial, nullptr,
+                                          ws, s);
         if (e == hipSuccess)
             e = km::launch_shift(shift_partial, km::mean_blocks(k, d), tol, info + 2, converged, s);
         int host_converged = 0;
@@ -313,7 +340,7 @@ int kmeans_fit(const float *X, const float *C_init, int64_t n, int64_t k, int64_
         n_iter = it + 1;
         if (host_converged) break;
     }
-    if (e == hipSuccess && n > 0 && run_assign(X, C_out, n, k, d, labels, md, cn, s) != KM_OK)
+    if (e == hipSuccess && n > 0 && run_assign(X, C_out, n, k, d, labels, md, true, cn, s) != KM_OK)
         return KM_ERR_HIP;
     if (e == hipSuccess) e = km::launch_count(labels, n, k, counts, nullptr, ws, s);
     if (e == hipSuccess) e = km::launch_inertia(md, n, info + 1, s);

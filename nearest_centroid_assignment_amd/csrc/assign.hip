@@ -7,7 +7,7 @@
 // reused by every sample tile.
 //
 // Kernels:
-//   row_sqnorms_kernel  ||c_j||^2 (and ||x_i||^2 when min_dist is wanted)
+//   row_sqnorms_kernel  ||c_j||^2 (and ||x_i||^2 for min_dist outside a Lloyd step)
 //   fill_keys_kernel    packed-key identity
 //   assign_tile_kernel  float32 MFMA product X_tile . C_tile^T, staged through
 //                       LDS, with the distance, the argmin and the merge across
@@ -406,13 +406,14 @@ using Tile128x128 = TileCfg<2, 2, 2, 2, 16>;  // 256 threads, 40 KiB LDS, 3 bloc
 using Tile64x64 = TileCfg<2, 2, 1, 1, 32>;    // 256 threads, 36 KiB LDS, small problems
 
 __global__ __launch_bounds__(256) void finalize_kernel(unsigned long long *__restrict__ keys,
-                                                       float *__restrict__ min_dist, int64_t n) {
+                                                       float *__restrict__ min_dist,
+                                                       bool add_norm, int64_t n) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
         const unsigned long long key = keys[i];
         if (min_dist) {
             const float partial = unordered_bits((uint32_t)(key >> 32));
-            min_dist[i] = fmaxf(min_dist[i] + partial, 0.0f);
+            min_dist[i] = add_norm ? fmaxf(min_dist[i] + partial, 0.0f) : partial;
         }
         keys[i] = key & 0xffffffffull;  // the int64 label
     }
@@ -517,10 +518,10 @@ hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, 
     return launch_tiles_cfg<Tile64x64, 4>(X, C, cn, n, k, d, keys, stream);
 }
 
-hipError_t launch_finalize(unsigned long long *keys, float *min_dist, int64_t n,
+hipError_t launch_finalize(unsigned long long *keys, float *min_dist, bool add_norm, int64_t n,
                            hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    finalize_kernel<<<grid_stride_blocks(n), 256, 0, stream>>>(keys, min_dist, n);
+    finalize_kernel<<<grid_stride_blocks(n), 256, 0, stream>>>(keys, min_dist, add_norm, n);
     return hipGetLastError();
 }
 

@@ -35,9 +35,11 @@ hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, 
                                int64_t k, int64_t d, unsigned long long *keys,
                                hipStream_t stream);
 
-// Turns packed keys into int64 labels in place; if min_dist != NULL it holds
-// ||x_i||^2 on entry and the clamped full squared distance on exit.
-hipError_t launch_finalize(unsigned long long *keys, float *min_dist, int64_t n,
+// Turns packed keys into int64 labels in place. min_dist (nullable): with
+// add_norm it holds ||x_i||^2 on entry and the clamped full squared distance
+// on exit; without, it receives the best ||c||^2 - 2 x.c, to which
+// launch_add_norms later adds the norms gathered by the update.
+hipError_t launch_finalize(unsigned long long *keys, float *min_dist, bool add_norm, int64_t n,
                            hipStream_t stream);
 
 // Counting phase of the update: per-cluster sizes (ws.cnt, counts) and the
@@ -48,18 +50,31 @@ hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t *co
 // Second phase: stable grouping of rows by label and the float64 segmented
 // sums and means (old centre kept for an empty cluster). If shift_partial is
 // not NULL, mean_blocks(k, d) partial sums of (new - old)^2 are written there.
+// If xn_part is not NULL (only when every label lies in [0, k), so that every
+// row is grouped), it receives norm_parts(d) x n float32 partial squared
+// norms of the rows, in grouped order: [c * n + p] is chunk c of row
+// ws.perm[p]. shift_partial and xn_part are not both set.
 // mean_blocks counts the blocks of both mean kernels (small and big clusters).
 hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const float *C_old,
                                  int64_t n, int64_t k, int64_t d, float *C_new,
-                                 double *shift_partial, const UpdateScratch &ws,
+                                 double *shift_partial, float *xn_part, const UpdateScratch &ws,
                                  hipStream_t stream);
 int64_t mean_blocks(int64_t k, int64_t d);
+// Column chunks of the mean kernel: partial norms per row.
+int64_t norm_parts(int64_t d);
 
 // The whole update: counts, stable grouping of rows by label, segmented sums
-// in float64 and the mean (old centre kept for empty clusters).
+// in float64 and the mean (old centre kept for empty clusters); xn_part as in
+// launch_group_and_mean.
 hipError_t launch_update(const float *X, const int64_t *labels, const float *C_old, int64_t n,
-                         int64_t k, int64_t d, float *C_new, int64_t *counts,
+                         int64_t k, int64_t d, float *C_new, int64_t *counts, float *xn_part,
                          const UpdateScratch &ws, hipStream_t stream);
+
+// min_dist[i] = max(0, ||x_i||^2 + min_dist[i]), ||x_i||^2 the float64 sum of
+// the row's partial norms from the update (xn_part and the grouping ws.perm
+// of that update), rounded once to float32.
+hipError_t launch_add_norms(float *min_dist, const float *xn_part, int64_t n, int64_t d,
+                            const UpdateScratch &ws, hipStream_t stream);
 
 // Workspace sections of the empty-cluster relocation (device pointers).
 struct RelocScratch {

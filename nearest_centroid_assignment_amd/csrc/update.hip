@@ -15,7 +15,10 @@
 //   segment_mean_kernel  float64 sums over each segment, coalesced row chunks,
 //                        then the mean rounded once to float32, or the old
 //                        centre for an empty cluster: a wave per cluster of at
-//                        most 64 rows, sixteen waves per larger one
+//                        most 64 rows, sixteen waves per larger one; in a
+//                        Lloyd step also the rows' partial squared norms
+//   add_norms_kernel     min_dist = max(0, ||x||^2 + best ||c||^2 - 2 x.c)
+//                        from those partial norms
 //
 // No float atomics: every sum has one fixed order, so results are
 // deterministic. For a cluster of at most 64 rows that order is increasing
@@ -176,16 +179,75 @@ __global__ __launch_bounds__(1024) void scatter_kernel(const int64_t *__restrict
     perm[pos] = (int)(row0 + r);
 }
 
+// Sum over the 64 lanes of a wave of each of B per-lane values (B a power of
+// two, at most 64), in a fixed tree order. Each level halves the list: a lane
+// keeps one half and adds the partner's copy of it (lanes O apart), so
+// B - 1 + log2(64 / B) exchanges give every lane one full sum; `row` says
+// which of the B it is. The lanes holding the same row differ only in their
+// low 6 - log2(B) bits. Written as a compile-time recursion so that every
+// index into q is a constant (q stays in registers).
+template <int CNT, int O, int B>
+__device__ __forceinline__ void halve_rows(float (&q)[B], int lane, int &row) {
+    if constexpr (CNT > 1) {
+        constexpr int half = CNT / 2;
+        const bool up = (lane & O) != 0;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            const float send = up ? q[i] : q[i + half];
+            const float keep = up ? q[i + half] : q[i];
+            q[i] = keep + __shfl_xor(send, O);
+        }
+        if (up) row += half;
+        halve_rows<half, O / 2, B>(q, lane, row);
+    } else {
+#pragma unroll
+        for (int o = O; o > 0; o >>= 1) q[0] += __shfl_xor(q[0], o);
+    }
+}
+
+template <int B>
+__device__ __forceinline__ float wave_sum_rows(float (&q)[B], int lane, int &row) {
+    row = 0;
+    halve_rows<B, 32, B>(q, lane, row);
+    return q[0];
+}
+
+// Squared norms of one round's rows over this chunk (q, one value per row
+// and lane): a fixed-order float32 sum over the wave; value u (u < m) is
+// written by one lane to xn[u]. The m values of a round sit side by side.
+template <int B>
+__device__ __forceinline__ void flush_norms(float (&q)[B], int m, int lane, float *xn) {
+    int u;
+    const float t = wave_sum_rows<B>(q, lane, u);
+    // One writer per row: the lane of its group whose low bits are 0.
+    if ((lane & (64 / B - 1)) == 0 && u < m) xn[u] = t;
+}
+
 // Rows are fetched in rounds of kBatch: the round's row indices, then all its
 // row loads, then the adds in order. kBatch is 16, or 8 when clusters hold 32
 // rows or fewer on average: the kernel then needs about 64 registers instead
 // of about 100, so two 16-wave blocks share a CU and more short clusters are
 // in flight at once. The order of the adds does not depend on kBatch.
-template <bool kVec, int kBatch>
+//
+// With kNorm (xn != NULL) the same loads also give each row's squared norm
+// over this chunk's columns: per lane a float32 fused multiply-add chain over
+// its (up to) 4 squares, then a fixed-order float32 sum over the wave (all
+// terms are non-negative, so the relative error stays below 9 * 2^-24, about
+// 5.4e-7), written to xn[p] for the p-th row of `rows`: the norms follow the
+// grouped order, so a wave's writes are contiguous. Float32 keeps the loaded
+// values from being held twice (as float and as the float64 the sums take).
+// A round's cross-lane sums run after the next round's loads are issued, so
+// their exchange latency overlaps the loads.
+template <bool kVec, int kBatch, bool kNorm>
 __device__ __forceinline__ void sum_rows(const float *__restrict__ X, const int *__restrict__ rows,
                                          int r0, int r1, int64_t d, const int64_t (&col)[4],
-                                         double (&s)[4]) {
+                                         double (&s)[4], float *__restrict__ xn) {
     constexpr int B = kVec ? kBatch : kBatch / 2;  // rows per round (the scalar path holds 4x)
+    static_assert((B & (B - 1)) == 0 && B <= 64, "rows per round must be a power of two");
+    const int lane = threadIdx.x & 63;
+    float qp[B];   // the previous round's per-lane squared norms (kNorm)
+    int pp = 0;    // its first row
+    int mp = 0;    // its row count (0: nothing pending)
     for (int p0 = r0; p0 < r1; p0 += B) {
         const int m = min(B, r1 - p0);
         int64_t base[B];
@@ -198,6 +260,7 @@ __device__ __forceinline__ void sum_rows(const float *__restrict__ X, const int 
                 v[u] = (base[u] >= 0 && col[0] < d)
                            ? *reinterpret_cast<const f32x4 *>(X + base[u] + col[0])
                            : f32x4{0.f, 0.f, 0.f, 0.f};
+            if (kNorm && mp > 0) flush_norms<B>(qp, mp, lane, xn + pp);
 #pragma unroll
             for (int u = 0; u < B; ++u) {
                 if (u < m) {
@@ -206,6 +269,9 @@ __device__ __forceinline__ void sum_rows(const float *__restrict__ X, const int 
                     s[2] += (double)v[u].z;
                     s[3] += (double)v[u].w;
                 }
+                if (kNorm)
+                    qp[u] = fmaf(v[u].w, v[u].w,
+                                 fmaf(v[u].z, v[u].z, fmaf(v[u].y, v[u].y, v[u].x * v[u].x)));
             }
         } else {
             float v[B][4];
@@ -214,13 +280,21 @@ __device__ __forceinline__ void sum_rows(const float *__restrict__ X, const int 
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     v[u][e] = (base[u] >= 0 && col[e] < d) ? X[base[u] + col[e]] : 0.f;
+            if (kNorm && mp > 0) flush_norms<B>(qp, mp, lane, xn + pp);
 #pragma unroll
-            for (int u = 0; u < B; ++u)
+            for (int u = 0; u < B; ++u) {
                 if (u < m)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) s[e] += (double)v[u][e];
+                if (kNorm)
+                    qp[u] = fmaf(v[u][3], v[u][3],
+                                 fmaf(v[u][2], v[u][2], fmaf(v[u][1], v[u][1], v[u][0] * v[u][0])));
+            }
         }
+        pp = p0;
+        mp = m;
     }
+    if (kNorm && mp > 0) flush_norms<B>(qp, mp, lane, xn + pp);
 }
 
 // Writes the new centre elements of this thread and, if kShift, adds their
@@ -258,12 +332,14 @@ __device__ __forceinline__ void write_mean(const float *C_old, float *C_new, int
 // each) x one chunk of kCols columns and sums the clusters of at most
 // kSplitMin rows alone, in increasing sample order; lane l owns 4 columns.
 // If kShift, block b writes the sum of its (new - old)^2 in a fixed order to
-// shift_partial[b].
-template <bool kVec, bool kShift, int kBatch>
+// shift_partial[b]. If kNorm, the squared norm over chunk c of the row at
+// position p of perm goes to xn_part[c * n + p] (chunks x n float32).
+template <bool kVec, bool kShift, int kBatch, bool kNorm>
 __global__ __launch_bounds__(kBigWaves * 64) void segment_mean_kernel(
     const float *__restrict__ X, const int *__restrict__ perm, const int *__restrict__ seg_start,
-    const int *__restrict__ cnt, const int *__restrict__ big, const float *C_old, int64_t k,
-    int64_t d, int chunks, float *C_new, double *__restrict__ shift_partial) {
+    const int *__restrict__ cnt, const int *__restrict__ big, const float *C_old, int64_t n,
+    int64_t k, int64_t d, int chunks, float *C_new, double *__restrict__ shift_partial,
+    float *__restrict__ xn_part) {
     // C_old and C_new may be the same array: each element is read and written
     // by the same thread only, so they carry no __restrict__.
     __shared__ double part[kBigWaves - 1][kCols];
@@ -284,7 +360,9 @@ __global__ __launch_bounds__(kBigWaves * 64) void segment_mean_kernel(
             const int q = (count + kBigWaves - 1) / kBigWaves;
             const int r0 = min(count, wave * q), r1 = min(count, r0 + q);
             double s[4] = {0.0, 0.0, 0.0, 0.0};
-            sum_rows<kVec, kBatch>(X, perm + seg_start[j], r0, r1, d, col, s);
+            const int64_t seg = seg_start[j];
+            sum_rows<kVec, kBatch, kNorm>(X, perm + seg, r0, r1, d, col, s,
+                                          kNorm ? xn_part + c * n + seg : nullptr);
             if (wave > 0)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) part[wave - 1][lc[e]] = s[e];
@@ -309,7 +387,9 @@ __global__ __launch_bounds__(kBigWaves * 64) void segment_mean_kernel(
             const int count = cnt[j];
             if (count <= kSplitMin) {
                 double s[4] = {0.0, 0.0, 0.0, 0.0};
-                sum_rows<kVec, kBatch>(X, perm + seg_start[j], 0, count, d, col, s);
+                const int64_t seg = seg_start[j];
+                sum_rows<kVec, kBatch, kNorm>(X, perm + seg, 0, count, d, col, s,
+                                              kNorm ? xn_part + c * n + seg : nullptr);
                 write_mean<kShift>(C_old, C_new, j, d, count, col, s, shift);
             }
         }
@@ -370,41 +450,69 @@ hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t *co
 
 int64_t mean_blocks(int64_t k, int64_t d) { return small_mean_blocks(k, d) + kBigBlocks; }
 
+int64_t norm_parts(int64_t d) { return cdiv(d, kCols); }
+
 namespace {
+
+// For the row i = perm[p] at every position p < rows:
+// min_dist[i] = max(0, ||x_i||^2 + min_dist[i]) with ||x_i||^2 the float64
+// sum of its `chunks` partial norms xn_part[c * n + p] (in chunk order),
+// rounded once to float32; min_dist holds the assignment's best
+// ||c||^2 - 2 x.c on entry. Threads take consecutive positions, so the
+// partial norms are read coalesced.
+__global__ __launch_bounds__(256) void add_norms_kernel(float *__restrict__ min_dist,
+                                                        const float *__restrict__ xn_part,
+                                                        const int *__restrict__ perm,
+                                                        int64_t rows, int64_t n, int chunks) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < rows; p += stride) {
+        double t = 0.0;
+        for (int c = 0; c < chunks; ++c) t += (double)xn_part[c * n + p];
+        const int i = perm[p];
+        min_dist[i] = fmaxf((float)t + min_dist[i], 0.0f);
+    }
+}
 
 struct MeanArgs {
     const float *X;
     const int *perm, *seg_start, *cnt, *big;
     const float *C_old;
-    int64_t k, d;
+    int64_t n, k, d;
     int chunks;
     float *C_new;
     double *shift_partial;  // NULL: no centre shift
+    float *xn_part;         // NULL: no row norms
 };
+
+template <bool kVec, int kBatch>
+void launch_mean_vec(const MeanArgs &a, unsigned blocks, unsigned bt, hipStream_t stream) {
+    if (a.shift_partial)
+        segment_mean_kernel<kVec, true, kBatch, false><<<blocks, bt, 0, stream>>>(
+            a.X, a.perm, a.seg_start, a.cnt, a.big, a.C_old, a.n, a.k, a.d, a.chunks, a.C_new,
+            a.shift_partial, nullptr);
+    else if (a.xn_part)  // rounds of at most 8 rows: 16 with the pending norms spill
+        segment_mean_kernel<kVec, false, (kBatch > 8 ? 8 : kBatch), true><<<blocks, bt, 0, stream>>>(
+            a.X, a.perm, a.seg_start, a.cnt, a.big, a.C_old, a.n, a.k, a.d, a.chunks, a.C_new,
+            nullptr, a.xn_part);
+    else
+        segment_mean_kernel<kVec, false, kBatch, false><<<blocks, bt, 0, stream>>>(
+            a.X, a.perm, a.seg_start, a.cnt, a.big, a.C_old, a.n, a.k, a.d, a.chunks, a.C_new,
+            nullptr, nullptr);
+}
 
 template <int kBatch>
 void launch_mean(const MeanArgs &a, bool vec, unsigned blocks, unsigned bt, hipStream_t stream) {
-    if (vec && a.shift_partial)
-        segment_mean_kernel<true, true, kBatch><<<blocks, bt, 0, stream>>>(
-            a.X, a.perm, a.seg_start, a.cnt, a.big, a.C_old, a.k, a.d, a.chunks, a.C_new,
-            a.shift_partial);
-    else if (vec)
-        segment_mean_kernel<true, false, kBatch><<<blocks, bt, 0, stream>>>(
-            a.X, a.perm, a.seg_start, a.cnt, a.big, a.C_old, a.k, a.d, a.chunks, a.C_new, nullptr);
-    else if (a.shift_partial)
-        segment_mean_kernel<false, true, kBatch><<<blocks, bt, 0, stream>>>(
-            a.X, a.perm, a.seg_start, a.cnt, a.big, a.C_old, a.k, a.d, a.chunks, a.C_new,
-            a.shift_partial);
+    if (vec)
+        launch_mean_vec<true, kBatch>(a, blocks, bt, stream);
     else
-        segment_mean_kernel<false, false, kBatch><<<blocks, bt, 0, stream>>>(
-            a.X, a.perm, a.seg_start, a.cnt, a.big, a.C_old, a.k, a.d, a.chunks, a.C_new, nullptr);
+        launch_mean_vec<false, kBatch>(a, blocks, bt, stream);
 }
 
 }  // namespace
 
 hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const float *C_old,
                                  int64_t n, int64_t k, int64_t d, float *C_new,
-                                 double *shift_partial, const UpdateScratch &ws,
+                                 double *shift_partial, float *xn_part, const UpdateScratch &ws,
                                  hipStream_t stream) {
     if (n > 0)
         scatter_kernel<<<(unsigned)ws.n_tiles, kTile, 0, stream>>>(labels, n, k, ws.n_tiles,
@@ -415,8 +523,8 @@ hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const fl
     const unsigned bt = kBigWaves * 64;
     const bool vec = (d % 4 == 0) && ((uintptr_t)X % 16 == 0) && ((uintptr_t)C_old % 16 == 0) &&
                      ((uintptr_t)C_new % 16 == 0);
-    const MeanArgs a{X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, k, d, chunks, C_new,
-                     shift_partial};
+    const MeanArgs a{X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, n, k, d, chunks, C_new,
+                     shift_partial, xn_part};
     if (n <= 32 * k)  // at most 32 rows per cluster on average
         launch_mean<8>(a, vec, blocks, bt, stream);
     else
@@ -424,12 +532,20 @@ hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const fl
     return hipGetLastError();
 }
 
+hipError_t launch_add_norms(float *min_dist, const float *xn_part, int64_t n, int64_t d,
+                            const UpdateScratch &ws, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    add_norms_kernel<<<grid_stride_blocks(n), 256, 0, stream>>>(min_dist, xn_part, ws.perm, n, n,
+                                                                (int)norm_parts(d));
+    return hipGetLastError();
+}
+
 hipError_t launch_update(const float *X, const int64_t *labels, const float *C_old, int64_t n,
-                         int64_t k, int64_t d, float *C_new, int64_t *counts,
+                         int64_t k, int64_t d, float *C_new, int64_t *counts, float *xn_part,
                          const UpdateScratch &ws, hipStream_t stream) {
     hipError_t e = launch_count(labels, n, k, counts, nullptr, ws, stream);
     if (e != hipSuccess) return e;
-    return launch_group_and_mean(X, labels, C_old, n, k, d, C_new, nullptr, ws, stream);
+    return launch_group_and_mean(X, labels, C_old, n, k, d, C_new, nullptr, xn_part, ws, stream);
 }
 
 }  // namespace km

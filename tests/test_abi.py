@@ -61,7 +61,13 @@ def test_workspace_bytes_rules(lib):
     assert ws(0, 1, 1, 0) > 0 and ws(0, 1, 1, 1) > 0
     for cfg in CONFIGS.values():
         a, u, l = (ws(cfg.n, cfg.k, cfg.d, op) for op in (0, 1, 2))
-        assert l >= max(a, u) and l <= a + u
+        # The Lloyd step adds the partial squared norms of the rows (one float
+        # per row and 256-column chunk) when that stays below 1/16 of an
+        # (n, k) float matrix, as it does for every workload here.
+        chunks = -(-cfg.d // 256)
+        assert chunks * 16 <= cfg.k
+        parts = 4 * cfg.n * chunks
+        assert l >= max(a, u) + parts and l <= a + u + parts + 256
         # The assignment needs only the centroid norms (k floats + alignment).
         assert a <= cfg.k * 4 + 512
         # The update: k x ceil(n/1024) tile counters, 2k words, n words, and
@@ -70,7 +76,24 @@ def test_workspace_bytes_rules(lib):
         assert u <= 4 * (cfg.k * n_tiles + 3 * cfg.k + 1 + cfg.n) + 6 * 256
         # Far below the (n, k) distance matrix and the (n, d) sample matrix.
         if cfg.n >= 4096:
-            assert l < cfg.n * cfg.k * 4 / 64 and l < cfg.n * cfg.d * 4 / 64
+            assert l < cfg.n * cfg.k * 4 / 16 and l < cfg.n * cfg.d * 4 / 128
+            assert u < cfg.n * cfg.k * 4 / 64 and u < cfg.n * cfg.d * 4 / 64
+
+
+def test_lloyd_norm_buffer_bound(lib):
+    """The partial-norm buffer of the Lloyd step exists only while
+    ceil(d / 256) * 16 <= k; beyond that the step computes the sample norms
+    in a separate pass and needs no more workspace than assign + update."""
+    ws = binding.kmeans_workspace_bytes
+    n = 10000
+    for k, d in ((16, 256), (32, 512), (4096, 16384), (17, 16384), (100, 4096), (1, 1)):
+        a, u, l = (ws(n, k, d, op) for op in (0, 1, 2))
+        chunks = -(-d // 256)
+        if chunks * 16 <= k:
+            assert l >= max(a, u) + 4 * n * chunks
+        else:
+            assert l <= a + u
+        assert l < n * k * 4 / 16 + a + u
 
 
 def test_launch_grid_limit(lib, monkeypatch):

@@ -98,6 +98,38 @@ def test_random_shapes(n, k, d):
     gu.full_parity(X, C)
 
 
+# The Lloyd step gathers the sample norms inside the update when
+# ceil(d / 256) * 16 <= k, else it takes a separate pass over X.
+NORM_PATHS = [
+    (3000, 20, 130, "gathered, scalar loads, clusters of ~150 rows"),
+    (3000, 32, 256, "gathered, 16-byte loads, clusters of ~94 rows"),
+    (2000, 64, 1024, "gathered, 4 chunks"),
+    (2000, 63, 1024, "separate pass (4 chunks * 16 > 63)"),
+    (700, 5, 300, "separate pass, k < 16"),
+]
+
+
+@pytest.mark.parametrize("n,k,d,what", NORM_PATHS, ids=[f"{n}x{k}x{d}" for n, k, d, _ in NORM_PATHS])
+def test_lloyd_min_dist_paths(n, k, d, what):
+    """min_dist of the Lloyd step on both of its paths: against the oracle
+    within the tolerance, and against kmeans_assign's min_dist (a separate
+    norm pass) to float32 rounding of ||x||^2."""
+    gu.announce(f"lloyd min_dist {n}x{k}x{d} ({what})")
+    rng = np.random.default_rng(n + k + d)
+    centres = 2.0 * rng.standard_normal((k, d))
+    X = (centres[rng.integers(0, k, n)] + rng.standard_normal((n, d))).astype(np.float32)
+    C = X[rng.choice(n, k, replace=False)].copy()
+    res = gu.full_parity(X, C)
+    assert res["mismatches"] <= res["near_ties"]
+    l_labels, l_md, _, _ = gu.gpu_lloyd(X, C)
+    a_labels, a_md = gu.gpu_assign(X, C)
+    assert np.array_equal(l_labels, a_labels)
+    xn = np.einsum("ij,ij->i", X.astype(np.float64), X.astype(np.float64))
+    # Both add a float32 ||x||^2 (each within ~1e-6 relative) to the same best
+    # value, so they differ by at most a few float32 ulps of ||x||^2.
+    assert np.all(np.abs(l_md.astype(np.float64) - a_md) <= 4e-6 * xn + 1e-6)
+
+
 @pytest.mark.parametrize("n,k,d", [(500, 37, 64), (1500, 260, 256), (129, 130, 12)])
 def test_integer_exact(n, k, d):
     """|values| <= 8, d <= 256: every float32 product and partial sum is an
