@@ -24,7 +24,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 bool lloyd_fuses_norms(int64_t k, int64_t d) { return km::norm_parts(d) * 16 <= k; }
 
 struct Layout {
-    size_t cn = 0, tile_hist = 0, cnt = 0, seg_start = 0, perm = 0, big = 0;
+    size_t cn = 0, tile_hist = 0, cnt = 0, seg_start = 0, perm = 0, big = 0, order = 0;
     // kmeans_lloyd_step only
     size_t xn_part = 0;
     // kmeans_fit only
@@ -57,6 +57,8 @@ Layout layout(int64_t n, int64_t k, int64_t d, int op) {
         off += round_up((size_t)n * sizeof(int));
         L.big = off;
         off += round_up(((size_t)k + 1) * sizeof(int));
+        L.order = off;
+        off += round_up((size_t)k * sizeof(int));
     }
     if (op == KM_OP_LLOYD && lloyd_fuses_norms(k, d)) {
         L.xn_part = off;
@@ -176,6 +178,7 @@ km::UpdateScratch update_scratch(char *base, const Layout &L, int64_t n) {
     ws.seg_start = (int *)(base + L.seg_start);
     ws.perm = (int *)(base + L.perm);
     ws.big = (int *)(base + L.big);
+    ws.order = (int *)(base + L.order);
     ws.n_tiles = cdiv(n, km::kSortTileRows);
     return ws;
 }

@@ -19,6 +19,7 @@ struct UpdateScratch {
     int *perm;       // n: row indices grouped by cluster, increasing within one
     int *big;        // k + 1: the number of clusters with more than 64 rows, then
                      // their indices in increasing order
+    int *order;      // k: the other clusters, grouped by load rounds (most first)
     int64_t n_tiles; // ceil(n / kSortTileRows)
 };
 

@@ -82,20 +82,38 @@ __global__ __launch_bounds__(256) void tile_scan_kernel(int *__restrict__ tile_h
     if (lane == 0) cnt[j] = carry;
 }
 
+// Load-round classes of the clusters summed by one wave (at most kSplitMin
+// rows): class ceil(count / 8), 0 .. kClasses - 1.
+constexpr int kClasses = kSplitMin / 8 + 1;
+
+__device__ __forceinline__ int round_class(int count) {
+    return count <= kSplitMin ? (count + 7) / 8 : -1;
+}
+
 // A single block of 1024 threads: exclusive scan over the k cluster sizes.
 // If num_empty != NULL it receives the number of clusters of size 0. big[0]
 // receives the number of clusters with more than kSplitMin rows and big[1 ..]
-// their indices in increasing order.
+// their indices in increasing order. order[0 .. k - big[0]) receives the
+// other clusters grouped by load-round class, most rounds first, increasing
+// index within a class (a stable partition: every rank comes from ballots, so
+// the order is the same on every run). The mean kernel gives 16 consecutive
+// entries of `order` to one block, so a block's waves run the same number of
+// load rounds instead of all waiting for the block's largest cluster.
 __global__ __launch_bounds__(1024) void cluster_scan_kernel(const int *__restrict__ cnt, int64_t k,
                                                             int *__restrict__ seg_start,
                                                             int64_t *__restrict__ counts,
                                                             int *__restrict__ num_empty,
-                                                            int *__restrict__ big) {
+                                                            int *__restrict__ big,
+                                                            int *__restrict__ order) {
     __shared__ int wave_tot[16];
     __shared__ int wave_big[16];
     __shared__ int wave_empty[16];
+    __shared__ int wave_cls[16][kClasses];
+    __shared__ int cls_next[kClasses];  // next free slot of each class in order
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const unsigned long long below = (1ull << lane) - 1ull;
     int carry = 0, empties = 0, big_carry = 0;
+    int cls_total = 0;  // thread c < kClasses: clusters of class c so far
     for (int64_t base = 0; base < k; base += 1024) {
         const int64_t j = base + tid;
         const int v = j < k ? cnt[j] : 0;
@@ -107,8 +125,14 @@ __global__ __launch_bounds__(1024) void cluster_scan_kernel(const int *__restric
         }
         const bool is_big = j < k && v > kSplitMin;
         const unsigned long long bm = __ballot(is_big);
+        const int cls = j < k ? round_class(v) : -1;
         if (lane == 63) wave_tot[wave] = incl;
         if (lane == 0) wave_big[wave] = __popcll(bm);
+#pragma unroll
+        for (int c = 0; c < kClasses; ++c) {
+            const unsigned long long cm = __ballot(cls == c);
+            if (lane == 0) wave_cls[wave][c] = __popcll(cm);
+        }
         __syncthreads();
         int before = 0, total = 0, big_before = 0, big_total = 0;
         for (int w = 0; w < 16; ++w) {
@@ -118,15 +142,49 @@ __global__ __launch_bounds__(1024) void cluster_scan_kernel(const int *__restric
             big_before += w < wave ? wb : 0;
             big_total += wb;
         }
+        if (tid < kClasses)
+            for (int w = 0; w < 16; ++w) cls_total += wave_cls[w][tid];
         if (j < k) {
             seg_start[j] = carry + before + incl - v;
             counts[j] = v;
         }
-        if (is_big)
-            big[1 + big_carry + big_before + __popcll(bm & ((1ull << lane) - 1ull))] = (int)j;
+        if (is_big) big[1 + big_carry + big_before + __popcll(bm & below)] = (int)j;
         carry += total;
         big_carry += big_total;
-        __syncthreads();  // wave_tot and wave_big are rewritten by the next chunk
+        __syncthreads();  // wave_tot, wave_big and wave_cls are rewritten by the next chunk
+    }
+    // Class c starts after every class with more rounds.
+    if (tid < kClasses) wave_cls[0][tid] = cls_total;
+    __syncthreads();
+    if (tid < kClasses) {
+        int start = 0;
+        for (int c = kClasses - 1; c > tid; --c) start += wave_cls[0][c];
+        cls_next[tid] = start;
+    }
+    __syncthreads();
+    for (int64_t base = 0; base < k; base += 1024) {
+        const int64_t j = base + tid;
+        const int cls = j < k ? round_class(cnt[j]) : -1;
+        int rank = 0;
+#pragma unroll
+        for (int c = 0; c < kClasses; ++c) {
+            const unsigned long long cm = __ballot(cls == c);
+            if (cls == c) rank = __popcll(cm & below);
+            if (lane == 0) wave_cls[wave][c] = __popcll(cm);
+        }
+        __syncthreads();
+        if (cls >= 0) {
+            int pos = cls_next[cls] + rank;
+            for (int w = 0; w < wave; ++w) pos += wave_cls[w][cls];
+            order[pos] = (int)j;
+        }
+        __syncthreads();  // every thread has read cls_next and wave_cls
+        if (tid < kClasses) {
+            int t = 0;
+            for (int w = 0; w < 16; ++w) t += wave_cls[w][tid];
+            cls_next[tid] += t;
+        }
+        __syncthreads();
     }
     if (tid == 0) big[0] = big_carry;
     if (num_empty) {
@@ -328,18 +386,19 @@ __device__ __forceinline__ void write_mean(const float *C_old, float *C_new, int
 // work items (cluster big[1 + i / chunks], chunk i % chunks), blocks taking
 // items blockIdx.x, + kBigBlocks, ...; wave p sums part p of the cluster's
 // rows (kBigWaves contiguous parts) and wave 0 adds the parts in order and
-// writes the mean. Every later block covers kBigWaves clusters (one wave
-// each) x one chunk of kCols columns and sums the clusters of at most
-// kSplitMin rows alone, in increasing sample order; lane l owns 4 columns.
+// writes the mean. Every later block covers kBigWaves consecutive entries
+// of `order` (the clusters of at most kSplitMin rows, grouped by load-round
+// class; one wave each) x one chunk of kCols columns, and sums each cluster
+// alone, in increasing sample order; lane l owns 4 columns.
 // If kShift, block b writes the sum of its (new - old)^2 in a fixed order to
 // shift_partial[b]. If kNorm, the squared norm over chunk c of the row at
 // position p of perm goes to xn_part[c * n + p] (chunks x n float32).
 template <bool kVec, bool kShift, int kBatch, bool kNorm>
 __global__ __launch_bounds__(kBigWaves * 64) void segment_mean_kernel(
     const float *__restrict__ X, const int *__restrict__ perm, const int *__restrict__ seg_start,
-    const int *__restrict__ cnt, const int *__restrict__ big, const float *C_old, int64_t n,
-    int64_t k, int64_t d, int chunks, float *C_new, double *__restrict__ shift_partial,
-    float *__restrict__ xn_part) {
+    const int *__restrict__ cnt, const int *__restrict__ big, const int *__restrict__ order,
+    const float *C_old, int64_t n, int64_t k, int64_t d, int chunks, float *C_new,
+    double *__restrict__ shift_partial, float *__restrict__ xn_part) {
     // C_old and C_new may be the same array: each element is read and written
     // by the same thread only, so they carry no __restrict__.
     __shared__ double part[kBigWaves - 1][kCols];
@@ -378,14 +437,15 @@ __global__ __launch_bounds__(kBigWaves * 64) void segment_mean_kernel(
         }
     } else {
         const unsigned sb = blockIdx.x - kBigBlocks;
-        const int64_t j = (int64_t)(sb / (unsigned)chunks) * kBigWaves + wave;
+        const int64_t i = (int64_t)(sb / (unsigned)chunks) * kBigWaves + wave;
         const int64_t c = sb % (unsigned)chunks;
         int64_t col[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) col[e] = c * kCols + lc[e];
-        if (j < k) {
-            const int count = cnt[j];
-            if (count <= kSplitMin) {
+        if (i < k - big[0]) {
+            const int64_t j = order[i];
+            const int count = cnt[j];  // <= kSplitMin
+            {
                 double s[4] = {0.0, 0.0, 0.0, 0.0};
                 const int64_t seg = seg_start[j];
                 sum_rows<kVec, kBatch, kNorm>(X, perm + seg, 0, count, d, col, s,
@@ -444,7 +504,7 @@ hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t *co
         fill_i32_kernel<<<grid_stride_blocks(k), 256, 0, stream>>>(ws.cnt, k);
     }
     cluster_scan_kernel<<<1, 1024, 0, stream>>>(ws.cnt, k, ws.seg_start, counts, num_empty,
-                                                ws.big);
+                                                ws.big, ws.order);
     return hipGetLastError();
 }
 
@@ -475,7 +535,7 @@ __global__ __launch_bounds__(256) void add_norms_kernel(float *__restrict__ min_
 
 struct MeanArgs {
     const float *X;
-    const int *perm, *seg_start, *cnt, *big;
+    const int *perm, *seg_start, *cnt, *big, *order;
     const float *C_old;
     int64_t n, k, d;
     int chunks;
@@ -488,15 +548,15 @@ template <bool kVec, int kBatch>
 void launch_mean_vec(const MeanArgs &a, unsigned blocks, unsigned bt, hipStream_t stream) {
     if (a.shift_partial)
         segment_mean_kernel<kVec, true, kBatch, false><<<blocks, bt, 0, stream>>>(
-            a.X, a.perm, a.seg_start, a.cnt, a.big, a.C_old, a.n, a.k, a.d, a.chunks, a.C_new,
+            a.X, a.perm, a.seg_start, a.cnt, a.big, a.order, a.C_old, a.n, a.k, a.d, a.chunks, a.C_new,
             a.shift_partial, nullptr);
     else if (a.xn_part)  // rounds of at most 8 rows: 16 with the pending norms spill
         segment_mean_kernel<kVec, false, (kBatch > 8 ? 8 : kBatch), true><<<blocks, bt, 0, stream>>>(
-            a.X, a.perm, a.seg_start, a.cnt, a.big, a.C_old, a.n, a.k, a.d, a.chunks, a.C_new,
+            a.X, a.perm, a.seg_start, a.cnt, a.big, a.order, a.C_old, a.n, a.k, a.d, a.chunks, a.C_new,
             nullptr, a.xn_part);
     else
         segment_mean_kernel<kVec, false, kBatch, false><<<blocks, bt, 0, stream>>>(
-            a.X, a.perm, a.seg_start, a.cnt, a.big, a.C_old, a.n, a.k, a.d, a.chunks, a.C_new,
+            a.X, a.perm, a.seg_start, a.cnt, a.big, a.order, a.C_old, a.n, a.k, a.d, a.chunks, a.C_new,
             nullptr, nullptr);
 }
 
@@ -523,7 +583,8 @@ hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const fl
     const unsigned bt = kBigWaves * 64;
     const bool vec = (d % 4 == 0) && ((uintptr_t)X % 16 == 0) && ((uintptr_t)C_old % 16 == 0) &&
                      ((uintptr_t)C_new % 16 == 0);
-    const MeanArgs a{X, ws.perm, ws.seg_start, ws.cnt, ws.big, C_old, n, k, d, chunks, C_new,
+    const MeanArgs a{X,      ws.perm, ws.seg_start, ws.cnt,      ws.big, ws.order,
+                     C_old,  n,       k,            d,           chunks, C_new,
                      shift_partial, xn_part};
     if (n <= 32 * k)  // at most 32 rows per cluster on average
         launch_mean<8>(a, vec, blocks, bt, stream);
