@@ -121,6 +121,11 @@ struct TileCfg {
     static constexpr int kRows = BM + BN;                // LDS rows per stage
     static constexpr int kRowStep = kThreads / kChunks;  // rows covered by one pass of loads
     static constexpr int Q = kRows / kRowStep;           // 16-byte loads per thread per stage
+    // The one-block-per-CU tiles (8 waves, up to 256 registers a lane) load
+    // the epilogue's centroid norms before the last stages, so their latency
+    // passes under MFMAs; the smaller tiles, bound to 168 or 128 registers,
+    // load them after the last stage.
+    static constexpr bool kEarlyNorms = BM * BN >= 128 * 256;
     static_assert(BK % 8 == 0 && kThreads % kChunks == 0, "bad stage depth");
     static_assert(kRows % kRowStep == 0, "tile rows must be a multiple of threads / chunks");
 };
@@ -329,6 +334,20 @@ __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
             __syncthreads();
         }
     }
+    // Centroid norms of this wave's rows for the epilogue. Accumulator
+    // element e of a 32 x 32 block sits at row 8 * (e / 4) + 4 * (lane / 32)
+    // + e % 4 and column lane % 32.
+    float cnv[Cfg::MB][16];
+    if constexpr (Cfg::kEarlyNorms) {
+#pragma unroll
+        for (int mb = 0; mb < Cfg::MB; ++mb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t m =
+                    m0 + (wm * Cfg::MB + mb) * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                cnv[mb][e] = m < k ? cn[m] : __builtin_inff();
+            }
+    }
     // The last 1 to 4 stages: it, it + 1, it + 2, it + 3 (it is even).
     {
         f32x4 a0[Cfg::MB], b0[Cfg::NB];
@@ -363,16 +382,17 @@ __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
     }
     mma_group<Cfg>(aL, bL, acc);
 
-    // Epilogue. Accumulator element e of a 32 x 32 block sits at row
-    // 8 * (e / 4) + 4 * (lane / 32) + e % 4 and column lane % 32.
-    float cnv[Cfg::MB][16];
+    // Epilogue.
+    if constexpr (!Cfg::kEarlyNorms) {
 #pragma unroll
-    for (int mb = 0; mb < Cfg::MB; ++mb)
+        for (int mb = 0; mb < Cfg::MB; ++mb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int64_t m = m0 + (wm * Cfg::MB + mb) * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            cnv[mb][e] = m < k ? cn[m] : __builtin_inff();
-        }
+            for (int e = 0; e < 16; ++e) {
+                const int64_t m =
+                    m0 + (wm * Cfg::MB + mb) * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                cnv[mb][e] = m < k ? cn[m] : __builtin_inff();
+            }
+    }
 #pragma unroll
     for (int nb = 0; nb < Cfg::NB; ++nb) {
         // Rows are visited in increasing centroid index and only a strictly
