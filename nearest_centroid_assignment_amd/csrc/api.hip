@@ -3,7 +3,8 @@
 // Every entry point validates its arguments on the host before the first HIP
 // call, carves its sections out of the caller's workspace, and enqueues the
 // kernels on the caller's stream. Nothing here allocates, frees or
-// synchronises, and there is no global state.
+// synchronises; the only global state is the assignment launcher's cached
+// compute-unit count per device.
 #include "../../include/kmeans_mi355x.h"
 #include "kernels.h"
 

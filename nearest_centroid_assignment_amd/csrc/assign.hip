@@ -246,7 +246,7 @@ __device__ __forceinline__ void mma_head(float (*lds)[Cfg::LDK], int lane, int w
     for (int nb = 0; nb < Cfg::NB; ++nb) bL[nb] = b[(G - 1) & 1][nb];
 }
 
-template <class Cfg, int Mode, int MinWaves>
+template <class Cfg, int Mode, int MinWaves, bool kPersistent>
 __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
     const float *__restrict__ X, const float *__restrict__ C, const float *__restrict__ cn,
     int64_t n, int64_t k, int64_t d, int tiles_m, int tiles_n,
@@ -254,14 +254,23 @@ __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
     __shared__ float lds[2][Cfg::kRows][Cfg::LDK];
 
     // Blocks are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8).
-    // Renumber so that each XCD gets one contiguous range of tiles, then walk
-    // that range in groups of kGroupM centroid tiles so that the tiles resident
-    // on one XCD at a time share centroid and sample rows in its L2.
-    const int nblk = gridDim.x;
-    const int bid = blockIdx.x;
-    const int per = nblk / 8, rem = nblk % 8, xcd = bid % 8, local = bid / 8;
-    const int linear = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
+    // The tiles are renumbered so that each XCD gets one contiguous range of
+    // them, walked in groups of kGroupM centroid tiles, so that the tiles
+    // resident on one XCD at a time share centroid and sample rows in its L2.
+    // Without kPersistent the grid has one block per tile and the loop below
+    // runs once. With it (full tiles of the one-block-per-CU shapes) the grid
+    // has at most one block per CU and each block takes every x_blocks-th
+    // tile of its XCD's range: the same tiles run side by side on an XCD as
+    // with one block per tile, and the per-block start-up and tear-down is
+    // paid once per CU instead of once per tile.
+    const int T = tiles_m * tiles_n;
+    const int per = T / 8, rem = T % 8, xcd = blockIdx.x % 8;
+    const int x_start = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+    const int x_count = per + (xcd < rem ? 1 : 0);
+    const int x_blocks = ((int)gridDim.x - xcd + 7) / 8;  // blocks on this XCD
     const int group_span = kGroupM * tiles_n;
+    for (int local = blockIdx.x / 8; !kPersistent || local < x_count; local += x_blocks) {
+    const int linear = x_start + local;
     const int first_m = (linear / group_span) * kGroupM;
     const int gsize = min(tiles_m - first_m, kGroupM);
     const int tm = first_m + (linear % group_span) % gsize;
@@ -417,6 +426,9 @@ __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
         const int64_t s = n0 + (wn * Cfg::NB + nb) * 32 + (lane & 31);
         if (lane < 32 && s < n) atomicMin(keys + s, key);
     }
+    if (!kPersistent) break;
+    __syncthreads();  // the next tile's LDS writes follow these reads
+    }
 }
 
 // Tile shapes (centroids x samples; the launcher picks one by problem shape).
@@ -474,22 +486,51 @@ hipError_t launch_fill_keys(unsigned long long *keys, int64_t n, hipStream_t str
 
 namespace {
 
+// Compute units of the current device, 0 if the query fails (cached per
+// device; threads that fill an entry at the same time write the same value).
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cached[dev] = v;
+    }
+    return cached[dev];
+}
+
 template <class Cfg, int MinWaves>
 hipError_t launch_tiles_cfg(const float *X, const float *C, const float *cn, int64_t n, int64_t k,
                             int64_t d, unsigned long long *keys, hipStream_t stream) {
     const int tiles_m = (int)cdiv(k, Cfg::BM);
     const int tiles_n = (int)cdiv(n, Cfg::BN);
-    const unsigned blocks = (unsigned)((int64_t)tiles_m * tiles_n);
+    const int64_t tiles = (int64_t)tiles_m * tiles_n;
+    const unsigned blocks = (unsigned)tiles;
     const bool vec = vec_ok(X, d) && vec_ok(C, d);
     const bool full = vec && n % Cfg::BN == 0 && k % Cfg::BM == 0 && d % Cfg::BK == 0;
+    if constexpr (Cfg::kThreads == 512) {
+        // Full tiles of the one-block-per-CU shapes: one persistent block per
+        // CU (no second block fits), each walking its share of the tiles. The
+        // walk covers every tile once when the grid has at least one block per
+        // XCD (8) or one block per tile, hence the 8-CU minimum.
+        const int cus = device_cus();
+        if (full && cus >= 8) {
+            const unsigned pblocks = (unsigned)(tiles < cus ? tiles : cus);
+            assign_tile_kernel<Cfg, kFull, MinWaves, true><<<pblocks, Cfg::kThreads, 0, stream>>>(
+                X, C, cn, n, k, d, tiles_m, tiles_n, keys);
+            return hipGetLastError();
+        }
+    }
     if (full)
-        assign_tile_kernel<Cfg, kFull, MinWaves><<<blocks, Cfg::kThreads, 0, stream>>>(
+        assign_tile_kernel<Cfg, kFull, MinWaves, false><<<blocks, Cfg::kThreads, 0, stream>>>(
             X, C, cn, n, k, d, tiles_m, tiles_n, keys);
     else if (vec)
-        assign_tile_kernel<Cfg, kVec, MinWaves><<<blocks, Cfg::kThreads, 0, stream>>>(
+        assign_tile_kernel<Cfg, kVec, MinWaves, false><<<blocks, Cfg::kThreads, 0, stream>>>(
             X, C, cn, n, k, d, tiles_m, tiles_n, keys);
     else
-        assign_tile_kernel<Cfg, kScalar, MinWaves><<<blocks, Cfg::kThreads, 0, stream>>>(
+        assign_tile_kernel<Cfg, kScalar, MinWaves, false><<<blocks, Cfg::kThreads, 0, stream>>>(
             X, C, cn, n, k, d, tiles_m, tiles_n, keys);
     return hipGetLastError();
 }

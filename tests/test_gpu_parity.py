@@ -300,6 +300,23 @@ def test_tile_variants(monkeypatch, tile, n, k, d):
     assert np.array_equal(g_md.astype(np.float64), best)
 
 
+@pytest.mark.parametrize("tile", ["128x256", "256x128"])
+@pytest.mark.parametrize("n,k,d", [(9472, 1280, 64), (1792, 640, 96), (33024, 1280, 32)])
+def test_persistent_tile_walk(monkeypatch, tile, n, k, d):
+    """Full tiles of the 512-thread shapes run as one persistent block per
+    CU walking its XCD's tiles: 370 tiles (more than the CUs, not a multiple
+    of 8), 35 tiles (fewer than the CUs) and 1290 tiles (several per block,
+    uneven XCD ranges). Integer data: labels and distances bit-exact."""
+    monkeypatch.setenv("KMEANS_ASSIGN_TILE", tile)
+    gu.announce(f"persistent walk {tile} {n}x{k}x{d}")
+    X, C = datagen.make_integer(n, k, d, seed=n + k + d)
+    C[k - 1] = C[3]
+    g_labels, g_md = gu.gpu_assign(X, C)
+    o_labels, best, _ = oracle.assign(X, C)
+    assert np.array_equal(g_labels, o_labels)
+    assert np.array_equal(g_md.astype(np.float64), best)
+
+
 @pytest.mark.parametrize("n,k,d,skew", [(5000, 3, 300, "mild"), (70000, 2, 520, "giant"),
                                         (20000, 50, 1030, "zipf"), (3000, 200, 64, "one-big")])
 def test_update_skewed_clusters(n, k, d, skew):
