@@ -45,18 +45,18 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int *__restrict__ p, int6
         p[i] = 0;
 }
 
-// One block per tile of kTile rows. Rows with a label outside [0, k) are skipped.
+// kParts blocks of 256 threads per tile of kTile rows, one row per thread
+// (one block per tile left most CUs idle). Rows with a label outside [0, k)
+// are skipped.
+constexpr int kParts = kTile / 256;
 __global__ __launch_bounds__(256) void tile_hist_kernel(const int64_t *__restrict__ labels,
                                                         int64_t n, int64_t k, int64_t n_tiles,
                                                         int *__restrict__ tile_hist) {
-    const int64_t b = blockIdx.x;
-#pragma unroll
-    for (int q = 0; q < kTile / 256; ++q) {
-        const int64_t i = b * kTile + q * 256 + threadIdx.x;
-        if (i < n) {
-            const int64_t l = labels[i];
-            if (l >= 0 && l < k) atomicAdd(tile_hist + l * n_tiles + b, 1);
-        }
+    const int64_t b = blockIdx.x / kParts;
+    const int64_t i = b * kTile + (blockIdx.x % kParts) * 256 + threadIdx.x;
+    if (i < n) {
+        const int64_t l = labels[i];
+        if (l >= 0 && l < k) atomicAdd(tile_hist + l * n_tiles + b, 1);
     }
 }
 
@@ -199,31 +199,37 @@ __global__ __launch_bounds__(1024) void cluster_scan_kernel(const int *__restric
     }
 }
 
-// One block per tile, one thread per row. The rank of a row among the rows of
-// the same tile with the same label and a smaller index is counted directly
-// from the tile's labels in LDS, which keeps the grouping stable (increasing
-// row order inside every cluster) and independent of thread timing. A wave
-// first counts over the whole chunks of 64 rows before its own, four labels
-// per (broadcast) LDS read with no divergence, then over the earlier rows of
-// its own chunk.
-static_assert(kTile == 1024, "scatter_kernel runs one 1024-thread block per tile");
-__global__ __launch_bounds__(1024) void scatter_kernel(const int64_t *__restrict__ labels, int64_t n,
-                                                       int64_t k, int64_t n_tiles,
-                                                       const int *__restrict__ tile_prefix,
-                                                       const int *__restrict__ seg_start,
-                                                       int *__restrict__ perm) {
+// kParts blocks of 256 threads per tile, one thread per row: part p takes
+// rows 256p .. 256p + 255 of the tile and loads the tile's labels up to its
+// last row into LDS. The rank of a row among the rows of the same tile with
+// the same label and a smaller index is counted directly from those labels,
+// which keeps the grouping stable (increasing row order inside every
+// cluster) and independent of thread timing. A wave first counts over the
+// whole chunks of 64 rows before its own, four labels per (broadcast) LDS
+// read with no divergence, then over the earlier rows of its own chunk.
+// (One 1024-thread block per tile used a quarter of the CUs at n = 65536.)
+static_assert(kTile == 1024 && kParts == 4, "scatter_kernel splits 1024-row tiles in 4 parts");
+__global__ __launch_bounds__(256) void scatter_kernel(const int64_t *__restrict__ labels, int64_t n,
+                                                      int64_t k, int64_t n_tiles,
+                                                      const int *__restrict__ tile_prefix,
+                                                      const int *__restrict__ seg_start,
+                                                      int *__restrict__ perm) {
     __shared__ __align__(16) int lab[kTile];
-    const int64_t b = blockIdx.x;
+    const int64_t b = blockIdx.x / kParts;
+    const int part = blockIdx.x % kParts;
     const int64_t row0 = b * kTile;
     const int rows = (int)min((int64_t)kTile, n - row0);
-    const int r = threadIdx.x;
-    int l = -1;
-    if (r < rows) {
-        const int64_t v = labels[row0 + r];
-        l = (v >= 0 && v < k) ? (int)v : -1;
+    for (int q = threadIdx.x; q < (part + 1) * 256; q += 256) {
+        int l = -1;
+        if (q < rows) {
+            const int64_t v = labels[row0 + q];
+            l = (v >= 0 && v < k) ? (int)v : -1;
+        }
+        lab[q] = l;
     }
-    lab[r] = l;
     __syncthreads();
+    const int r = part * 256 + threadIdx.x;
+    const int l = lab[r];
     if (l < 0) return;
     const int chunk0 = r & ~63;
     const int4 *lab4 = reinterpret_cast<const int4 *>(lab);
@@ -482,7 +488,7 @@ static int64_t small_mean_blocks(int64_t k, int64_t d) {
 
 int64_t update_grid_threads(int64_t n, int64_t k, int64_t d) {
     const int64_t mean = (small_mean_blocks(k, d) + kBigBlocks) * (kBigWaves * 64);
-    const int64_t scatter = cdiv(n, kTile) * kTile;  // tile_hist uses a quarter of this
+    const int64_t scatter = cdiv(n, kTile) * kTile;  // tile_hist and scatter: 256 per row quarter
     const int64_t scan = cdiv(k, 4) * 256;
     const int64_t m = mean > scatter ? mean : scatter;
     return m > scan ? m : scan;
@@ -495,8 +501,8 @@ hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t *co
         fill_i32_kernel<<<grid_stride_blocks(hist_words), 256, 0, stream>>>(ws.tile_hist,
                                                                            hist_words);
         if (n > 0)
-            tile_hist_kernel<<<(unsigned)ws.n_tiles, 256, 0, stream>>>(labels, n, k, ws.n_tiles,
-                                                                       ws.tile_hist);
+            tile_hist_kernel<<<(unsigned)(ws.n_tiles * kParts), 256, 0, stream>>>(
+                labels, n, k, ws.n_tiles, ws.tile_hist);
         tile_scan_kernel<<<(unsigned)cdiv(k, 4), 256, 0, stream>>>(ws.tile_hist, k, ws.n_tiles,
                                                                    ws.cnt);
     } else {
@@ -575,9 +581,8 @@ hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const fl
                                  double *shift_partial, float *xn_part, const UpdateScratch &ws,
                                  hipStream_t stream) {
     if (n > 0)
-        scatter_kernel<<<(unsigned)ws.n_tiles, kTile, 0, stream>>>(labels, n, k, ws.n_tiles,
-                                                                 ws.tile_hist, ws.seg_start,
-                                                                 ws.perm);
+        scatter_kernel<<<(unsigned)(ws.n_tiles * kParts), 256, 0, stream>>>(
+            labels, n, k, ws.n_tiles, ws.tile_hist, ws.seg_start, ws.perm);
     const int chunks = (int)cdiv(d, kCols);
     const unsigned blocks = (unsigned)mean_blocks(k, d);
     const unsigned bt = kBigWaves * 64;
