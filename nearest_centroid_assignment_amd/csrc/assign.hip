@@ -17,6 +17,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "kernels.h"
 
 namespace km {
@@ -486,19 +488,20 @@ hipError_t launch_fill_keys(unsigned long long *keys, int64_t n, hipStream_t str
 
 namespace {
 
-// Compute units of the current device, 0 if the query fails (cached per
-// device; threads that fill an entry at the same time write the same value).
+// Compute units of the current device, 0 if the query fails. Cached per
+// device in atomics: threads that fill an entry at the same time store the
+// same value.
 int device_cus() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cached[dev] == 0) {
-        int v = 0;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
-        cached[dev] = v;
+        cached[dev].store(v, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return v;
 }
 
 template <class Cfg, int MinWaves>
