@@ -433,6 +433,220 @@ __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
     }
 }
 
+// ------------------------------------------------ DMA-staged 256 x 256 tiles
+//
+// Full tiles only (n % 256 == 0, k % 256 == 0, d % 64 == 0, 16-byte aligned
+// rows). 8 waves in 2 x 4; each wave owns 128 centroids x 64 samples (4 x 2
+// blocks of 32 x 32), so a fragment read from LDS feeds more MFMAs than in
+// the 128 x 256 tile (6 reads per 32 MFMAs instead of 4 per 16), a stage
+// holds twice the MFMAs per barrier, and the 128 accumulators per lane fit
+// because the operands never pass through registers: buffer loads with the
+// LDS bit move them from global memory straight into LDS (16 bytes per lane;
+// lane i of an instruction writes the 16 bytes at its LDS base + 16 i), one
+// stage ahead. The buffer form, not global_load_lds, because the compiler
+// treats a pending global (FLAT) LDS load as both a memory and an LDS access
+// and then waits for every outstanding LDS read (lgkmcnt(0)) before using
+// any fragment; with buffer loads it waits only for the reads it needs.
+// LDS rows are 32 floats, unpadded (two 64 KiB stage buffers); the 16-byte
+// chunks of a row are XOR-swizzled so that the fragment reads of
+// consecutive rows hit distinct banks.
+namespace dma {
+constexpr int BM = 256, BN = 256, BK = 32, ROWS = BM + BN;
+constexpr int WM = 2, WN = 4, MB = 4, NB = 2, NT = WM * WN * 64;
+constexpr int SLOTS = ROWS * (BK / 4);           // 16-byte slots per stage
+constexpr int PER_WAVE = SLOTS / NT;             // DMA instructions per wave and stage
+static_assert(PER_WAVE * NT == SLOTS, "slots must split evenly over the threads");
+// Chunk swizzle: rows 2r and 2r + 1 share one, consecutive pairs differ, so
+// the 16-byte fragment reads of 16 consecutive rows cover all 64 banks once
+// (measured: no bank conflicts; the row % 8 swizzle conflicts, which shows
+// the 64 banks).
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+}  // namespace dma
+
+// One stage of this wave's DMA: instruction j moves 64 slots (8 rows x 8
+// chunks) into buf + (wave * PER_WAVE + j) * 64 slots. voff[p] is the lane's
+// byte offset inside the wave's source block for instructions of parity p
+// (the swizzled chunk alternates with j), soff the uniform part.
+__device__ __forceinline__ void dma_stage(__amdgpu_buffer_rsrc_t rsrc, const int (&voff)[2],
+                                          int row_bytes8, int kbytes, float *buf, int wave) {
+#pragma unroll
+    for (int j = 0; j < dma::PER_WAVE; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (__attribute__((address_space(3))) void *)(buf + (wave * dma::PER_WAVE + j) * 64 * 4),
+            16, voff[j & 1], j * row_bytes8 + kbytes, 0, 0);
+}
+
+// Fragments of group g (features 8g .. 8g + 7) for this lane: A rows
+// a_base + 32 mb, B rows b_base + 32 nb, chunk 2g + lane / 32 swizzled.
+__device__ __forceinline__ void dma_frags(const float *buf, int a_base, int b_base, int lane, int g,
+                                          f32x4 (&a)[dma::MB], f32x4 (&b)[dma::NB]) {
+    const int h = lane >> 5;
+#pragma unroll
+    for (int mb = 0; mb < dma::MB; ++mb) {
+        const int row = a_base + 32 * mb;
+        a[mb] = *reinterpret_cast<const f32x4 *>(buf + row * dma::BK +
+                                                 (((2 * g + h) ^ dma::swz(row)) << 2));
+    }
+#pragma unroll
+    for (int nb = 0; nb < dma::NB; ++nb) {
+        const int row = b_base + 32 * nb;
+        b[nb] = *reinterpret_cast<const f32x4 *>(buf + row * dma::BK +
+                                                 (((2 * g + h) ^ dma::swz(row)) << 2));
+    }
+}
+
+__device__ __forceinline__ void dma_mma(const f32x4 (&a)[dma::MB], const f32x4 (&b)[dma::NB],
+                                        f32x16 (&acc)[dma::MB][dma::NB]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int mb = 0; mb < dma::MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < dma::NB; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[mb][e], b[nb][e],
+                                                                  acc[mb][nb], 0, 0, 0);
+}
+
+// One stage read from buf: the deferred group of the previous stage, then
+// groups 0 .. 2 of this one with the next group's fragments read ahead; the
+// fragments of group 3 are left in aL / bL for the next stage.
+__device__ __forceinline__ void dma_compute(const float *buf, int a_base, int b_base, int lane,
+                                            f32x4 (&aL)[dma::MB], f32x4 (&bL)[dma::NB],
+                                            f32x16 (&acc)[dma::MB][dma::NB]) {
+    f32x4 a[2][dma::MB], b[2][dma::NB];
+    dma_frags(buf, a_base, b_base, lane, 0, a[0], b[0]);
+    dma_mma(aL, bL, acc);
+#pragma unroll
+    for (int g = 0; g < 3; ++g) {
+        dma_frags(buf, a_base, b_base, lane, g + 1, a[(g + 1) & 1], b[(g + 1) & 1]);
+        dma_mma(a[g & 1], b[g & 1], acc);
+    }
+    // Order: fragment reads of group g + 1 ahead of the MFMAs of group g.
+    __builtin_amdgcn_sched_group_barrier(0x100, dma::MB + dma::NB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * dma::MB * dma::NB, 0);
+#pragma unroll
+    for (int g = 0; g < 3; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x100, dma::MB + dma::NB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * dma::MB * dma::NB, 0);
+    }
+#pragma unroll
+    for (int mb = 0; mb < dma::MB; ++mb) aL[mb] = a[1][mb];
+#pragma unroll
+    for (int nb = 0; nb < dma::NB; ++nb) bL[nb] = b[1][nb];
+}
+
+__global__ __launch_bounds__(dma::NT, 2) void assign_dma_kernel(
+    const float *__restrict__ X, const float *__restrict__ C, const float *__restrict__ cn,
+    int64_t n, int64_t k, int64_t d, int tiles_m, int tiles_n,
+    unsigned long long *__restrict__ keys) {
+    __shared__ __align__(16) float buf0[dma::ROWS * dma::BK];
+    __shared__ __align__(16) float buf1[dma::ROWS * dma::BK];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % dma::WM, wn = wave / dma::WM;
+    const int a_base = wm * dma::MB * 32 + (lane & 31);
+    const int b_base = dma::BM + wn * dma::NB * 32 + (lane & 31);
+    const int64_t nk = d / dma::BK;  // even
+    const int T = tiles_m * tiles_n;
+    const int per = T / 8, rem = T % 8, xcd = blockIdx.x % 8;
+    const int x_start = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+    const int x_count = per + (xcd < rem ? 1 : 0);
+    const int x_blocks = ((int)gridDim.x - xcd + 7) / 8;
+    const int group_span = kGroupM * tiles_n;
+    for (int local = blockIdx.x / 8; local < x_count; local += x_blocks) {
+        const int linear = x_start + local;
+        const int first_m = (linear / group_span) * kGroupM;
+        const int gsize = min(tiles_m - first_m, kGroupM);
+        const int64_t m0 = (int64_t)(first_m + (linear % group_span) % gsize) * dma::BM;
+        const int64_t n0 = (int64_t)((linear % group_span) / gsize) * dma::BN;
+        // This wave's DMA source: waves 0-3 copy centroid rows, 4-7 sample
+        // rows, 64 rows each. Slot s of the wave's block is row s / 8 of it,
+        // stored chunk s % 8, which holds logical chunk (s % 8) ^ swz(row);
+        // with the (row / 2) % 8 swizzle that is (lane % 8) ^ (lane / 16),
+        // flipped by 4 on odd instructions.
+        const int half = wave / (dma::PER_WAVE / 2);  // 0: centroids, 1: samples
+        const float *blk = half == 0 ? C + (m0 + (wave % 4) * 64) * d : X + (n0 + (wave % 4) * 64) * d;
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void *)blk, 0, (int)(64 * d * 4), 0x00020000);
+        const int c0 = (lane & 7) ^ (lane >> 4);
+        const int voff[2] = {(int)((lane >> 3) * d * 4 + c0 * 16),
+                             (int)((lane >> 3) * d * 4 + (c0 ^ 4) * 16)};
+        const int row_bytes8 = (int)(8 * d * 4);
+        f32x16 acc[dma::MB][dma::NB];
+#pragma unroll
+        for (int i = 0; i < dma::MB; ++i)
+#pragma unroll
+            for (int j = 0; j < dma::NB; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+        f32x4 aL[dma::MB], bL[dma::NB];
+#pragma unroll
+        for (int mb = 0; mb < dma::MB; ++mb) aL[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int nb = 0; nb < dma::NB; ++nb) bL[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        dma_stage(rsrc, voff, row_bytes8, 0, buf0, wave);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        // Two stages per iteration: stage s from buf0 while s + 1 lands in
+        // buf1, then stage s + 1 from buf1 while s + 2 lands in buf0 (on the
+        // last iteration that load repeats stage s + 1 into buf0, which no one
+        // reads any more; it completes before the tile's final barrier).
+        for (int64_t s = 0; s < nk; s += 2) {
+            dma_stage(rsrc, voff, row_bytes8, (int)((s + 1) * dma::BK * 4), buf1, wave);
+            __builtin_amdgcn_sched_barrier(0);  // issue the DMA before the MFMAs
+            dma_compute(buf0, a_base, b_base, lane, aL, bL, acc);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            const int64_t s2 = s + 2 < nk ? s + 2 : s + 1;
+            dma_stage(rsrc, voff, row_bytes8, (int)(s2 * dma::BK * 4), buf0, wave);
+            __builtin_amdgcn_sched_barrier(0);
+            dma_compute(buf1, a_base, b_base, lane, aL, bL, acc);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        dma_mma(aL, bL, acc);
+
+        // Epilogue, as in assign_tile_kernel, one block of 32 centroid rows at
+        // a time (16 norms live instead of 64); rows are still visited in
+        // increasing index for each sample, strict less-than keeps the lowest.
+        float best[dma::NB];
+        uint32_t bidx[dma::NB];
+#pragma unroll
+        for (int nb = 0; nb < dma::NB; ++nb) {
+            best[nb] = __builtin_inff();
+            bidx[nb] = 0xffffffffu;
+        }
+#pragma unroll
+        for (int mb = 0; mb < dma::MB; ++mb) {
+            float cnv[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                cnv[e] = cn[m0 + (wm * dma::MB + mb) * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)];
+#pragma unroll
+            for (int nb = 0; nb < dma::NB; ++nb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int64_t m = m0 + (wm * dma::MB + mb) * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    const float v = cnv[e] - 2.0f * acc[mb][nb][e];
+                    if (v < best[nb]) {
+                        best[nb] = v;
+                        bidx[nb] = (uint32_t)m;
+                    }
+                }
+        }
+#pragma unroll
+        for (int nb = 0; nb < dma::NB; ++nb) {
+            unsigned long long key = pack_key(best[nb], bidx[nb]);
+            const unsigned long long other = __shfl_xor(key, 32);
+            key = other < key ? other : key;
+            const int64_t smp = n0 + (wn * dma::NB + nb) * 32 + (lane & 31);
+            if (lane < 32) atomicMin(keys + smp, key);
+        }
+        __syncthreads();  // the next tile's first DMA follows this tile's reads
+    }
+}
+
 // Tile shapes (centroids x samples; the launcher picks one by problem shape).
 using Tile128x256 = TileCfg<2, 4, 2, 2, 32>;  // 512 threads, 108 KiB LDS, 1 block per CU
 using Tile256x128 = TileCfg<4, 2, 2, 2, 32>;  // 512 threads, 108 KiB LDS, 1 block per CU
@@ -545,15 +759,27 @@ int64_t tile_blocks(int64_t n, int64_t k) {
 
 }  // namespace
 
+// Whether a shape's tiles are all full 256 x 256 ones with two 32-feature
+// stages per pass (the DMA-staged kernel's shapes; 32-bit buffer offsets
+// need 64 * d * 4 < 2^31).
+static bool dma_shape(int64_t n, int64_t k, int64_t d) {
+    return n % dma::BN == 0 && k % dma::BM == 0 && d % (2 * dma::BK) == 0 && d < (1 << 22);
+}
+
 static const char *assign_tile_name(int64_t n, int64_t k, int64_t d) {
-    // KMEANS_ASSIGN_TILE=128x256 | 256x128 | 128x128 | 64x64 forces a tile (tuning).
+    // KMEANS_ASSIGN_TILE=256x256 | 128x256 | 256x128 | 128x128 | 64x64 forces
+    // a tile (tuning); 256x256 falls back to 128x256 where it does not apply.
     const char *forced = getenv("KMEANS_ASSIGN_TILE");
     if (forced && (!strcmp(forced, "256x128") || !strcmp(forced, "128x128") ||
-                   !strcmp(forced, "64x64") || !strcmp(forced, "128x256")))
+                   !strcmp(forced, "64x64") || !strcmp(forced, "128x256") ||
+                   !strcmp(forced, "256x256")))
         return forced;
-    // The largest tile (fewest operand bytes per flop) when it gives at least
-    // two blocks per CU; otherwise 128 x 128 with short stages (3 blocks per
-    // CU), unless that leaves CUs idle, then 64 x 64.
+    // The DMA-staged 256 x 256 tile where every tile is full and there are
+    // enough to give each CU one; else the largest register-staged tile
+    // (fewest operand bytes per flop) when it gives at least two blocks per
+    // CU; otherwise 128 x 128 with short stages (3 blocks per CU), unless
+    // that leaves CUs idle, then 64 x 64.
+    if (dma_shape(n, k, d) && (n / dma::BN) * (k / dma::BM) >= 256) return "256x256";
     if (tile_blocks<Tile128x256>(n, k) >= 512) return "128x256";
     if (tile_blocks<Tile128x128>(n, k) >= 256) return "128x128";
     return "64x64";
@@ -564,7 +790,10 @@ int64_t assign_grid_threads(int64_t n, int64_t k, int64_t d) {
     const char *tile = assign_tile_name(n, k, d);
     if (!strcmp(tile, "256x128")) return tile_blocks<Tile256x128>(n, k) * Tile256x128::kThreads;
     if (!strcmp(tile, "128x128")) return tile_blocks<Tile128x128>(n, k) * Tile128x128::kThreads;
-    if (!strcmp(tile, "128x256")) return tile_blocks<Tile128x256>(n, k) * Tile128x256::kThreads;
+    // 256x256 launches at most one block per CU, but falls back to the
+    // 128 x 256 grid for unaligned rows: bound both by the latter.
+    if (!strcmp(tile, "128x256") || !strcmp(tile, "256x256"))
+        return tile_blocks<Tile128x256>(n, k) * Tile128x256::kThreads;
     return tile_blocks<Tile64x64>(n, k) * Tile64x64::kThreads;
 }
 
@@ -573,6 +802,19 @@ hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, 
                                hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     const char *tile = assign_tile_name(n, k, d);
+    if (!strcmp(tile, "256x256")) {
+        // One persistent block per CU (128 KiB of LDS: one fits), each walking
+        // its XCD's tiles; the walk needs at least 8 blocks or one per tile.
+        const int cus = device_cus();
+        if (dma_shape(n, k, d) && vec_ok(X, d) && vec_ok(C, d) && cus >= 8) {
+            const int tm = (int)(k / dma::BM), tn = (int)(n / dma::BN);
+            const int64_t tiles = (int64_t)tm * tn;
+            const unsigned blocks = (unsigned)(tiles < cus ? tiles : cus);
+            assign_dma_kernel<<<blocks, dma::NT, 0, stream>>>(X, C, cn, n, k, d, tm, tn, keys);
+            return hipGetLastError();
+        }
+        return launch_tiles_cfg<Tile128x256, 2>(X, C, cn, n, k, d, keys, stream);
+    }
     if (!strcmp(tile, "256x128"))
         return launch_tiles_cfg<Tile256x128, 2>(X, C, cn, n, k, d, keys, stream);
     if (!strcmp(tile, "128x128"))

@@ -31,7 +31,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ASSIGN_SOURCE = os.path.join(HERE, "csrc", "assign.hip")
 COPY_BYTES = 1 << 30
 COPY_KERNEL = "copy_kernel"
-ASSIGN_KERNEL = "assign_tile_kernel"
+# The assignment's product kernel: the DMA-staged 256 x 256 one on the full
+# large shapes, the register-staged one elsewhere.
+ASSIGN_KERNELS = ("assign_dma_kernel", "assign_tile_kernel")
 
 
 def kernel_digest() -> str:
@@ -84,11 +86,22 @@ def _counter_rows(run_dir: str, counter: str):
     return rows
 
 
-def _per_kernel(rows, name_part: str):
-    vals = [float(r["Counter_Value"]) for r in rows if name_part in r.get("Kernel_Name", "")]
-    if not vals:
-        raise ValueError(f"no dispatch of a kernel named *{name_part}* in the counter rows")
-    return vals
+def _per_kernel(rows, name_part):
+    """Counter values of the dispatches whose kernel name contains name_part
+    (a string, or a tuple of alternatives tried in order)."""
+    parts = (name_part,) if isinstance(name_part, str) else tuple(name_part)
+    for part in parts:
+        vals = [float(r["Counter_Value"]) for r in rows if part in r.get("Kernel_Name", "")]
+        if vals:
+            return vals
+    raise ValueError(f"no dispatch of a kernel named *{parts}* in the counter rows")
+
+
+def _kernel_found(rows, parts) -> str:
+    for part in parts:
+        if any(part in r.get("Kernel_Name", "") for r in rows):
+            return part
+    return ""
 
 
 def summarize(fetch_dir: str, write_dir: str, out: str, workload: str) -> dict:
@@ -100,7 +113,8 @@ def summarize(fetch_dir: str, write_dir: str, out: str, workload: str) -> dict:
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(d, counter)
         copy_kib = _per_kernel(rows, COPY_KERNEL)[0]
-        assign_kib = _per_kernel(rows, ASSIGN_KERNEL)
+        assign_kib = _per_kernel(rows, ASSIGN_KERNELS)
+        rec["assign_kernel"] = _kernel_found(rows, ASSIGN_KERNELS)
         scale = (COPY_BYTES / 1024.0) / copy_kib
         per_launch = sum(assign_kib) / len(assign_kib) * scale * 1024.0
         rec[counter] = {"copy_kib": copy_kib, "assign_kib_per_launch": assign_kib,

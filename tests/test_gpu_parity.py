@@ -278,7 +278,7 @@ def test_library_allocates_nothing():
     assert wsb < n * k * 4 / 64 and wsb < n * d * 4 / 64
 
 
-@pytest.mark.parametrize("tile", ["128x256", "256x128", "128x128", "64x64"])
+@pytest.mark.parametrize("tile", ["256x256", "128x256", "256x128", "128x128", "64x64"])
 @pytest.mark.parametrize("n,k,d", [(1000, 300, 1028), (130, 129, 33), (2048, 512, 256),
                                    (777, 260, 64), (512, 256, 48), (300, 260, 150),
                                    (257, 130, 100), (260, 257, 16)])
@@ -298,6 +298,43 @@ def test_tile_variants(monkeypatch, tile, n, k, d):
     o_labels, best, _ = oracle.assign(X, C)
     assert np.array_equal(g_labels, o_labels)
     assert np.array_equal(g_md.astype(np.float64), best)
+
+
+@pytest.mark.parametrize("n,k,d", [(9472, 2304, 64), (1792, 1280, 128), (16384, 4096, 64)])
+def test_dma_tile_walk(monkeypatch, n, k, d):
+    """The DMA-staged 256 x 256 kernel (operands moved from global memory
+    straight into LDS): 333 tiles (more than the CUs, not a multiple of 8),
+    35 tiles (fewer than the CUs) and 1024 tiles (four per block). Integer
+    data: labels and distances bit-exact."""
+    monkeypatch.setenv("KMEANS_ASSIGN_TILE", "256x256")
+    gu.announce(f"dma walk {n}x{k}x{d}")
+    X, C = datagen.make_integer(n, k, d, seed=n + k + d + 1)
+    C[k - 1] = C[5]
+    g_labels, g_md = gu.gpu_assign(X, C)
+    o_labels, best, _ = oracle.assign(X, C)
+    assert np.array_equal(g_labels, o_labels)
+    assert np.array_equal(g_md.astype(np.float64), best)
+
+
+def test_dma_tile_unaligned_falls_back(monkeypatch):
+    """A 256 x 256 shape whose samples are not 16-byte aligned runs on the
+    register-staged kernel instead (scalar loads), with the same results."""
+    import torch
+    from nearest_centroid_assignment_amd import binding
+
+    monkeypatch.setenv("KMEANS_ASSIGN_TILE", "256x256")
+    n, k, d = 2048, 512, 128
+    gu.announce(f"dma fallback unaligned {n}x{k}x{d}")
+    X, C = datagen.make_integer(n, k, d, seed=77)
+    flat = torch.zeros(n * d + 1, dtype=torch.float32, device="cuda:0")
+    Xg = flat[1:].view(n, d)
+    Xg.copy_(torch.from_numpy(X))
+    assert Xg.data_ptr() % 16 != 0
+    labels, md = binding.assign(Xg, gu.to_gpu(C))
+    torch.cuda.synchronize()
+    o_labels, best, _ = oracle.assign(X, C)
+    assert np.array_equal(labels.cpu().numpy(), o_labels)
+    assert np.array_equal(md.cpu().numpy().astype(np.float64), best)
 
 
 @pytest.mark.parametrize("tile", ["128x256", "256x128"])
