@@ -507,23 +507,36 @@ __device__ __forceinline__ void dma_mma(const f32x4 (&a)[dma::MB], const f32x4 (
                                                                   acc[mb][nb], 0, 0, 0);
 }
 
-// One stage read from buf: the deferred group of the previous stage, then
-// groups 0 .. 2 of this one with the next group's fragments read ahead; the
-// fragments of group 3 are left in aL / bL for the next stage.
-__device__ __forceinline__ void dma_compute(const float *buf, int a_base, int b_base, int lane,
+// One stage read from buf while this wave's share of the next stage moves
+// into dst: the deferred group of the previous stage, then groups 0 .. 2 of
+// this one with the next group's fragments read ahead; the fragments of
+// group 3 are left in aL / bL for the next stage. The eight DMA instructions
+// are spread over the deferred group's MFMAs, one per four: issued back to
+// back, all 64 of a CU queue at the texture unit right after the barrier and
+// hold up the MFMAs behind them.
+__device__ __forceinline__ void dma_compute(const float *buf, float *dst, __amdgpu_buffer_rsrc_t rsrc,
+                                            const int (&voff)[2], int row_bytes8, int kbytes, int wave,
+                                            int a_base, int b_base, int lane,
                                             f32x4 (&aL)[dma::MB], f32x4 (&bL)[dma::NB],
                                             f32x16 (&acc)[dma::MB][dma::NB]) {
     f32x4 a[2][dma::MB], b[2][dma::NB];
     dma_frags(buf, a_base, b_base, lane, 0, a[0], b[0]);
+    dma_stage(rsrc, voff, row_bytes8, kbytes, dst, wave);
     dma_mma(aL, bL, acc);
 #pragma unroll
     for (int g = 0; g < 3; ++g) {
         dma_frags(buf, a_base, b_base, lane, g + 1, a[(g + 1) & 1], b[(g + 1) & 1]);
         dma_mma(a[g & 1], b[g & 1], acc);
     }
-    // Order: fragment reads of group g + 1 ahead of the MFMAs of group g.
+    // Order: group 0's fragment reads, the deferred MFMAs with a DMA
+    // instruction after every fourth, then the fragment reads of group g + 1
+    // ahead of the MFMAs of group g.
     __builtin_amdgcn_sched_group_barrier(0x100, dma::MB + dma::NB, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * dma::MB * dma::NB, 0);
+#pragma unroll
+    for (int j = 0; j < dma::PER_WAVE; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * dma::MB * dma::NB / dma::PER_WAVE, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
 #pragma unroll
     for (int g = 0; g < 3; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x100, dma::MB + dma::NB, 0);
@@ -593,15 +606,13 @@ __global__ __launch_bounds__(dma::NT, 2) void assign_dma_kernel(
         // last iteration that load repeats stage s + 1 into buf0, which no one
         // reads any more; it completes before the tile's final barrier).
         for (int64_t s = 0; s < nk; s += 2) {
-            dma_stage(rsrc, voff, row_bytes8, (int)((s + 1) * dma::BK * 4), buf1, wave);
-            __builtin_amdgcn_sched_barrier(0);  // issue the DMA before the MFMAs
-            dma_compute(buf0, a_base, b_base, lane, aL, bL, acc);
+            dma_compute(buf0, buf1, rsrc, voff, row_bytes8, (int)((s + 1) * dma::BK * 4), wave,
+                        a_base, b_base, lane, aL, bL, acc);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             const int64_t s2 = s + 2 < nk ? s + 2 : s + 1;
-            dma_stage(rsrc, voff, row_bytes8, (int)(s2 * dma::BK * 4), buf0, wave);
-            __builtin_amdgcn_sched_barrier(0);
-            dma_compute(buf1, a_base, b_base, lane, aL, bL, acc);
+            dma_compute(buf1, buf0, rsrc, voff, row_bytes8, (int)(s2 * dma::BK * 4), wave,
+                        a_base, b_base, lane, aL, bL, acc);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
