@@ -46,8 +46,9 @@
  *     call returns a negative km_status and enqueues nothing.
  *   - Arithmetic: float32 MFMA products with float32 accumulation for the
  *     assignment; per-cluster sums accumulated in float64 (in increasing
- *     sample order for a cluster of at most 64 samples; as sixteen
- *     contiguous parts of its samples, added in order, for a larger one),
+ *     sample order for a cluster of at most 64 samples, or 128 when
+ *     n * d >= 2^26 and n >= 32 k; as sixteen contiguous parts of its
+ *     samples, added in order, for a larger one),
  *     divided in float64 and rounded once to float32. Every reduction has a fixed
  *     order: the same inputs give the same bits.
  */

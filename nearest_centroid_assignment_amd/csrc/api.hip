@@ -327,10 +327,10 @@ int kmeans_fit(const float *X, const float *C_init, int64_t n, int64_t k, int64_
     for (int64_t it = 0; it < max_iter && e == hipSuccess; ++it) {
         if (n > 0 && run_assign(X, C_out, n, k, d, labels, nullptr, true, cn, s) != KM_OK)
             return KM_ERR_HIP;
-        e = km::launch_count(labels, n, k, counts, relocate ? rs.num_empty : nullptr, ws, s);
+        e = km::launch_count(labels, n, k, d, counts, relocate ? rs.num_empty : nullptr, ws, s);
         if (e == hipSuccess && relocate) {
             e = km::launch_relocate(X, C_out, labels, n, k, d, rs, ws, s);
-            if (e == hipSuccess) e = km::launch_count(labels, n, k, counts, nullptr, ws, s);
+            if (e == hipSuccess) e = km::launch_count(labels, n, k, d, counts, nullptr, ws, s);
         }
         if (e == hipSuccess)
             e = km::launch_group_and_mean(X, labels, C_out, n, k, d, C_out, shift_partial, nullptr,
@@ -346,7 +346,7 @@ int kmeans_fit(const float *X, const float *C_init, int64_t n, int64_t k, int64_
     }
     if (e == hipSuccess && n > 0 && run_assign(X, C_out, n, k, d, labels, md, true, cn, s) != KM_OK)
         return KM_ERR_HIP;
-    if (e == hipSuccess) e = km::launch_count(labels, n, k, counts, nullptr, ws, s);
+    if (e == hipSuccess) e = km::launch_count(labels, n, k, d, counts, nullptr, ws, s);
     if (e == hipSuccess) e = km::launch_inertia(md, n, info + 1, s);
     if (e == hipSuccess) e = km::launch_store_f64(info, (double)n_iter, s);
     return e == hipSuccess ? KM_OK : KM_ERR_HIP;

@@ -43,9 +43,17 @@ hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, 
 hipError_t launch_finalize(unsigned long long *keys, float *min_dist, bool add_norm, int64_t n,
                            hipStream_t stream);
 
+// Clusters of more rows than this are summed in parts by the mean kernel;
+// smaller ones by one wave in sample order: 64, or 128 when X has at least
+// 2^26 elements and clusters average 32 rows or more (then clusters of 65 to
+// 128 rows are common, and a wave summing one alone is still far from the
+// critical path, while the split's per-part barrier and merge are not).
+int split_rows(int64_t n, int64_t k, int64_t d);
+
 // Counting phase of the update: per-cluster sizes (ws.cnt, counts) and the
-// segment starts; num_empty (nullable) receives the number of empty clusters.
-hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t *counts,
+// segment starts, and the split of the clusters by split_rows(n, k, d);
+// num_empty (nullable) receives the number of empty clusters.
+hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t d, int64_t *counts,
                         int *num_empty, const UpdateScratch &ws, hipStream_t stream);
 
 // Second phase: stable grouping of rows by label and the float64 segmented

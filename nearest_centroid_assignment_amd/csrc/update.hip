@@ -33,7 +33,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = (int)kSortTileRows;  // rows per sort tile
 constexpr int kCols = 256;                 // columns per segment_mean block (64 lanes x 4)
-constexpr int kSplitMin = 64;              // larger clusters are split in kBigWaves parts
+constexpr int kSplitSmall = 64;            // larger clusters are split in kBigWaves parts ...
+constexpr int kSplitLarge = 128;           // ... or larger than this, on big inputs
 constexpr int kBigWaves = 16;              // waves (parts) per big-cluster block
 constexpr int kBigBlocks = 256;            // segment_mean blocks that take the large clusters
 
@@ -82,29 +83,30 @@ __global__ __launch_bounds__(256) void tile_scan_kernel(int *__restrict__ tile_h
     if (lane == 0) cnt[j] = carry;
 }
 
-// Load-round classes of the clusters summed by one wave (at most kSplitMin
-// rows): class ceil(count / 8), 0 .. kClasses - 1.
-constexpr int kClasses = kSplitMin / 8 + 1;
-
+// Load-round classes of the clusters summed by one wave (at most kSplit
+// rows): class ceil(count / 8), 0 .. kSplit / 8.
+template <int kSplit>
 __device__ __forceinline__ int round_class(int count) {
-    return count <= kSplitMin ? (count + 7) / 8 : -1;
+    return count <= kSplit ? (count + 7) / 8 : -1;
 }
 
 // A single block of 1024 threads: exclusive scan over the k cluster sizes.
 // If num_empty != NULL it receives the number of clusters of size 0. big[0]
-// receives the number of clusters with more than kSplitMin rows and big[1 ..]
+// receives the number of clusters with more than kSplit rows and big[1 ..]
 // their indices in increasing order. order[0 .. k - big[0]) receives the
 // other clusters grouped by load-round class, most rounds first, increasing
 // index within a class (a stable partition: every rank comes from ballots, so
 // the order is the same on every run). The mean kernel gives 16 consecutive
 // entries of `order` to one block, so a block's waves run the same number of
 // load rounds instead of all waiting for the block's largest cluster.
+template <int kSplit>
 __global__ __launch_bounds__(1024) void cluster_scan_kernel(const int *__restrict__ cnt, int64_t k,
                                                             int *__restrict__ seg_start,
                                                             int64_t *__restrict__ counts,
                                                             int *__restrict__ num_empty,
                                                             int *__restrict__ big,
                                                             int *__restrict__ order) {
+    constexpr int kClasses = kSplit / 8 + 1;
     __shared__ int wave_tot[16];
     __shared__ int wave_big[16];
     __shared__ int wave_empty[16];
@@ -123,9 +125,9 @@ __global__ __launch_bounds__(1024) void cluster_scan_kernel(const int *__restric
             const int up = __shfl_up(incl, off);
             if (lane >= off) incl += up;
         }
-        const bool is_big = j < k && v > kSplitMin;
+        const bool is_big = j < k && v > kSplit;
         const unsigned long long bm = __ballot(is_big);
-        const int cls = j < k ? round_class(v) : -1;
+        const int cls = j < k ? round_class<kSplit>(v) : -1;
         if (lane == 63) wave_tot[wave] = incl;
         if (lane == 0) wave_big[wave] = __popcll(bm);
 #pragma unroll
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(1024) void cluster_scan_kernel(const int *__restric
     __syncthreads();
     for (int64_t base = 0; base < k; base += 1024) {
         const int64_t j = base + tid;
-        const int cls = j < k ? round_class(cnt[j]) : -1;
+        const int cls = j < k ? round_class<kSplit>(cnt[j]) : -1;
         int rank = 0;
 #pragma unroll
         for (int c = 0; c < kClasses; ++c) {
@@ -388,12 +390,12 @@ __device__ __forceinline__ void write_mean(const float *C_old, float *C_new, int
 
 // One launch for both kinds of cluster, 16 waves per block. Blocks 0 ..
 // kBigBlocks-1 come first, so they run beside the others: they take the
-// clusters with more than kSplitMin rows (listed in big[1 .. big[0]]) as
+// clusters above the split size (listed in big[1 .. big[0]] by the scan) as
 // work items (cluster big[1 + i / chunks], chunk i % chunks), blocks taking
 // items blockIdx.x, + kBigBlocks, ...; wave p sums part p of the cluster's
 // rows (kBigWaves contiguous parts) and wave 0 adds the parts in order and
 // writes the mean. Every later block covers kBigWaves consecutive entries
-// of `order` (the clusters of at most kSplitMin rows, grouped by load-round
+// of `order` (the clusters up to the split size, grouped by load-round
 // class; one wave each) x one chunk of kCols columns, and sums each cluster
 // alone, in increasing sample order; lane l owns 4 columns.
 // If kShift, block b writes the sum of its (new - old)^2 in a fixed order to
@@ -421,7 +423,7 @@ __global__ __launch_bounds__(kBigWaves * 64) void segment_mean_kernel(
             int64_t col[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) col[e] = c * kCols + lc[e];
-            const int count = cnt[j];  // > kSplitMin
+            const int count = cnt[j];  // > the split size
             const int q = (count + kBigWaves - 1) / kBigWaves;
             const int r0 = min(count, wave * q), r1 = min(count, r0 + q);
             double s[4] = {0.0, 0.0, 0.0, 0.0};
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(kBigWaves * 64) void segment_mean_kernel(
         for (int e = 0; e < 4; ++e) col[e] = c * kCols + lc[e];
         if (i < k - big[0]) {
             const int64_t j = order[i];
-            const int count = cnt[j];  // <= kSplitMin
+            const int count = cnt[j];  // <= the split size
             {
                 double s[4] = {0.0, 0.0, 0.0, 0.0};
                 const int64_t seg = seg_start[j];
@@ -494,7 +496,11 @@ int64_t update_grid_threads(int64_t n, int64_t k, int64_t d) {
     return m > scan ? m : scan;
 }
 
-hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t *counts,
+int split_rows(int64_t n, int64_t k, int64_t d) {
+    return (n * d >= ((int64_t)1 << 26) && n >= 32 * k) ? kSplitLarge : kSplitSmall;
+}
+
+hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t d, int64_t *counts,
                         int *num_empty, const UpdateScratch &ws, hipStream_t stream) {
     const int64_t hist_words = k * ws.n_tiles;
     if (hist_words > 0) {
@@ -509,8 +515,12 @@ hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t *co
         // n == 0: every cluster is empty.
         fill_i32_kernel<<<grid_stride_blocks(k), 256, 0, stream>>>(ws.cnt, k);
     }
-    cluster_scan_kernel<<<1, 1024, 0, stream>>>(ws.cnt, k, ws.seg_start, counts, num_empty,
-                                                ws.big, ws.order);
+    if (split_rows(n, k, d) == kSplitLarge)
+        cluster_scan_kernel<kSplitLarge><<<1, 1024, 0, stream>>>(ws.cnt, k, ws.seg_start, counts,
+                                                                 num_empty, ws.big, ws.order);
+    else
+        cluster_scan_kernel<kSplitSmall><<<1, 1024, 0, stream>>>(ws.cnt, k, ws.seg_start, counts,
+                                                                 num_empty, ws.big, ws.order);
     return hipGetLastError();
 }
 
@@ -619,7 +629,7 @@ hipError_t launch_add_norms(float *min_dist, const float *xn_part, int64_t n, in
 hipError_t launch_update(const float *X, const int64_t *labels, const float *C_old, int64_t n,
                          int64_t k, int64_t d, float *C_new, int64_t *counts, float *xn_part,
                          const UpdateScratch &ws, hipStream_t stream) {
-    hipError_t e = launch_count(labels, n, k, counts, nullptr, ws, stream);
+    hipError_t e = launch_count(labels, n, k, d, counts, nullptr, ws, stream);
     if (e != hipSuccess) return e;
     return launch_group_and_mean(X, labels, C_old, n, k, d, C_new, nullptr, xn_part, ws, stream);
 }

@@ -10,9 +10,10 @@ Parity rules (all checked, none relaxed):
 * counts  - bit-exact against the oracle's update applied to the GPU's labels;
   against the oracle's own labels they may differ only by the moved rows.
 * centroids - the oracle's update on the GPU's labels: per row,
-  max |dC| <= 1e-4 * max |C_ref|. Clusters of at most 64 rows are summed in
-  increasing sample order in float64 on both sides, so those rows must also
-  be bit-exact; bigger clusters add sixteen row parts (a different order).
+  max |dC| <= 1e-4 * max |C_ref|. Clusters of at most 64 rows (128 once X
+  has 2^26 elements or more and n >= 32 k) are summed in increasing sample order in float64
+  on both sides, so those rows must also be bit-exact; bigger clusters add
+  sixteen row parts (a different order).
 * min_dist - |dD| <= 1e-4 * D_ref or |dD| <= 1e-5 * (||x||^2 + ||c||^2), D_ref
   the float64 distance to the GPU's chosen centroid.
 """
@@ -110,20 +111,25 @@ def check_min_dist(X, C, g_labels, g_md, rows=None):
     assert np.all(g_md[rows] >= 0)
 
 
-EXACT_MAX_ROWS = 64  # clusters up to this size are summed in sample order on the GPU
+def exact_max_rows(n, k, d):
+    """Clusters up to this size are summed by one wave in sample order on the
+    GPU: 64 rows, or 128 when X has at least 2^26 elements and n >= 32 k."""
+    return 128 if n * d >= 1 << 26 and n >= 32 * k else 64
 
 
 def check_update(X, g_labels, C_old, g_Cnew, g_counts):
     """Update rules against the oracle's update on the GPU's labels. Returns
-    the fraction of bit-exact centroid elements in clusters above 64 rows."""
+    the fraction of bit-exact centroid elements in the clusters summed in
+    parts (above exact_max_rows)."""
     C_ref, cnt_ref, _ = oracle.update(X, g_labels, C_old)
+    exact_rows = exact_max_rows(X.shape[0], C_old.shape[0], X.shape[1])
     assert np.array_equal(g_counts, cnt_ref), "counts differ"
     scale = np.abs(C_ref).max(axis=1, keepdims=True)
     err = np.abs(g_Cnew.astype(np.float64) - C_ref)
     assert np.all(err <= REL_TOL * scale), f"centroids off, worst {err.max()}"
-    small = cnt_ref <= EXACT_MAX_ROWS
+    small = cnt_ref <= exact_rows
     assert np.array_equal(g_Cnew[small].view(np.uint32), C_ref[small].view(np.uint32)), \
-        "centroids of clusters with <= 64 rows not bit-exact against the in-order float64 mean"
+        f"centroids of clusters with <= {exact_rows} rows not bit-exact against the in-order float64 mean"
     big = ~small
     if big.any():
         return float(np.mean(g_Cnew[big].view(np.uint32) == C_ref[big].view(np.uint32)))

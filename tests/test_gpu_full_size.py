@@ -52,7 +52,7 @@ def test_feature_heavy_lloyd():
     gu.announce("feature_heavy: oracle update on the GPU labels")
     frac = gu.check_update(X, g_labels, C, g_Cnew, g_counts)
     assert g_counts.sum() == len(X)
-    gu.announce(f"feature_heavy: done (bit-exact fraction in clusters > 64 rows: {frac:.6f})")
+    gu.announce(f"feature_heavy: done (bit-exact fraction in clusters summed in parts: {frac:.6f})")
 
 
 def test_centroid_heavy_lloyd():
@@ -65,4 +65,4 @@ def test_centroid_heavy_lloyd():
     gu.announce("centroid_heavy: oracle update on the GPU labels")
     frac = gu.check_update(X, g_labels, C, g_Cnew, g_counts)
     assert g_counts.sum() == len(X)
-    gu.announce(f"centroid_heavy: done (bit-exact fraction in clusters > 64 rows: {frac:.6f})")
+    gu.announce(f"centroid_heavy: done (bit-exact fraction in clusters summed in parts: {frac:.6f})")

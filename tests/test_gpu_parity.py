@@ -355,10 +355,14 @@ def test_persistent_tile_walk(monkeypatch, tile, n, k, d):
 
 
 @pytest.mark.parametrize("n,k,d,skew", [(5000, 3, 300, "mild"), (70000, 2, 520, "giant"),
-                                        (20000, 50, 1030, "zipf"), (3000, 200, 64, "one-big")])
+                                        (20000, 50, 1030, "zipf"), (3000, 200, 64, "one-big"),
+                                        (70125, 375, 512, "ramp"), (70125, 375, 1024, "ramp")])
 def test_update_skewed_clusters(n, k, d, skew):
     """Cluster sizes far from balanced: big clusters take the split-row path,
-    small ones the in-order path; both must meet the update rules."""
+    small ones the in-order path; both must meet the update rules. The ramp
+    (cluster j holds j rows, shuffled) covers every size from empty to 374 on
+    both sides of the 2^26-element line where the one-wave path grows from
+    64 to 128 rows."""
     from nearest_centroid_assignment_amd import binding
     import torch
 
@@ -372,6 +376,9 @@ def test_update_skewed_clusters(n, k, d, skew):
         labels = np.minimum(rng.zipf(1.5, size=n) - 1, k - 1).astype(np.int64)
     elif skew == "one-big":
         labels = np.where(rng.random(n) < 0.5, 7, rng.integers(0, k, size=n)).astype(np.int64)
+    elif skew == "ramp":
+        assert n == k * (k - 1) // 2
+        labels = rng.permutation(np.repeat(np.arange(k), np.arange(k))).astype(np.int64)
     else:
         labels = rng.integers(0, k, size=n).astype(np.int64)
     C_new, counts = binding.update(gu.to_gpu(X), gu.to_gpu(labels), gu.to_gpu(C))
