@@ -9,10 +9,14 @@
 // Kernels:
 //   row_sqnorms_kernel  ||c_j||^2 (and ||x_i||^2 for min_dist outside a Lloyd step)
 //   fill_keys_kernel    packed-key identity
-//   assign_tile_kernel  float32 MFMA product X_tile . C_tile^T, staged through
-//                       LDS, with the distance, the argmin and the merge across
-//                       centroid tiles done on the accumulators: the (n, k)
-//                       distance matrix never exists in memory
+//   assign_dma_kernel   float32 MFMA product X_tile . C_tile^T for full
+//                       256 x 256 tiles, the operands moved from global memory
+//                       straight into LDS by buffer loads, with the distance,
+//                       the argmin and the merge across centroid tiles done on
+//                       the accumulators: the (n, k) distance matrix never
+//                       exists in memory
+//   assign_tile_kernel  the same for any shape, operands staged through
+//                       registers into LDS, several tile sizes
 //   finalize_kernel     packed key -> int64 label, full squared distance
 #include <stdlib.h>
 #include <string.h>
@@ -264,7 +268,9 @@ __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
     // has at most one block per CU and each block takes every x_blocks-th
     // tile of its XCD's range: the same tiles run side by side on an XCD as
     // with one block per tile, and the per-block start-up and tear-down is
-    // paid once per CU instead of once per tile.
+    // paid once per CU instead of once per tile. Tile counts fit an int: the
+    // library rejects shapes whose launch grid would exceed 2^32 - 1
+    // work-items, far fewer than 2^31 tiles.
     const int T = tiles_m * tiles_n;
     const int per = T / 8, rem = T % 8, xcd = blockIdx.x % 8;
     const int x_start = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
@@ -560,6 +566,8 @@ __global__ __launch_bounds__(dma::NT, 2) void assign_dma_kernel(
     const int a_base = wm * dma::MB * 32 + (lane & 31);
     const int b_base = dma::BM + wn * dma::NB * 32 + (lane & 31);
     const int64_t nk = d / dma::BK;  // even
+    // Tile counts fit an int: the library rejects shapes whose launch grid
+    // would exceed 2^32 - 1 work-items, far fewer than 2^31 tiles.
     const int T = tiles_m * tiles_n;
     const int per = T / 8, rem = T % 8, xcd = blockIdx.x % 8;
     const int x_start = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
