@@ -289,11 +289,11 @@ __device__ __forceinline__ void flush_norms(float (&q)[B], int m, int lane, floa
     if ((lane & (64 / B - 1)) == 0 && u < m) xn[u] = t;
 }
 
-// Rows are fetched in rounds of kBatch: the round's row indices, then all its
-// row loads, then the adds in order. kBatch is 16, or 8 when clusters hold 32
-// rows or fewer on average: the kernel then needs about 64 registers instead
-// of about 100, so two 16-wave blocks share a CU and more short clusters are
-// in flight at once. The order of the adds does not depend on kBatch.
+// Rows are fetched in rounds of kBatch: all the round's row loads, then the
+// adds in order. kBatch is 16, or 8 when clusters hold 32 rows or fewer on
+// average (measured faster there: fewer load slots of a round go unused on
+// short clusters, and the kernel needs about 66 registers instead of about
+// 100). The order of the adds does not depend on kBatch.
 //
 // With kNorm (xn != NULL) the same loads also give each row's squared norm
 // over this chunk's columns: per lane a float32 fused multiply-add chain over
@@ -314,11 +314,23 @@ __device__ __forceinline__ void sum_rows(const float *__restrict__ X, const int 
     float qp[B];   // the previous round's per-lane squared norms (kNorm)
     int pp = 0;    // its first row
     int mp = 0;    // its row count (0: nothing pending)
+    // Row indices come 64 at a time, one per lane (rows[c0 + lane]), the
+    // next 64 loaded a chunk ahead; a round takes its own with readlane, so
+    // its row loads do not wait for an index load.
+    int c0 = r0;
+    int idx = r0 + lane < r1 ? rows[r0 + lane] : 0;
+    int idx_next = r0 + 64 + lane < r1 ? rows[r0 + 64 + lane] : 0;
     for (int p0 = r0; p0 < r1; p0 += B) {
+        if (p0 - c0 == 64) {
+            c0 = p0;
+            idx = idx_next;
+            idx_next = p0 + 64 + lane < r1 ? rows[p0 + 64 + lane] : 0;
+        }
         const int m = min(B, r1 - p0);
         int64_t base[B];
 #pragma unroll
-        for (int u = 0; u < B; ++u) base[u] = u < m ? (int64_t)rows[p0 + u] * d : -1;
+        for (int u = 0; u < B; ++u)
+            base[u] = u < m ? (int64_t)__builtin_amdgcn_readlane(idx, p0 - c0 + u) * d : -1;
         if (kVec) {
             f32x4 v[B];
 #pragma unroll
