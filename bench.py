@@ -314,9 +314,10 @@ def main() -> int:
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the per-GPU shard would run the same kernels; see the sharding design).",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(a sample-sharded run would give each GPU n/G rows and a copy of C, run "
+              "the same kernels on its shard and all-reduce the per-cluster sums and "
+              "counts).", file=sys.stderr)
         return 2
 
     import numpy as np
