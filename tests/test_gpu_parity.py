@@ -356,13 +356,15 @@ def test_persistent_tile_walk(monkeypatch, tile, n, k, d):
 
 @pytest.mark.parametrize("n,k,d,skew", [(5000, 3, 300, "mild"), (70000, 2, 520, "giant"),
                                         (20000, 50, 1030, "zipf"), (3000, 200, 64, "one-big"),
-                                        (70125, 375, 512, "ramp"), (70125, 375, 1024, "ramp")])
+                                        (70125, 375, 512, "ramp"), (70125, 375, 1024, "ramp"),
+                                        (65536, 2048, 1024, "edge")])
 def test_update_skewed_clusters(n, k, d, skew):
     """Cluster sizes far from balanced: big clusters take the split-row path,
     small ones the in-order path; both must meet the update rules. The ramp
     (cluster j holds j rows, shuffled) covers every size from empty to 374 on
     both sides of the 2^26-element line where the one-wave path grows from
-    64 to 128 rows."""
+    64 to 128 rows; "edge" sits exactly on that line and on n = 32 k (both
+    inclusive), with clusters of 0 to 255 rows and the rest of about 18."""
     from nearest_centroid_assignment_amd import binding
     import torch
 
@@ -379,6 +381,13 @@ def test_update_skewed_clusters(n, k, d, skew):
     elif skew == "ramp":
         assert n == k * (k - 1) // 2
         labels = rng.permutation(np.repeat(np.arange(k), np.arange(k))).astype(np.int64)
+    elif skew == "edge":
+        assert n * d == 1 << 26 and n == 32 * k
+        sizes = np.concatenate([np.arange(256), np.zeros(k - 256, dtype=np.int64)])
+        rest = n - int(sizes.sum())
+        sizes[256:] = rest // (k - 256)
+        sizes[256:256 + rest % (k - 256)] += 1
+        labels = rng.permutation(np.repeat(np.arange(k), sizes)).astype(np.int64)
     else:
         labels = rng.integers(0, k, size=n).astype(np.int64)
     C_new, counts = binding.update(gu.to_gpu(X), gu.to_gpu(labels), gu.to_gpu(C))
