@@ -200,25 +200,35 @@ def kmeanspp(X, k, first, trials, rand):
 
 
 def default_trials(k: int) -> int:
-    """The pages' trial count, 2 + log(k) (natural log, truncated)."""
+    """The pages' trial count 2 + log(k) ("004 - tile sizes ...", section
+    k-means++), read as the natural logarithm truncated to an integer:
+    2 + floor(ln k), e.g. 8 at k = 1024 and 2 at k = 1."""
     import math
 
     return 2 + int(math.log(k)) if k > 0 else 2
 
 
-def sq_norms(A) -> np.ndarray:
-    """Row squared norms in float64."""
-    A64 = np.asarray(A, dtype=np.float64)
-    return np.einsum("ij,ij->i", A64, A64)
+def sq_norms(A, rows_per_chunk: int = 4096) -> np.ndarray:
+    """Row squared norms, every element widened to float64 (a chunk of rows
+    at a time, so a large float32 matrix is never copied whole)."""
+    A = np.asarray(A)
+    out = np.empty(A.shape[0], dtype=np.float64)
+    for r0 in range(0, A.shape[0], rows_per_chunk):
+        A64 = A[r0:r0 + rows_per_chunk].astype(np.float64)
+        out[r0:r0 + rows_per_chunk] = np.einsum("ij,ij->i", A64, A64)
+    return out
+
+
+def tie_band(X, C, labels, rtol: float = 1e-5) -> np.ndarray:
+    """Width of the near-tie band of every row: rtol * (||x_i||^2 +
+    ||c_label_i||^2), norms in float64, c the row's oracle winner."""
+    return rtol * (sq_norms(X) + sq_norms(C)[np.asarray(labels)])
 
 
 def near_ties(X, C, labels, best, second, rtol: float = 1e-5) -> np.ndarray:
-    """Boolean mask of rows whose best-to-second gap is within the tie band.
-
-    The band is ``rtol * (||x_i||^2 + ||c_label_i||^2)`` with norms in float64.
-    """
-    scale = sq_norms(X) + sq_norms(C)[np.asarray(labels)]
-    return (np.asarray(second) - np.asarray(best)) <= rtol * scale
+    """Boolean mask of rows whose best-to-second gap is within the tie band:
+    second - best <= rtol * (||x_i||^2 + ||c_label_i||^2) (``tie_band``)."""
+    return (np.asarray(second) - np.asarray(best)) <= tie_band(X, C, labels, rtol)
 
 
 for _name in ("num_threads", "assign", "update", "lloyd_step", "kmeanspp"):

@@ -65,50 +65,66 @@ def gpu_assign(X, C, min_dist=True):
 
 
 def sq_norms(A):
-    A64 = np.asarray(A, dtype=np.float64)
-    return np.einsum("ij,ij->i", A64, A64)
+    return oracle.sq_norms(A)
 
 
-def exact_dist(X, C, rows, cols):
-    """float64 difference-form distance of X[rows[i]] to C[cols[i]]."""
-    diff = X[rows].astype(np.float64) - C[cols].astype(np.float64)
-    return np.einsum("ij,ij->i", diff, diff)
+def exact_dist(X, C, rows, cols, rows_per_chunk: int = 4096):
+    """float64 difference-form distance of X[rows[i]] to C[cols[i]] (a chunk
+    of rows at a time, so no (n, d) float64 copy of a large X is made)."""
+    rows, cols = np.asarray(rows), np.asarray(cols)
+    out = np.empty(len(rows), dtype=np.float64)
+    for r0 in range(0, len(rows), rows_per_chunk):
+        sl = slice(r0, r0 + rows_per_chunk)
+        diff = X[rows[sl]].astype(np.float64) - C[cols[sl]].astype(np.float64)
+        out[sl] = np.einsum("ij,ij->i", diff, diff)
+    return out
+
+
+def _rows_of(X, rows):
+    return X if rows is None else X[rows]
 
 
 def check_labels(X, C, g_labels, o_labels, best, second, rows=None):
     """Labels rule; returns the number of near-tie rows and of mismatches.
 
     ``rows`` maps the oracle's rows to rows of X (sampled parity); X and C are
-    the full arrays.
+    the full arrays. The band and the near-tie mask are the oracle's own
+    (``oracle.tie_band``, ``oracle.near_ties``).
     """
-    if rows is None:
-        rows = np.arange(len(o_labels))
-    g = g_labels[rows]
+    idx = np.arange(len(o_labels)) if rows is None else np.asarray(rows)
+    g = g_labels[idx]
     assert g.min() >= 0 and g.max() < len(C)
-    xn = sq_norms(X[rows])
-    cn = sq_norms(C)
-    band = TIE_RTOL * (xn + cn[o_labels])
-    ties = (second - best) <= band
+    Xr = _rows_of(X, rows)
+    band = oracle.tie_band(Xr, C, o_labels, TIE_RTOL)
+    ties = oracle.near_ties(Xr, C, o_labels, best, second, TIE_RTOL)
     mism = np.nonzero(g != o_labels)[0]
     assert np.all(ties[mism]), (
         f"{len(mism)} label mismatches, {int((~ties[mism]).sum())} outside the near-tie band; "
-        f"first rows {rows[mism[~ties[mism]]][:5]}")
+        f"first rows {idx[mism[~ties[mism]]][:5]}")
     if len(mism):
-        dg = exact_dist(X, C, rows[mism], g[mism])
+        dg = exact_dist(X, C, idx[mism], g[mism])
         assert np.all(dg - best[mism] <= band[mism])
     return int(ties.sum()), int(len(mism))
 
 
-def check_min_dist(X, C, g_labels, g_md, rows=None):
-    if rows is None:
-        rows = np.arange(len(X))
-    g = g_labels[rows]
-    ref = exact_dist(X, C, rows, g)
-    scale = sq_norms(X[rows]) + sq_norms(C)[g]
-    err = np.abs(g_md[rows].astype(np.float64) - ref)
+def check_min_dist(X, C, g_labels, g_md, rows=None, o_labels=None, best=None):
+    """min_dist rule. With the oracle's labels and best distances for these
+    rows, rows where the GPU picked the oracle's label take ``best`` as the
+    reference and only the others are recomputed."""
+    idx = np.arange(len(X)) if rows is None else np.asarray(rows)
+    g = g_labels[idx]
+    if o_labels is not None:
+        ref = np.array(best, dtype=np.float64, copy=True)
+        diff_rows = np.nonzero(g != o_labels)[0]
+        if len(diff_rows):
+            ref[diff_rows] = exact_dist(X, C, idx[diff_rows], g[diff_rows])
+    else:
+        ref = exact_dist(X, C, idx, g)
+    scale = sq_norms(_rows_of(X, rows)) + sq_norms(C)[g]
+    err = np.abs(g_md[idx].astype(np.float64) - ref)
     ok = (err <= REL_TOL * ref) | (err <= TIE_RTOL * scale)
     assert np.all(ok), f"min_dist off on {int((~ok).sum())} rows, worst {err[~ok].max()}"
-    assert np.all(g_md[rows] >= 0)
+    assert np.all(g_md[idx] >= 0)
 
 
 def exact_max_rows(n, k, d):

@@ -290,3 +290,76 @@ def pin_kmeanspp_greedy(orc, seed: int = 7):
 
 
 ALL_PINS += [pin_kmeanspp_hand, pin_kmeanspp_d2_quadrature, pin_kmeanspp_greedy]
+
+
+# ------------------------------------------------- the oracle's Python helpers
+#
+# centre_shift, near_ties and default_trials live in oracle/__init__.py, not
+# in the C library. Their pins take a namespace holding the helper under test
+# (the oracle module itself, or a copy with one helper replaced by a planted
+# mistake in tests/test_oracle_mutants.py) and an Oracle for the assignment.
+
+
+def pin_centre_shift(ns, orc):
+    """The driver's convergence measure sum_j ||C_new_j - C_old_j||^2 in
+    float64. The pages time fixed iteration counts ("004 - tile sizes ...",
+    section Cython timing); the stopping test on the squared centre movement
+    summed over centres is the reading the driver takes."""
+    # Worked by hand: moves (3, 4), (0, 1) and (0, 0) -> 25 + 1 + 0 = 26.
+    C_old = np.array([[0, 0], [1, 1], [2, -3]], dtype=np.float32)
+    C_new = np.array([[3, 4], [1, 2], [2, -3]], dtype=np.float32)
+    assert ns.centre_shift(C_new, C_old) == 26.0
+    assert ns.centre_shift(C_old, C_new) == 26.0  # symmetric in its arguments
+    # A common translation v moves every centre by ||v||^2: k * ||v||^2.
+    rng = np.random.default_rng(12)
+    C = rng.integers(-50, 51, size=(7, 5)).astype(np.float32)
+    v = np.array([1, -2, 3, 0, 5], dtype=np.float32)
+    assert ns.centre_shift(C + v, C) == 7.0 * float(v.astype(np.int64) @ v.astype(np.int64))
+    # 4097^2 = 16785409 has no float32 representation (it needs 25 bits):
+    # the squares and the sum are float64.
+    assert ns.centre_shift(np.array([[4097.0]], np.float32), np.zeros((1, 1), np.float32)) \
+        == 16785409.0
+
+
+def pin_near_tie_band(ns, orc):
+    """The band of the parity rule: a row is a near tie when its gap between
+    the best and the second-best distance is <= 1e-5 * (||x||^2 + ||c||^2),
+    c the winning centroid, norms in float64 ("004 - tile sizes ...", section
+    Same arrays as the Cython iteration, for why such rows may differ)."""
+    # Gap exactly on the band: x = (100, 200, 0) is itself centroid 0 (D = 0)
+    # and centroid 1 is one unit away (D = 1); ||x||^2 + ||c_0||^2 = 100000,
+    # band = 1e-5 * 100000 = 1 (exactly, in float64) = the gap: a tie.
+    assert 1e-5 * 100000.0 == 1.0
+    X = np.array([[100, 200, 0]], dtype=np.float32)
+    C = np.array([[100, 200, 0], [101, 200, 0]], dtype=np.float32)
+    labels, best, second = orc.assign(X, C)
+    assert labels.tolist() == [0] and best.tolist() == [0.0] and second.tolist() == [1.0]
+    assert ns.near_ties(X, C, labels, best, second).tolist() == [True]
+    # Gap just outside the band, and only the winner's norm says so:
+    # x = (150, 163, 30), ||x||^2 = 49969; c_0 = (150, 163, 31), D = 1,
+    # ||c_0||^2 = 50030; c_1 = (150, 164, 29), D = 2, ||c_1||^2 = 50237.
+    # Gap 1 > 1e-5 * 99999 = 0.99999: not a tie (with c_1's norm the band
+    # would be 1.00206 and the row would count as one).
+    X = np.array([[150, 163, 30]], dtype=np.float32)
+    C = np.array([[150, 163, 31], [150, 164, 29]], dtype=np.float32)
+    labels, best, second = orc.assign(X, C)
+    assert labels.tolist() == [0] and best.tolist() == [1.0] and second.tolist() == [2.0]
+    assert ns.near_ties(X, C, labels, best, second).tolist() == [False]
+    # Same geometry seen from the other side: a far second centroid is never
+    # a tie, an exact duplicate always is.
+    X = np.array([[0.0, 1.0], [5.0, 5.0]], dtype=np.float32)
+    C = np.array([[0.0, 0.0], [0.0, 0.0], [9.0, 9.0]], dtype=np.float32)
+    labels, best, second = orc.assign(X, C)
+    assert ns.near_ties(X, C, labels, best, second).tolist() == [True, False]
+
+
+def pin_default_trials(ns, orc):
+    """k-means++ trials per centre: 2 + log(k) ("004 - tile sizes ...",
+    section k-means++), read as 2 + floor(ln k). Values from the definition:
+    ln 2 = 0.69, ln 3 = 1.10, ln 7 = 1.95, ln 8 = 2.08, ln 20 = 3.00 (just
+    below 3), ln 21 = 3.04, ln 1024 = 6.93."""
+    table = {1: 2, 2: 2, 3: 3, 7: 3, 8: 4, 20: 4, 21: 5, 1024: 8}
+    assert {k: ns.default_trials(k) for k in table} == table
+
+
+PY_PINS = [pin_centre_shift, pin_near_tie_band, pin_default_trials]

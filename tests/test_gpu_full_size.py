@@ -1,17 +1,28 @@
 """Parity at the full workload sizes, in the launch configuration the benchmark
-times: the GPU runs the whole problem; the oracle recomputes a seeded sample of
-rows one by one against every centroid; the update is checked in full (the
-oracle's float64 update applied to the GPU's labels)."""
+times: the GPU runs the whole problem and EVERY row is compared with the
+oracle.
+
+The oracle's labels, best and second-best distances of every row are stored
+in tests/golden/full_<name>.npz, written by
+tests/golden/make_full_size_expected.py, which calls only ``oracle/`` on the
+seeded inputs (minutes of host time per workload). Each test first proves it
+is looking at the same problem: the regenerated X and C must hash to the
+stored SHA-256, and the oracle, run live on a seeded sample of rows, must
+reproduce the stored values bit for bit. The update is checked in full: the
+oracle's float64 update applied to the GPU's labels."""
+import os
+
 import numpy as np
 import pytest
 
 import oracle
 from nearest_centroid_assignment_amd import datagen
 from tests import gpu_util as gu
+from tests.golden import make_full_size_expected as golden
 
 pytestmark = pytest.mark.gpu
 
-SAMPLE_ROWS = 2048  # oracle rows per full-size workload (a few seconds each on the host)
+LIVE_ROWS = 256  # rows the oracle recomputes live to vouch for the stored file
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -21,34 +32,50 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-def _sampled_assign_parity(name, X, C, g_labels, g_md):
-    rows = np.sort(np.random.default_rng(123).choice(len(X), SAMPLE_ROWS, replace=False))
-    o_labels, best, second = oracle.assign(X[rows], C)
-    ties, mism = gu.check_labels(X, C, g_labels, o_labels, best, second, rows=rows)
-    gu.check_min_dist(X, C, g_labels, g_md, rows=rows)
-    gu.announce(f"{name}: sampled rows {SAMPLE_ROWS}, near-ties {ties}, mismatches {mism}")
+def _inputs_and_expected(name):
+    """(X, C, stored oracle results) after checking they belong together."""
+    path = golden.path_for(name)
+    assert os.path.exists(path), f"{path} missing: run tests/golden/make_full_size_expected.py"
+    gu.announce(f"{name}: generating inputs")
+    X, C = datagen.make(name)
+    with np.load(path, allow_pickle=False) as z:
+        exp = {key: z[key] for key in z.files}
+    assert (int(exp["n"]), int(exp["k"]), int(exp["d"])) == (X.shape[0], C.shape[0], X.shape[1])
+    assert str(exp["x_sha256"]) == golden.sha256_of(X), "X differs from the stored oracle run"
+    assert str(exp["c_sha256"]) == golden.sha256_of(C), "C differs from the stored oracle run"
+    rows = np.sort(np.random.default_rng(321).choice(len(X), LIVE_ROWS, replace=False))
+    lab, best, second = oracle.assign(X[rows], C)
+    assert np.array_equal(lab, exp["labels"][rows].astype(np.int64))
+    assert np.array_equal(best, exp["best"][rows]) and np.array_equal(second, exp["second"][rows])
+    return X, C, exp
+
+
+def _all_rows_parity(name, X, C, exp, g_labels, g_md):
+    o_labels = exp["labels"].astype(np.int64)
+    ties, mism = gu.check_labels(X, C, g_labels, o_labels, exp["best"], exp["second"])
+    gu.check_min_dist(X, C, g_labels, g_md, o_labels=o_labels, best=exp["best"])
+    gu.announce(f"{name}: all {len(X)} rows, near-ties {ties}, mismatches {mism}")
+    return o_labels, mism
 
 
 def test_sample_heavy_assign():
     """131072 x 8192 x 8192: fused assignment only."""
-    gu.announce("sample_heavy: generating inputs")
-    X, C = datagen.make("sample_heavy")
+    X, C, exp = _inputs_and_expected("sample_heavy")
     gu.announce("sample_heavy: GPU assignment")
     g_labels, g_md = gu.gpu_assign(X, C)
-    assert g_labels.min() >= 0 and g_labels.max() < len(C)
-    _sampled_assign_parity("sample_heavy", X, C, g_labels, g_md)
-    # C is made of rows of X, so each of those rows is at distance 0 from its
-    # own centroid (or an exact duplicate with a lower index).
+    o_labels, mism = _all_rows_parity("sample_heavy", X, C, exp, g_labels, g_md)
+    gu.check_counts_vs_oracle_labels(np.bincount(g_labels, minlength=len(C)), o_labels, len(C),
+                                     mism)
     gu.announce("sample_heavy: done")
 
 
 def test_feature_heavy_lloyd():
     """65536 x 4096 x 16384: fused assignment + segmented update."""
-    gu.announce("feature_heavy: generating inputs")
-    X, C = datagen.make("feature_heavy")
+    X, C, exp = _inputs_and_expected("feature_heavy")
     gu.announce("feature_heavy: GPU Lloyd step")
     g_labels, g_md, g_Cnew, g_counts = gu.gpu_lloyd(X, C)
-    _sampled_assign_parity("feature_heavy", X, C, g_labels, g_md)
+    o_labels, mism = _all_rows_parity("feature_heavy", X, C, exp, g_labels, g_md)
+    gu.check_counts_vs_oracle_labels(g_counts, o_labels, len(C), mism)
     gu.announce("feature_heavy: oracle update on the GPU labels")
     frac = gu.check_update(X, g_labels, C, g_Cnew, g_counts)
     assert g_counts.sum() == len(X)
@@ -57,11 +84,11 @@ def test_feature_heavy_lloyd():
 
 def test_centroid_heavy_lloyd():
     """65536 x 16384 x 8192: about 4 samples per cluster, C = 512 MiB."""
-    gu.announce("centroid_heavy: generating inputs")
-    X, C = datagen.make("centroid_heavy")
+    X, C, exp = _inputs_and_expected("centroid_heavy")
     gu.announce("centroid_heavy: GPU Lloyd step")
     g_labels, g_md, g_Cnew, g_counts = gu.gpu_lloyd(X, C)
-    _sampled_assign_parity("centroid_heavy", X, C, g_labels, g_md)
+    o_labels, mism = _all_rows_parity("centroid_heavy", X, C, exp, g_labels, g_md)
+    gu.check_counts_vs_oracle_labels(g_counts, o_labels, len(C), mism)
     gu.announce("centroid_heavy: oracle update on the GPU labels")
     frac = gu.check_update(X, g_labels, C, g_Cnew, g_counts)
     assert g_counts.sum() == len(X)

@@ -22,14 +22,20 @@ def test_round_to_f32_helper():
     assert pins.round_to_f32(Fraction(1, 3)) == np.float32(1 / 3)
 
 
-def test_near_tie_band(oracle_mod):
-    """A duplicated centroid is an exact tie: gap 0, inside the band."""
-    X = np.array([[0.0, 1.0], [5.0, 5.0]], dtype=np.float32)
-    C = np.array([[0.0, 0.0], [0.0, 0.0], [9.0, 9.0]], dtype=np.float32)
-    labels, best, second = oracle_mod.assign(X, C)
-    ties = oracle_mod.near_ties(X, C, labels, best, second)
-    assert labels.tolist() == [0, 2]  # (5,5): 50 to the origin, 32 to (9,9)
-    assert ties.tolist() == [True, False]
+@pytest.mark.parametrize("pin", pins.PY_PINS, ids=lambda f: f.__name__)
+def test_py_pin(oracle_mod, pin):
+    """The oracle's Python helpers (centre shift, near-tie band, trial count)."""
+    pin(oracle_mod, oracle_mod.default())
+
+
+def test_sq_norms_chunked(oracle_mod):
+    """Row norms taken a chunk at a time equal the one-shot float64 sum."""
+    rng = np.random.default_rng(5)
+    A = rng.standard_normal((1000, 37)).astype(np.float32)
+    A64 = A.astype(np.float64)
+    want = np.einsum("ij,ij->i", A64, A64)
+    assert np.array_equal(oracle_mod.sq_norms(A, rows_per_chunk=64), want)
+    assert np.array_equal(oracle_mod.sq_norms(A), want)
 
 
 def test_second_formulation_small_configs(oracle_mod):
