@@ -91,10 +91,12 @@ def assign_kernel_name(n: int, k: int, d: int) -> str:
 
 
 def traffic_record(cfg):
-    """HBM bytes per launch of the assignment kernel from committed rocprofv3
-    counter runs (FETCH_SIZE and WRITE_SIZE, scaled by the factor a plain copy
-    kernel of known size gives), or None when absent or when the kernel source
-    has changed since the counters were taken."""
+    """Bytes per launch of the assignment kernel beyond its L2 from committed
+    rocprofv3 counter runs (FETCH_SIZE + WRITE_SIZE, each scaled by the factor
+    a plain copy kernel of known size gives; FETCH_SIZE includes what the
+    MALL in front of HBM serves, so this bounds the HBM bytes from above), or
+    None when absent or when the kernel source has changed since the counters
+    were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -104,7 +106,7 @@ def traffic_record(cfg):
 
     if rec.get("assign_kernel_sha256") != kernel_digest() or rec.get("workload") != cfg.name:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("beyond_l2_bytes_per_launch")
 
 
 def cpu_baseline(X, C, target_s: float):

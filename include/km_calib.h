@@ -24,6 +24,15 @@ extern "C" {
 int km_calib_copy(void *dst, const void *src, size_t bytes, void *stream);
 
 /*
+ * Read `bytes` bytes of src once with 16-byte vector loads (blocks x 256
+ * threads striding over the buffer, 8 loads in flight per thread) and write
+ * one float per thread to out (blocks * 256 floats): the attainable read
+ * bandwidth. Requires bytes % 16 == 0, src 16-byte aligned, blocks >= 1.
+ * Returns 0, -1 on invalid arguments, -6 if the launch is rejected.
+ */
+int km_calib_read(const void *src, size_t bytes, float *out, int blocks, void *stream);
+
+/*
  * Run `blocks` blocks of 256 threads, each wave issuing iters x 4
  * v_mfma_f32_32x32x2_f32 (4096 flop each) on four independent accumulators,
  * with no memory traffic but one float per thread written to out

@@ -28,7 +28,7 @@
  *     on entry do not matter; it is clobbered. Two calls that may run at the
  *     same time need two workspaces.
  *   - stream is a hipStream_t (NULL = the default stream). Every call except
- *     kmeans_fit only enqueues kernels on it and returns: no host
+ *     kmeans_fit (see there) only enqueues kernels on it and returns: no host
  *     synchronisation, no memset, no copy. Results are ready when the stream
  *     has reached that point. Such a call can also be captured into a HIP
  *     graph and replayed; a replay reads the buffers' contents at replay
@@ -159,8 +159,12 @@ int kmeans_lloyd_step(const float *X, const float *C_old, int64_t n, int64_t k, 
  *   info      device array of 3 doubles, output: iterations run, inertia
  *             (sum of the final squared distances, float64), and the centre
  *             shift of the last iteration.
- * Synchronisation: waits on `stream` once per iteration to read a 4-byte
- * convergence flag back to the host; it is the only entry point that does.
+ * Synchronisation: iterations are enqueued in batches, 4 first, then 8;
+ * between batches the call waits on `stream` to read a 4-byte convergence
+ * flag back to the host (the only entry point that ever waits). Iterations
+ * enqueued after the one that converged do nothing on the GPU: every kernel
+ * of an iteration returns at once once the flag is set. With max_iter <= 4
+ * the call never waits.
  */
 int kmeans_fit(const float *X, const float *C_init, int64_t n, int64_t k, int64_t d,
                int64_t max_iter, double tol, int flags,

@@ -120,13 +120,41 @@ def _stream(stream, device):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _workspace(workspace, nbytes, device):
+def _side_stream(stream, device):
+    """The torch stream the kernels go to when it is not the current stream
+    (None otherwise, or when the caller passed a raw handle)."""
+    torch = _torch()
+    if isinstance(stream, torch.cuda.Stream) and stream != torch.cuda.current_stream(device):
+        return stream
+    return None
+
+
+def _workspace(workspace, nbytes, device, stream=None):
+    """The caller's workspace, or a new one. A new one is allocated on the
+    stream the kernels run on, so the caching allocator does not hand its
+    memory to other work before those kernels are done with it."""
     torch = _torch()
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        side = _side_stream(stream, device)
+        if side is not None:
+            with torch.cuda.stream(side):
+                workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        else:
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
     if workspace.dtype != torch.uint8 or workspace.device.type != "cuda":
         raise TypeError("workspace must be a uint8 GPU tensor")
     return workspace
+
+
+def _record(stream, device, *tensors):
+    """Mark tensors as used by a side stream: their memory is not reused until
+    the work enqueued there so far is done (raw stream handles cannot be
+    tracked; such callers keep the tensors alive themselves)."""
+    side = _side_stream(stream, device)
+    if side is not None:
+        for t in tensors:
+            if t is not None and t.numel():
+                t.record_stream(side)
 
 
 def _check(rc: int, where: str):
@@ -142,10 +170,12 @@ def kmeans_assign(X, C, labels, min_dist=None, workspace=None, stream=None):
     args = (_ptr(X, torch.float32, (n, d), "X"), _ptr(C, torch.float32, (k, d), "C"), n, k, d,
             _ptr(labels, torch.int64, (n,), "labels"),
             _ptr(min_dist, torch.float32, (n,), "min_dist"))
-    workspace = _workspace(workspace, kmeans_workspace_bytes(n, k, d, KM_OP_ASSIGN), X.device)
+    workspace = _workspace(workspace, kmeans_workspace_bytes(n, k, d, KM_OP_ASSIGN), X.device,
+                           stream)
     rc = lib().kmeans_assign(*args, workspace.data_ptr(), workspace.numel(),
                              _stream(stream, X.device))
     _check(rc, "kmeans_assign")
+    _record(stream, X.device, X, C, labels, min_dist, workspace)
 
 
 def kmeans_update(X, labels, C_old, C_new, counts, workspace=None, stream=None):
@@ -156,10 +186,12 @@ def kmeans_update(X, labels, C_old, C_new, counts, workspace=None, stream=None):
     args = (_ptr(X, torch.float32, (n, d), "X"), _ptr(labels, torch.int64, (n,), "labels"),
             _ptr(C_old, torch.float32, (k, d), "C_old"), n, k, d,
             _ptr(C_new, torch.float32, (k, d), "C_new"), _ptr(counts, torch.int64, (k,), "counts"))
-    workspace = _workspace(workspace, kmeans_workspace_bytes(n, k, d, KM_OP_UPDATE), X.device)
+    workspace = _workspace(workspace, kmeans_workspace_bytes(n, k, d, KM_OP_UPDATE), X.device,
+                           stream)
     rc = lib().kmeans_update(*args, workspace.data_ptr(), workspace.numel(),
                              _stream(stream, X.device))
     _check(rc, "kmeans_update")
+    _record(stream, X.device, X, labels, C_old, C_new, counts, workspace)
 
 
 def kmeans_lloyd_step(X, C_old, labels, min_dist, C_new, counts, workspace=None, stream=None):
@@ -171,10 +203,12 @@ def kmeans_lloyd_step(X, C_old, labels, min_dist, C_new, counts, workspace=None,
             n, k, d, _ptr(labels, torch.int64, (n,), "labels"),
             _ptr(min_dist, torch.float32, (n,), "min_dist"),
             _ptr(C_new, torch.float32, (k, d), "C_new"), _ptr(counts, torch.int64, (k,), "counts"))
-    workspace = _workspace(workspace, kmeans_workspace_bytes(n, k, d, KM_OP_LLOYD), X.device)
+    workspace = _workspace(workspace, kmeans_workspace_bytes(n, k, d, KM_OP_LLOYD), X.device,
+                           stream)
     rc = lib().kmeans_lloyd_step(*args, workspace.data_ptr(), workspace.numel(),
                                  _stream(stream, X.device))
     _check(rc, "kmeans_lloyd_step")
+    _record(stream, X.device, X, C_old, labels, min_dist, C_new, counts, workspace)
 
 
 def kmeans_fit(X, C_init, max_iter, tol, flags, C_out, labels, min_dist, counts, info,
@@ -188,10 +222,12 @@ def kmeans_fit(X, C_init, max_iter, tol, flags, C_out, labels, min_dist, counts,
             _ptr(C_out, torch.float32, (k, d), "C_out"), _ptr(labels, torch.int64, (n,), "labels"),
             _ptr(min_dist, torch.float32, (n,), "min_dist"),
             _ptr(counts, torch.int64, (k,), "counts"), _ptr(info, torch.float64, (3,), "info"))
-    workspace = _workspace(workspace, kmeans_workspace_bytes(n, k, d, KM_OP_FIT), X.device)
+    workspace = _workspace(workspace, kmeans_workspace_bytes(n, k, d, KM_OP_FIT), X.device,
+                           stream)
     rc = lib().kmeans_fit(*args, workspace.data_ptr(), workspace.numel(),
                           _stream(stream, X.device))
     _check(rc, "kmeans_fit")
+    _record(stream, X.device, X, C_init, C_out, labels, min_dist, counts, info, workspace)
 
 
 def kmeans_plusplus(X, k, first, trials, rand, centres, chosen, workspace=None, stream=None):
@@ -201,10 +237,12 @@ def kmeans_plusplus(X, k, first, trials, rand, centres, chosen, workspace=None, 
     args = (_ptr(X, torch.float32, (n, d), "X"), n, d, int(k), int(first), int(trials),
             _ptr(rand, torch.float64, (max(k - 1, 0) * trials,), "rand") if k > 1 else None,
             _ptr(centres, torch.float32, (k, d), "centres"), _ptr(chosen, torch.int64, (k,), "chosen"))
-    workspace = _workspace(workspace, kmeans_workspace_bytes(n, k, d, KM_OP_KMEANSPP), X.device)
+    workspace = _workspace(workspace, kmeans_workspace_bytes(n, k, d, KM_OP_KMEANSPP),
+                           X.device, stream)
     rc = lib().kmeans_plusplus(*args, workspace.data_ptr(), workspace.numel(),
                                _stream(stream, X.device))
     _check(rc, "kmeans_plusplus")
+    _record(stream, X.device, X, rand, centres, chosen, workspace)
 
 
 # ------------------------------------------------------ allocating wrappers
@@ -255,6 +293,11 @@ def fit(X, C_init, max_iter: int = 300, tol: float = 0.0, relocate_empty: bool =
     info = torch.empty(3, dtype=torch.float64, device=X.device)
     kmeans_fit(X, C_init, max_iter, tol, KM_FIT_RELOCATE_EMPTY if relocate_empty else 0,
                C_out, labels, md, counts, info, stream=stream)
+    # info is read on the host: wait for the stream the fit ran on.
+    if stream is None or isinstance(stream, torch.cuda.Stream):
+        (stream or torch.cuda.current_stream(X.device)).synchronize()
+    else:
+        torch.cuda.synchronize(X.device)
     n_iter, inertia, shift = info.cpu().tolist()
     return {"centres": C_out, "labels": labels, "min_dist": md, "counts": counts,
             "n_iter": int(n_iter), "inertia": inertia, "shift": shift}

@@ -3,7 +3,11 @@
 ``python -m nearest_centroid_assignment_amd.calib`` prints one JSON line with
 * the fp32 MFMA rate of a kernel doing nothing but v_mfma_f32_32x32x2_f32 on
   four independent accumulators per wave, 8 waves per SIMD;
-* the bandwidth of a streaming 16-byte copy of a 2 GiB buffer.
+* the bandwidth of a streaming 16-byte copy of a 2 GiB buffer;
+* the bandwidth of a streaming 16-byte read of a 4 GiB buffer (every byte
+  read once; the ceiling of the update and k-means++ distance kernels, which
+  mostly read), at 1024 to 8192 blocks of 256 threads (the largest figure is
+  reported as ``read_gbps``).
 Both timed with HIP events on the launch stream (median of 5 after a warmup).
 The published peaks (157.3 TFLOP/s fp32 matrix, 8 TB/s HBM) stay the roofline;
 these numbers say how much of them the chip sustains here.
@@ -26,6 +30,9 @@ def lib():
     L = ctypes.CDLL(CALIB_PATH)
     L.km_calib_copy.restype = ctypes.c_int
     L.km_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.km_calib_read.restype = ctypes.c_int
+    L.km_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                ctypes.c_void_p]
     L.km_calib_mfma_f32.restype = ctypes.c_int
     L.km_calib_mfma_f32.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     return L
@@ -57,7 +64,8 @@ def copy_once(dst, src, nbytes, L=None):
         raise RuntimeError(f"km_calib_copy returned {rc}")
 
 
-def run(copy_bytes: int = 2 << 30, blocks: int = 256 * 8, iters: int = 20000) -> dict:
+def run(copy_bytes: int = 2 << 30, blocks: int = 256 * 8, iters: int = 20000,
+        read_bytes: int = 4 << 30) -> dict:
     import torch
 
     L = lib()
@@ -73,7 +81,21 @@ def run(copy_bytes: int = 2 << 30, blocks: int = 256 * 8, iters: int = 20000) ->
     src = torch.empty(copy_bytes, dtype=torch.uint8, device="cuda:0")
     dst = torch.empty_like(src)
     t_copy = _time(lambda: copy_once(dst, src, copy_bytes, L))
+    del src, dst
+    big = torch.ones(read_bytes // 4, dtype=torch.float32, device="cuda:0")
+    reads = {}
+    for rb in (256 * 4, 256 * 8, 256 * 16, 256 * 32):
+        sink = torch.empty(rb * 256, dtype=torch.float32, device="cuda:0")
+
+        def read():
+            if L.km_calib_read(big.data_ptr(), read_bytes, sink.data_ptr(), rb, stream) != 0:
+                raise RuntimeError("km_calib_read failed")
+
+        reads[rb] = read_bytes / (_time(read) * 1e-3) / 1e9
     return {
+        "read_gbps": max(reads.values()),
+        "read_gbps_by_blocks": reads,
+        "read_bytes": read_bytes,
         "mfma_f32_tflops": flop / (t_mfma * 1e-3) / 1e12,
         "mfma_ms": t_mfma,
         "copy_gbps": 2 * copy_bytes / (t_copy * 1e-3) / 1e9,

@@ -2,9 +2,12 @@
 //
 // Every entry point validates its arguments on the host before the first HIP
 // call, carves its sections out of the caller's workspace, and enqueues the
-// kernels on the caller's stream. Nothing here allocates, frees or
-// synchronises; the only global state is the assignment launcher's cached
-// compute-unit count per device.
+// kernels on the caller's stream. Nothing here allocates or frees device
+// memory. kmeans_fit is the one call that may wait on its stream: it reads the
+// 4-byte convergence flag back to the host between batches of iterations
+// (after the first 4, then every 8). Global state:
+// the assignment launcher's cached compute-unit count per device and the
+// per-device address of `scratch`.
 #include "../../include/kmeans_mi355x.h"
 #include "kernels.h"
 
@@ -25,7 +28,8 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 bool lloyd_fuses_norms(int64_t k, int64_t d) { return km::norm_parts(d) * 16 <= k; }
 
 struct Layout {
-    size_t cn = 0, tile_hist = 0, cnt = 0, seg_start = 0, perm = 0, big = 0, order = 0;
+    size_t cn = 0, tile_hist = 0, rank = 0, cnt = 0, seg_start = 0, perm = 0, big = 0, order = 0,
+           flags = 0;
     // kmeans_lloyd_step only
     size_t xn_part = 0;
     // kmeans_fit only
@@ -60,6 +64,10 @@ Layout layout(int64_t n, int64_t k, int64_t d, int op) {
         off += round_up(((size_t)k + 1) * sizeof(int));
         L.order = off;
         off += round_up((size_t)k * sizeof(int));
+        L.rank = off;
+        off += round_up((size_t)n * sizeof(unsigned short));
+        L.flags = off;  // scan completion counter, no-empty flag
+        off += round_up(2 * sizeof(int));
     }
     if (op == KM_OP_LLOYD && lloyd_fuses_norms(k, d)) {
         L.xn_part = off;
@@ -160,15 +168,23 @@ int check_alias(const Out *outs, int n_outs, const Out *ins, int n_ins, int inpl
 // squared distance (a separate pass computes ||x||^2 first); with min_dist
 // and !add_norm it receives only the best ||c||^2 - 2 x.c, and the caller
 // adds ||x||^2 later (the Lloyd step gets it from the update's reads of X).
+// With count_ws the finalize also takes the update's first counting step on
+// the labels it writes (per-tile histograms and ranks into count_ws). Every
+// kernel is gated by `gate` (the assignment's product kernel by gate.a).
 int run_assign(const float *X, const float *C, int64_t n, int64_t k, int64_t d, int64_t *labels,
-               float *min_dist, bool add_norm, float *cn, hipStream_t s) {
-    hipError_t e = km::launch_row_sqnorms(C, k, d, cn, s);
-    if (e == hipSuccess) e = km::launch_fill_keys((unsigned long long *)labels, n, s);
-    if (e == hipSuccess && min_dist && add_norm) e = km::launch_row_sqnorms(X, n, d, min_dist, s);
+               float *min_dist, bool add_norm, float *cn, const km::UpdateScratch *count_ws,
+               km::Gate gate, hipStream_t s) {
+    hipError_t e = km::launch_row_sqnorms(C, k, d, cn, s, gate);
+    if (e == hipSuccess) e = km::launch_fill_keys((unsigned long long *)labels, n, s, gate);
+    if (e == hipSuccess && min_dist && add_norm)
+        e = km::launch_row_sqnorms(X, n, d, min_dist, s, gate);
     if (e == hipSuccess)
-        e = km::launch_assign_tiles(X, C, cn, n, k, d, (unsigned long long *)labels, s);
+        e = km::launch_assign_tiles(X, C, cn, n, k, d, (unsigned long long *)labels, s, gate.a);
     if (e == hipSuccess)
-        e = km::launch_finalize((unsigned long long *)labels, min_dist, add_norm, n, s);
+        e = count_ws ? km::launch_finalize_rank_hist((unsigned long long *)labels, min_dist,
+                                                     add_norm, n, k, *count_ws, gate, s)
+                     : km::launch_finalize((unsigned long long *)labels, min_dist, add_norm, n, k,
+                                           s);
     return e == hipSuccess ? KM_OK : KM_ERR_HIP;
 }
 
@@ -180,8 +196,53 @@ km::UpdateScratch update_scratch(char *base, const Layout &L, int64_t n) {
     ws.perm = (int *)(base + L.perm);
     ws.big = (int *)(base + L.big);
     ws.order = (int *)(base + L.order);
+    ws.rank = (unsigned short *)(base + L.rank);
+    ws.done = (unsigned *)(base + L.flags);
+    ws.no_empty = (int *)(base + L.flags) + 1;
     ws.n_tiles = cdiv(n, km::kSortTileRows);
     return ws;
+}
+
+// Argument checks of the Lloyd step (workspace != NULL is checked by the
+// caller).
+int check_lloyd(const float *X, const float *C_old, int64_t n, int64_t k, int64_t d,
+                const int64_t *labels, const float *min_dist, const float *C_new,
+                const int64_t *counts, const void *workspace, size_t workspace_bytes) {
+    if (!shape_ok(n, k, d) || !grid_ok(n, k, d)) return KM_ERR_SHAPE;
+    if (!C_old || !C_new || !counts || (n > 0 && (!X || !labels))) return KM_ERR_NULL;
+    if (!aligned(X, 4) || !aligned(C_old, 4) || !aligned(labels, 8) || !aligned(min_dist, 4) ||
+        !aligned(C_new, 4) || !aligned(counts, 8))
+        return KM_ERR_ALIGN;
+    if (workspace_bytes < layout(n, k, d, KM_OP_LLOYD).total) return KM_ERR_WORKSPACE;
+    const Out outs[] = {{labels, n, 8},
+                        {min_dist, n, 4},
+                        {C_new, k * d, 4},
+                        {counts, k, 8},
+                        {workspace, workspace ? (int64_t)workspace_bytes : 0, 1}};
+    const Out ins[] = {{X, n * d, 4}, {C_old, k * d, 4}};
+    return check_alias(outs, 5, ins, 2, /*C_new*/ 2, /*C_old*/ 1);
+}
+
+// The Lloyd step's kernels, with the workspace sections at `base`.
+int run_lloyd(const float *X, const float *C_old, int64_t n, int64_t k, int64_t d,
+              int64_t *labels, float *min_dist, float *C_new, int64_t *counts, char *base,
+              hipStream_t s) {
+    const Layout L = layout(n, k, d, KM_OP_LLOYD);
+    // min_dist: the assignment leaves the best ||c||^2 - 2 x.c there; the
+    // update, which reads every row of X anyway, gathers the partial squared
+    // norms of the rows, and a last pass adds them: X is read twice per
+    // step (assignment and update), not three times.
+    float *xn_part =
+        (min_dist && lloyd_fuses_norms(k, d)) ? (float *)(base + L.xn_part) : nullptr;
+    const km::UpdateScratch ws = update_scratch(base, L, n);
+    if (n > 0) {
+        const int rc = run_assign(X, C_old, n, k, d, labels, min_dist, xn_part == nullptr,
+                                  (float *)(base + L.cn), &ws, km::Gate{}, s);
+        if (rc != KM_OK) return rc;
+    }
+    hipError_t e = km::launch_update(X, labels, C_old, n, k, d, C_new, counts, xn_part, n > 0, ws, s);
+    if (e == hipSuccess && xn_part) e = km::launch_add_norms(min_dist, xn_part, n, d, ws, s);
+    return e == hipSuccess ? KM_OK : KM_ERR_HIP;
 }
 
 }  // namespace
@@ -226,8 +287,8 @@ int kmeans_assign(const float *X, const float *C, int64_t n, int64_t k, int64_t 
     if (int rc = check_alias(outs, 3, ins, 2, -1, -1)) return rc;
     if (n == 0) return KM_OK;
     char *base = ws_base(workspace);
-    return run_assign(X, C, n, k, d, labels, min_dist, true, (float *)(base + L.cn),
-                      (hipStream_t)stream);
+    return run_assign(X, C, n, k, d, labels, min_dist, true, (float *)(base + L.cn), nullptr,
+                      km::Gate{}, (hipStream_t)stream);
 }
 
 int kmeans_update(const float *X, const int64_t *labels, const float *C_old, int64_t n, int64_t k,
@@ -246,45 +307,19 @@ int kmeans_update(const float *X, const int64_t *labels, const float *C_old, int
     if (int rc = check_alias(outs, 3, ins, 3, /*C_new*/ 0, /*C_old*/ 2)) return rc;
     char *base = ws_base(workspace);
     const hipError_t e = km::launch_update(X, labels, C_old, n, k, d, C_new, counts, nullptr,
-                                           update_scratch(base, L, n), (hipStream_t)stream);
+                                           false, update_scratch(base, L, n), (hipStream_t)stream);
     return e == hipSuccess ? KM_OK : KM_ERR_HIP;
 }
 
 int kmeans_lloyd_step(const float *X, const float *C_old, int64_t n, int64_t k, int64_t d,
                       int64_t *labels, float *min_dist, float *C_new, int64_t *counts,
                       void *workspace, size_t workspace_bytes, void *stream) {
-    if (!shape_ok(n, k, d) || !grid_ok(n, k, d)) return KM_ERR_SHAPE;
-    if (!C_old || !C_new || !counts || !workspace || (n > 0 && (!X || !labels)))
-        return KM_ERR_NULL;
-    if (!aligned(X, 4) || !aligned(C_old, 4) || !aligned(labels, 8) || !aligned(min_dist, 4) ||
-        !aligned(C_new, 4) || !aligned(counts, 8))
-        return KM_ERR_ALIGN;
-    const Layout L = layout(n, k, d, KM_OP_LLOYD);
-    if (workspace_bytes < L.total) return KM_ERR_WORKSPACE;
-    const Out outs[] = {{labels, n, 8},
-                        {min_dist, n, 4},
-                        {C_new, k * d, 4},
-                        {counts, k, 8},
-                        {workspace, (int64_t)workspace_bytes, 1}};
-    const Out ins[] = {{X, n * d, 4}, {C_old, k * d, 4}};
-    if (int rc = check_alias(outs, 5, ins, 2, /*C_new*/ 2, /*C_old*/ 1)) return rc;
-    hipStream_t s = (hipStream_t)stream;
-    char *base = ws_base(workspace);
-    // min_dist: the assignment leaves the best ||c||^2 - 2 x.c there; the
-    // update, which reads every row of X anyway, gathers the partial squared
-    // norms of the rows, and a last pass adds them: X is read twice per
-    // step (assignment and update), not three times.
-    float *xn_part =
-        (min_dist && lloyd_fuses_norms(k, d)) ? (float *)(base + L.xn_part) : nullptr;
-    if (n > 0) {
-        const int rc = run_assign(X, C_old, n, k, d, labels, min_dist, xn_part == nullptr,
-                                  (float *)(base + L.cn), s);
-        if (rc != KM_OK) return rc;
-    }
-    const km::UpdateScratch ws = update_scratch(base, L, n);
-    hipError_t e = km::launch_update(X, labels, C_old, n, k, d, C_new, counts, xn_part, ws, s);
-    if (e == hipSuccess && xn_part) e = km::launch_add_norms(min_dist, xn_part, n, d, ws, s);
-    return e == hipSuccess ? KM_OK : KM_ERR_HIP;
+    if (!workspace) return shape_ok(n, k, d) && grid_ok(n, k, d) ? KM_ERR_NULL : KM_ERR_SHAPE;
+    if (int rc = check_lloyd(X, C_old, n, k, d, labels, min_dist, C_new, counts, workspace,
+                             workspace_bytes))
+        return rc;
+    return run_lloyd(X, C_old, n, k, d, labels, min_dist, C_new, counts, ws_base(workspace),
+                     (hipStream_t)stream);
 }
 
 int kmeans_fit(const float *X, const float *C_init, int64_t n, int64_t k, int64_t d,
@@ -319,36 +354,62 @@ int kmeans_fit(const float *X, const float *C_init, int64_t n, int64_t k, int64_
     rs.sort_idx = (int *)(base + L.sort_idx);
     rs.num_empty = scalars;
     int *converged = scalars + 1;
+    int *iterations = scalars + 2;
     double *shift_partial = (double *)(base + L.shift_partial);
     const bool relocate = (flags & KM_FIT_RELOCATE_EMPTY) != 0;
+    // Every kernel of an iteration returns at once once the converged flag
+    // is set, so iterations are enqueued in batches and the host reads the
+    // flag only between batches (a call of at most kFirstBatch iterations
+    // never waits).
+    const km::Gate loop{converged, nullptr};
 
-    hipError_t e = km::launch_copy_f32(C_out, C_init, k * d, s);
-    int64_t n_iter = 0;
-    for (int64_t it = 0; it < max_iter && e == hipSuccess; ++it) {
-        if (n > 0 && run_assign(X, C_out, n, k, d, labels, nullptr, true, cn, s) != KM_OK)
-            return KM_ERR_HIP;
-        e = km::launch_count(labels, n, k, d, counts, relocate ? rs.num_empty : nullptr, ws, s);
+    auto iteration = [&]() -> hipError_t {
+        hipError_t e = hipSuccess;
+        if (n > 0) {
+            if (run_assign(X, C_out, n, k, d, labels, nullptr, true, cn, &ws, loop, s) != KM_OK)
+                return hipErrorLaunchFailure;
+        } else {
+            e = km::launch_rank_hist(labels, n, k, ws, loop, s);
+        }
+        if (e == hipSuccess)
+            e = km::launch_scan(n, k, d, counts, relocate ? rs.num_empty : nullptr, ws, loop, s);
         if (e == hipSuccess && relocate) {
-            e = km::launch_relocate(X, C_out, labels, n, k, d, rs, ws, s);
-            if (e == hipSuccess) e = km::launch_count(labels, n, k, d, counts, nullptr, ws, s);
+            e = km::launch_relocate(X, C_out, labels, n, k, d, rs, ws, s, loop);
+            // Count again only if a cluster was empty (something moved).
+            if (e == hipSuccess)
+                e = km::launch_count(labels, n, k, d, counts, nullptr, ws,
+                                     km::Gate{converged, ws.no_empty}, s);
         }
         if (e == hipSuccess)
             e = km::launch_group_and_mean(X, labels, C_out, n, k, d, C_out, shift_partial, nullptr,
-                                          ws, s);
+                                          ws, loop, s);
         if (e == hipSuccess)
-            e = km::launch_shift(shift_partial, km::mean_blocks(k, d), tol, info + 2, converged, s);
+            e = km::launch_shift(shift_partial, km::mean_blocks(k, d), tol, info + 2, converged,
+                                 iterations, s);
+        return e;
+    };
+
+    constexpr int64_t kFirstBatch = 4, kBatch = 8;
+    hipError_t e = km::launch_copy_f32(C_out, C_init, k * d, s);
+    if (e == hipSuccess) e = km::launch_zero_i32(scalars, 4, s);
+    for (int64_t enqueued = 0; e == hipSuccess && enqueued < max_iter;) {
+        const int64_t want = enqueued == 0 ? kFirstBatch : kBatch;
+        const int64_t batch = want < max_iter - enqueued ? want : max_iter - enqueued;
+        for (int64_t b = 0; b < batch && e == hipSuccess; ++b) e = iteration();
+        enqueued += batch;
+        if (e != hipSuccess || enqueued >= max_iter) break;
         int host_converged = 0;
-        if (e == hipSuccess)
-            e = hipMemcpyAsync(&host_converged, converged, sizeof(int), hipMemcpyDeviceToHost, s);
+        e = hipMemcpyAsync(&host_converged, converged, sizeof(int), hipMemcpyDeviceToHost, s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
-        n_iter = it + 1;
-        if (host_converged) break;
+        if (e == hipSuccess && host_converged) break;
     }
-    if (e == hipSuccess && n > 0 && run_assign(X, C_out, n, k, d, labels, md, true, cn, s) != KM_OK)
+    if (e == hipSuccess && n > 0 &&
+        run_assign(X, C_out, n, k, d, labels, md, true, cn, &ws, km::Gate{}, s) != KM_OK)
         return KM_ERR_HIP;
-    if (e == hipSuccess) e = km::launch_count(labels, n, k, d, counts, nullptr, ws, s);
+    if (e == hipSuccess && n <= 0) e = km::launch_rank_hist(labels, n, k, ws, km::Gate{}, s);
+    if (e == hipSuccess) e = km::launch_scan(n, k, d, counts, nullptr, ws, km::Gate{}, s);
     if (e == hipSuccess) e = km::launch_inertia(md, n, info + 1, s);
-    if (e == hipSuccess) e = km::launch_store_f64(info, (double)n_iter, s);
+    if (e == hipSuccess) e = km::launch_store_count(info, iterations, s);
     return e == hipSuccess ? KM_OK : KM_ERR_HIP;
 }
 

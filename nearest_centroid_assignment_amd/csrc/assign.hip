@@ -62,7 +62,8 @@ __device__ __forceinline__ unsigned long long pack_key(float dist, uint32_t idx)
 template <bool kVec>
 __global__ __launch_bounds__(256) void row_sqnorms_kernel(const float *__restrict__ A,
                                                           int64_t rows, int64_t d,
-                                                          float *__restrict__ out) {
+                                                          float *__restrict__ out, Gate gate) {
+    if (gated(gate)) return;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
@@ -81,7 +82,8 @@ __global__ __launch_bounds__(256) void row_sqnorms_kernel(const float *__restric
 }
 
 __global__ __launch_bounds__(256) void fill_keys_kernel(unsigned long long *__restrict__ keys,
-                                                        int64_t n) {
+                                                        int64_t n, Gate gate) {
+    if (gated(gate)) return;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
         keys[i] = ~0ull;
@@ -256,8 +258,9 @@ template <class Cfg, int Mode, int MinWaves, bool kPersistent>
 __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
     const float *__restrict__ X, const float *__restrict__ C, const float *__restrict__ cn,
     int64_t n, int64_t k, int64_t d, int tiles_m, int tiles_n,
-    unsigned long long *__restrict__ keys) {
+    unsigned long long *__restrict__ keys, const int *__restrict__ stop) {
     __shared__ float lds[2][Cfg::kRows][Cfg::LDK];
+    if (stop != nullptr && *stop != 0) return;  // kmeans_fit: converged
 
     // Blocks are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8).
     // The tiles are renumbered so that each XCD gets one contiguous range of
@@ -413,9 +416,14 @@ __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
 #pragma unroll
     for (int nb = 0; nb < Cfg::NB; ++nb) {
         // Rows are visited in increasing centroid index and only a strictly
-        // smaller distance replaces the winner: lowest index on ties.
+        // smaller distance replaces the winner: lowest index on ties. The
+        // winner starts as the lane's first (lowest) valid centroid at +inf,
+        // so a lane whose candidates are all +inf or NaN (a norm that
+        // overflows float32) still names a centroid in [0, k): +inf ties go
+        // to the lowest index like any other tie, and NaN never wins.
+        const int64_t m_first = m0 + wm * Cfg::MB * 32 + 4 * (lane >> 5);
         float best = __builtin_inff();
-        uint32_t bidx = 0xffffffffu;
+        uint32_t bidx = m_first < k ? (uint32_t)m_first : 0xffffffffu;
 #pragma unroll
         for (int mb = 0; mb < Cfg::MB; ++mb)
 #pragma unroll
@@ -557,9 +565,10 @@ __device__ __forceinline__ void dma_compute(const float *buf, float *dst, __amdg
 __global__ __launch_bounds__(dma::NT, 2) void assign_dma_kernel(
     const float *__restrict__ X, const float *__restrict__ C, const float *__restrict__ cn,
     int64_t n, int64_t k, int64_t d, int tiles_m, int tiles_n,
-    unsigned long long *__restrict__ keys) {
+    unsigned long long *__restrict__ keys, const int *__restrict__ stop) {
     __shared__ __align__(16) float buf0[dma::ROWS * dma::BK];
     __shared__ __align__(16) float buf1[dma::ROWS * dma::BK];
+    if (stop != nullptr && *stop != 0) return;  // kmeans_fit: converged
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % dma::WM, wn = wave / dma::WM;
@@ -629,12 +638,15 @@ __global__ __launch_bounds__(dma::NT, 2) void assign_dma_kernel(
         // Epilogue, as in assign_tile_kernel, one block of 32 centroid rows at
         // a time (16 norms live instead of 64); rows are still visited in
         // increasing index for each sample, strict less-than keeps the lowest.
+        // The winner starts as the lane's first centroid at +inf (as in
+        // assign_tile_kernel: all-+inf or NaN candidates still give a valid
+        // index, the lowest one).
         float best[dma::NB];
         uint32_t bidx[dma::NB];
 #pragma unroll
         for (int nb = 0; nb < dma::NB; ++nb) {
             best[nb] = __builtin_inff();
-            bidx[nb] = 0xffffffffu;
+            bidx[nb] = (uint32_t)(m0 + wm * dma::MB * 32 + 4 * (lane >> 5));
         }
 #pragma unroll
         for (int mb = 0; mb < dma::MB; ++mb) {
@@ -672,9 +684,12 @@ using Tile256x128 = TileCfg<4, 2, 2, 2, 32>;  // 512 threads, 108 KiB LDS, 1 blo
 using Tile128x128 = TileCfg<2, 2, 2, 2, 16>;  // 256 threads, 40 KiB LDS, 3 blocks per CU
 using Tile64x64 = TileCfg<2, 2, 1, 1, 32>;    // 256 threads, 36 KiB LDS, small problems
 
+// The epilogues always name a centroid in [0, k) (see there); the clamp keeps
+// every later index into C, the counts and the grouping in bounds even if a
+// key were never lowered.
 __global__ __launch_bounds__(256) void finalize_kernel(unsigned long long *__restrict__ keys,
                                                        float *__restrict__ min_dist,
-                                                       bool add_norm, int64_t n) {
+                                                       bool add_norm, int64_t n, int64_t k) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
         const unsigned long long key = keys[i];
@@ -682,7 +697,8 @@ __global__ __launch_bounds__(256) void finalize_kernel(unsigned long long *__res
             const float partial = unordered_bits((uint32_t)(key >> 32));
             min_dist[i] = add_norm ? fmaxf(min_dist[i] + partial, 0.0f) : partial;
         }
-        keys[i] = key & 0xffffffffull;  // the int64 label
+        const unsigned long long idx = key & 0xffffffffull;
+        keys[i] = idx < (unsigned long long)k ? idx : 0ull;  // the int64 label
     }
 }
 
@@ -703,19 +719,19 @@ inline unsigned grid_stride_blocks(int64_t n) {
 
 
 hipError_t launch_row_sqnorms(const float *A, int64_t rows, int64_t d, float *out,
-                              hipStream_t stream) {
+                              hipStream_t stream, Gate gate) {
     if (rows <= 0) return hipSuccess;
     const unsigned blocks = (unsigned)cdiv(rows, 4);
     if (vec_ok(A, d))
-        row_sqnorms_kernel<true><<<blocks, 256, 0, stream>>>(A, rows, d, out);
+        row_sqnorms_kernel<true><<<blocks, 256, 0, stream>>>(A, rows, d, out, gate);
     else
-        row_sqnorms_kernel<false><<<blocks, 256, 0, stream>>>(A, rows, d, out);
+        row_sqnorms_kernel<false><<<blocks, 256, 0, stream>>>(A, rows, d, out, gate);
     return hipGetLastError();
 }
 
-hipError_t launch_fill_keys(unsigned long long *keys, int64_t n, hipStream_t stream) {
+hipError_t launch_fill_keys(unsigned long long *keys, int64_t n, hipStream_t stream, Gate gate) {
     if (n <= 0) return hipSuccess;
-    fill_keys_kernel<<<grid_stride_blocks(n), 256, 0, stream>>>(keys, n);
+    fill_keys_kernel<<<grid_stride_blocks(n), 256, 0, stream>>>(keys, n, gate);
     return hipGetLastError();
 }
 
@@ -739,7 +755,8 @@ int device_cus() {
 
 template <class Cfg, int MinWaves>
 hipError_t launch_tiles_cfg(const float *X, const float *C, const float *cn, int64_t n, int64_t k,
-                            int64_t d, unsigned long long *keys, hipStream_t stream) {
+                            int64_t d, unsigned long long *keys, const int *stop,
+                            hipStream_t stream) {
     const int tiles_m = (int)cdiv(k, Cfg::BM);
     const int tiles_n = (int)cdiv(n, Cfg::BN);
     const int64_t tiles = (int64_t)tiles_m * tiles_n;
@@ -755,19 +772,19 @@ hipError_t launch_tiles_cfg(const float *X, const float *C, const float *cn, int
         if (full && cus >= 8) {
             const unsigned pblocks = (unsigned)(tiles < cus ? tiles : cus);
             assign_tile_kernel<Cfg, kFull, MinWaves, true><<<pblocks, Cfg::kThreads, 0, stream>>>(
-                X, C, cn, n, k, d, tiles_m, tiles_n, keys);
+                X, C, cn, n, k, d, tiles_m, tiles_n, keys, stop);
             return hipGetLastError();
         }
     }
     if (full)
         assign_tile_kernel<Cfg, kFull, MinWaves, false><<<blocks, Cfg::kThreads, 0, stream>>>(
-            X, C, cn, n, k, d, tiles_m, tiles_n, keys);
+            X, C, cn, n, k, d, tiles_m, tiles_n, keys, stop);
     else if (vec)
         assign_tile_kernel<Cfg, kVec, MinWaves, false><<<blocks, Cfg::kThreads, 0, stream>>>(
-            X, C, cn, n, k, d, tiles_m, tiles_n, keys);
+            X, C, cn, n, k, d, tiles_m, tiles_n, keys, stop);
     else
         assign_tile_kernel<Cfg, kScalar, MinWaves, false><<<blocks, Cfg::kThreads, 0, stream>>>(
-            X, C, cn, n, k, d, tiles_m, tiles_n, keys);
+            X, C, cn, n, k, d, tiles_m, tiles_n, keys, stop);
     return hipGetLastError();
 }
 
@@ -818,7 +835,7 @@ int64_t assign_grid_threads(int64_t n, int64_t k, int64_t d) {
 
 hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, int64_t n,
                                int64_t k, int64_t d, unsigned long long *keys,
-                               hipStream_t stream) {
+                               hipStream_t stream, const int *stop) {
     if (n <= 0) return hipSuccess;
     const char *tile = assign_tile_name(n, k, d);
     if (!strcmp(tile, "256x256")) {
@@ -829,24 +846,25 @@ hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, 
             const int tm = (int)(k / dma::BM), tn = (int)(n / dma::BN);
             const int64_t tiles = (int64_t)tm * tn;
             const unsigned blocks = (unsigned)(tiles < cus ? tiles : cus);
-            assign_dma_kernel<<<blocks, dma::NT, 0, stream>>>(X, C, cn, n, k, d, tm, tn, keys);
+            assign_dma_kernel<<<blocks, dma::NT, 0, stream>>>(X, C, cn, n, k, d, tm, tn, keys,
+                                                              stop);
             return hipGetLastError();
         }
-        return launch_tiles_cfg<Tile128x256, 2>(X, C, cn, n, k, d, keys, stream);
+        return launch_tiles_cfg<Tile128x256, 2>(X, C, cn, n, k, d, keys, stop, stream);
     }
     if (!strcmp(tile, "256x128"))
-        return launch_tiles_cfg<Tile256x128, 2>(X, C, cn, n, k, d, keys, stream);
+        return launch_tiles_cfg<Tile256x128, 2>(X, C, cn, n, k, d, keys, stop, stream);
     if (!strcmp(tile, "128x128"))
-        return launch_tiles_cfg<Tile128x128, 3>(X, C, cn, n, k, d, keys, stream);
+        return launch_tiles_cfg<Tile128x128, 3>(X, C, cn, n, k, d, keys, stop, stream);
     if (!strcmp(tile, "128x256"))
-        return launch_tiles_cfg<Tile128x256, 2>(X, C, cn, n, k, d, keys, stream);
-    return launch_tiles_cfg<Tile64x64, 4>(X, C, cn, n, k, d, keys, stream);
+        return launch_tiles_cfg<Tile128x256, 2>(X, C, cn, n, k, d, keys, stop, stream);
+    return launch_tiles_cfg<Tile64x64, 4>(X, C, cn, n, k, d, keys, stop, stream);
 }
 
 hipError_t launch_finalize(unsigned long long *keys, float *min_dist, bool add_norm, int64_t n,
-                           hipStream_t stream) {
+                           int64_t k, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
-    finalize_kernel<<<grid_stride_blocks(n), 256, 0, stream>>>(keys, min_dist, add_norm, n);
+    finalize_kernel<<<grid_stride_blocks(n), 256, 0, stream>>>(keys, min_dist, add_norm, n, k);
     return hipGetLastError();
 }
 

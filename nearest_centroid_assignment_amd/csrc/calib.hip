@@ -1,8 +1,11 @@
 // calib.hip - calibration kernels for the measurements (not part of the k-means
 // path): a streaming copy of known size, whose HBM counters give the scale
 // factor of the FETCH_SIZE / WRITE_SIZE counters and the attainable copy
-// bandwidth, and a loop of nothing but fp32 MFMAs, which gives the attainable
-// fp32 matrix rate under the clocks the chip actually holds.
+// bandwidth; a streaming read (every byte read once, one float written per
+// thread), which gives the attainable read bandwidth, the ceiling of kernels
+// that mostly read (the update, the k-means++ distances); and a loop of nothing
+// but fp32 MFMAs, which gives the attainable fp32 matrix rate under the clocks
+// the chip actually holds.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -18,6 +21,34 @@ __global__ __launch_bounds__(256) void copy_kernel(f32x4 *__restrict__ dst,
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
         dst[i] = src[i];
+}
+
+// Each thread sums its share of the buffer (8 independent 16-byte loads in
+// flight per loop trip) and writes one float, so the reads cannot be dropped.
+__global__ __launch_bounds__(256) void read_kernel(const f32x4 *__restrict__ src, int64_t n,
+                                                   float *__restrict__ out) {
+    constexpr int U = 8;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    float a[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) a[u] = 0.f;
+    int64_t i = tid;
+    for (; i + (U - 1) * stride < n; i += U * stride) {
+        f32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < U; ++u) a[u] += (v[u].x + v[u].y) + (v[u].z + v[u].w);
+    }
+    for (; i < n; i += stride) {
+        const f32x4 v = src[i];
+        a[0] += (v.x + v.y) + (v.z + v.w);
+    }
+    float t = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) t += a[u];
+    out[tid] = t;
 }
 
 // Four independent 32x32 accumulators per wave; iters x 4 MFMAs per wave.
@@ -53,6 +84,13 @@ int km_calib_copy(void *dst, const void *src, size_t bytes, void *stream) {
     int64_t blocks = (n + 255) / 256;
     if (blocks > 256 * 32) blocks = 256 * 32;
     copy_kernel<<<(unsigned)blocks, 256, 0, (hipStream_t)stream>>>((f32x4 *)dst, (const f32x4 *)src, n);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+int km_calib_read(const void *src, size_t bytes, float *out, int blocks, void *stream) {
+    if (!src || !out || blocks < 1 || bytes % 16 != 0 || (uintptr_t)src % 16) return -1;
+    read_kernel<<<(unsigned)blocks, 256, 0, (hipStream_t)stream>>>((const f32x4 *)src,
+                                                                   (int64_t)(bytes / 16), out);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

@@ -19,6 +19,7 @@
 //                        ascending, and relabel the r-th to E[r]
 //   shift_kernel         one block: centre shift = sum of the update's
 //                        per-block partials, in block order; converged flag
+//                        and the count of iterations run
 //   inertia_kernel       one block: sum of the final squared distances
 // Every reduction runs in a fixed order, so results are deterministic.
 #include "kernels.h"
@@ -31,8 +32,8 @@ __global__ __launch_bounds__(256) void reloc_dist_kernel(const float *__restrict
                                                          const int64_t *__restrict__ labels,
                                                          int64_t n, int64_t d,
                                                          const int *__restrict__ num_empty,
-                                                         double *__restrict__ dist) {
-    if (*num_empty == 0) return;  // uniform: nothing to relocate
+                                                         double *__restrict__ dist, Gate gate) {
+    if (gated(gate) || *num_empty == 0) return;  // uniform: nothing to relocate
     const int lane = threadIdx.x & 63;
     for (int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); i < n;
          i += (int64_t)gridDim.x * 4) {
@@ -83,14 +84,14 @@ constexpr int kSelWaves = 16;  // reloc_select_kernel: 1024 threads
 __global__ __launch_bounds__(1024) void reloc_select_kernel(
     const int *__restrict__ cnt, int64_t k, int64_t n, const double *__restrict__ dist,
     const int *__restrict__ num_empty, int *__restrict__ empty, unsigned long long *sort_key,
-    int *sort_idx, int64_t sort_cap, int64_t *__restrict__ labels) {
+    int *sort_idx, int64_t sort_cap, int64_t *__restrict__ labels, Gate gate) {
     __shared__ int lds16[16];
     __shared__ int hist[kSelWaves][256];
     __shared__ int bins[256];
     __shared__ int sel_digit, sel_above;
     __shared__ int wave_gt[kSelWaves], wave_eq[kSelWaves];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (*num_empty == 0) return;
+    if (gated(gate) || *num_empty == 0) return;
     // E: empty clusters in increasing index.
     int n_empty = 0;
     for (int64_t base = 0; base < k; base += 1024) {
@@ -256,17 +257,23 @@ __device__ double block_sum(double v, double *lds16) {
     return t;
 }
 
+// One iteration's convergence check; once *converged is set it does nothing
+// (kmeans_fit enqueues iterations in batches, and the ones after convergence
+// are skipped by every kernel).
 __global__ __launch_bounds__(1024) void shift_kernel(const double *__restrict__ partial,
                                                      int64_t blocks, double tol,
                                                      double *__restrict__ shift_out,
-                                                     int *__restrict__ converged) {
+                                                     int *__restrict__ converged,
+                                                     int *__restrict__ iterations) {
     __shared__ double lds16[16];
+    if (*converged != 0) return;
     double s = 0.0;
     for (int64_t b = threadIdx.x; b < blocks; b += 1024) s += partial[b];
     const double tot = block_sum(s, lds16);
     if (threadIdx.x == 0) {
         *shift_out = tot;
         *converged = tot <= tol;
+        *iterations += 1;
     }
 }
 
@@ -287,7 +294,13 @@ __global__ __launch_bounds__(256) void copy_f32_kernel(float *__restrict__ dst,
         dst[i] = src[i];
 }
 
-__global__ void store_f64_kernel(double *dst, double v) { *dst = v; }
+__global__ void store_count_kernel(double *dst, const int *count) { *dst = (double)*count; }
+
+__global__ __launch_bounds__(256) void zero_i32_kernel(int *__restrict__ p, int64_t count) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride)
+        p[i] = 0;
+}
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -302,21 +315,21 @@ int64_t reloc_sort_cap(int64_t n, int64_t k) {
 
 hipError_t launch_relocate(const float *X, const float *C_old, int64_t *labels, int64_t n,
                            int64_t k, int64_t d, const RelocScratch &rs, const UpdateScratch &ws,
-                           hipStream_t stream) {
+                           hipStream_t stream, Gate gate) {
     if (n <= 0) return hipSuccess;
     int64_t b = cdiv(n, 4);
     if (b > 65536) b = 65536;
     reloc_dist_kernel<<<(unsigned)b, 256, 0, stream>>>(X, C_old, labels, n, d, rs.num_empty,
-                                                       rs.dist);
+                                                       rs.dist, gate);
     reloc_select_kernel<<<1, 1024, 0, stream>>>(ws.cnt, k, n, rs.dist, rs.num_empty, rs.empty,
                                                 rs.sort_key, rs.sort_idx, reloc_sort_cap(n, k),
-                                                labels);
+                                                labels, gate);
     return hipGetLastError();
 }
 
 hipError_t launch_shift(const double *partial, int64_t blocks, double tol, double *shift_out,
-                        int *converged, hipStream_t stream) {
-    shift_kernel<<<1, 1024, 0, stream>>>(partial, blocks, tol, shift_out, converged);
+                        int *converged, int *iterations, hipStream_t stream) {
+    shift_kernel<<<1, 1024, 0, stream>>>(partial, blocks, tol, shift_out, converged, iterations);
     return hipGetLastError();
 }
 
@@ -333,8 +346,16 @@ hipError_t launch_copy_f32(float *dst, const float *src, int64_t count, hipStrea
     return hipGetLastError();
 }
 
-hipError_t launch_store_f64(double *dst, double v, hipStream_t stream) {
-    store_f64_kernel<<<1, 1, 0, stream>>>(dst, v);
+hipError_t launch_store_count(double *dst, const int *count, hipStream_t stream) {
+    store_count_kernel<<<1, 1, 0, stream>>>(dst, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_i32(int *p, int64_t count, hipStream_t stream) {
+    if (count <= 0) return hipSuccess;
+    int64_t b = cdiv(count, 256);
+    if (b > 1024) b = 1024;
+    zero_i32_kernel<<<(unsigned)b, 256, 0, stream>>>(p, count);
     return hipGetLastError();
 }
 

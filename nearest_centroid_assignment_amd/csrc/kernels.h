@@ -12,36 +12,63 @@ constexpr int64_t kSortTileRows = 1024;
 
 // Workspace sections used by the update (all device pointers, caller-owned).
 struct UpdateScratch {
-    int *tile_hist;  // k * n_tiles: per (cluster, row tile) counts, then their
-                     // exclusive prefix over tiles
-    int *cnt;        // k: rows per cluster
-    int *seg_start;  // k: first position of each cluster in perm
-    int *perm;       // n: row indices grouped by cluster, increasing within one
-    int *big;        // k + 1: the number of clusters with more than 64 rows, then
-                     // their indices in increasing order
-    int *order;      // k: the other clusters, grouped by load rounds (most first)
-    int64_t n_tiles; // ceil(n / kSortTileRows)
+    int *tile_hist;          // n_tiles * k: [b * k + j] = rows of tile b with label j,
+                             // then their exclusive prefix over tiles
+    unsigned short *rank;    // n: rank of a row among the rows of its tile with the
+                             // same label and a lower index
+    int *cnt;                // k: rows per cluster
+    int *seg_start;          // k: first position of each cluster in perm
+    int *perm;               // n: row indices grouped by cluster, increasing within one
+    int *big;                // k + 1: the number of clusters with more than the split
+                             // size, then their indices in increasing order
+    int *order;              // k: the other clusters, grouped by load rounds (most first)
+    unsigned *done;          // 1: blocks of the scan kernel that have finished
+    int *no_empty;           // 1: set by a count that reports empty clusters: 1 when
+                             // there are none
+    int64_t n_tiles;         // ceil(n / kSortTileRows)
 };
+
+// A kernel given a Gate returns at once, in every block, when either flag it
+// points to is non-zero (NULL pointers count as zero). kmeans_fit gates the
+// kernels of iterations enqueued after convergence, and the recount after a
+// relocation that moved nothing.
+struct Gate {
+    const int *a = nullptr;
+    const int *b = nullptr;
+};
+
+__device__ __forceinline__ bool gated(const Gate &g) {
+    return (g.a != nullptr && *g.a != 0) || (g.b != nullptr && *g.b != 0);
+}
+
+// Inverse of the assignment's order-preserving map of a float to 32 bits
+// (the distance half of a packed key).
+__device__ __forceinline__ float key_distance(unsigned long long key) {
+    const uint32_t u = (uint32_t)(key >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
 
 // out[r] = sum_t A[r, t]^2 for r < rows (float64 accumulation, rounded once).
 hipError_t launch_row_sqnorms(const float *A, int64_t rows, int64_t d, float *out,
-                              hipStream_t stream);
+                              hipStream_t stream, Gate gate = Gate{});
 
 // keys[i] = UINT64_MAX for i < n (the identity of the packed-key minimum).
-hipError_t launch_fill_keys(unsigned long long *keys, int64_t n, hipStream_t stream);
+hipError_t launch_fill_keys(unsigned long long *keys, int64_t n, hipStream_t stream,
+                            Gate gate = Gate{});
 
 // Fused Gram product + argmin epilogue: for every sample, atomically lowers
 // keys[i] to the packed (distance', index) of its best centroid per tile.
+// With stop != NULL every block returns at once if *stop is non-zero.
 hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, int64_t n,
                                int64_t k, int64_t d, unsigned long long *keys,
-                               hipStream_t stream);
+                               hipStream_t stream, const int *stop = nullptr);
 
 // Turns packed keys into int64 labels in place. min_dist (nullable): with
 // add_norm it holds ||x_i||^2 on entry and the clamped full squared distance
 // on exit; without, it receives the best ||c||^2 - 2 x.c, to which
 // launch_add_norms later adds the norms gathered by the update.
 hipError_t launch_finalize(unsigned long long *keys, float *min_dist, bool add_norm, int64_t n,
-                           hipStream_t stream);
+                           int64_t k, hipStream_t stream);
 
 // Clusters of more rows than this are summed in parts by the mean kernel;
 // smaller ones by one wave in sample order: 64, or 128 when X has at least
@@ -50,11 +77,29 @@ hipError_t launch_finalize(unsigned long long *keys, float *min_dist, bool add_n
 // critical path, while the split's per-part barrier and merge are not).
 int split_rows(int64_t n, int64_t k, int64_t d);
 
-// Counting phase of the update: per-cluster sizes (ws.cnt, counts) and the
-// segment starts, and the split of the clusters by split_rows(n, k, d);
-// num_empty (nullable) receives the number of empty clusters.
+// Counting phase of the update, first step, on labels: per tile of
+// kSortTileRows rows, the histogram column tile_hist[b * k + .] and the
+// stable ranks of the rows. Rows with a label outside [0, k) are skipped.
+hipError_t launch_rank_hist(const int64_t *labels, int64_t n, int64_t k, const UpdateScratch &ws,
+                            Gate gate, hipStream_t stream);
+
+// The same step fused with the assignment's finalize: packed keys become int64
+// labels in place (and min_dist as in launch_finalize), then the histogram
+// and the ranks of those labels.
+hipError_t launch_finalize_rank_hist(unsigned long long *keys, float *min_dist, bool add_norm,
+                                     int64_t n, int64_t k, const UpdateScratch &ws, Gate gate,
+                                     hipStream_t stream);
+
+// Counting phase, second step (after one of the two above): per-cluster
+// sizes (ws.cnt, counts), segment starts, the tiles' prefixes, and the split
+// of the clusters by split_rows(n, k, d); num_empty (nullable) receives the
+// number of empty clusters and ws.no_empty whether there are none.
+hipError_t launch_scan(int64_t n, int64_t k, int64_t d, int64_t *counts, int *num_empty,
+                       const UpdateScratch &ws, Gate gate, hipStream_t stream);
+
+// Both steps on labels.
 hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t d, int64_t *counts,
-                        int *num_empty, const UpdateScratch &ws, hipStream_t stream);
+                        int *num_empty, const UpdateScratch &ws, Gate gate, hipStream_t stream);
 
 // Second phase: stable grouping of rows by label and the float64 segmented
 // sums and means (old centre kept for an empty cluster). If shift_partial is
@@ -67,17 +112,18 @@ hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t d, 
 hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const float *C_old,
                                  int64_t n, int64_t k, int64_t d, float *C_new,
                                  double *shift_partial, float *xn_part, const UpdateScratch &ws,
-                                 hipStream_t stream);
+                                 Gate gate, hipStream_t stream);
 int64_t mean_blocks(int64_t k, int64_t d);
 // Column chunks of the mean kernel: partial norms per row.
 int64_t norm_parts(int64_t d);
 
 // The whole update: counts, stable grouping of rows by label, segmented sums
 // in float64 and the mean (old centre kept for empty clusters); xn_part as in
-// launch_group_and_mean.
+// launch_group_and_mean. With counted = true the first counting step has
+// already run (launch_finalize_rank_hist on these labels).
 hipError_t launch_update(const float *X, const int64_t *labels, const float *C_old, int64_t n,
                          int64_t k, int64_t d, float *C_new, int64_t *counts, float *xn_part,
-                         const UpdateScratch &ws, hipStream_t stream);
+                         bool counted, const UpdateScratch &ws, hipStream_t stream);
 
 // min_dist[i] = max(0, ||x_i||^2 + min_dist[i]), ||x_i||^2 the float64 sum of
 // the row's partial norms from the update (xn_part and the grouping ws.perm
@@ -101,18 +147,24 @@ int64_t reloc_sort_cap(int64_t n, int64_t k);
 // taken into ws.cnt with num_empty set): relabels the moved samples.
 hipError_t launch_relocate(const float *X, const float *C_old, int64_t *labels, int64_t n,
                            int64_t k, int64_t d, const RelocScratch &rs, const UpdateScratch &ws,
-                           hipStream_t stream);
+                           hipStream_t stream, Gate gate = Gate{});
 
-// shift_out = sum of the first `blocks` partials (fixed order); converged =
-// (shift_out <= tol).
+// Unless *converged is already set (then nothing happens): shift_out = sum of
+// the first `blocks` partials (fixed order); converged = (shift_out <= tol);
+// ++*iterations.
 hipError_t launch_shift(const double *partial, int64_t blocks, double tol, double *shift_out,
-                        int *converged, hipStream_t stream);
+                        int *converged, int *iterations, hipStream_t stream);
+
+// p[0 .. count) = 0 (a kernel, so that the call can be captured in a graph).
+hipError_t launch_zero_i32(int *p, int64_t count, hipStream_t stream);
+
+// *dst = (double)*count.
+hipError_t launch_store_count(double *dst, const int *count, hipStream_t stream);
 
 // out = sum of min_dist[0 .. n) in float64 (fixed order).
 hipError_t launch_inertia(const float *min_dist, int64_t n, double *out, hipStream_t stream);
 
 hipError_t launch_copy_f32(float *dst, const float *src, int64_t count, hipStream_t stream);
-hipError_t launch_store_f64(double *dst, double v, hipStream_t stream);
 
 // Workspace sections of the k-means++ seeding (device pointers).
 struct PPScratch {

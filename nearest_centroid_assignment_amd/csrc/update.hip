@@ -7,11 +7,16 @@
 // by label with a stable counting sort, then every (cluster, column chunk)
 // block adds its cluster's rows in increasing sample order:
 //
-//   tile_hist_kernel     counts per (cluster, tile of 1024 rows)
-//   tile_scan_kernel     exclusive prefix over tiles, per cluster; cluster sizes
-//   cluster_scan_kernel  exclusive prefix over clusters -> segment starts; counts
+//   rank_hist_kernel     per tile of 1024 rows: every row's rank among the
+//                        tile's rows with the same label (stable), and the
+//                        tile's histogram column; in a Lloyd step fused with
+//                        the assignment's finalize (keys -> labels)
+//   scan_kernel          per cluster: exclusive prefix over tiles, cluster
+//                        size; the last block to finish: exclusive prefix
+//                        over clusters -> segment starts, counts, and the
+//                        lists the mean kernel schedules by
 //   scatter_kernel       perm[segment start + rows of the cluster in earlier
-//                        tiles + rank within the tile] = row   (stable)
+//                        tiles + rank] = row   (stable)
 //   segment_mean_kernel  float64 sums over each segment, coalesced row chunks,
 //                        then the mean rounded once to float32, or the old
 //                        centre for an empty cluster: a wave per cluster of at
@@ -32,6 +37,9 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = (int)kSortTileRows;  // rows per sort tile
+constexpr int kTileWaves = kTile / 64;     // one thread per row
+constexpr int kRankLdsMax = 16384;         // rank_hist keeps up to this many label counters in LDS
+constexpr int kScanRegMax = 16;            // scan: clusters per thread held in registers
 constexpr int kCols = 256;                 // columns per segment_mean block (64 lanes x 4)
 constexpr int kSplitSmall = 64;            // larger clusters are split in kBigWaves parts ...
 constexpr int kSplitLarge = 128;           // ... or larger than this, on big inputs
@@ -40,47 +48,113 @@ constexpr int kBigBlocks = 256;            // segment_mean blocks that take the 
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-__global__ __launch_bounds__(256) void fill_i32_kernel(int *__restrict__ p, int64_t count) {
+__global__ __launch_bounds__(256) void fill_u32_kernel(unsigned *__restrict__ p, int64_t count) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride)
-        p[i] = 0;
+        p[i] = 0u;
 }
 
-// kParts blocks of 256 threads per tile of kTile rows, one row per thread
-// (one block per tile left most CUs idle). Rows with a label outside [0, k)
-// are skipped.
-constexpr int kParts = kTile / 256;
-__global__ __launch_bounds__(256) void tile_hist_kernel(const int64_t *__restrict__ labels,
-                                                        int64_t n, int64_t k, int64_t n_tiles,
-                                                        int *__restrict__ tile_hist) {
-    const int64_t b = blockIdx.x / kParts;
-    const int64_t i = b * kTile + (blockIdx.x % kParts) * 256 + threadIdx.x;
-    if (i < n) {
-        const int64_t l = labels[i];
-        if (l >= 0 && l < k) atomicAdd(tile_hist + l * n_tiles + b, 1);
-    }
-}
-
-// One wave per cluster: exclusive scan of its n_tiles counters, in place.
-__global__ __launch_bounds__(256) void tile_scan_kernel(int *__restrict__ tile_hist, int64_t k,
-                                                        int64_t n_tiles, int *__restrict__ cnt) {
+// Rank of each lane's label among the lanes below it with the same label
+// (stable), and how many lanes hold that label. Lanes with valid == false
+// take no part (rank and count 0). One round per distinct label: the lowest
+// pending lane names a label, a ballot finds its lanes.
+__device__ __forceinline__ void wave_match(int label, bool valid, int &rank, int &count) {
     const int lane = threadIdx.x & 63;
-    const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (j >= k) return;
-    int *h = tile_hist + j * n_tiles;
-    int carry = 0;
-    for (int64_t base = 0; base < n_tiles; base += 64) {
-        const int64_t t = base + lane;
-        const int v = t < n_tiles ? h[t] : 0;
-        int incl = v;
-        for (int off = 1; off < 64; off <<= 1) {
-            const int up = __shfl_up(incl, off);
-            if (lane >= off) incl += up;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    unsigned long long todo = __ballot(valid);
+    rank = 0;
+    count = 0;
+    while (todo != 0ull) {
+        const int leader = __builtin_ctzll(todo);
+        const int l0 = __builtin_amdgcn_readlane(label, leader);
+        const bool eq = valid && label == l0;
+        const unsigned long long m = __ballot(eq);
+        if (eq) {
+            rank = __popcll(m & below);
+            count = __popcll(m);
         }
-        if (t < n_tiles) h[t] = carry + incl - v;
-        carry += __shfl(incl, 63);
+        todo &= ~m;
     }
-    if (lane == 0) cnt[j] = carry;
+}
+
+__device__ __forceinline__ int coherent_load(const int *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The label table of rank_hist_kernel: LDS, or global memory read and written
+// past the compute unit's cache, so that one wave sees what another stored
+// before the barrier between their turns.
+template <bool kLds>
+__device__ __forceinline__ int table_load(const int *p) {
+    return kLds ? *p : coherent_load(p);
+}
+template <bool kLds>
+__device__ __forceinline__ void table_store(int *p, int v) {
+    if (kLds)
+        *p = v;
+    else
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One block of kTile threads per tile of kTile rows, a thread per row.
+// rank[i] = number of rows of the tile before row i with the same label;
+// tile_hist[b * k + j] = rows of tile b with label j, for every j. Each wave
+// first ranks its 64 rows among themselves (wave_match); then the waves take
+// turns in row order, behind a barrier each: a wave adds to its rows' ranks
+// the counts of their labels over the earlier waves, kept per label in a
+// table, and adds its own counts to the table. The table is in LDS when k <=
+// kRankLdsMax (kLds), else the tile's own histogram column in global memory.
+// Rows with a label outside [0, k) are skipped.
+// kFromKeys: the labels come from the assignment's packed keys, turned into
+// int64 labels in place first (and min_dist, as finalize_kernel does; the
+// index of a key is always < k, and is clamped to be sure).
+// Block 0 also zeroes the scan kernel's completion counter.
+template <bool kLds, bool kFromKeys>
+__global__ __launch_bounds__(kTile) void rank_hist_kernel(const int64_t *__restrict__ labels,
+                                                          unsigned long long *__restrict__ keys,
+                                                          float *__restrict__ min_dist,
+                                                          bool add_norm, int64_t n, int64_t k,
+                                                          int *__restrict__ tile_hist,
+                                                          unsigned short *__restrict__ rank_out,
+                                                          unsigned *__restrict__ done, Gate gate) {
+    extern __shared__ int lds_table[];
+    if (gated(gate)) return;
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int64_t b = blockIdx.x;
+    const int64_t i = b * kTile + tid;
+    int l = -1;
+    if (i < n) {
+        if (kFromKeys) {
+            const unsigned long long key = keys[i];
+            if (min_dist) {
+                const float partial = key_distance(key);
+                min_dist[i] = add_norm ? fmaxf(min_dist[i] + partial, 0.0f) : partial;
+            }
+            const unsigned long long idx = key & 0xffffffffull;
+            l = idx < (unsigned long long)k ? (int)idx : 0;
+            keys[i] = (unsigned long long)l;  // the int64 label
+        } else {
+            const int64_t v = labels[i];
+            l = (v >= 0 && v < k) ? (int)v : -1;
+        }
+    }
+    if (b == 0 && tid == 0) *done = 0u;
+    int *table = kLds ? lds_table : tile_hist + b * k;
+    for (int64_t j = tid; j < k; j += kTile) table_store<kLds>(table + j, 0);
+    int rank, count;
+    wave_match(l, l >= 0, rank, count);
+    for (int w = 0; w < kTileWaves; ++w) {
+        __syncthreads();  // the table holds the counts of waves 0 .. w-1
+        if (wave == w && l >= 0) {
+            const int before = table_load<kLds>(table + l);
+            if (rank == count - 1) table_store<kLds>(table + l, before + count);  // one writer per label
+            rank += before;
+        }
+    }
+    __syncthreads();
+    if (l >= 0) rank_out[i] = (unsigned short)rank;
+    if (kLds)
+        for (int64_t j = tid; j < k; j += kTile) tile_hist[b * k + j] = lds_table[j];
 }
 
 // Load-round classes of the clusters summed by one wave (at most kSplit
@@ -90,159 +164,283 @@ __device__ __forceinline__ int round_class(int count) {
     return count <= kSplit ? (count + 7) / 8 : -1;
 }
 
-// A single block of 1024 threads: exclusive scan over the k cluster sizes.
-// If num_empty != NULL it receives the number of clusters of size 0. big[0]
-// receives the number of clusters with more than kSplit rows and big[1 ..]
-// their indices in increasing order. order[0 .. k - big[0]) receives the
-// other clusters grouped by load-round class, most rounds first, increasing
-// index within a class (a stable partition: every rank comes from ballots, so
-// the order is the same on every run). The mean kernel gives 16 consecutive
-// entries of `order` to one block, so a block's waves run the same number of
-// load rounds instead of all waiting for the block's largest cluster.
-template <int kSplit>
-__global__ __launch_bounds__(1024) void cluster_scan_kernel(const int *__restrict__ cnt, int64_t k,
-                                                            int *__restrict__ seg_start,
-                                                            int64_t *__restrict__ counts,
-                                                            int *__restrict__ num_empty,
-                                                            int *__restrict__ big,
-                                                            int *__restrict__ order) {
-    constexpr int kClasses = kSplit / 8 + 1;
-    __shared__ int wave_tot[16];
-    __shared__ int wave_big[16];
-    __shared__ int wave_empty[16];
-    __shared__ int wave_cls[16][kClasses];
-    __shared__ int cls_next[kClasses];  // next free slot of each class in order
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+    for (int off = 1; off < 64; off <<= 1) {
+        const int up = __shfl_up(x, off);
+        if (lane >= off) x += up;
+    }
+    return x;
+}
+
+// Exclusive prefixes of Q values over the block's 1024 threads in thread
+// order (excl) and their block totals (total): a shuffle scan per wave, the
+// wave totals through LDS, a prefix over the 16 waves by the first Q threads.
+// Three barriers for all Q values; every thread must call it.
+template <int Q>
+__device__ __forceinline__ void block_excl_scan(const int (&x)[Q], int (&excl)[Q], int (&total)[Q]) {
+    __shared__ int wsum[16][Q];
+    __shared__ int wpre[16][Q];
+    __shared__ int btot[Q];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const unsigned long long below = (1ull << lane) - 1ull;
-    int carry = 0, empties = 0, big_carry = 0;
-    int cls_total = 0;  // thread c < kClasses: clusters of class c so far
-    for (int64_t base = 0; base < k; base += 1024) {
-        const int64_t j = base + tid;
-        const int v = j < k ? cnt[j] : 0;
-        empties += (j < k && v == 0);
-        int incl = v;
-        for (int off = 1; off < 64; off <<= 1) {
-            const int up = __shfl_up(incl, off);
-            if (lane >= off) incl += up;
-        }
-        const bool is_big = j < k && v > kSplit;
-        const unsigned long long bm = __ballot(is_big);
-        const int cls = j < k ? round_class<kSplit>(v) : -1;
-        if (lane == 63) wave_tot[wave] = incl;
-        if (lane == 0) wave_big[wave] = __popcll(bm);
 #pragma unroll
-        for (int c = 0; c < kClasses; ++c) {
-            const unsigned long long cm = __ballot(cls == c);
-            if (lane == 0) wave_cls[wave][c] = __popcll(cm);
-        }
-        __syncthreads();
-        int before = 0, total = 0, big_before = 0, big_total = 0;
+    for (int q = 0; q < Q; ++q) {
+        const int incl = wave_incl_scan(x[q], lane);
+        excl[q] = incl - x[q];
+        if (lane == 63) wsum[wave][q] = incl;
+    }
+    __syncthreads();
+    if (tid < Q) {
+        int run = 0;
         for (int w = 0; w < 16; ++w) {
-            const int wt = wave_tot[w], wb = wave_big[w];
-            before += w < wave ? wt : 0;
-            total += wt;
-            big_before += w < wave ? wb : 0;
-            big_total += wb;
+            wpre[w][tid] = run;
+            run += wsum[w][tid];
         }
-        if (tid < kClasses)
-            for (int w = 0; w < 16; ++w) cls_total += wave_cls[w][tid];
-        if (j < k) {
-            seg_start[j] = carry + before + incl - v;
-            counts[j] = v;
-        }
-        if (is_big) big[1 + big_carry + big_before + __popcll(bm & below)] = (int)j;
-        carry += total;
-        big_carry += big_total;
-        __syncthreads();  // wave_tot, wave_big and wave_cls are rewritten by the next chunk
-    }
-    // Class c starts after every class with more rounds.
-    if (tid < kClasses) wave_cls[0][tid] = cls_total;
-    __syncthreads();
-    if (tid < kClasses) {
-        int start = 0;
-        for (int c = kClasses - 1; c > tid; --c) start += wave_cls[0][c];
-        cls_next[tid] = start;
+        btot[tid] = run;
     }
     __syncthreads();
-    for (int64_t base = 0; base < k; base += 1024) {
-        const int64_t j = base + tid;
-        const int cls = j < k ? round_class<kSplit>(cnt[j]) : -1;
-        int rank = 0;
 #pragma unroll
-        for (int c = 0; c < kClasses; ++c) {
-            const unsigned long long cm = __ballot(cls == c);
-            if (cls == c) rank = __popcll(cm & below);
-            if (lane == 0) wave_cls[wave][c] = __popcll(cm);
-        }
-        __syncthreads();
-        if (cls >= 0) {
-            int pos = cls_next[cls] + rank;
-            for (int w = 0; w < wave; ++w) pos += wave_cls[w][cls];
-            order[pos] = (int)j;
-        }
-        __syncthreads();  // every thread has read cls_next and wave_cls
-        if (tid < kClasses) {
-            int t = 0;
-            for (int w = 0; w < 16; ++w) t += wave_cls[w][tid];
-            cls_next[tid] += t;
-        }
-        __syncthreads();
+    for (int q = 0; q < Q; ++q) {
+        excl[q] += wpre[wave][q];
+        total[q] = btot[q];
     }
-    if (tid == 0) big[0] = big_carry;
-    if (num_empty) {
-        for (int off = 32; off > 0; off >>= 1) empties += __shfl_xor(empties, off);
-        if (lane == 0) wave_empty[wave] = empties;
-        __syncthreads();
-        if (tid == 0) {
-            int t = 0;
-            for (int w = 0; w < 16; ++w) t += wave_empty[w];
-            *num_empty = t;
+    __syncthreads();  // the arrays are rewritten by the next call
+}
+
+// Class counts travel packed two to an int, 16 bits each: every count is at
+// most the number of clusters the scan covers at once (<= 16384 < 2^16), so
+// sums of packed ints add the halves independently.
+template <int kClasses>
+__device__ __forceinline__ void add_class(int (&packed)[(kClasses + 1) / 2], int cl) {
+#pragma unroll
+    for (int p = 0; p < (kClasses + 1) / 2; ++p)
+        packed[p] += (cl >= 0 && (cl >> 1) == p) ? (1 << (16 * (cl & 1))) : 0;
+}
+
+__device__ __forceinline__ int unpack_half(int packed, int half) {
+    return (packed >> (16 * half)) & 0xffff;
+}
+
+// The cluster scan of the last scan block, for k <= 1024 * R: thread t holds
+// clusters t*R .. t*R + R - 1 in registers. Writes seg_start (exclusive prefix
+// of the sizes), counts (int64 sizes), big[0] = number of clusters above
+// kSplit rows and big[1 ..] their indices in increasing order, order = the
+// other clusters grouped by load-round class, most rounds first, increasing
+// index within a class (ranks from scans, so the order is the same on every
+// run; the mean kernel gives 16 consecutive entries of `order` to one block,
+// so a block's waves run the same number of load rounds), and the number of
+// empty clusters.
+template <int R, int kSplit>
+__device__ void cluster_scan_regs(const int *cnt, int64_t k, int *seg_start, int64_t *counts,
+                                  int *num_empty, int *no_empty, int *big, int *order) {
+    static_assert(R * 1024 < 65536, "packed class counts need k < 2^16");
+    constexpr int kClasses = kSplit / 8 + 1;
+    constexpr int kPacked = (kClasses + 1) / 2;
+    constexpr int Q = 2 + kPacked;  // sizes; above-split | empty << 16; classes, two per int
+    const int tid = threadIdx.x;
+    const int64_t j0 = (int64_t)tid * R;
+    int v[R];
+#pragma unroll
+    for (int e = 0; e < R; ++e) v[e] = j0 + e < k ? coherent_load(cnt + j0 + e) : -1;
+    int x[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) x[q] = 0;
+#pragma unroll
+    for (int e = 0; e < R; ++e) {
+        if (v[e] < 0) continue;
+        x[0] += v[e];
+        x[1] += (v[e] > kSplit ? 1 : 0) + (v[e] == 0 ? 1 << 16 : 0);
+        int (&cls)[kPacked] = *reinterpret_cast<int (*)[kPacked]>(&x[2]);
+        add_class<kClasses>(cls, round_class<kSplit>(v[e]));
+    }
+    int pos[Q], tot[Q];
+    block_excl_scan<Q>(x, pos, tot);
+    // Class c starts after every class with more rounds: fold that start into
+    // the thread's packed positions.
+    int start = 0;
+#pragma unroll
+    for (int c = kClasses - 1; c >= 0; --c) {
+        pos[2 + c / 2] += start << (16 * (c & 1));
+        start += unpack_half(tot[2 + c / 2], c & 1);
+    }
+    int seg = pos[0], bpos = pos[1] & 0xffff;
+#pragma unroll
+    for (int e = 0; e < R; ++e) {
+        if (v[e] < 0) continue;
+        const int64_t j = j0 + e;
+        seg_start[j] = seg;
+        counts[j] = v[e];
+        seg += v[e];
+        if (v[e] > kSplit) big[1 + bpos++] = (int)j;
+        const int cl = round_class<kSplit>(v[e]);
+        if (cl >= 0) {
+            int at = 0;
+#pragma unroll
+            for (int p = 0; p < kPacked; ++p)
+                if ((cl >> 1) == p) {
+                    at = unpack_half(pos[2 + p], cl & 1);
+                    pos[2 + p] += 1 << (16 * (cl & 1));
+                }
+            order[at] = (int)j;
+        }
+    }
+    if (tid == 0) {
+        big[0] = tot[1] & 0xffff;
+        if (num_empty) {
+            const int empty = unpack_half(tot[1], 1);
+            *num_empty = empty;
+            *no_empty = empty == 0;
         }
     }
 }
 
-// kParts blocks of 256 threads per tile, one thread per row: part p takes
-// rows 256p .. 256p + 255 of the tile and loads the tile's labels up to its
-// last row into LDS. The rank of a row among the rows of the same tile with
-// the same label and a smaller index is counted directly from those labels,
-// which keeps the grouping stable (increasing row order inside every
-// cluster) and independent of thread timing. A wave first counts over the
-// whole chunks of 64 rows before its own, four labels per (broadcast) LDS
-// read with no divergence, then over the earlier rows of its own chunk.
-// (One 1024-thread block per tile used a quarter of the CUs at n = 65536.)
-static_assert(kTile == 1024 && kParts == 4, "scatter_kernel splits 1024-row tiles in 4 parts");
-__global__ __launch_bounds__(256) void scatter_kernel(const int64_t *__restrict__ labels, int64_t n,
-                                                      int64_t k, int64_t n_tiles,
-                                                      const int *__restrict__ tile_prefix,
-                                                      const int *__restrict__ seg_start,
-                                                      int *__restrict__ perm) {
-    __shared__ __align__(16) int lab[kTile];
-    const int64_t b = blockIdx.x / kParts;
-    const int part = blockIdx.x % kParts;
-    const int64_t row0 = b * kTile;
-    const int rows = (int)min((int64_t)kTile, n - row0);
-    for (int q = threadIdx.x; q < (part + 1) * 256; q += 256) {
-        int l = -1;
-        if (q < rows) {
-            const int64_t v = labels[row0 + q];
-            l = (v >= 0 && v < k) ? (int)v : -1;
+// The same for any k, 1024 clusters at a time, a cluster per thread (each
+// chunk's sizes loaded in turn; a first pass takes the class totals): used
+// when k > 1024 * kScanRegMax. Running totals across chunks are full ints.
+template <int kSplit>
+__device__ void cluster_scan_chunked(const int *cnt, int64_t k, int *seg_start, int64_t *counts,
+                                     int *num_empty, int *no_empty, int *big, int *order) {
+    constexpr int kClasses = kSplit / 8 + 1;
+    constexpr int kPacked = (kClasses + 1) / 2;
+    constexpr int Q = 2 + kPacked;
+    const int tid = threadIdx.x;
+    int cls_carry[kClasses];
+#pragma unroll
+    for (int c = 0; c < kClasses; ++c) cls_carry[c] = 0;
+    // Pass 1: class totals.
+    for (int64_t base = 0; base < k; base += 1024) {
+        const int64_t j = base + tid;
+        const int v = j < k ? coherent_load(cnt + j) : -1;
+        int x[Q], p[Q], t[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) x[q] = 0;
+        int (&cls)[kPacked] = *reinterpret_cast<int (*)[kPacked]>(&x[2]);
+        add_class<kClasses>(cls, v >= 0 ? round_class<kSplit>(v) : -1);
+        block_excl_scan<Q>(x, p, t);
+#pragma unroll
+        for (int c = 0; c < kClasses; ++c) cls_carry[c] += unpack_half(t[2 + c / 2], c & 1);
+    }
+    {
+        int start = 0;
+#pragma unroll
+        for (int c = kClasses - 1; c >= 0; --c) {
+            const int tc = cls_carry[c];
+            cls_carry[c] = start;
+            start += tc;
         }
-        lab[q] = l;
     }
-    __syncthreads();
-    const int r = part * 256 + threadIdx.x;
-    const int l = lab[r];
-    if (l < 0) return;
-    const int chunk0 = r & ~63;
-    const int4 *lab4 = reinterpret_cast<const int4 *>(lab);
-    int rank = 0;
-    for (int q = 0; q < chunk0; q += 4) {
-        const int4 v = lab4[q >> 2];
-        rank += (v.x == l) + (v.y == l) + (v.z == l) + (v.w == l);
+    // Pass 2: placement.
+    int seg_carry = 0, big_carry = 0, empty_carry = 0;
+    for (int64_t base = 0; base < k; base += 1024) {
+        const int64_t j = base + tid;
+        const int v = j < k ? coherent_load(cnt + j) : -1;
+        const int cl = v >= 0 ? round_class<kSplit>(v) : -1;
+        int x[Q], p[Q], t[Q];
+        x[0] = v >= 0 ? v : 0;
+        x[1] = (v > kSplit ? 1 : 0) + (v == 0 ? 1 << 16 : 0);
+#pragma unroll
+        for (int q = 2; q < Q; ++q) x[q] = 0;
+        int (&cls)[kPacked] = *reinterpret_cast<int (*)[kPacked]>(&x[2]);
+        add_class<kClasses>(cls, cl);
+        block_excl_scan<Q>(x, p, t);
+        if (v >= 0) {
+            seg_start[j] = seg_carry + p[0];
+            counts[j] = v;
+        }
+        if (v > kSplit) big[1 + big_carry + (p[1] & 0xffff)] = (int)j;
+#pragma unroll
+        for (int c = 0; c < kClasses; ++c) {
+            if (cl == c) order[cls_carry[c] + unpack_half(p[2 + c / 2], c & 1)] = (int)j;
+            cls_carry[c] += unpack_half(t[2 + c / 2], c & 1);
+        }
+        seg_carry += t[0];
+        big_carry += t[1] & 0xffff;
+        empty_carry += unpack_half(t[1], 1);
     }
-    for (int q = chunk0; q < r; ++q) rank += lab[q] == l;
-    const int64_t pos = (int64_t)seg_start[l] + tile_prefix[(int64_t)l * n_tiles + b] + rank;
-    perm[pos] = (int)(row0 + r);
+    if (tid == 0) {
+        big[0] = big_carry;
+        if (num_empty) {
+            *num_empty = empty_carry;
+            *no_empty = empty_carry == 0;
+        }
+    }
+}
+
+// Per cluster j (a thread each, 1024 per block): the exclusive prefix of its
+// tile counts over the tiles, in place, and its size cnt[j]. The loads of a
+// wave read 64 consecutive clusters of one tile (the tile's histogram column
+// is contiguous); the next U tiles' loads are issued before the current U
+// tiles' stores, so a thread waits for memory once per U tiles. Then the
+// cluster scan runs in one block: with one block it is that block; otherwise
+// the last block to finish (a counter zeroed by rank_hist_kernel; every block
+// fences its writes before counting itself; on this chip those fences write
+// back and invalidate the L2, so a one-block grid skips them).
+template <int R, int kSplit>
+__global__ __launch_bounds__(1024) void scan_kernel(int *__restrict__ tile_hist, int64_t k,
+                                                    int64_t n_tiles, int *__restrict__ cnt,
+                                                    int *__restrict__ seg_start,
+                                                    int64_t *__restrict__ counts,
+                                                    int *__restrict__ num_empty,
+                                                    int *__restrict__ no_empty,
+                                                    int *__restrict__ big,
+                                                    int *__restrict__ order,
+                                                    unsigned *__restrict__ done, Gate gate) {
+    __shared__ int is_last;
+    if (gated(gate)) return;
+    const int64_t j = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+    if (j < k) {
+        constexpr int U = 32;  // tile counts in flight per thread
+        int run = 0;
+        int v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = u < n_tiles ? tile_hist[u * k + j] : 0;
+        for (int64_t b0 = 0; b0 < n_tiles; b0 += U) {
+            int nxt[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                nxt[u] = b0 + U + u < n_tiles ? tile_hist[(b0 + U + u) * k + j] : 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (b0 + u < n_tiles) tile_hist[(b0 + u) * k + j] = run;
+                run += v[u];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = nxt[u];
+        }
+        cnt[j] = run;
+    }
+    if (gridDim.x > 1) {
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0) is_last = atomicAdd(done, 1u) == gridDim.x - 1;
+        __syncthreads();
+        if (!is_last) return;
+        __threadfence();
+    } else {
+        __syncthreads();  // cnt written by the block's own threads
+    }
+    if (R > 0)
+        cluster_scan_regs<(R > 0 ? R : 1), kSplit>(cnt, k, seg_start, counts, num_empty, no_empty,
+                                                   big, order);
+    else
+        cluster_scan_chunked<kSplit>(cnt, k, seg_start, counts, num_empty, no_empty, big, order);
+}
+
+// One thread per row: perm[segment start + rows of the cluster in earlier
+// tiles + rank within the tile] = row. Stable: inside a cluster, rows keep
+// increasing sample order.
+__global__ __launch_bounds__(256) void scatter_kernel(const int64_t *__restrict__ labels, int64_t n,
+                                                      int64_t k,
+                                                      const int *__restrict__ tile_prefix,
+                                                      const unsigned short *__restrict__ rank,
+                                                      const int *__restrict__ seg_start,
+                                                      int *__restrict__ perm, Gate gate) {
+    if (gated(gate)) return;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int64_t l = labels[i];
+    if (l < 0 || l >= k) return;
+    const int64_t b = i / kTile;
+    perm[(int64_t)seg_start[l] + tile_prefix[b * k + l] + rank[i]] = (int)i;
 }
 
 // Sum over the 64 lanes of a wave of each of B per-lane values (B a power of
@@ -418,10 +616,11 @@ __global__ __launch_bounds__(kBigWaves * 64) void segment_mean_kernel(
     const float *__restrict__ X, const int *__restrict__ perm, const int *__restrict__ seg_start,
     const int *__restrict__ cnt, const int *__restrict__ big, const int *__restrict__ order,
     const float *C_old, int64_t n, int64_t k, int64_t d, int chunks, float *C_new,
-    double *__restrict__ shift_partial, float *__restrict__ xn_part) {
+    double *__restrict__ shift_partial, float *__restrict__ xn_part, Gate gate) {
     // C_old and C_new may be the same array: each element is read and written
     // by the same thread only, so they carry no __restrict__.
     __shared__ double part[kBigWaves - 1][kCols];
+    if (gated(gate)) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     int lc[4];  // columns within a chunk
 #pragma unroll
@@ -502,9 +701,11 @@ static int64_t small_mean_blocks(int64_t k, int64_t d) {
 
 int64_t update_grid_threads(int64_t n, int64_t k, int64_t d) {
     const int64_t mean = (small_mean_blocks(k, d) + kBigBlocks) * (kBigWaves * 64);
-    const int64_t scatter = cdiv(n, kTile) * kTile;  // tile_hist and scatter: 256 per row quarter
-    const int64_t scan = cdiv(k, 4) * 256;
-    const int64_t m = mean > scatter ? mean : scatter;
+    const int64_t rank = cdiv(n, kTile) * kTile;  // rank_hist: a thread per row, whole tiles
+    const int64_t scatter = cdiv(n, 256) * 256;
+    const int64_t scan = cdiv(k, 1024) * 1024;
+    int64_t m = mean > rank ? mean : rank;
+    m = m > scatter ? m : scatter;
     return m > scan ? m : scan;
 }
 
@@ -512,28 +713,79 @@ int split_rows(int64_t n, int64_t k, int64_t d) {
     return (n * d >= ((int64_t)1 << 26) && n >= 32 * k) ? kSplitLarge : kSplitSmall;
 }
 
-hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t d, int64_t *counts,
-                        int *num_empty, const UpdateScratch &ws, hipStream_t stream) {
-    const int64_t hist_words = k * ws.n_tiles;
-    if (hist_words > 0) {
-        fill_i32_kernel<<<grid_stride_blocks(hist_words), 256, 0, stream>>>(ws.tile_hist,
-                                                                           hist_words);
-        if (n > 0)
-            tile_hist_kernel<<<(unsigned)(ws.n_tiles * kParts), 256, 0, stream>>>(
-                labels, n, k, ws.n_tiles, ws.tile_hist);
-        tile_scan_kernel<<<(unsigned)cdiv(k, 4), 256, 0, stream>>>(ws.tile_hist, k, ws.n_tiles,
-                                                                   ws.cnt);
-    } else {
-        // n == 0: every cluster is empty.
-        fill_i32_kernel<<<grid_stride_blocks(k), 256, 0, stream>>>(ws.cnt, k);
+namespace {
+
+template <bool kFromKeys>
+hipError_t launch_rank_hist_impl(const int64_t *labels, unsigned long long *keys,
+                                 float *min_dist, bool add_norm, int64_t n, int64_t k,
+                                 const UpdateScratch &ws, Gate gate, hipStream_t stream) {
+    if (n <= 0) {
+        // No tile: the scan kernel's counter is zeroed here instead.
+        fill_u32_kernel<<<1, 256, 0, stream>>>(ws.done, 1);
+        return hipGetLastError();
     }
-    if (split_rows(n, k, d) == kSplitLarge)
-        cluster_scan_kernel<kSplitLarge><<<1, 1024, 0, stream>>>(ws.cnt, k, ws.seg_start, counts,
-                                                                 num_empty, ws.big, ws.order);
+    const unsigned blocks = (unsigned)ws.n_tiles;
+    if (k <= kRankLdsMax)
+        rank_hist_kernel<true, kFromKeys><<<blocks, kTile, (size_t)k * sizeof(int), stream>>>(
+            labels, keys, min_dist, add_norm, n, k, ws.tile_hist, ws.rank, ws.done, gate);
     else
-        cluster_scan_kernel<kSplitSmall><<<1, 1024, 0, stream>>>(ws.cnt, k, ws.seg_start, counts,
-                                                                 num_empty, ws.big, ws.order);
+        rank_hist_kernel<false, kFromKeys><<<blocks, kTile, 0, stream>>>(
+            labels, keys, min_dist, add_norm, n, k, ws.tile_hist, ws.rank, ws.done, gate);
     return hipGetLastError();
+}
+
+template <int kSplit>
+void launch_scan_split(int64_t k, int64_t *counts, int *num_empty, const UpdateScratch &ws,
+                       Gate gate, unsigned blocks, hipStream_t stream) {
+    const int64_t r = cdiv(k, 1024);  // clusters per thread in the final scan
+#define KM_SCAN(R)                                                                             \
+    scan_kernel<R, kSplit><<<blocks, 1024, 0, stream>>>(ws.tile_hist, k, ws.n_tiles, ws.cnt,   \
+                                                        ws.seg_start, counts, num_empty,       \
+                                                        ws.no_empty, ws.big, ws.order, ws.done, \
+                                                        gate)
+    if (r <= 1)
+        KM_SCAN(1);
+    else if (r <= 2)
+        KM_SCAN(2);
+    else if (r <= 4)
+        KM_SCAN(4);
+    else if (r <= 8)
+        KM_SCAN(8);
+    else if (r <= kScanRegMax)
+        KM_SCAN(kScanRegMax);
+    else
+        KM_SCAN(0);
+#undef KM_SCAN
+}
+
+}  // namespace
+
+hipError_t launch_rank_hist(const int64_t *labels, int64_t n, int64_t k, const UpdateScratch &ws,
+                            Gate gate, hipStream_t stream) {
+    return launch_rank_hist_impl<false>(labels, nullptr, nullptr, false, n, k, ws, gate, stream);
+}
+
+hipError_t launch_finalize_rank_hist(unsigned long long *keys, float *min_dist, bool add_norm,
+                                     int64_t n, int64_t k, const UpdateScratch &ws, Gate gate,
+                                     hipStream_t stream) {
+    return launch_rank_hist_impl<true>(nullptr, keys, min_dist, add_norm, n, k, ws, gate, stream);
+}
+
+hipError_t launch_scan(int64_t n, int64_t k, int64_t d, int64_t *counts, int *num_empty,
+                       const UpdateScratch &ws, Gate gate, hipStream_t stream) {
+    const unsigned blocks = (unsigned)cdiv(k, 1024);
+    if (split_rows(n, k, d) == kSplitLarge)
+        launch_scan_split<kSplitLarge>(k, counts, num_empty, ws, gate, blocks, stream);
+    else
+        launch_scan_split<kSplitSmall>(k, counts, num_empty, ws, gate, blocks, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t d, int64_t *counts,
+                        int *num_empty, const UpdateScratch &ws, Gate gate, hipStream_t stream) {
+    hipError_t e = launch_rank_hist(labels, n, k, ws, gate, stream);
+    if (e == hipSuccess) e = launch_scan(n, k, d, counts, num_empty, ws, gate, stream);
+    return e;
 }
 
 int64_t mean_blocks(int64_t k, int64_t d) { return small_mean_blocks(k, d) + kBigBlocks; }
@@ -580,6 +832,7 @@ struct MeanArgs {
     float *C_new;
     double *shift_partial;  // NULL: no centre shift
     float *xn_part;         // NULL: no row norms
+    Gate gate;
 };
 
 template <bool kVec, int kBatch>
@@ -587,15 +840,15 @@ void launch_mean_vec(const MeanArgs &a, unsigned blocks, unsigned bt, hipStream_
     if (a.shift_partial)
         segment_mean_kernel<kVec, true, kBatch, false><<<blocks, bt, 0, stream>>>(
             a.X, a.perm, a.seg_start, a.cnt, a.big, a.order, a.C_old, a.n, a.k, a.d, a.chunks, a.C_new,
-            a.shift_partial, nullptr);
+            a.shift_partial, nullptr, a.gate);
     else if (a.xn_part)  // rounds of at most 8 rows: 16 with the pending norms spill
         segment_mean_kernel<kVec, false, (kBatch > 8 ? 8 : kBatch), true><<<blocks, bt, 0, stream>>>(
             a.X, a.perm, a.seg_start, a.cnt, a.big, a.order, a.C_old, a.n, a.k, a.d, a.chunks, a.C_new,
-            nullptr, a.xn_part);
+            nullptr, a.xn_part, a.gate);
     else
         segment_mean_kernel<kVec, false, kBatch, false><<<blocks, bt, 0, stream>>>(
             a.X, a.perm, a.seg_start, a.cnt, a.big, a.order, a.C_old, a.n, a.k, a.d, a.chunks, a.C_new,
-            nullptr, nullptr);
+            nullptr, nullptr, a.gate);
 }
 
 template <int kBatch>
@@ -611,18 +864,18 @@ void launch_mean(const MeanArgs &a, bool vec, unsigned blocks, unsigned bt, hipS
 hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const float *C_old,
                                  int64_t n, int64_t k, int64_t d, float *C_new,
                                  double *shift_partial, float *xn_part, const UpdateScratch &ws,
-                                 hipStream_t stream) {
+                                 Gate gate, hipStream_t stream) {
     if (n > 0)
-        scatter_kernel<<<(unsigned)(ws.n_tiles * kParts), 256, 0, stream>>>(
-            labels, n, k, ws.n_tiles, ws.tile_hist, ws.seg_start, ws.perm);
+        scatter_kernel<<<(unsigned)cdiv(n, 256), 256, 0, stream>>>(
+            labels, n, k, ws.tile_hist, ws.rank, ws.seg_start, ws.perm, gate);
     const int chunks = (int)cdiv(d, kCols);
     const unsigned blocks = (unsigned)mean_blocks(k, d);
     const unsigned bt = kBigWaves * 64;
     const bool vec = (d % 4 == 0) && ((uintptr_t)X % 16 == 0) && ((uintptr_t)C_old % 16 == 0) &&
                      ((uintptr_t)C_new % 16 == 0);
-    const MeanArgs a{X,      ws.perm, ws.seg_start, ws.cnt,      ws.big, ws.order,
-                     C_old,  n,       k,            d,           chunks, C_new,
-                     shift_partial, xn_part};
+    const MeanArgs a{X,      ws.perm, ws.seg_start, ws.cnt,        ws.big,  ws.order,
+                     C_old,  n,       k,            d,             chunks,  C_new,
+                     shift_partial, xn_part, gate};
     if (n <= 32 * k)  // at most 32 rows per cluster on average
         launch_mean<8>(a, vec, blocks, bt, stream);
     else
@@ -640,10 +893,12 @@ hipError_t launch_add_norms(float *min_dist, const float *xn_part, int64_t n, in
 
 hipError_t launch_update(const float *X, const int64_t *labels, const float *C_old, int64_t n,
                          int64_t k, int64_t d, float *C_new, int64_t *counts, float *xn_part,
-                         const UpdateScratch &ws, hipStream_t stream) {
-    hipError_t e = launch_count(labels, n, k, d, counts, nullptr, ws, stream);
+                         bool counted, const UpdateScratch &ws, hipStream_t stream) {
+    hipError_t e = counted ? launch_scan(n, k, d, counts, nullptr, ws, Gate{}, stream)
+                           : launch_count(labels, n, k, d, counts, nullptr, ws, Gate{}, stream);
     if (e != hipSuccess) return e;
-    return launch_group_and_mean(X, labels, C_old, n, k, d, C_new, nullptr, xn_part, ws, stream);
+    return launch_group_and_mean(X, labels, C_old, n, k, d, C_new, nullptr, xn_part, ws, Gate{},
+                                 stream);
 }
 
 }  // namespace km

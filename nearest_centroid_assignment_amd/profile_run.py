@@ -2,10 +2,13 @@
 
 run (default):
     python3 -m nearest_centroid_assignment_amd.profile_run [--workload feature_heavy]
+        [--op assign|update]
   launches, in order and each once: a 1 GiB streaming copy (calibration), then
-  one ``kmeans_assign`` (no min_dist) on the workload's seeded inputs. Meant to
-  be run under ``rocprofv3 --pmc FETCH_SIZE`` and, separately, under
-  ``rocprofv3 --pmc WRITE_SIZE`` (csv output).
+  on the workload's seeded inputs either one ``kmeans_assign`` (no min_dist;
+  op assign) or one ``kmeans_assign`` followed by one ``kmeans_update`` with
+  its labels (op update). Meant to be run under ``rocprofv3 --pmc FETCH_SIZE``
+  and, separately, under ``rocprofv3 --pmc WRITE_SIZE`` (csv output), or with
+  other counters.
 
 summarize:
     python3 -m nearest_centroid_assignment_amd.profile_run summarize \
@@ -13,9 +16,18 @@ summarize:
         --out profiles/assign_tile_feature_heavy_traffic.json
   reads the counter_collection csv files, scales each counter of the
   assignment kernel by (known copy bytes / what the same counter read for the
-  copy kernel), and records the HBM bytes per launch together with a SHA-256
-  of csrc/assign.hip and its compile flags, so that a later change to the
-  kernel voids it.
+  copy kernel), and records the bytes per launch together with a SHA-256 of
+  csrc/assign.hip and its compile flags, so that a later change to the kernel
+  voids it. FETCH_SIZE counts what the L2 fetches from beyond itself (HBM and
+  the MALL in front of it), so the figure is beyond-L2 traffic, an upper
+  bound of the HBM bytes.
+
+kernels:
+    python3 -m nearest_centroid_assignment_amd.profile_run kernels \
+        --dir <run dir> [--dir <run dir> ...]
+  prints, for every kernel in the runs' counter_collection csv files, each
+  counter's average per dispatch; FETCH_SIZE and WRITE_SIZE are also given in
+  bytes, scaled by what the counter read for the copy kernel.
 """
 from __future__ import annotations
 
@@ -48,7 +60,7 @@ def kernel_digest() -> str:
     return h.hexdigest()
 
 
-def run(workload: str) -> None:
+def run(workload: str, op: str = "assign") -> None:
     import torch
 
     from . import binding, calib, datagen
@@ -70,6 +82,12 @@ def run(workload: str) -> None:
     print(f"[profile_run] kmeans_assign {cfg.name} {cfg.n}x{cfg.k}x{cfg.d}", flush=True)
     binding.kmeans_assign(Xg, Cg, labels, None)
     torch.cuda.synchronize()
+    if op == "update":
+        C_new = torch.empty_like(Cg)
+        counts = torch.empty(cfg.k, dtype=torch.int64, device=dev)
+        print(f"[profile_run] kmeans_update {cfg.name}", flush=True)
+        binding.kmeans_update(Xg, labels, Cg, C_new, counts)
+        torch.cuda.synchronize()
     print("[profile_run] done", flush=True)
 
 
@@ -121,7 +139,7 @@ def summarize(fetch_dir: str, write_dir: str, out: str, workload: str) -> dict:
                         "scale": scale, "assign_bytes_per_launch": per_launch}
         total += per_launch
     alg = 4.0 * (cfg.n * cfg.d + cfg.k * cfg.d) + 8.0 * cfg.n
-    rec["hbm_bytes_per_launch"] = total
+    rec["beyond_l2_bytes_per_launch"] = total
     rec["algorithmic_min_bytes"] = alg
     rec["traffic_over_min"] = total / alg
     rec["assign_kernel_sha256"] = kernel_digest()
@@ -130,18 +148,52 @@ def summarize(fetch_dir: str, write_dir: str, out: str, workload: str) -> dict:
     return rec
 
 
+def kernel_table(dirs) -> list:
+    """Per kernel (full name) and counter: dispatches and average value; for
+    FETCH_SIZE / WRITE_SIZE also bytes per dispatch, scaled by the copy."""
+    by = {}
+    for d in dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        for f in files:
+            with open(f, newline="") as fh:
+                for r in csv.DictReader(fh):
+                    key = (r.get("Kernel_Name", ""), r.get("Counter_Name", ""))
+                    by.setdefault(key, {}).setdefault(r.get("Dispatch_Id", len(by)), 0.0)
+                    by[key][r.get("Dispatch_Id", len(by))] += float(r["Counter_Value"])
+    scale = {}
+    for (kname, cname), disp in by.items():
+        if COPY_KERNEL in kname and cname in ("FETCH_SIZE", "WRITE_SIZE"):
+            scale[cname] = (COPY_BYTES / 1024.0) / (sum(disp.values()) / len(disp))
+    rows = []
+    for (kname, cname), disp in sorted(by.items()):
+        avg = sum(disp.values()) / len(disp)
+        row = {"kernel": kname, "counter": cname, "dispatches": len(disp), "average": avg}
+        if cname in scale:
+            row["bytes"] = avg * scale[cname] * 1024.0
+            row["scale"] = scale[cname]
+        rows.append(row)
+    return rows
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
-    ap.add_argument("mode", nargs="?", default="run", choices=["run", "summarize"])
+    ap.add_argument("mode", nargs="?", default="run", choices=["run", "summarize", "kernels"])
     ap.add_argument("--workload", default="feature_heavy")
+    ap.add_argument("--op", default="assign", choices=["assign", "update"])
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--out")
+    ap.add_argument("--dir", action="append", default=[])
     a = ap.parse_args(argv)
     if a.mode == "run":
-        run(a.workload)
-    else:
+        run(a.workload, a.op)
+    elif a.mode == "summarize":
         print(json.dumps(summarize(a.fetch, a.write, a.out, a.workload), indent=1))
+    else:
+        for r in kernel_table(a.dir):
+            extra = f"  {r['bytes']:.4e} B (x{r['scale']:.3f})" if "bytes" in r else ""
+            print(f"{r['kernel'][:90]:90s} {r['counter']:22s} n={r['dispatches']:3d} "
+                  f"avg={r['average']:.6g}{extra}")
     return 0
 
 

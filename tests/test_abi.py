@@ -71,13 +71,13 @@ def test_workspace_bytes_rules(lib):
         # The assignment needs only the centroid norms (k floats + alignment).
         assert a <= cfg.k * 4 + 512
         # The update: k x ceil(n/1024) tile counters, 2k words, n words, the
-        # list of large clusters (k + 1 words) and the order of the others
-        # (k words).
+        # list of large clusters (k + 1 words), the order of the others
+        # (k words), a 16-bit rank per row and two flag words.
         n_tiles = -(-cfg.n // 1024)
-        assert u <= 4 * (cfg.k * n_tiles + 4 * cfg.k + 1 + cfg.n) + 7 * 256
+        assert u <= 4 * (cfg.k * n_tiles + 4 * cfg.k + 1 + cfg.n) + 2 * cfg.n + 8 + 9 * 256
         # Far below the (n, k) distance matrix and the (n, d) sample matrix.
         if cfg.n >= 4096:
-            assert l < cfg.n * cfg.k * 4 / 16 and l < cfg.n * cfg.d * 4 / 128
+            assert l < cfg.n * cfg.k * 4 / 16 and l < cfg.n * cfg.d * 4 / 64
             assert u < cfg.n * cfg.k * 4 / 64 and u < cfg.n * cfg.d * 4 / 64
 
 

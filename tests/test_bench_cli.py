@@ -25,7 +25,7 @@ def test_traffic_record_requires_matching_kernel(tmp_path, monkeypatch):
     from nearest_centroid_assignment_amd.profile_run import kernel_digest
 
     cfg = datagen.CONFIGS["feature_heavy"]
-    rec = {"workload": "feature_heavy", "hbm_bytes_per_launch": 123.0,
+    rec = {"workload": "feature_heavy", "beyond_l2_bytes_per_launch": 123.0,
            "assign_kernel_sha256": kernel_digest()}
     f = tmp_path / "t.json"
     f.write_text(json.dumps(rec))
