@@ -71,7 +71,9 @@ typedef enum {
     KM_ERR_WORKSPACE = -4, /* workspace_bytes < kmeans_workspace_bytes(...)       */
     KM_ERR_ALIAS = -5,     /* an output overlaps an input, output or workspace    */
     KM_ERR_HIP = -6,       /* a kernel launch was rejected by the HIP runtime     */
-    KM_ERR_OP = -7         /* unknown op code or flag                             */
+    KM_ERR_OP = -7,        /* unknown op code or flag                             */
+    KM_ERR_SCRATCH = -8    /* kmeans_lloyd_step_noalloc: the shape needs more than
+                              KM_NOALLOC_SCRATCH_BYTES of scratch                 */
 } km_status;
 
 /* Op codes for kmeans_workspace_bytes. */
@@ -135,6 +137,29 @@ int kmeans_update(const float *X, const int64_t *labels, const float *C_old,
 int kmeans_lloyd_step(const float *X, const float *C_old, int64_t n, int64_t k, int64_t d,
                       int64_t *labels, float *min_dist, float *C_new, int64_t *counts,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kmeans_lloyd_step for callers that cannot allocate device memory at all
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels and results, but no workspace argument. The
+ * scratch lives in a static device array of KM_NOALLOC_SCRATCH_BYTES bytes
+ * that each GPU the library runs on holds from the library's first use on it
+ * until the process ends; its address is looked up once per device on the
+ * first call there. Nothing is allocated or freed by the call itself.
+ *   Shapes whose kmeans_workspace_bytes(n, k, d, KM_OP_LLOYD) exceeds
+ *   KM_NOALLOC_SCRATCH_BYTES return KM_ERR_SCRATCH before any HIP call (the
+ *   five workloads of the pages need at most about 22 MiB).
+ *   The array is shared by every call on a GPU: two calls that may overlap
+ *   on one GPU (different streams, or host threads) race on it and give
+ *   undefined results; calls on one stream are ordered and safe. Every part
+ *   of it a call reads is written earlier in the same call.
+ *   The scratch is on the device of `stream` (the current device for NULL).
+ * Other arguments, checks and return codes as in kmeans_lloyd_step.
+ */
+#define KM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int kmeans_lloyd_step_noalloc(const float *X, const float *C_old, int64_t n, int64_t k,
+                              int64_t d, int64_t *labels, float *min_dist, float *C_new,
+                              int64_t *counts, void *stream);
 
 /*
  * Lloyd iterations from C_init: assignment, optional empty-cluster

@@ -6,7 +6,7 @@ step of the computation runs in the library's HIP kernels. There is no CPU
 fallback: if the library is missing, loading fails with an error.
 
 The functions ``kmeans_assign``, ``kmeans_update``, ``kmeans_lloyd_step``,
-``kmeans_fit``, ``kmeans_plusplus``, ``kmeans_workspace_bytes`` and
+``kmeans_lloyd_step_noalloc``, ``kmeans_fit``, ``kmeans_plusplus``, ``kmeans_workspace_bytes`` and
 ``kmeans_status_string`` mirror the C entry points of the same names;
 ``assign``, ``update``, ``lloyd_step``, ``fit`` and ``plusplus`` also allocate
 the outputs.
@@ -32,6 +32,7 @@ STATUS_NAMES = {
     -5: "KM_ERR_ALIAS",
     -6: "KM_ERR_HIP",
     -7: "KM_ERR_OP",
+    -8: "KM_ERR_SCRATCH",
 }
 
 _lock = threading.Lock()
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.kmeans_update.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
         L.kmeans_lloyd_step.restype = ctypes.c_int
         L.kmeans_lloyd_step.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+        L.kmeans_lloyd_step_noalloc.restype = ctypes.c_int
+        L.kmeans_lloyd_step_noalloc.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, vp]
         L.kmeans_plusplus.restype = ctypes.c_int
         L.kmeans_plusplus.argtypes = [vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, sz, vp]
         L.kmeans_fit.restype = ctypes.c_int
@@ -209,6 +212,21 @@ def kmeans_lloyd_step(X, C_old, labels, min_dist, C_new, counts, workspace=None,
                                  _stream(stream, X.device))
     _check(rc, "kmeans_lloyd_step")
     _record(stream, X.device, X, C_old, labels, min_dist, C_new, counts, workspace)
+
+
+def kmeans_lloyd_step_noalloc(X, C_old, labels, min_dist, C_new, counts, stream=None):
+    """Enqueue one Lloyd iteration with the library's static scratch (no
+    workspace; allocates nothing)."""
+    torch = _torch()
+    n, d = X.shape
+    k = C_old.shape[0]
+    args = (_ptr(X, torch.float32, (n, d), "X"), _ptr(C_old, torch.float32, (k, d), "C_old"),
+            n, k, d, _ptr(labels, torch.int64, (n,), "labels"),
+            _ptr(min_dist, torch.float32, (n,), "min_dist"),
+            _ptr(C_new, torch.float32, (k, d), "C_new"), _ptr(counts, torch.int64, (k,), "counts"))
+    rc = lib().kmeans_lloyd_step_noalloc(*args, _stream(stream, X.device))
+    _check(rc, "kmeans_lloyd_step_noalloc")
+    _record(stream, X.device, X, C_old, labels, min_dist, C_new, counts)
 
 
 def kmeans_fit(X, C_init, max_iter, tol, flags, C_out, labels, min_dist, counts, info,

@@ -1,15 +1,24 @@
 // api.hip - the C ABI declared in include/kmeans_mi355x.h.
 //
 // Every entry point validates its arguments on the host before the first HIP
-// call, carves its sections out of the caller's workspace, and enqueues the
-// kernels on the caller's stream. Nothing here allocates or frees device
+// call, carves its sections out of the caller's workspace (or, in
+// kmeans_lloyd_step_noalloc, out of the static `scratch` array), and enqueues
+// the kernels on the caller's stream. Nothing here allocates or frees device
 // memory. kmeans_fit is the one call that may wait on its stream: it reads the
 // 4-byte convergence flag back to the host between batches of iterations
 // (after the first 4, then every 8). Global state:
 // the assignment launcher's cached compute-unit count per device and the
 // per-device address of `scratch`.
+#include <atomic>
+
 #include "../../include/kmeans_mi355x.h"
 #include "kernels.h"
+
+// Scratch of kmeans_lloyd_step_noalloc: one copy per GPU, alive until the
+// process ends. In host code `scratch` only names the symbol; its device
+// address comes from hipGetSymbolAddress (see noalloc_scratch below) and that
+// address is what the kernels get.
+__device__ __align__(256) unsigned char scratch[KM_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -188,6 +197,29 @@ int run_assign(const float *X, const float *C, int64_t n, int64_t k, int64_t d, 
     return e == hipSuccess ? KM_OK : KM_ERR_HIP;
 }
 
+// Device address of `scratch` on the device of `stream`, looked up once per
+// device (with that device current) and cached.
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_noalloc_scratch[kMaxDevices];
+
+int noalloc_scratch(hipStream_t stream, void **out) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return KM_ERR_HIP;
+    int dev = cur;
+    if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return KM_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return KM_ERR_HIP;
+    void *p = g_noalloc_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return KM_ERR_HIP;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return KM_ERR_HIP;
+        if (e != hipSuccess || p == nullptr) return KM_ERR_HIP;
+        g_noalloc_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return KM_OK;
+}
+
 km::UpdateScratch update_scratch(char *base, const Layout &L, int64_t n) {
     km::UpdateScratch ws;
     ws.tile_hist = (int *)(base + L.tile_hist);
@@ -203,8 +235,9 @@ km::UpdateScratch update_scratch(char *base, const Layout &L, int64_t n) {
     return ws;
 }
 
-// Argument checks of the Lloyd step (workspace != NULL is checked by the
-// caller).
+// Argument checks of the Lloyd step. workspace == NULL means the static
+// scratch of kmeans_lloyd_step_noalloc (its size is checked by the caller, and
+// it cannot overlap a caller's buffer).
 int check_lloyd(const float *X, const float *C_old, int64_t n, int64_t k, int64_t d,
                 const int64_t *labels, const float *min_dist, const float *C_new,
                 const int64_t *counts, const void *workspace, size_t workspace_bytes) {
@@ -269,6 +302,9 @@ const char *kmeans_status_string(int status) {
         case KM_ERR_ALIAS: return "an output overlaps an input, another output or the workspace";
         case KM_ERR_HIP: return "the HIP runtime rejected a kernel launch";
         case KM_ERR_OP: return "unknown op code or flag";
+        case KM_ERR_SCRATCH:
+            return "the shape needs more scratch than the static buffer of "
+                   "kmeans_lloyd_step_noalloc holds";
         default: return "unknown status";
     }
 }
@@ -319,6 +355,20 @@ int kmeans_lloyd_step(const float *X, const float *C_old, int64_t n, int64_t k, 
                              workspace_bytes))
         return rc;
     return run_lloyd(X, C_old, n, k, d, labels, min_dist, C_new, counts, ws_base(workspace),
+                     (hipStream_t)stream);
+}
+
+int kmeans_lloyd_step_noalloc(const float *X, const float *C_old, int64_t n, int64_t k,
+                              int64_t d, int64_t *labels, float *min_dist, float *C_new,
+                              int64_t *counts, void *stream) {
+    if (!shape_ok(n, k, d) || !grid_ok(n, k, d)) return KM_ERR_SHAPE;
+    if (layout(n, k, d, KM_OP_LLOYD).total > KM_NOALLOC_SCRATCH_BYTES) return KM_ERR_SCRATCH;
+    if (int rc = check_lloyd(X, C_old, n, k, d, labels, min_dist, C_new, counts, nullptr,
+                             KM_NOALLOC_SCRATCH_BYTES))
+        return rc;
+    void *ws = nullptr;
+    if (int rc = noalloc_scratch((hipStream_t)stream, &ws)) return rc;
+    return run_lloyd(X, C_old, n, k, d, labels, min_dist, C_new, counts, ws_base(ws),
                      (hipStream_t)stream);
 }
 

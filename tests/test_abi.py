@@ -13,7 +13,7 @@ from nearest_centroid_assignment_amd.datagen import CONFIGS
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kmeans_mi355x.h")
 
-OK, NULL, SHAPE, ALIGN, WORKSPACE, ALIAS, HIP, OP = 0, -1, -2, -3, -4, -5, -6, -7
+OK, NULL, SHAPE, ALIGN, WORKSPACE, ALIAS, HIP, OP, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
 # Fake, far-apart device addresses: validation never dereferences them. These
 # tests only run where no GPU is present, so a validation bug that let such a
@@ -39,14 +39,14 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"kmeans_workspace_bytes", "kmeans_assign", "kmeans_update",
-                          "kmeans_lloyd_step", "kmeans_fit", "kmeans_plusplus",
-                          "kmeans_status_string"}
+                          "kmeans_lloyd_step", "kmeans_lloyd_step_noalloc", "kmeans_fit",
+                          "kmeans_plusplus", "kmeans_status_string"}
     for name in names:
         assert hasattr(lib, name), name
 
 
 def test_status_strings(lib):
-    for code in (OK, NULL, SHAPE, ALIGN, WORKSPACE, ALIAS, HIP, OP):
+    for code in (OK, NULL, SHAPE, ALIGN, WORKSPACE, ALIAS, HIP, OP, SCRATCH):
         s = binding.kmeans_status_string(code)
         assert s and s != "unknown status"
     assert binding.kmeans_status_string(12345) == "unknown status"
@@ -190,6 +190,33 @@ def test_lloyd_validation(lib):
     assert call(counts=LAB_P + 16) == ALIAS
     assert call(md=CN_P) == ALIAS
     assert call(C_new=C_P + 4) == ALIAS
+
+
+@no_gpu
+def test_lloyd_noalloc_validation(lib):
+    """The no-allocation Lloyd step checks everything on the host before its
+    first HIP call: the scratch limit first, then the Lloyd step's checks."""
+    n, k, d = 100, 10, 8
+
+    def call(n=n, **kw):
+        a = dict(X=X_P, C_old=C_P, labels=LAB_P, md=MD_P, C_new=CN_P, counts=CNT_P)
+        a.update(kw)
+        return lib.kmeans_lloyd_step_noalloc(a["X"], a["C_old"], n, k, d, a["labels"], a["md"],
+                                             a["C_new"], a["counts"], None)
+
+    # 2^23 rows: the row permutation alone fills the 32 MiB scratch.
+    big_n = 1 << 23
+    assert binding.kmeans_workspace_bytes(big_n, k, d, 2) > 32 << 20
+    assert call(n=big_n) == SCRATCH
+    assert "static buffer" in binding.kmeans_status_string(SCRATCH)
+    assert call(n=-1) == SHAPE
+    assert call(C_new=None) == NULL
+    assert call(labels=LAB_P + 2) == ALIGN
+    assert call(counts=LAB_P + 16) == ALIAS
+    assert call(C_new=C_P + 4) == ALIAS
+    # Every workload of the pages fits.
+    for cfg in CONFIGS.values():
+        assert binding.kmeans_workspace_bytes(cfg.n, cfg.k, cfg.d, 2) <= 32 << 20
 
 
 def test_binding_rejects_cpu_tensors():
