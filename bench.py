@@ -109,6 +109,26 @@ def traffic_record(cfg):
     return rec.get("beyond_l2_bytes_per_launch")
 
 
+def host_info() -> dict:
+    """What the CPU baseline ran on: the CPU model, the CPUs this process may
+    use and OMP_NUM_THREADS as set (None when unset)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cpus = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        cpus = os.cpu_count()
+    return {"cpu_model": model, "cpus_available": cpus,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
 def cpu_baseline(X, C, target_s: float):
     """Time the float64 oracle's assignment on a seeded sample of rows against
     all centroids; scale to TFLOP/s of the same 2*rows*k*d work. The sample
@@ -136,6 +156,7 @@ def cpu_baseline(X, C, target_s: float):
         "kind": "oracle",
         "sample": f"{m} seeded rows x all {k} centroids x {d} features "
                   f"(float64 difference-form assignment, {t:.1f} s)",
+        **host_info(),
     }
 
 
@@ -162,6 +183,7 @@ def cpu_baseline_kmeanspp(X, k, first, trials, rand, target_s: float):
         "kind": "oracle",
         "sample": f"first {m} of {k} centres of the same seeding (float64 difference form, "
                   f"{t:.1f} s), scaled by (k - 1) / (m - 1)",
+        **host_info(),
     }
 
 

@@ -45,6 +45,7 @@ def test_cpu_baselines_report_their_sample():
     b = bench.cpu_baseline(X, C, 0.05)
     assert b["kind"] == "oracle" and b["unit"] == "TFLOP/s" and b["value"] > 0
     assert b["cores"] >= 1 and "rows" in b["sample"]
+    assert b["cpus_available"] >= 1 and "omp_num_threads" in b and "cpu_model" in b
     k, trials = 17, 4
     first, rand = datagen.make_seeding_draws(len(X), k, trials)
     p = bench.cpu_baseline_kmeanspp(X, k, first, trials, rand, 0.05)

@@ -395,3 +395,29 @@ def test_update_skewed_clusters(n, k, d, skew):
     frac = gu.check_update(X, labels, C, C_new.cpu().numpy(), counts.cpu().numpy())
     gu.announce(f"skewed update {skew}: bit-exact fraction in big clusters {frac:.6f}")
     assert frac > 0.99
+
+
+@pytest.mark.parametrize("n,k,d,tile", [(1000, 37, 64, None), (4096, 32, 64, None),
+                                        (65536, 256, 256, "256x256")])
+def test_overflowing_centroid_norms_keep_labels_in_range(monkeypatch, n, k, d, tile):
+    """Finite centroids whose float32 squared norm overflows: every candidate
+    distance of a row is +inf, so the lowest index wins the +inf tie, as for
+    any exact tie; labels stay in [0, k) and the update and the norms of a
+    Lloyd step (fused at k >= 16 ceil(d / 256)) only ever index valid rows.
+    With one finite centroid among them, that one wins every row."""
+    if tile:
+        monkeypatch.setenv("KMEANS_ASSIGN_TILE", tile)
+    gu.announce(f"overflowing norms {n}x{k}x{d} tile {tile}")
+    rng = np.random.default_rng(9)
+    X = rng.standard_normal((n, d)).astype(np.float32)
+    C = (np.float32(1e20) * np.sign(rng.standard_normal((k, d)))).astype(np.float32)
+    assert np.square(C.astype(np.float64)).sum(axis=1).min() > np.finfo(np.float32).max
+    labels, md, C_new, counts = gu.gpu_lloyd(X, C)
+    assert labels.min() >= 0 and labels.max() < k
+    assert np.all(labels == 0) and counts[0] == n and counts[1:].sum() == 0
+    assert np.all(np.isinf(md))
+    gu.check_update(X, labels, C, C_new, counts)
+    C[k // 2] = X[7]
+    labels, md, C_new, counts = gu.gpu_lloyd(X, C)
+    assert np.all(labels == k // 2) and counts[k // 2] == n
+    gu.check_update(X, labels, C, C_new, counts)
