@@ -25,12 +25,14 @@ int km_calib_copy(void *dst, const void *src, size_t bytes, void *stream);
 
 /*
  * Read `bytes` bytes of src once with 16-byte vector loads (blocks x 256
- * threads striding over the buffer, 8 loads in flight per thread) and write
- * one float per thread to out (blocks * 256 floats): the attainable read
- * bandwidth. Requires bytes % 16 == 0, src 16-byte aligned, blocks >= 1.
+ * threads striding over the buffer, 8 loads in flight per thread; ordinary
+ * or, with nontemporal != 0, non-temporal loads) and write one float per
+ * thread to out (blocks * 256 floats): the attainable read bandwidth.
+ * Requires bytes % 16 == 0, src 16-byte aligned, blocks >= 1.
  * Returns 0, -1 on invalid arguments, -6 if the launch is rejected.
  */
-int km_calib_read(const void *src, size_t bytes, float *out, int blocks, void *stream);
+int km_calib_read(const void *src, size_t bytes, float *out, int blocks, int nontemporal,
+                  void *stream);
 
 /*
  * Run `blocks` blocks of 256 threads, each wave issuing iters x 4

@@ -6,8 +6,8 @@
 * the bandwidth of a streaming 16-byte copy of a 2 GiB buffer;
 * the bandwidth of a streaming 16-byte read of a 4 GiB buffer (every byte
   read once; the ceiling of the update and k-means++ distance kernels, which
-  mostly read), at 1024 to 8192 blocks of 256 threads (the largest figure is
-  reported as ``read_gbps``).
+  mostly read), with ordinary and with non-temporal loads, at 512 to 2048
+  blocks of 256 threads (the largest figure is reported as ``read_gbps``).
 Both timed with HIP events on the launch stream (median of 5 after a warmup).
 The published peaks (157.3 TFLOP/s fp32 matrix, 8 TB/s HBM) stay the roofline;
 these numbers say how much of them the chip sustains here.
@@ -32,7 +32,7 @@ def lib():
     L.km_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     L.km_calib_read.restype = ctypes.c_int
     L.km_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
-                                ctypes.c_void_p]
+                                ctypes.c_int, ctypes.c_void_p]
     L.km_calib_mfma_f32.restype = ctypes.c_int
     L.km_calib_mfma_f32.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     return L
@@ -84,14 +84,17 @@ def run(copy_bytes: int = 2 << 30, blocks: int = 256 * 8, iters: int = 20000,
     del src, dst
     big = torch.ones(read_bytes // 4, dtype=torch.float32, device="cuda:0")
     reads = {}
-    for rb in (256 * 4, 256 * 8, 256 * 16, 256 * 32):
-        sink = torch.empty(rb * 256, dtype=torch.float32, device="cuda:0")
+    for nt in (0, 1):
+        for rb in (256 * 2, 256 * 3, 256 * 4, 256 * 6, 256 * 8):
+            sink = torch.empty(rb * 256, dtype=torch.float32, device="cuda:0")
 
-        def read():
-            if L.km_calib_read(big.data_ptr(), read_bytes, sink.data_ptr(), rb, stream) != 0:
-                raise RuntimeError("km_calib_read failed")
+            def read():
+                if L.km_calib_read(big.data_ptr(), read_bytes, sink.data_ptr(), rb, nt,
+                                   stream) != 0:
+                    raise RuntimeError("km_calib_read failed")
 
-        reads[rb] = read_bytes / (_time(read) * 1e-3) / 1e9
+            reads[f"{'nontemporal' if nt else 'ordinary'} {rb} blocks"] = \
+                read_bytes / (_time(read) * 1e-3) / 1e9
     return {
         "read_gbps": max(reads.values()),
         "read_gbps_by_blocks": reads,

@@ -25,6 +25,9 @@ __global__ __launch_bounds__(256) void copy_kernel(f32x4 *__restrict__ dst,
 
 // Each thread sums its share of the buffer (8 independent 16-byte loads in
 // flight per loop trip) and writes one float, so the reads cannot be dropped.
+// kNT: non-temporal loads (the data is not kept in the caches for reuse),
+// the fastest way found to stream a buffer that is read once.
+template <bool kNT>
 __global__ __launch_bounds__(256) void read_kernel(const f32x4 *__restrict__ src, int64_t n,
                                                    float *__restrict__ out) {
     constexpr int U = 8;
@@ -37,7 +40,8 @@ __global__ __launch_bounds__(256) void read_kernel(const f32x4 *__restrict__ src
     for (; i + (U - 1) * stride < n; i += U * stride) {
         f32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = src[i + u * stride];
+        for (int u = 0; u < U; ++u)
+            v[u] = kNT ? __builtin_nontemporal_load(src + i + u * stride) : src[i + u * stride];
 #pragma unroll
         for (int u = 0; u < U; ++u) a[u] += (v[u].x + v[u].y) + (v[u].z + v[u].w);
     }
@@ -87,10 +91,15 @@ int km_calib_copy(void *dst, const void *src, size_t bytes, void *stream) {
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
-int km_calib_read(const void *src, size_t bytes, float *out, int blocks, void *stream) {
+int km_calib_read(const void *src, size_t bytes, float *out, int blocks, int nontemporal,
+                  void *stream) {
     if (!src || !out || blocks < 1 || bytes % 16 != 0 || (uintptr_t)src % 16) return -1;
-    read_kernel<<<(unsigned)blocks, 256, 0, (hipStream_t)stream>>>((const f32x4 *)src,
-                                                                   (int64_t)(bytes / 16), out);
+    if (nontemporal)
+        read_kernel<true><<<(unsigned)blocks, 256, 0, (hipStream_t)stream>>>(
+            (const f32x4 *)src, (int64_t)(bytes / 16), out);
+    else
+        read_kernel<false><<<(unsigned)blocks, 256, 0, (hipStream_t)stream>>>(
+            (const f32x4 *)src, (int64_t)(bytes / 16), out);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

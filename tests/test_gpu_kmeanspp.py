@@ -70,19 +70,33 @@ def test_pp_blobs(name):
     assert np.array_equal(ch, want)
 
 
-def test_pp_pages_shape_prefix():
-    """65536 x 1024 x 8192 (the pages' k-means++ timing shape): the GPU seeds
-    all 1024 centres; seeding is sequential, so its first 12 centres must be
-    the oracle's 12 centres from the same draws."""
+def test_pp_pages_shape_all_centres():
+    """65536 x 1024 x 8192 (the pages' k-means++ timing shape): all 1024
+    centres the GPU seeds equal the oracle's, in order, from the same draws.
+    The oracle's full seeding (minutes of host time) is stored in
+    tests/golden/kmeanspp_seeding.npz by tests/golden/make_kmeanspp_expected.py;
+    the test checks that X and the draws hash as they did there, and re-runs
+    the oracle live on the first 12 centres to vouch for the file."""
+    from tests.golden import make_full_size_expected as golden
+    from tests.golden import make_kmeanspp_expected as golden_pp
+
     gu.announce("kmeans++ 65536x1024x8192: generating")
     cfg = datagen.CONFIGS["kmeanspp"]
     X, _ = datagen.make(cfg)
     trials = oracle.default_trials(cfg.k)
     first, rand = datagen.make_seeding_draws(cfg.n, cfg.k, trials)
+    with np.load(golden_pp.PATH, allow_pickle=False) as z:
+        exp = {key: z[key] for key in z.files}
+    assert (int(exp["n"]), int(exp["k"]), int(exp["d"])) == (cfg.n, cfg.k, cfg.d)
+    assert int(exp["first"]) == first and int(exp["trials"]) == trials
+    assert str(exp["x_sha256"]) == golden.sha256_of(X)
+    assert str(exp["rand_sha256"]) == golden.sha256_of(rand)
     gu.announce("kmeans++ 65536x1024x8192: GPU seeding")
     C, ch = gpu_pp(X, cfg.k, first, trials, rand)
-    assert len(set(ch.tolist())) == cfg.k
-    gu.announce("kmeans++ 65536x1024x8192: oracle prefix of 12 centres")
+    assert np.array_equal(ch, exp["chosen"]), \
+        f"first difference at centre {int(np.argmax(ch != exp['chosen']))}"
+    assert np.array_equal(C, X[exp["chosen"]])
+    gu.announce("kmeans++ 65536x1024x8192: oracle prefix of 12 centres, live")
     want = oracle.kmeanspp(X, 12, first, trials, rand[:11])
-    assert np.array_equal(ch[:12], want)
-    assert np.array_equal(C[:12], X[want])
+    assert np.array_equal(want, exp["chosen"][:12])
+    gu.announce("kmeans++ 65536x1024x8192: all 1024 centres equal")
