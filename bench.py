@@ -36,7 +36,7 @@ HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E bandwidth (published)
 PAGES_KMEANSPP_MS = 10300.0
 # The pages' Lloyd-iteration times on an NVIDIA L4, per workload (context).
 PAGES_LLOYD_MS = {"feature_heavy": 1700.0, "centroid_heavy": 3853.0}
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "assign_tile_feature_heavy_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "assign_dma_feature_heavy_traffic.json")
 
 
 def log(msg: str) -> None:

@@ -109,11 +109,24 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 // three blocks per CU, 96 KiB of samples per CU.
 // Output layout (probed on the chip): lane l, value i is sample (l / 16) +
 // 4 i of the wave's 16, candidate slot l % 16.
+//
+// With at most 8 trials (kSlots = 8; 8 at the pages' k = 1024) half of those
+// 16 slots would multiply zeros, so the product runs on
+// v_mfma_f64_4x4x4_4b_f64 instead: four independent 4 x 4 x 4 blocks per
+// instruction, a quarter of the 16 x 16 x 4 work. Its layout (probed on the
+// chip): lane 16k + 4b + i holds A[b][i][k], lane 16k + 4b + j holds
+// B[b][k][j], and lane 16i + 4b + j receives D[b][i][j]. Block b takes samples
+// 4b .. 4b+3 of the wave: the A operand is sample l % 16, feature k-group
+// l / 16 -- the same lane layout as the 16 x 16 x 4 product, so the sample
+// staging is unchanged -- and B is candidate 4h + l % 4 in the two
+// instructions h = 0, 1 of each feature step. Each lane then ends with two
+// values: sample 4 ((l / 4) % 4) + l / 16 against candidates l % 4 and
+// 4 + l % 4.
 constexpr int kMfF = 128;           // features per stage
 constexpr int kMfRun = kMfF / 4;    // contiguous features per lane per stage
 constexpr int kMfLdk = kMfF + 4;    // padded LDS row of a candidate
 
-template <bool kVec>
+template <bool kVec, int kSlots>
 __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
     const float *__restrict__ X, const double *__restrict__ xnorm, int64_t n, int64_t d,
     int trials, const long long *__restrict__ cand, const PPState *__restrict__ st,
@@ -175,7 +188,8 @@ __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
     store_c(0, cv);
     __syncthreads();
 
-    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};  // kSlots == 16
+    double acc8[2] = {0.0, 0.0};       // kSlots == 8: candidates l % 4 and 4 + l % 4
     for (int64_t c = 0; c < chunks; ++c) {
         const int cur = (int)(c & 1);
         // This lane's A operands of the stage (its own wave's slice: the
@@ -190,14 +204,32 @@ __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
             load_c(c + 1, cv);
         }
         // Features beyond d were loaded as 0 for samples and candidates alike.
-        const float *brow = &cs[cur][lane & 15][grp * kMfRun];
+        if constexpr (kSlots == 16) {
+            const float *brow = &cs[cur][lane & 15][grp * kMfRun];
 #pragma unroll
-        for (int q = 0; q < kMfRun / 4; ++q) {
-            const float4 bv = *reinterpret_cast<const float4 *>(brow + 4 * q);
-            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[q].x, (double)bv.x, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[q].y, (double)bv.y, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[q].z, (double)bv.z, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[q].w, (double)bv.w, acc, 0, 0, 0);
+            for (int q = 0; q < kMfRun / 4; ++q) {
+                const float4 bv = *reinterpret_cast<const float4 *>(brow + 4 * q);
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[q].x, (double)bv.x, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[q].y, (double)bv.y, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[q].z, (double)bv.z, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[q].w, (double)bv.w, acc, 0, 0, 0);
+            }
+        } else {
+            const float *b0 = &cs[cur][lane & 3][grp * kMfRun];
+            const float *b1 = &cs[cur][4 + (lane & 3)][grp * kMfRun];
+#pragma unroll
+            for (int q = 0; q < kMfRun / 4; ++q) {
+                const float4 v0 = *reinterpret_cast<const float4 *>(b0 + 4 * q);
+                const float4 v1 = *reinterpret_cast<const float4 *>(b1 + 4 * q);
+                acc8[0] = __builtin_amdgcn_mfma_f64_4x4x4f64((double)xa[q].x, (double)v0.x, acc8[0], 0, 0, 0);
+                acc8[1] = __builtin_amdgcn_mfma_f64_4x4x4f64((double)xa[q].x, (double)v1.x, acc8[1], 0, 0, 0);
+                acc8[0] = __builtin_amdgcn_mfma_f64_4x4x4f64((double)xa[q].y, (double)v0.y, acc8[0], 0, 0, 0);
+                acc8[1] = __builtin_amdgcn_mfma_f64_4x4x4f64((double)xa[q].y, (double)v1.y, acc8[1], 0, 0, 0);
+                acc8[0] = __builtin_amdgcn_mfma_f64_4x4x4f64((double)xa[q].z, (double)v0.z, acc8[0], 0, 0, 0);
+                acc8[1] = __builtin_amdgcn_mfma_f64_4x4x4f64((double)xa[q].z, (double)v1.z, acc8[1], 0, 0, 0);
+                acc8[0] = __builtin_amdgcn_mfma_f64_4x4x4f64((double)xa[q].w, (double)v0.w, acc8[0], 0, 0, 0);
+                acc8[1] = __builtin_amdgcn_mfma_f64_4x4x4f64((double)xa[q].w, (double)v1.w, acc8[1], 0, 0, 0);
+            }
         }
         if (c + 1 < chunks) {
             store_x(xn);
@@ -206,42 +238,73 @@ __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
         __syncthreads();
     }
 
-    // D for this lane's 4 samples against candidate slot t; the sample that is
-    // the candidate itself gets exactly 0.
-    const int t = lane & 15;
-    double part = 0.0;
+    // D for this lane's samples against its candidate slots; the sample that
+    // is the candidate itself gets exactly 0.
+    auto dist_of = [&](int64_t gi, int t, double dot) {
+        const double dist =
+            gi == cand_row[t] ? 0.0 : __builtin_fma(-2.0, dot, xnorm[gi] + cand_norm[t]);
+        const double pos = dist > 0.0 ? dist : 0.0;
+        const double cur_d = closest ? closest[gi] : __builtin_inf();
+        const double nd = pos < cur_d ? pos : cur_d;
+        out_buf[(int64_t)t * n + gi] = nd;
+        return nd;
+    };
+    if constexpr (kSlots == 16) {
+        // Lane l: samples l / 16 + 4 i against slot l % 16.
+        const int t = lane & 15;
+        double part = 0.0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t gi = row0 + grp + 4 * i;
-        if (t < trials && gi < n) {
-            const double dist =
-                gi == cand_row[t] ? 0.0 : __builtin_fma(-2.0, acc[i], xnorm[gi] + cand_norm[t]);
-            const double pos = dist > 0.0 ? dist : 0.0;
-            const double cur_d = closest ? closest[gi] : __builtin_inf();
-            const double nd = pos < cur_d ? pos : cur_d;
-            out_buf[(int64_t)t * n + gi] = nd;
-            part += nd;
+        for (int i = 0; i < 4; ++i) {
+            const int64_t gi = row0 + grp + 4 * i;
+            if (t < trials && gi < n) part += dist_of(gi, t, acc[i]);
+        }
+        // The four lanes of candidate t (t, t + 16, t + 32, t + 48), then
+        // the waves in order.
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        if (lane < 16) wpart[wave][lane] = part;
+    } else {
+        // Lane l: sample 4 ((l / 4) % 4) + l / 16 against slots l % 4 and
+        // 4 + l % 4; the 16 lanes of a slot differ in bits 2 .. 5.
+        const int64_t gi = row0 + 4 * ((lane >> 2) & 3) + grp;
+        double part[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int t = 4 * h + (lane & 3);
+            part[h] = (t < trials && gi < n) ? dist_of(gi, t, acc8[h]) : 0.0;
+#pragma unroll
+            for (int o = 4; o < 64; o <<= 1) part[h] += __shfl_xor(part[h], o);
+        }
+        if (lane < 4) {
+            wpart[wave][lane] = part[0];
+            wpart[wave][4 + lane] = part[1];
         }
     }
-    // The four lanes of candidate t (t, t + 16, t + 32, t + 48), then the
-    // waves in order.
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-    if (lane < 16) wpart[wave][lane] = part;
     __syncthreads();
     if (tid < trials)
         out_parts[(int64_t)tid * nb + b] = ((wpart[0][tid] + wpart[1][tid]) + wpart[2][tid]) + wpart[3][tid];
 }
 
+template <int kSlots>
+void launch_dist_slots(bool vec, int trials, unsigned nb, hipStream_t stream, const float *X,
+                       const double *xnorm, int64_t n, int64_t d, const long long *cand,
+                       const PPState *st, const double *prev, double *out, double *parts) {
+    if (vec)
+        pp_dist_kernel<true, kSlots><<<nb, 256, 0, stream>>>(X, xnorm, n, d, trials, cand, st,
+                                                             prev, out, parts, nb);
+    else
+        pp_dist_kernel<false, kSlots><<<nb, 256, 0, stream>>>(X, xnorm, n, d, trials, cand, st,
+                                                              prev, out, parts, nb);
+}
+
 void launch_dist(int trials, bool vec, unsigned nb, hipStream_t stream, const float *X,
                  const double *xnorm, int64_t n, int64_t d, const long long *cand,
                  const PPState *st, const double *prev, double *out, double *parts) {
-    if (vec)
-        pp_dist_kernel<true><<<nb, 256, 0, stream>>>(X, xnorm, n, d, trials, cand, st, prev, out,
-                                                     parts, nb);
+    if (trials <= 8)
+        launch_dist_slots<8>(vec, trials, nb, stream, X, xnorm, n, d, cand, st, prev, out, parts);
     else
-        pp_dist_kernel<false><<<nb, 256, 0, stream>>>(X, xnorm, n, d, trials, cand, st, prev, out,
-                                                      parts, nb);
+        launch_dist_slots<16>(vec, trials, nb, stream, X, xnorm, n, d, cand, st, prev, out,
+                              parts);
 }
 
 constexpr int kSelWaves = 16;  // pp_select_kernel: one 1024-thread block

@@ -2,11 +2,12 @@
 
 run (default):
     python3 -m nearest_centroid_assignment_amd.profile_run [--workload feature_heavy]
-        [--op assign|update]
+        [--op assign|update|kmeanspp]
   launches, in order and each once: a 1 GiB streaming copy (calibration), then
   on the workload's seeded inputs either one ``kmeans_assign`` (no min_dist;
   op assign) or one ``kmeans_assign`` followed by one ``kmeans_update`` with
-  its labels (op update). Meant to be run under ``rocprofv3 --pmc FETCH_SIZE``
+  its labels (op update), or one k-means++ seeding of k centres (op kmeanspp).
+  Meant to be run under ``rocprofv3 --pmc FETCH_SIZE``
   and, separately, under ``rocprofv3 --pmc WRITE_SIZE`` (csv output), or with
   other counters.
 
@@ -77,6 +78,20 @@ def run(workload: str, op: str = "assign") -> None:
     cfg = datagen.CONFIGS[workload]
     X, C = datagen.make(cfg)
     Xg, Cg = torch.from_numpy(X).to(dev), torch.from_numpy(C).to(dev)
+    if op == "kmeanspp":
+        # The seeding's trial count 2 + floor(ln k) (the pages' 2 + log k), here
+        # written out so that this module needs nothing from the oracle.
+        import math
+
+        trials = 2 + int(math.log(cfg.k))
+        first, rand = datagen.make_seeding_draws(cfg.n, cfg.k, trials)
+        rg = torch.from_numpy(rand.reshape(-1).copy()).to(dev)
+        torch.cuda.synchronize()
+        print(f"[profile_run] kmeans_plusplus {cfg.name} {cfg.n}x{cfg.d}, k={cfg.k}", flush=True)
+        binding.plusplus(Xg, cfg.k, first, trials, rg)
+        torch.cuda.synchronize()
+        print("[profile_run] done", flush=True)
+        return
     labels = torch.empty(cfg.n, dtype=torch.int64, device=dev)
     torch.cuda.synchronize()
     print(f"[profile_run] kmeans_assign {cfg.name} {cfg.n}x{cfg.k}x{cfg.d}", flush=True)
@@ -179,7 +194,7 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("mode", nargs="?", default="run", choices=["run", "summarize", "kernels"])
     ap.add_argument("--workload", default="feature_heavy")
-    ap.add_argument("--op", default="assign", choices=["assign", "update"])
+    ap.add_argument("--op", default="assign", choices=["assign", "update", "kmeanspp"])
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--out")
