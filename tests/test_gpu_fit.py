@@ -146,3 +146,33 @@ def test_fit_relocates_many_empty_clusters(n, k_near, k_far, seed):
     g = gpu_fit(X, C, 5, 0.0, True)
     o = oracle.fit(X, C, 5, 0.0, True)
     compare(g, o, X)
+
+
+def test_fit_large_k_relocation():
+    """k = 17000 (above the 16384 clusters the counting sort keeps in LDS and
+    scans in registers): 16600 far centres win nothing and take 16600 of the
+    40000 samples in one relocation; each becomes the centre of its own
+    cluster, so no cluster is empty after it. One iteration is compared with
+    the oracle's driver outright. Later iterations mix integer one-sample
+    centres with float32-rounded means whose exact distances to integer
+    samples are rationals that can equal an integer distance: such rows are
+    true ties broken by rounding, so the trajectories may part there. After
+    three iterations the result is checked for what the driver promises: the
+    labels are the nearest-centroid labels of the returned centres (near-tie
+    rule), and counts, min_dist and inertia agree with them."""
+    gu.announce("fit k=17000 with 16600 empty clusters")
+    X, C = datagen.make_integer(40000, 400, 16, seed=21)
+    C = np.concatenate([C, np.full((16600, 16), 1e4, np.float32)]).astype(np.float32)
+    g = gpu_fit(X, C, 1, 0.0, True)
+    o = oracle.fit(X, C, 1, 0.0, True)
+    compare(g, o, X)
+    assert g["counts"].min() >= 1
+    g = gpu_fit(X, C, 3, 0.0, True)
+    assert g["n_iter"] == 3
+    Cf = g["centres"]
+    o_labels, best, second = oracle.assign(X, Cf)
+    ties, mism = gu.check_labels(X, Cf, g["labels"], o_labels, best, second)
+    gu.announce(f"fit k=17000, 3 iterations: near-ties {ties}, label mismatches {mism}")
+    gu.check_min_dist(X, Cf, g["labels"], g["min_dist"], o_labels=o_labels, best=best)
+    assert np.array_equal(g["counts"], np.bincount(g["labels"], minlength=len(C)))
+    assert abs(g["inertia"] - float(np.sum(g["min_dist"].astype(np.float64)))) <= 1e-9 * g["inertia"]

@@ -130,6 +130,52 @@ def test_lloyd_min_dist_paths(n, k, d, what):
     assert np.all(np.abs(l_md.astype(np.float64) - a_md) <= 4e-6 * xn + 1e-6)
 
 
+# The counting sort's paths by k: the cluster scan holds 1, 2, 4, 8 or 16
+# clusters per thread in registers up to k = 16384 and takes 1024-cluster
+# chunks above; the per-tile label table sits in LDS up to k = 16384 and in the
+# tile's global histogram column above; more than 64 sort tiles of 1024 rows
+# take the batched tile prefix.
+COUNT_PATHS = [
+    (30000, 1025, 8, "2 clusters per thread, 2 scan blocks"),
+    (66000, 2049, 8, "4 per thread, 65 sort tiles"),
+    (30000, 8193, 8, "16 per thread, 9 scan blocks"),
+    (20000, 16385, 8, "global label table, chunked scan"),
+    (12000, 40000, 4, "k > n: global table, chunked scan, 40 scan blocks"),
+]
+
+
+@pytest.mark.parametrize("n,k,d,what", COUNT_PATHS,
+                         ids=[f"{n}x{k}x{d}" for n, k, d, _ in COUNT_PATHS])
+def test_lloyd_count_paths(n, k, d, what):
+    """The whole Lloyd step (labels from the assignment's packed keys) on every
+    row, at k on each side of the counting sort's limits."""
+    gu.announce(f"lloyd count path {n}x{k}x{d} ({what})")
+    rng = np.random.default_rng(n ^ k)
+    X = rng.standard_normal((n, d), dtype=np.float32)
+    C = rng.standard_normal((k, d), dtype=np.float32)
+    res = gu.full_parity(X, C)
+    assert res["mismatches"] <= res["near_ties"]
+
+
+@pytest.mark.parametrize("n,k,d", [(50000, 20000, 33), (70000, 17000, 16), (3000, 16384, 8)])
+def test_update_count_paths(n, k, d):
+    """kmeans_update on given labels (the other entry to the counting sort)
+    with k at and above the LDS table limit, up to 69 sort tiles."""
+    from nearest_centroid_assignment_amd import binding
+    import torch
+
+    gu.announce(f"update count path {n}x{k}x{d}")
+    rng = np.random.default_rng(n + 3 * k)
+    X = rng.standard_normal((n, d), dtype=np.float32)
+    C = rng.standard_normal((k, d), dtype=np.float32)
+    labels = rng.integers(0, k, size=n).astype(np.int64)
+    C_new, counts = binding.update(gu.to_gpu(X), gu.to_gpu(labels), gu.to_gpu(C))
+    torch.cuda.synchronize()
+    counts = counts.cpu().numpy()
+    assert np.array_equal(counts, np.bincount(labels, minlength=k))
+    gu.check_update(X, labels, C, C_new.cpu().numpy(), counts)
+
+
 @pytest.mark.parametrize("n,k,d", [(500, 37, 64), (1500, 260, 256), (129, 130, 12)])
 def test_integer_exact(n, k, d):
     """|values| <= 8, d <= 256: every float32 product and partial sum is an
