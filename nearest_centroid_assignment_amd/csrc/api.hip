@@ -75,8 +75,8 @@ Layout layout(int64_t n, int64_t k, int64_t d, int op) {
         off += round_up((size_t)k * sizeof(int));
         L.rank = off;
         off += round_up((size_t)n * sizeof(unsigned short));
-        L.flags = off;  // scan completion counter, no-empty flag
-        off += round_up(2 * sizeof(int));
+        L.flags = off;  // no-empty flag
+        off += round_up(sizeof(int));
     }
     if (op == KM_OP_LLOYD && lloyd_fuses_norms(k, d)) {
         L.xn_part = off;
@@ -229,8 +229,7 @@ km::UpdateScratch update_scratch(char *base, const Layout &L, int64_t n) {
     ws.big = (int *)(base + L.big);
     ws.order = (int *)(base + L.order);
     ws.rank = (unsigned short *)(base + L.rank);
-    ws.done = (unsigned *)(base + L.flags);
-    ws.no_empty = (int *)(base + L.flags) + 1;
+    ws.no_empty = (int *)(base + L.flags);
     ws.n_tiles = cdiv(n, km::kSortTileRows);
     return ws;
 }

@@ -22,7 +22,6 @@ struct UpdateScratch {
     int *big;                // k + 1: the number of clusters with more than the split
                              // size, then their indices in increasing order
     int *order;              // k: the other clusters, grouped by load rounds (most first)
-    unsigned *done;          // 1: blocks of the scan kernel that have finished
     int *no_empty;           // 1: set by a count that reports empty clusters: 1 when
                              // there are none
     int64_t n_tiles;         // ceil(n / kSortTileRows)

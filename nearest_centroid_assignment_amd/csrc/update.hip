@@ -11,10 +11,11 @@
 //                        tile's rows with the same label (stable), and the
 //                        tile's histogram column; in a Lloyd step fused with
 //                        the assignment's finalize (keys -> labels)
-//   scan_kernel          per cluster: exclusive prefix over tiles, cluster
-//                        size; the last block to finish: exclusive prefix
-//                        over clusters -> segment starts, counts, and the
-//                        lists the mean kernel schedules by
+//   tile_prefix_kernel   per cluster: exclusive prefix over tiles, cluster
+//                        size
+//   cluster_scan_kernel  one block: exclusive prefix over clusters ->
+//                        segment starts, counts, and the lists the mean
+//                        kernel schedules by
 //   scatter_kernel       perm[segment start + rows of the cluster in earlier
 //                        tiles + rank] = row   (stable)
 //   segment_mean_kernel  float64 sums over each segment, coalesced row chunks,
@@ -47,12 +48,6 @@ constexpr int kBigWaves = 16;              // waves (parts) per big-cluster bloc
 constexpr int kBigBlocks = 256;            // segment_mean blocks that take the large clusters
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-__global__ __launch_bounds__(256) void fill_u32_kernel(unsigned *__restrict__ p, int64_t count) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride)
-        p[i] = 0u;
-}
 
 // Rank of each lane's label among the lanes below it with the same label
 // (stable), and how many lanes hold that label. Lanes with valid == false
@@ -108,7 +103,6 @@ __device__ __forceinline__ void table_store(int *p, int v) {
 // kFromKeys: the labels come from the assignment's packed keys, turned into
 // int64 labels in place first (and min_dist, as finalize_kernel does; the
 // index of a key is always < k, and is clamped to be sure).
-// Block 0 also zeroes the scan kernel's completion counter.
 template <bool kLds, bool kFromKeys>
 __global__ __launch_bounds__(kTile) void rank_hist_kernel(const int64_t *__restrict__ labels,
                                                           unsigned long long *__restrict__ keys,
@@ -116,7 +110,7 @@ __global__ __launch_bounds__(kTile) void rank_hist_kernel(const int64_t *__restr
                                                           bool add_norm, int64_t n, int64_t k,
                                                           int *__restrict__ tile_hist,
                                                           unsigned short *__restrict__ rank_out,
-                                                          unsigned *__restrict__ done, Gate gate) {
+                                                          Gate gate) {
     extern __shared__ int lds_table[];
     if (gated(gate)) return;
     const int tid = threadIdx.x, wave = tid >> 6;
@@ -138,7 +132,6 @@ __global__ __launch_bounds__(kTile) void rank_hist_kernel(const int64_t *__restr
             l = (v >= 0 && v < k) ? (int)v : -1;
         }
     }
-    if (b == 0 && tid == 0) *done = 0u;
     int *table = kLds ? lds_table : tile_hist + b * k;
     for (int64_t j = tid; j < k; j += kTile) table_store<kLds>(table + j, 0);
     int rank, count;
@@ -220,30 +213,52 @@ __device__ __forceinline__ int unpack_half(int packed, int half) {
     return (packed >> (16 * half)) & 0xffff;
 }
 
-// The cluster scan of the last scan block, for k <= 1024 * R: thread t holds
-// clusters t*R .. t*R + R - 1 in registers. Writes seg_start (exclusive prefix
-// of the sizes), counts (int64 sizes), big[0] = number of clusters above
-// kSplit rows and big[1 ..] their indices in increasing order, order = the
-// other clusters grouped by load-round class, most rounds first, increasing
-// index within a class (ranks from scans, so the order is the same on every
-// run; the mean kernel gives 16 consecutive entries of `order` to one block,
-// so a block's waves run the same number of load rounds), and the number of
-// empty clusters.
+// The cluster scan, one block of 1024 threads, for k <= 1024 * R: thread t
+// takes clusters t*R .. t*R + R - 1. Writes seg_start (exclusive prefix of the
+// sizes), counts (int64 sizes), big[0] = number of clusters above kSplit rows
+// and big[1 ..] their indices in increasing order, order = the other clusters
+// grouped by load-round class, most rounds first, increasing index within a
+// class (ranks from scans, so the order is the same on every run; the mean
+// kernel gives 16 consecutive entries of `order` to one block, so a block's
+// waves run the same number of load rounds), and the number of empty
+// clusters. With R > 1 the sizes come in and the segment starts and the order
+// go out through LDS, so that every global access of a wave covers
+// consecutive clusters (a thread's own R clusters are R apart from its
+// neighbours'); the size table is padded by one word every 32 so that the
+// threads' strided LDS accesses fall in distinct banks.
+template <int R>
+__device__ __forceinline__ int padded(int j) {
+    return R > 1 ? j + (j >> 5) : j;
+}
+
 template <int R, int kSplit>
 __device__ void cluster_scan_regs(const int *cnt, int64_t k, int *seg_start, int64_t *counts,
-                                  int *num_empty, int *no_empty, int *big, int *order, int own) {
+                                  int *num_empty, int *no_empty, int *big, int *order) {
     static_assert(R * 1024 < 65536, "packed class counts need k < 2^16");
     constexpr int kClasses = kSplit / 8 + 1;
     constexpr int kPacked = (kClasses + 1) / 2;
     constexpr int Q = 2 + kPacked;  // sizes; above-split | empty << 16; classes, two per int
+    constexpr int N = 1024 * R;
+    __shared__ int sizes[R > 1 ? N + N / 32 : 1];  // sizes, then segment starts
+    __shared__ int placed[R > 1 ? N : 1];          // the order list
     const int tid = threadIdx.x;
     const int64_t j0 = (int64_t)tid * R;
     int v[R];
-    if (R == 1 && cnt == nullptr) {
-        v[0] = j0 < k ? own : -1;  // one block: the thread's own cluster, in a register
+    if (R == 1) {
+        v[0] = j0 < k ? cnt[j0] : -1;
     } else {
 #pragma unroll
-        for (int e = 0; e < R; ++e) v[e] = j0 + e < k ? coherent_load(cnt + j0 + e) : -1;
+        for (int e = 0; e < R; ++e) {
+            const int j = e * 1024 + tid;
+            const int c = cnt[j < k ? j : k - 1];  // no condition on the load: all R in flight
+            if (j < k) {
+                sizes[padded<R>(j)] = c;
+                counts[j] = c;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < R; ++e) v[e] = j0 + e < k ? sizes[padded<R>((int)j0 + e)] : -1;
     }
     int x[Q];
 #pragma unroll
@@ -257,7 +272,7 @@ __device__ void cluster_scan_regs(const int *cnt, int64_t k, int *seg_start, int
         add_class<kClasses>(cls, round_class<kSplit>(v[e]));
     }
     int pos[Q], tot[Q];
-    block_excl_scan<Q>(x, pos, tot);
+    block_excl_scan<Q>(x, pos, tot);  // (its barriers also order the LDS reads above)
     // Class c starts after every class with more rounds: fold that start into
     // the thread's packed positions.
     int start = 0;
@@ -266,15 +281,20 @@ __device__ void cluster_scan_regs(const int *cnt, int64_t k, int *seg_start, int
         pos[2 + c / 2] += start << (16 * (c & 1));
         start += unpack_half(tot[2 + c / 2], c & 1);
     }
+    const int n_ordered = start;
     int seg = pos[0], bpos = pos[1] & 0xffff;
 #pragma unroll
     for (int e = 0; e < R; ++e) {
         if (v[e] < 0) continue;
-        const int64_t j = j0 + e;
-        seg_start[j] = seg;
-        counts[j] = v[e];
+        const int j = (int)j0 + e;
+        if (R == 1) {
+            seg_start[j] = seg;
+            counts[j] = v[e];
+        } else {
+            sizes[padded<R>(j)] = seg;  // this thread's own slots only
+        }
         seg += v[e];
-        if (v[e] > kSplit) big[1 + bpos++] = (int)j;
+        if (v[e] > kSplit) big[1 + bpos++] = j;
         const int cl = round_class<kSplit>(v[e]);
         if (cl >= 0) {
             int at = 0;
@@ -284,7 +304,19 @@ __device__ void cluster_scan_regs(const int *cnt, int64_t k, int *seg_start, int
                     at = unpack_half(pos[2 + p], cl & 1);
                     pos[2 + p] += 1 << (16 * (cl & 1));
                 }
-            order[at] = (int)j;
+            if (R == 1)
+                order[at] = j;
+            else
+                placed[at] = j;
+        }
+    }
+    if (R > 1) {
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < R; ++e) {
+            const int j = e * 1024 + tid;
+            if (j < k) seg_start[j] = sizes[padded<R>(j)];
+            if (j < n_ordered) order[j] = placed[j];
         }
     }
     if (tid == 0) {
@@ -313,7 +345,7 @@ __device__ void cluster_scan_chunked(const int *cnt, int64_t k, int *seg_start, 
     // Pass 1: class totals.
     for (int64_t base = 0; base < k; base += 1024) {
         const int64_t j = base + tid;
-        const int v = j < k ? coherent_load(cnt + j) : -1;
+        const int v = j < k ? cnt[j] : -1;
         int x[Q], p[Q], t[Q];
 #pragma unroll
         for (int q = 0; q < Q; ++q) x[q] = 0;
@@ -336,7 +368,7 @@ __device__ void cluster_scan_chunked(const int *cnt, int64_t k, int *seg_start, 
     int seg_carry = 0, big_carry = 0, empty_carry = 0;
     for (int64_t base = 0; base < k; base += 1024) {
         const int64_t j = base + tid;
-        const int v = j < k ? coherent_load(cnt + j) : -1;
+        const int v = j < k ? cnt[j] : -1;
         const int cl = v >= 0 ? round_class<kSplit>(v) : -1;
         int x[Q], p[Q], t[Q];
         x[0] = v >= 0 ? v : 0;
@@ -369,77 +401,64 @@ __device__ void cluster_scan_chunked(const int *cnt, int64_t k, int *seg_start, 
     }
 }
 
-// Per cluster j (a thread each, 1024 per block): the exclusive prefix of its
-// tile counts over the tiles, in place, and its size cnt[j]. The loads of a
-// wave read 64 consecutive clusters of one tile (the tile's histogram column
-// is contiguous); the next U tiles' loads are issued before the current U
-// tiles' stores, so a thread waits for memory once per U tiles. Then the
-// cluster scan runs in one block: with one block it is that block; otherwise
-// the last block to finish (a counter zeroed by rank_hist_kernel; every block
-// fences its writes before counting itself; on this chip those fences write
-// back and invalidate the L2, so a one-block grid skips them).
-template <int R, int kSplit>
-__global__ __launch_bounds__(1024) void scan_kernel(int *__restrict__ tile_hist, int64_t k,
-                                                    int64_t n_tiles, int *__restrict__ cnt,
-                                                    int *__restrict__ seg_start,
-                                                    int64_t *__restrict__ counts,
-                                                    int *__restrict__ num_empty,
-                                                    int *__restrict__ no_empty,
-                                                    int *__restrict__ big,
-                                                    int *__restrict__ order,
-                                                    unsigned *__restrict__ done, Gate gate) {
-    __shared__ int is_last;
+// Per cluster j (a thread each, one wave per block, so that the loads and
+// stores spread over k / 64 compute units): the exclusive prefix of its tile
+// counts over the tiles, in place, and its size cnt[j]. The loads of a wave
+// read 64 consecutive clusters of one tile (the tile's histogram column is
+// contiguous); the next U tiles' loads are issued before the current U
+// tiles' stores, so a thread waits for memory once per U tiles.
+__global__ __launch_bounds__(64) void tile_prefix_kernel(int *__restrict__ tile_hist, int64_t k,
+                                                         int64_t n_tiles, int *__restrict__ cnt,
+                                                         Gate gate) {
     if (gated(gate)) return;
-    const int64_t j = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+    const int64_t j = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (j >= k) return;
     int run = 0;
-    if (j < k) {
-        constexpr int U = 32;  // tile counts in flight per thread
-        if (n_tiles <= 2 * U) {
-            // Every tile's count in flight at once: one wait for memory.
-            int v[2 * U];
+    constexpr int U = 32;  // tile counts in flight per thread
+    if (n_tiles <= 2 * U) {
+        // Every tile's count in flight at once: one wait for memory.
+        int v[2 * U];
 #pragma unroll
-            for (int u = 0; u < 2 * U; ++u) v[u] = u < n_tiles ? tile_hist[u * k + j] : 0;
+        for (int u = 0; u < 2 * U; ++u) v[u] = u < n_tiles ? tile_hist[u * k + j] : 0;
 #pragma unroll
-            for (int u = 0; u < 2 * U; ++u) {
-                if (u < n_tiles) tile_hist[u * k + j] = run;
+        for (int u = 0; u < 2 * U; ++u) {
+            if (u < n_tiles) tile_hist[u * k + j] = run;
+            run += v[u];
+        }
+    } else {
+        int v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = tile_hist[u * k + j];
+        for (int64_t b0 = 0; b0 < n_tiles; b0 += U) {
+            int nxt[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                nxt[u] = b0 + U + u < n_tiles ? tile_hist[(b0 + U + u) * k + j] : 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (b0 + u < n_tiles) tile_hist[(b0 + u) * k + j] = run;
                 run += v[u];
             }
-        } else {
-            int v[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = tile_hist[u * k + j];
-            for (int64_t b0 = 0; b0 < n_tiles; b0 += U) {
-                int nxt[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    nxt[u] = b0 + U + u < n_tiles ? tile_hist[(b0 + U + u) * k + j] : 0;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    if (b0 + u < n_tiles) tile_hist[(b0 + u) * k + j] = run;
-                    run += v[u];
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) v[u] = nxt[u];
-            }
+            for (int u = 0; u < U; ++u) v[u] = nxt[u];
         }
-        cnt[j] = run;
     }
-    if (gridDim.x > 1) {
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0) is_last = atomicAdd(done, 1u) == gridDim.x - 1;
-        __syncthreads();
-        if (!is_last) return;
-        __threadfence();
-    } else {
-        __syncthreads();  // (only cnt readers need it; one block always has R == 1)
-    }
-    // One block (k <= 1024, R == 1): every thread already holds its own
-    // cluster's size; no trip through memory.
-    const bool single = gridDim.x == 1 && R == 1;
+    cnt[j] = run;
+}
+
+// The cluster scan over cnt, one block (R = 0: any k, in 1024-cluster chunks).
+template <int R, int kSplit>
+__global__ __launch_bounds__(1024) void cluster_scan_kernel(const int *__restrict__ cnt, int64_t k,
+                                                            int *__restrict__ seg_start,
+                                                            int64_t *__restrict__ counts,
+                                                            int *__restrict__ num_empty,
+                                                            int *__restrict__ no_empty,
+                                                            int *__restrict__ big,
+                                                            int *__restrict__ order, Gate gate) {
+    if (gated(gate)) return;
     if (R > 0)
-        cluster_scan_regs<(R > 0 ? R : 1), kSplit>(single ? nullptr : cnt, k, seg_start, counts,
-                                                   num_empty, no_empty, big, order, run);
+        cluster_scan_regs<(R > 0 ? R : 1), kSplit>(cnt, k, seg_start, counts, num_empty, no_empty,
+                                                   big, order);
     else
         cluster_scan_chunked<kSplit>(cnt, k, seg_start, counts, num_empty, no_empty, big, order);
 }
@@ -743,30 +762,25 @@ template <bool kFromKeys>
 hipError_t launch_rank_hist_impl(const int64_t *labels, unsigned long long *keys,
                                  float *min_dist, bool add_norm, int64_t n, int64_t k,
                                  const UpdateScratch &ws, Gate gate, hipStream_t stream) {
-    if (n <= 0) {
-        // No tile: the scan kernel's counter is zeroed here instead.
-        fill_u32_kernel<<<1, 256, 0, stream>>>(ws.done, 1);
-        return hipGetLastError();
-    }
+    if (n <= 0) return hipSuccess;  // no tile (the tile prefix then gives every size 0)
     const unsigned blocks = (unsigned)ws.n_tiles;
     if (k <= kRankLdsMax)
         rank_hist_kernel<true, kFromKeys><<<blocks, kTile, (size_t)k * sizeof(int), stream>>>(
-            labels, keys, min_dist, add_norm, n, k, ws.tile_hist, ws.rank, ws.done, gate);
+            labels, keys, min_dist, add_norm, n, k, ws.tile_hist, ws.rank, gate);
     else
         rank_hist_kernel<false, kFromKeys><<<blocks, kTile, 0, stream>>>(
-            labels, keys, min_dist, add_norm, n, k, ws.tile_hist, ws.rank, ws.done, gate);
+            labels, keys, min_dist, add_norm, n, k, ws.tile_hist, ws.rank, gate);
     return hipGetLastError();
 }
 
 template <int kSplit>
-void launch_scan_split(int64_t k, int64_t *counts, int *num_empty, const UpdateScratch &ws,
-                       Gate gate, unsigned blocks, hipStream_t stream) {
-    const int64_t r = cdiv(k, 1024);  // clusters per thread in the final scan
-#define KM_SCAN(R)                                                                             \
-    scan_kernel<R, kSplit><<<blocks, 1024, 0, stream>>>(ws.tile_hist, k, ws.n_tiles, ws.cnt,   \
-                                                        ws.seg_start, counts, num_empty,       \
-                                                        ws.no_empty, ws.big, ws.order, ws.done, \
-                                                        gate)
+void launch_cluster_scan(int64_t k, int64_t *counts, int *num_empty, const UpdateScratch &ws,
+                         Gate gate, hipStream_t stream) {
+    const int64_t r = cdiv(k, 1024);  // clusters per thread
+#define KM_SCAN(R)                                                                        \
+    cluster_scan_kernel<R, kSplit><<<1, 1024, 0, stream>>>(ws.cnt, k, ws.seg_start, counts, \
+                                                           num_empty, ws.no_empty, ws.big, \
+                                                           ws.order, gate)
     if (r <= 1)
         KM_SCAN(1);
     else if (r <= 2)
@@ -797,11 +811,12 @@ hipError_t launch_finalize_rank_hist(unsigned long long *keys, float *min_dist, 
 
 hipError_t launch_scan(int64_t n, int64_t k, int64_t d, int64_t *counts, int *num_empty,
                        const UpdateScratch &ws, Gate gate, hipStream_t stream) {
-    const unsigned blocks = (unsigned)cdiv(k, 1024);
+    tile_prefix_kernel<<<(unsigned)cdiv(k, 64), 64, 0, stream>>>(ws.tile_hist, k, ws.n_tiles, ws.cnt,
+                                                                  gate);
     if (split_rows(n, k, d) == kSplitLarge)
-        launch_scan_split<kSplitLarge>(k, counts, num_empty, ws, gate, blocks, stream);
+        launch_cluster_scan<kSplitLarge>(k, counts, num_empty, ws, gate, stream);
     else
-        launch_scan_split<kSplitSmall>(k, counts, num_empty, ws, gate, blocks, stream);
+        launch_cluster_scan<kSplitSmall>(k, counts, num_empty, ws, gate, stream);
     return hipGetLastError();
 }
 
@@ -831,18 +846,24 @@ __global__ __launch_bounds__(256) void add_norms_kernel(float *__restrict__ min_
                                                         int64_t rows, int64_t n, int chunks) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < rows; p += stride) {
+        const int i = perm[p];
         // Partials are fetched G at a time (G >= chunks on the common shapes:
-        // one memory round trip per row), all loads before the adds; the adds
-        // stay in chunk order.
+        // one memory round trip per row). The loads carry no condition (past
+        // the last chunk the index is clamped and the value then ignored), so
+        // all G are in flight together: a branch around each would make the
+        // compiler wait for every load before issuing the next. The adds stay
+        // in chunk order; the ignored ones add +0.0 to a sum of squares.
         double t = 0.0;
         for (int c0 = 0; c0 < chunks; c0 += G) {
             float v[G];
 #pragma unroll
-            for (int u = 0; u < G; ++u) v[u] = c0 + u < chunks ? xn_part[(c0 + u) * n + p] : 0.0f;
+            for (int u = 0; u < G; ++u) {
+                const int c = c0 + u < chunks ? c0 + u : chunks - 1;
+                v[u] = xn_part[(int64_t)c * n + p];
+            }
 #pragma unroll
-            for (int u = 0; u < G; ++u) t += (double)v[u];
+            for (int u = 0; u < G; ++u) t += c0 + u < chunks ? (double)v[u] : 0.0;
         }
-        const int i = perm[p];
         min_dist[i] = fmaxf((float)t + min_dist[i], 0.0f);
     }
 }
@@ -911,12 +932,20 @@ hipError_t launch_add_norms(float *min_dist, const float *xn_part, int64_t n, in
                             const UpdateScratch &ws, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     const int chunks = (int)norm_parts(d);
-    if (chunks <= 16)
-        add_norms_kernel<16><<<grid_stride_blocks(n), 256, 0, stream>>>(min_dist, xn_part, ws.perm,
-                                                                        n, n, chunks);
+    const unsigned blocks = grid_stride_blocks(n);
+#define KM_ADD_NORMS(G) \
+    add_norms_kernel<G><<<blocks, 256, 0, stream>>>(min_dist, xn_part, ws.perm, n, n, chunks)
+    if (chunks <= 4)
+        KM_ADD_NORMS(4);
+    else if (chunks <= 8)
+        KM_ADD_NORMS(8);
+    else if (chunks <= 16)
+        KM_ADD_NORMS(16);
+    else if (chunks <= 32)
+        KM_ADD_NORMS(32);
     else
-        add_norms_kernel<64><<<grid_stride_blocks(n), 256, 0, stream>>>(min_dist, xn_part, ws.perm,
-                                                                        n, n, chunks);
+        KM_ADD_NORMS(64);
+#undef KM_ADD_NORMS
     return hipGetLastError();
 }
 
