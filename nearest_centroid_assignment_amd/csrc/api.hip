@@ -421,7 +421,8 @@ int kmeans_fit(const float *X, const float *C_init, int64_t n, int64_t k, int64_
             e = km::launch_rank_hist(labels, n, k, ws, loop, s);
         }
         if (e == hipSuccess)
-            e = km::launch_scan(n, k, d, counts, relocate ? rs.num_empty : nullptr, ws, loop, s);
+            e = km::launch_scan(labels, n, k, d, counts, relocate ? rs.num_empty : nullptr, ws,
+                                loop, s);
         if (e == hipSuccess && relocate) {
             e = km::launch_relocate(X, C_out, labels, n, k, d, rs, ws, s, loop);
             // Count again only if a cluster was empty (something moved).
@@ -456,7 +457,7 @@ int kmeans_fit(const float *X, const float *C_init, int64_t n, int64_t k, int64_
         run_assign(X, C_out, n, k, d, labels, md, true, cn, &ws, km::Gate{}, s) != KM_OK)
         return KM_ERR_HIP;
     if (e == hipSuccess && n <= 0) e = km::launch_rank_hist(labels, n, k, ws, km::Gate{}, s);
-    if (e == hipSuccess) e = km::launch_scan(n, k, d, counts, nullptr, ws, km::Gate{}, s);
+    if (e == hipSuccess) e = km::launch_scan(labels, n, k, d, counts, nullptr, ws, km::Gate{}, s);
     if (e == hipSuccess) e = km::launch_inertia(md, n, info + 1, s);
     if (e == hipSuccess) e = km::launch_store_count(info, iterations, s);
     return e == hipSuccess ? KM_OK : KM_ERR_HIP;

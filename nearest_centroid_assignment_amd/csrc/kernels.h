@@ -89,12 +89,14 @@ hipError_t launch_finalize_rank_hist(unsigned long long *keys, float *min_dist, 
                                      int64_t n, int64_t k, const UpdateScratch &ws, Gate gate,
                                      hipStream_t stream);
 
-// Counting phase, second step (after one of the two above): per-cluster
-// sizes (ws.cnt, counts), segment starts, the tiles' prefixes, and the split
-// of the clusters by split_rows(n, k, d); num_empty (nullable) receives the
-// number of empty clusters and ws.no_empty whether there are none.
-hipError_t launch_scan(int64_t n, int64_t k, int64_t d, int64_t *counts, int *num_empty,
-                       const UpdateScratch &ws, Gate gate, hipStream_t stream);
+// Counting phase, second step (after one of the two above, on the same
+// labels): per-cluster sizes (ws.cnt, counts), segment starts, the tiles'
+// prefixes, and the split of the clusters by split_rows(n, k, d); num_empty
+// (nullable) receives the number of empty clusters and ws.no_empty whether
+// there are none. For k <= 1024 and n <= 64 * kSortTileRows it also groups
+// the rows (ws.perm), which launch_group_and_mean then leaves as it is.
+hipError_t launch_scan(const int64_t *labels, int64_t n, int64_t k, int64_t d, int64_t *counts,
+                       int *num_empty, const UpdateScratch &ws, Gate gate, hipStream_t stream);
 
 // Both steps on labels.
 hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t d, int64_t *counts,

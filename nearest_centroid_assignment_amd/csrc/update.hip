@@ -232,8 +232,9 @@ __device__ __forceinline__ int padded(int j) {
 }
 
 template <int R, int kSplit>
-__device__ void cluster_scan_regs(const int *cnt, int64_t k, int *seg_start, int64_t *counts,
-                                  int *num_empty, int *no_empty, int *big, int *order) {
+__device__ int cluster_scan_regs(const int *cnt, int own, int64_t k, int *seg_start,
+                                 int64_t *counts, int *num_empty, int *no_empty, int *big,
+                                 int *order) {
     static_assert(R * 1024 < 65536, "packed class counts need k < 2^16");
     constexpr int kClasses = kSplit / 8 + 1;
     constexpr int kPacked = (kClasses + 1) / 2;
@@ -245,7 +246,8 @@ __device__ void cluster_scan_regs(const int *cnt, int64_t k, int *seg_start, int
     const int64_t j0 = (int64_t)tid * R;
     int v[R];
     if (R == 1) {
-        v[0] = j0 < k ? cnt[j0] : -1;
+        // From cnt, or (cnt == NULL) the thread's own cluster size, -1 past k.
+        v[0] = cnt == nullptr ? own : j0 < k ? cnt[j0] : -1;
     } else {
 #pragma unroll
         for (int e = 0; e < R; ++e) {
@@ -282,6 +284,7 @@ __device__ void cluster_scan_regs(const int *cnt, int64_t k, int *seg_start, int
         start += unpack_half(tot[2 + c / 2], c & 1);
     }
     const int n_ordered = start;
+    const int first_seg = pos[0];
     int seg = pos[0], bpos = pos[1] & 0xffff;
 #pragma unroll
     for (int e = 0; e < R; ++e) {
@@ -327,6 +330,7 @@ __device__ void cluster_scan_regs(const int *cnt, int64_t k, int *seg_start, int
             *no_empty = empty == 0;
         }
     }
+    return first_seg;
 }
 
 // The same for any k, 1024 clusters at a time, a cluster per thread (each
@@ -457,8 +461,8 @@ __global__ __launch_bounds__(1024) void cluster_scan_kernel(const int *__restric
                                                             int *__restrict__ order, Gate gate) {
     if (gated(gate)) return;
     if (R > 0)
-        cluster_scan_regs<(R > 0 ? R : 1), kSplit>(cnt, k, seg_start, counts, num_empty, no_empty,
-                                                   big, order);
+        cluster_scan_regs<(R > 0 ? R : 1), kSplit>(cnt, 0, k, seg_start, counts, num_empty,
+                                                   no_empty, big, order);
     else
         cluster_scan_chunked<kSplit>(cnt, k, seg_start, counts, num_empty, no_empty, big, order);
 }
@@ -479,6 +483,71 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int64_t *__restrict_
     if (l < 0 || l >= k) return;
     const int64_t b = i / kTile;
     perm[(int64_t)seg_start[l] + tile_prefix[b * k + l] + rank[i]] = (int)i;
+}
+
+// For k <= 1024 clusters and at most kPlaceTiles tiles: the tile prefix, the
+// cluster scan and the scatter in one launch, a block per tile (the three
+// launches they replace cost more in launch gaps than the work they do at
+// these sizes). Thread j of every block reads cluster j's counts in all the
+// tiles (at most 64 K words in all, from the L2) and takes the rows of j in
+// the tiles before its own and in all of them; one block scan of the sizes
+// gives the segment starts, and the block places its own tile's rows:
+// perm[segment start + rows in earlier tiles + rank] = row. Block 0 also
+// writes the per-cluster results of the cluster scan (cnt, counts,
+// seg_start, the lists of the mean kernel). The integer sums are the same in
+// every block.
+constexpr int kPlaceTiles = 64;
+
+template <int kSplit>
+__global__ __launch_bounds__(1024) void place_kernel(
+    const int64_t *__restrict__ labels, int64_t n, int64_t k, const int *__restrict__ tile_hist,
+    const unsigned short *__restrict__ rank, int64_t n_tiles, int *__restrict__ cnt,
+    int *__restrict__ seg_start, int64_t *__restrict__ counts, int *__restrict__ num_empty,
+    int *__restrict__ no_empty, int *__restrict__ big, int *__restrict__ order,
+    int *__restrict__ perm, Gate gate) {
+    __shared__ int base[1024];  // per cluster: segment start + rows in earlier tiles
+    if (gated(gate)) return;
+    const int tid = threadIdx.x;
+    const int64_t b = blockIdx.x;
+    const int64_t i = b * kTile + tid;
+    int64_t lv = -1;
+    int r = 0;
+    if (i < n) {
+        lv = labels[i];
+        r = rank[i];  // (meaningless, and unused, for a label outside [0, k))
+    }
+    int before = 0, total = -1;
+    if (tid < k) {
+        total = 0;
+        if (n_tiles > 0) {
+            int v[kPlaceTiles];
+            // Past the last tile the index is clamped and the value ignored,
+            // so the loads carry no condition and are all in flight at once.
+#pragma unroll
+            for (int u = 0; u < kPlaceTiles; ++u)
+                v[u] = tile_hist[(int64_t)(u < n_tiles ? u : n_tiles - 1) * k + tid];
+#pragma unroll
+            for (int u = 0; u < kPlaceTiles; ++u) {
+                const int c = u < n_tiles ? v[u] : 0;
+                before += u < b ? c : 0;
+                total += c;
+            }
+        }
+    }
+    int seg;
+    if (b == 0) {
+        seg = cluster_scan_regs<1, kSplit>(nullptr, total, k, seg_start, counts, num_empty,
+                                           no_empty, big, order);
+        if (tid < k) cnt[tid] = total;
+    } else {
+        const int x[1] = {total > 0 ? total : 0};
+        int p[1], t[1];
+        block_excl_scan<1>(x, p, t);
+        seg = p[0];
+    }
+    if (tid < k) base[tid] = seg + before;
+    __syncthreads();
+    if (lv >= 0 && lv < k) perm[base[lv] + r] = (int)i;
 }
 
 // Sum over the 64 lanes of a wave of each of B per-lane values (B a power of
@@ -752,6 +821,11 @@ int64_t update_grid_threads(int64_t n, int64_t k, int64_t d) {
     return m > scan ? m : scan;
 }
 
+namespace {
+// The counting's last steps and the scatter run as one place_kernel launch.
+bool place_fused(int64_t n, int64_t k) { return k <= 1024 && cdiv(n, kTile) <= kPlaceTiles; }
+}  // namespace
+
 int split_rows(int64_t n, int64_t k, int64_t d) {
     return (n * d >= ((int64_t)1 << 26) && n >= 32 * k) ? kSplitLarge : kSplitSmall;
 }
@@ -771,6 +845,16 @@ hipError_t launch_rank_hist_impl(const int64_t *labels, unsigned long long *keys
         rank_hist_kernel<false, kFromKeys><<<blocks, kTile, 0, stream>>>(
             labels, keys, min_dist, add_norm, n, k, ws.tile_hist, ws.rank, gate);
     return hipGetLastError();
+}
+
+template <int kSplit>
+void launch_place(const int64_t *labels, int64_t n, int64_t k, int64_t *counts, int *num_empty,
+                  const UpdateScratch &ws, Gate gate, hipStream_t stream) {
+    const unsigned blocks = ws.n_tiles > 0 ? (unsigned)ws.n_tiles : 1u;  // block 0 always runs
+    place_kernel<kSplit><<<blocks, 1024, 0, stream>>>(labels, n, k, ws.tile_hist, ws.rank,
+                                                      ws.n_tiles, ws.cnt, ws.seg_start, counts,
+                                                      num_empty, ws.no_empty, ws.big, ws.order,
+                                                      ws.perm, gate);
 }
 
 template <int kSplit>
@@ -809,8 +893,15 @@ hipError_t launch_finalize_rank_hist(unsigned long long *keys, float *min_dist, 
     return launch_rank_hist_impl<true>(nullptr, keys, min_dist, add_norm, n, k, ws, gate, stream);
 }
 
-hipError_t launch_scan(int64_t n, int64_t k, int64_t d, int64_t *counts, int *num_empty,
-                       const UpdateScratch &ws, Gate gate, hipStream_t stream) {
+hipError_t launch_scan(const int64_t *labels, int64_t n, int64_t k, int64_t d, int64_t *counts,
+                       int *num_empty, const UpdateScratch &ws, Gate gate, hipStream_t stream) {
+    if (place_fused(n, k)) {
+        if (split_rows(n, k, d) == kSplitLarge)
+            launch_place<kSplitLarge>(labels, n, k, counts, num_empty, ws, gate, stream);
+        else
+            launch_place<kSplitSmall>(labels, n, k, counts, num_empty, ws, gate, stream);
+        return hipGetLastError();
+    }
     tile_prefix_kernel<<<(unsigned)cdiv(k, 64), 64, 0, stream>>>(ws.tile_hist, k, ws.n_tiles, ws.cnt,
                                                                   gate);
     if (split_rows(n, k, d) == kSplitLarge)
@@ -823,7 +914,7 @@ hipError_t launch_scan(int64_t n, int64_t k, int64_t d, int64_t *counts, int *nu
 hipError_t launch_count(const int64_t *labels, int64_t n, int64_t k, int64_t d, int64_t *counts,
                         int *num_empty, const UpdateScratch &ws, Gate gate, hipStream_t stream) {
     hipError_t e = launch_rank_hist(labels, n, k, ws, gate, stream);
-    if (e == hipSuccess) e = launch_scan(n, k, d, counts, num_empty, ws, gate, stream);
+    if (e == hipSuccess) e = launch_scan(labels, n, k, d, counts, num_empty, ws, gate, stream);
     return e;
 }
 
@@ -910,7 +1001,7 @@ hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const fl
                                  int64_t n, int64_t k, int64_t d, float *C_new,
                                  double *shift_partial, float *xn_part, const UpdateScratch &ws,
                                  Gate gate, hipStream_t stream) {
-    if (n > 0)
+    if (n > 0 && !place_fused(n, k))  // (else the count has placed the rows)
         scatter_kernel<<<(unsigned)cdiv(n, 256), 256, 0, stream>>>(
             labels, n, k, ws.tile_hist, ws.rank, ws.seg_start, ws.perm, gate);
     const int chunks = (int)cdiv(d, kCols);
@@ -952,7 +1043,7 @@ hipError_t launch_add_norms(float *min_dist, const float *xn_part, int64_t n, in
 hipError_t launch_update(const float *X, const int64_t *labels, const float *C_old, int64_t n,
                          int64_t k, int64_t d, float *C_new, int64_t *counts, float *xn_part,
                          bool counted, const UpdateScratch &ws, hipStream_t stream) {
-    hipError_t e = counted ? launch_scan(n, k, d, counts, nullptr, ws, Gate{}, stream)
+    hipError_t e = counted ? launch_scan(labels, n, k, d, counts, nullptr, ws, Gate{}, stream)
                            : launch_count(labels, n, k, d, counts, nullptr, ws, Gate{}, stream);
     if (e != hipSuccess) return e;
     return launch_group_and_mean(X, labels, C_old, n, k, d, C_new, nullptr, xn_part, ws, Gate{},
