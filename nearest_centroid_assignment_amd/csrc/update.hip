@@ -597,10 +597,11 @@ __device__ __forceinline__ void flush_norms(float (&q)[B], int m, int lane, floa
 // Rows are fetched in rounds of kBatch: all the round's row loads, then the
 // adds in order. X is read once, with non-temporal loads (streamed past the
 // caches; measured 10 % faster at 65536 x 1024 x 2048 and 4 % at
-// 65536 x 4096 x 16384 than ordinary loads, same bits). kBatch is 16, or 8 when clusters hold 32 rows or fewer on
-// average (measured faster there: fewer load slots of a round go unused on
-// short clusters, and the kernel needs about 66 registers instead of about
-// 100). The order of the adds does not depend on kBatch.
+// 65536 x 4096 x 16384 than ordinary loads, same bits). kBatch is 8: with
+// 16, fewer rows are in flight per wave on short clusters (load slots of a
+// round go unused) and the kernel needs about 100 registers instead of about
+// 66; measured slower at every workload, also at 65536 x 1024 x 2048 with 64
+// rows per cluster. The order of the adds does not depend on kBatch.
 //
 // With kNorm (xn != NULL) the same loads also give each row's squared norm
 // over this chunk's columns: per lane a float32 fused multiply-add chain over
@@ -977,8 +978,8 @@ void launch_mean_vec(const MeanArgs &a, unsigned blocks, unsigned bt, hipStream_
         segment_mean_kernel<kVec, true, kBatch, false><<<blocks, bt, 0, stream>>>(
             a.X, a.perm, a.seg_start, a.cnt, a.big, a.order, a.C_old, a.n, a.k, a.d, a.chunks, a.C_new,
             a.shift_partial, nullptr, a.gate);
-    else if (a.xn_part)  // rounds of at most 8 rows: 16 with the pending norms spill
-        segment_mean_kernel<kVec, false, (kBatch > 8 ? 8 : kBatch), true><<<blocks, bt, 0, stream>>>(
+    else if (a.xn_part)
+        segment_mean_kernel<kVec, false, kBatch, true><<<blocks, bt, 0, stream>>>(
             a.X, a.perm, a.seg_start, a.cnt, a.big, a.order, a.C_old, a.n, a.k, a.d, a.chunks, a.C_new,
             nullptr, a.xn_part, a.gate);
     else
@@ -1012,10 +1013,7 @@ hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const fl
     const MeanArgs a{X,      ws.perm, ws.seg_start, ws.cnt,        ws.big,  ws.order,
                      C_old,  n,       k,            d,             chunks,  C_new,
                      shift_partial, xn_part, gate};
-    if (n <= 32 * k)  // at most 32 rows per cluster on average
-        launch_mean<8>(a, vec, blocks, bt, stream);
-    else
-        launch_mean<16>(a, vec, blocks, bt, stream);
+    launch_mean<8>(a, vec, blocks, bt, stream);
     return hipGetLastError();
 }
 
