@@ -157,11 +157,18 @@ __device__ __forceinline__ int round_class(int count) {
     return count <= kSplit ? (count + 7) / 8 : -1;
 }
 
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-    for (int off = 1; off < 64; off <<= 1) {
-        const int up = __shfl_up(x, off);
-        if (lane >= off) x += up;
-    }
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no trip
+// through LDS): a Hillis-Steele scan inside each row of 16 lanes (row_shr by
+// 1, 2, 4, 8; lanes shifted in from outside the row read 0), then the total of
+// row 0 is added to row 1 and that of row 2 to row 3 (row_bcast:15, rows 1
+// and 3 only), then that of rows 0-1 to rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
     return x;
 }
 
@@ -177,7 +184,7 @@ __device__ __forceinline__ void block_excl_scan(const int (&x)[Q], int (&excl)[Q
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
-        const int incl = wave_incl_scan(x[q], lane);
+        const int incl = wave_incl_scan(x[q]);
         excl[q] = incl - x[q];
         if (lane == 63) wsum[wave][q] = incl;
     }
