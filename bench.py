@@ -407,11 +407,13 @@ def main() -> int:
     # The fused assignment alone, one event pair per call, for the roofline of
     # its dominant kernel (the three tiny kernels around it are included, so
     # the kernel's own rate is slightly higher than reported).
-    log(f"timing {args.steps} assignments")
+    # Launch-bound shapes (tiny, probe) take at least 50 calls.
+    areps = args.steps if cfg.flops >= 1e10 else max(args.steps, 50)
+    log(f"timing {areps} assignments")
     assign_only()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+           for _ in range(areps)]
     for a, b in evs:
         a.record(stream)
         assign_only()
@@ -472,11 +474,16 @@ def main() -> int:
         "lloyd_wall_ms": round(wall_ms, 3),
         "assign_ms": round(assign_ms, 3),
         "assign_ms_min": round(per_call[0], 3),
+        "assign_ms_median": round(per_call[len(per_call) // 2], 3),
+        "assign_calls": len(per_call),
         "assign_tflops": round(assign_tflops, 3),
         "update_ms": round(update_ms, 3),
         "update_hbm_gbps": round(update_gbps, 1),
         "update_frac_of_hbm_peak": round(update_gbps / HBM_PEAK_GBPS, 4),
         "workspace_bytes": ws_bytes,
+        # labels 8n + min_dist 4n + C_new 4kd + counts 8k, allocated by the caller
+        "outputs_bytes": 12 * n + 4 * k * d + 8 * k,
+        "workspace_plus_outputs_bytes": ws_bytes + 12 * n + 4 * k * d + 8 * k,
         "peak_extra_bytes_during_step": int(peak_extra),
         "roofline": roofline,
     }
