@@ -161,7 +161,8 @@ __device__ __forceinline__ int round_class(int count) {
 // through LDS): a Hillis-Steele scan inside each row of 16 lanes (row_shr by
 // 1, 2, 4, 8; lanes shifted in from outside the row read 0), then the total of
 // row 0 is added to row 1 and that of row 2 to row 3 (row_bcast:15, rows 1
-// and 3 only), then that of rows 0-1 to rows 2 and 3 (row_bcast:31).
+// and 3 only), then that of rows 0-1 to rows 2 and 3 (row_bcast:31). Every
+// lane of the wave must be active.
 __device__ __forceinline__ int wave_incl_scan(int x) {
     x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
     x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
@@ -173,9 +174,10 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 }
 
 // Exclusive prefixes of Q values over the block's 1024 threads in thread
-// order (excl) and their block totals (total): a shuffle scan per wave, the
-// wave totals through LDS, a prefix over the 16 waves by the first Q threads.
-// Three barriers for all Q values; every thread must call it.
+// order (excl) and their block totals (total): a DPP scan per wave, the wave
+// totals through LDS, a prefix over the 16 waves by the first Q threads.
+// Three barriers for all Q values; every thread must call it (all lanes
+// active).
 template <int Q>
 __device__ __forceinline__ void block_excl_scan(const int (&x)[Q], int (&excl)[Q], int (&total)[Q]) {
     __shared__ int wsum[16][Q];
