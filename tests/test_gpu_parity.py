@@ -248,19 +248,30 @@ def test_update_ignores_invalid_labels():
     gu.check_update(X[keep], labels[keep], C, C_new.cpu().numpy(), counts.cpu().numpy())
 
 
-def test_update_with_no_samples():
+@pytest.mark.parametrize("k", [17, 2000, 17000])
+def test_update_with_no_samples(k):
+    """n = 0 on each counting path (one launch for k <= 1024, the tile prefix
+    and cluster scan above, chunked above 16384): every cluster is empty and
+    keeps its centre, in kmeans_update and in a Lloyd step."""
     import torch
 
     from nearest_centroid_assignment_amd import binding
 
-    gu.announce("update with n = 0")
-    C = np.random.default_rng(1).standard_normal((17, 9), dtype=np.float32)
+    gu.announce(f"update with n = 0, k = {k}")
+    C = np.random.default_rng(1).standard_normal((k, 9), dtype=np.float32)
     X = torch.empty((0, 9), dtype=torch.float32, device="cuda:0")
     labels = torch.empty((0,), dtype=torch.int64, device="cuda:0")
     C_new, counts = binding.update(X, labels, gu.to_gpu(C))
     torch.cuda.synchronize()
     assert np.all(counts.cpu().numpy() == 0)
     assert np.array_equal(C_new.cpu().numpy(), C)
+    md = torch.empty((0,), dtype=torch.float32, device="cuda:0")
+    C_new2 = torch.full((k, 9), float("nan"), dtype=torch.float32, device="cuda:0")
+    counts2 = torch.full((k,), -1, dtype=torch.int64, device="cuda:0")
+    binding.kmeans_lloyd_step(X, gu.to_gpu(C), labels, md, C_new2, counts2)
+    torch.cuda.synchronize()
+    assert np.all(counts2.cpu().numpy() == 0)
+    assert np.array_equal(C_new2.cpu().numpy(), C)
 
 
 def test_unaligned_inputs_take_scalar_path():
