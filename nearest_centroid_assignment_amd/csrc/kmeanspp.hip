@@ -182,8 +182,14 @@ __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
     };
 
     float4 xn[8], cv[2];
-    load_x(0, xn);
-    load_c(0, cv);
+    // Block b walks the feature stages from stage 5b mod chunks (wrapping
+    // round), so the blocks in flight read different column strips of X at
+    // any moment rather than all the same one: 1 % faster at 65536 x 8192.
+    // The float64 sums then run in that rotated stage order, the same on
+    // every call.
+    const int64_t rot = (b * 5) % chunks;
+    load_x(rot, xn);
+    load_c(rot, cv);
     store_x(xn);
     store_c(0, cv);
     __syncthreads();
@@ -200,8 +206,9 @@ __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
 #pragma unroll
         for (int q = 0; q < kMfRun / 4; ++q) xa[q] = *reinterpret_cast<const float4 *>(arow + 4 * q);
         if (c + 1 < chunks) {
-            load_x(c + 1, xn);
-            load_c(c + 1, cv);
+            const int64_t next = (c + 1 + rot) % chunks;
+            load_x(next, xn);
+            load_c(next, cv);
         }
         // Features beyond d were loaded as 0 for samples and candidates alike.
         if constexpr (kSlots == 16) {
