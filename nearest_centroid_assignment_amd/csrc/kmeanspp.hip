@@ -17,11 +17,12 @@
 // roundings are those of the float64 sums; a sample's distance to itself is
 // set to exactly 0.
 //
-// Per call, pp_norm_kernel computes |x_i|^2 once. Per centre, two launches
-// and nothing on the host:
+// Per call, pp_norm_kernel computes |x_i|^2 once and pp_gather_kernel copies
+// the chosen rows out as the centres at the end. Per centre, two launches and
+// nothing on the host:
 //   pp_select_kernel  one 1024-thread block: potentials of the previous
 //                     trials from the per-block partials (fixed-order
-//                     reduction), the winner, its row copied out as a centre,
+//                     reduction), the winner recorded as a centre index,
 //                     then the next candidates: a scan over the block sums of
 //                     D finds the block each draw falls in, one wave per draw
 //                     walks its rows
@@ -320,11 +321,11 @@ constexpr int kSelWaves = 16;  // pp_select_kernel: one 1024-thread block
 // is not NULL, the next candidates. One block of 1024 threads; every sum has
 // a fixed order.
 __global__ __launch_bounds__(kSelWaves * 64) void pp_select_kernel(
-    const float *__restrict__ X, int64_t n, int64_t d, const double *__restrict__ prev_buf,
-    const double *__restrict__ prev_parts, int64_t nb, int trials_prev,
+    int64_t n, const double *__restrict__ prev_buf, const double *__restrict__ prev_parts,
+    int64_t nb, int trials_prev,
     const long long *__restrict__ cand_prev, PPState *st, int64_t c_rec,
-    long long *__restrict__ chosen, float *__restrict__ centres,
-    const double *__restrict__ rand_row, int trials_next, long long *__restrict__ cand_next) {
+    long long *__restrict__ chosen, const double *__restrict__ rand_row, int trials_next,
+    long long *__restrict__ cand_next) {
     constexpr int kThreads = kSelWaves * 64;
     __shared__ double wsum[kPPMaxTrials][kSelWaves];
     __shared__ double pots[kPPMaxTrials];
@@ -376,7 +377,6 @@ __global__ __launch_bounds__(kSelWaves * 64) void pp_select_kernel(
         st->pot = pot;
         chosen[c_rec] = row;
     }
-    for (int64_t f = tid; f < d; f += kThreads) centres[c_rec * d + f] = X[row * d + f];
     if (!rand_row) return;
 
     // Candidate draws: the first sample whose running sum of D reaches
@@ -464,6 +464,36 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
 
+namespace {
+
+// centres[c] = X[chosen[c]] for every centre, a block per centre; each
+// thread's loads go out before its stores (the row copies leave the
+// per-centre chain of launches, where each would be one more memory round
+// trip per centre).
+__global__ __launch_bounds__(256) void pp_gather_kernel(const float *__restrict__ X, int64_t d,
+                                                        const int64_t *__restrict__ chosen,
+                                                        float *__restrict__ centres) {
+    constexpr int kU = 8;
+    const int64_t c = blockIdx.x;
+    const float *src = X + chosen[c] * d;
+    float *dst = centres + c * d;
+    for (int64_t f0 = 0; f0 < d; f0 += 256 * kU) {
+        float v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t f = f0 + u * 256 + threadIdx.x;
+            v[u] = src[f < d ? f : d - 1];  // clamped, so the loads carry no condition
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t f = f0 + u * 256 + threadIdx.x;
+            if (f < d) dst[f] = v[u];
+        }
+    }
+}
+
+}  // namespace
+
 int64_t pp_blocks(int64_t n) { return cdiv(n, kPPRowsPerBlock); }
 int pp_max_trials() { return kPPMaxTrials; }
 int pp_block_threads() { return 256; }
@@ -487,15 +517,15 @@ hipError_t launch_kmeanspp(const float *X, int64_t n, int64_t d, int64_t k, int6
     for (int64_t c = 1; c <= k; ++c) {
         const bool more = c < k;
         pp_select_kernel<<<1, kSelWaves * 64, 0, stream>>>(
-            X, n, d, buf[cur], parts[cur], nb, trials_prev, cand[cur], st, c - 1,
-            (long long *)chosen, centres, more ? rand + (c - 1) * trials : nullptr, trials,
-            cand[cur ^ 1]);
+            n, buf[cur], parts[cur], nb, trials_prev, cand[cur], st, c - 1,
+            (long long *)chosen, more ? rand + (c - 1) * trials : nullptr, trials, cand[cur ^ 1]);
         if (!more) break;
         launch_dist(trials, vec, (unsigned)nb, stream, X, ws.xnorm, n, d, cand[cur ^ 1], st,
                     buf[cur], buf[cur ^ 1], parts[cur ^ 1]);
         cur ^= 1;
         trials_prev = trials;
     }
+    pp_gather_kernel<<<(unsigned)k, 256, 0, stream>>>(X, d, chosen, centres);
     return hipGetLastError();
 }
 
