@@ -85,7 +85,10 @@ enum { KM_FIT_RELOCATE_EMPTY = 1 };
 /*
  * Workspace bytes needed by one call of the given op at shape (n, k, d).
  * The size is O(k + n + k * ceil(n / 1024)) 4-byte words, plus about
- * k * d / 1024 doubles for kmeans_fit and, when ceil(d / 256) <= k / 16,
+ * k * d / 4096 + 256 doubles for kmeans_fit (per-block partial sums of the
+ * centre shift), n doubles, n floats and 12 bytes per entry of a sort buffer
+ * of the next power of two >= min(n, k) entries (relocation and min_dist
+ * scratch), and, when ceil(d / 256) <= k / 16,
  * n * ceil(d / 256) floats for kmeans_lloyd_step (partial squared norms of
  * the rows: at most 1/256 of the size of X and 1/16 of an (n, k) matrix):
  * far below the (n, k) distance matrix and the (n, d) sample matrix.
