@@ -229,14 +229,18 @@ def test_in_place_update():
     gu.check_update(X, labels.cpu().numpy(), C, Cg.cpu().numpy(), counts.cpu().numpy())
 
 
-def test_update_ignores_invalid_labels():
+@pytest.mark.parametrize("n,k,d", [(3000, 40, 70), (70000, 40, 70), (5000, 2000, 70),
+                                   (5000, 20000, 16)])
+def test_update_ignores_invalid_labels(n, k, d):
+    """Rows labelled -1 or k + 3 are left out of every count and sum, on each
+    counting path (one launch; four with 69 sort tiles; two clusters per
+    scan thread; the global label table)."""
     import torch
 
     from nearest_centroid_assignment_amd import binding
 
-    gu.announce("update with out-of-range labels")
+    gu.announce(f"update with out-of-range labels {n}x{k}x{d}")
     rng = np.random.default_rng(9)
-    n, k, d = 3000, 40, 70
     X = rng.standard_normal((n, d), dtype=np.float32)
     C = rng.standard_normal((k, d), dtype=np.float32)
     labels = rng.integers(0, k, size=n)
