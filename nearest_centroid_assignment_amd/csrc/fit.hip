@@ -199,7 +199,7 @@ __global__ __launch_bounds__(1024) void reloc_select_kernel(
         const bool is_eq = i < hi && b == t;
         const unsigned long long eq_mask = __ballot(is_eq);
         const bool take =
-            i < hi && (b > t || (is_eq && eq_seen + __popcll(eq_mask & below) < need_ties));
+            i < hi && (b > t || (is_eq && eq_seen + (int)__popcll(eq_mask & below) < need_ties));
         const unsigned long long take_mask = __ballot(take);
         const int pos = out + __popcll(take_mask & below);
         if (take && pos < m) {
