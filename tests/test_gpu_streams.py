@@ -60,13 +60,29 @@ def test_side_stream_matches_default_stream():
         assert _same(a, b)
 
 
-def test_lloyd_step_graph_replays():
+GRAPH_SHAPES = [
+    ("probe", None),                       # 64 x 64 tiles, the one-launch counting path
+    ("blobs", (2048, 512, 256)),           # full 256 x 256 tiles (the DMA kernel)
+    ("blobs", (3000, 1500, 96)),           # k > 1024: the four-launch counting path
+]
+
+
+@pytest.mark.parametrize("noalloc", [False, True], ids=["workspace", "noalloc"])
+@pytest.mark.parametrize("name,shape", GRAPH_SHAPES, ids=["probe", "2048x512x256", "3000x1500x96"])
+def test_lloyd_step_graph_replays(name, shape, noalloc):
+    """kmeans_lloyd_step (with a workspace) or kmeans_lloyd_step_noalloc (the
+    static scratch) captured once; four replays alternate two centre sets,
+    with the outputs (and the workspace) overwritten eagerly between them, and
+    each must equal the eager step on its centres bit for bit."""
     import torch
 
     from nearest_centroid_assignment_amd import binding
 
-    gu.announce("lloyd step captured in a graph")
-    X, C = datagen.make("probe")
+    gu.announce(f"lloyd step captured in a graph: {name} {shape} noalloc={noalloc}")
+    if shape is None:
+        X, C = datagen.make(name)
+    else:
+        X, C = datagen.make_blobs(*shape, kb=shape[1], sigma_c=1.0, sigma=0.5, seed=11)
     n, d = X.shape
     k = C.shape[0]
     Xg, Cg = gu.to_gpu(X), gu.to_gpu(C)
@@ -75,7 +91,13 @@ def test_lloyd_step_graph_replays():
     ws = torch.empty(binding.kmeans_workspace_bytes(n, k, d, binding.KM_OP_LLOYD),
                      dtype=torch.uint8, device="cuda:0")
 
-    # Eager references for both centre sets.
+    def step(Cin, outs):
+        if noalloc:
+            binding.kmeans_lloyd_step_noalloc(Xg, Cin, *outs)
+        else:
+            binding.kmeans_lloyd_step(Xg, Cin, *outs, workspace=ws)
+
+    # Eager references for both centre sets (a separate workspace each call).
     refs = []
     for Cin in (Cg, C2):
         r = _outputs(n, k, d)
@@ -86,13 +108,13 @@ def test_lloyd_step_graph_replays():
     Cin = Cg.clone()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):  # warm-up outside the capture
-        binding.kmeans_lloyd_step(Xg, Cin, *out, workspace=ws)
+    with torch.cuda.stream(side):  # warm-up (and one-time set-up) outside the capture
+        step(Cin, out)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        binding.kmeans_lloyd_step(Xg, Cin, *out, workspace=ws)
+        step(Cin, out)
     torch.cuda.synchronize()
 
     for replay in range(4):
