@@ -610,7 +610,11 @@ __device__ __forceinline__ void flush_norms(float (&q)[B], int m, int lane, floa
 // 16, fewer rows are in flight per wave on short clusters (load slots of a
 // round go unused) and the kernel needs about 100 registers instead of about
 // 66; measured slower at every workload, also at 65536 x 1024 x 2048 with 64
-// rows per cluster. The order of the adds does not depend on kBatch.
+// rows per cluster. When clusters average at most 8 rows, kBatch is 4: under
+// 64 registers, so two 16-wave blocks share a CU, which doubles the rows in
+// flight where a cluster fills only one or two rounds (4 % faster at
+// 65536 x 16384 x 8192, 4 rows per cluster; the same or slower at 16 rows).
+// The order of the adds does not depend on kBatch.
 //
 // With kNorm (xn != NULL) the same loads also give each row's squared norm
 // over this chunk's columns: per lane a float32 fused multiply-add chain over
@@ -1022,7 +1026,10 @@ hipError_t launch_group_and_mean(const float *X, const int64_t *labels, const fl
     const MeanArgs a{X,      ws.perm, ws.seg_start, ws.cnt,        ws.big,  ws.order,
                      C_old,  n,       k,            d,             chunks,  C_new,
                      shift_partial, xn_part, gate};
-    launch_mean<8>(a, vec, blocks, bt, stream);
+    if (n <= 8 * k)  // clusters of at most 8 rows on average: rounds of 4 (see sum_rows)
+        launch_mean<4>(a, vec, blocks, bt, stream);
+    else
+        launch_mean<8>(a, vec, blocks, bt, stream);
     return hipGetLastError();
 }
 
