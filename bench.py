@@ -81,12 +81,25 @@ def parse_args():
     return ap.parse_args()
 
 
-def assign_kernel_name(n: int, k: int, d: int) -> str:
+def assign_kernel_name(n: int, k: int, d: int, cus: int = 256) -> str:
     """The product kernel kmeans_assign runs for 16-byte aligned inputs of
-    this shape (the launcher's rule: DMA-staged 256 x 256 tiles when every
-    tile is full, d is a multiple of 64 and there are at least 256 tiles)."""
-    if n % 256 == 0 and k % 256 == 0 and d % 64 == 0 and (n // 256) * (k // 256) >= 256:
-        return "assign_dma_kernel"
+    this shape on a device with `cus` compute units (the launcher's rule:
+    DMA-staged 256 x 256 tiles when d is a multiple of 64, there are at least
+    256 of them and either every tile is full or 1.8 rounds of 128 x 256
+    tiles per round of them still come out ahead)."""
+    def cdiv(a, b):
+        return -(-a // b)
+
+    def rounds(tiles):
+        return cdiv(cdiv(tiles, 8), max(cus // 8, 1))
+
+    big = cdiv(n, 256) * cdiv(k, 256)
+    mid = cdiv(n, 256) * cdiv(k, 128)
+    if d % 64 == 0 and big >= 256:
+        if n % 256 == 0 and k % 256 == 0:
+            return "assign_dma_kernel"
+        if mid >= 512 and 9 * rounds(big) < 5 * rounds(mid):
+            return "assign_dma_kernel"
     return "assign_tile_kernel"
 
 
@@ -449,7 +462,7 @@ def main() -> int:
         "unit": "TFLOP/s",
         "frac": round(assign_tflops / MFMA_FP32_PEAK_TFLOPS, 4),
         "traffic": traffic,
-        "kernel": assign_kernel_name(n, k, d),
+        "kernel": assign_kernel_name(n, k, d, torch.cuda.get_device_properties(0).multi_processor_count),
         "algorithmic_per_launch": f"2*n*k*d = {flops:.4e} flop",
     }
 

@@ -9,12 +9,13 @@
 // Kernels:
 //   row_sqnorms_kernel  ||c_j||^2 (and ||x_i||^2 for min_dist outside a Lloyd step)
 //   fill_keys_kernel    packed-key identity
-//   assign_dma_kernel   float32 MFMA product X_tile . C_tile^T for full
-//                       256 x 256 tiles, the operands moved from global memory
-//                       straight into LDS by buffer loads, with the distance,
-//                       the argmin and the merge across centroid tiles done on
-//                       the accumulators: the (n, k) distance matrix never
-//                       exists in memory
+//   assign_dma_kernel   float32 MFMA product X_tile . C_tile^T in 256 x 256
+//                       tiles (d a multiple of 64; edge tiles cut short where
+//                       n or k is not a multiple of 256), the operands moved
+//                       from global memory straight into LDS by buffer loads,
+//                       with the distance, the argmin and the merge across
+//                       centroid tiles done on the accumulators: the (n, k)
+//                       distance matrix never exists in memory
 //   assign_tile_kernel  the same for any shape, operands staged through
 //                       registers into LDS, several tile sizes
 //   finalize_kernel     packed key -> int64 label, full squared distance
@@ -449,8 +450,8 @@ __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
 
 // ------------------------------------------------ DMA-staged 256 x 256 tiles
 //
-// Full tiles only (n % 256 == 0, k % 256 == 0, d % 64 == 0, 16-byte aligned
-// rows). 8 waves in 2 x 4; each wave owns 128 centroids x 64 samples (4 x 2
+// d % 64 == 0 and 16-byte aligned rows; any n and k (the ragged instance
+// reads only the rows below n and k and skips the rest). 8 waves in 2 x 4; each wave owns 128 centroids x 64 samples (4 x 2
 // blocks of 32 x 32), so a fragment read from LDS feeds more MFMAs than in
 // the 128 x 256 tile (6 reads per 32 MFMAs instead of 4 per 16), a stage
 // holds twice the MFMAs per barrier, and the 128 accumulators per lane fit
@@ -480,14 +481,20 @@ __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 // One stage of this wave's DMA: instruction j moves 64 slots (8 rows x 8
 // chunks) into buf + (wave * PER_WAVE + j) * 64 slots. voff[p] is the lane's
 // byte offset inside the wave's source block for instructions of parity p
-// (the swizzled chunk alternates with j), soff the uniform part.
+// (the swizzled chunk alternates with j). The offset of the instruction's
+// rows (j * row_bytes8) goes with the uniform part, except in ragged tiles:
+// there it joins the lane's offset, which the buffer's range check covers
+// (the uniform offset may not be checked), so that every row past the
+// buffer's last record reads as zero instead of touching memory.
+template <bool kRagged>
 __device__ __forceinline__ void dma_stage(__amdgpu_buffer_rsrc_t rsrc, const int (&voff)[2],
                                           int row_bytes8, int kbytes, float *buf, int wave) {
 #pragma unroll
     for (int j = 0; j < dma::PER_WAVE; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rsrc, (__attribute__((address_space(3))) void *)(buf + (wave * dma::PER_WAVE + j) * 64 * 4),
-            16, voff[j & 1], j * row_bytes8 + kbytes, 0, 0);
+            16, kRagged ? voff[j & 1] + j * row_bytes8 : voff[j & 1],
+            kRagged ? kbytes : j * row_bytes8 + kbytes, 0, 0);
 }
 
 // Fragments of group g (features 8g .. 8g + 7) for this lane: A rows
@@ -528,6 +535,7 @@ __device__ __forceinline__ void dma_mma(const f32x4 (&a)[dma::MB], const f32x4 (
 // are spread over the deferred group's MFMAs, one per four: issued back to
 // back, all 64 of a CU queue at the texture unit right after the barrier and
 // hold up the MFMAs behind them.
+template <bool kRagged>
 __device__ __forceinline__ void dma_compute(const float *buf, float *dst, __amdgpu_buffer_rsrc_t rsrc,
                                             const int (&voff)[2], int row_bytes8, int kbytes, int wave,
                                             int a_base, int b_base, int lane,
@@ -535,7 +543,7 @@ __device__ __forceinline__ void dma_compute(const float *buf, float *dst, __amdg
                                             f32x16 (&acc)[dma::MB][dma::NB]) {
     f32x4 a[2][dma::MB], b[2][dma::NB];
     dma_frags(buf, a_base, b_base, lane, 0, a[0], b[0]);
-    dma_stage(rsrc, voff, row_bytes8, kbytes, dst, wave);
+    dma_stage<kRagged>(rsrc, voff, row_bytes8, kbytes, dst, wave);
     dma_mma(aL, bL, acc);
 #pragma unroll
     for (int g = 0; g < 3; ++g) {
@@ -562,6 +570,7 @@ __device__ __forceinline__ void dma_compute(const float *buf, float *dst, __amdg
     for (int nb = 0; nb < dma::NB; ++nb) bL[nb] = b[1][nb];
 }
 
+template <bool kRagged>
 __global__ __launch_bounds__(dma::NT, 2) void assign_dma_kernel(
     const float *__restrict__ X, const float *__restrict__ C, const float *__restrict__ cn,
     int64_t n, int64_t k, int64_t d, int tiles_m, int tiles_n,
@@ -587,17 +596,34 @@ __global__ __launch_bounds__(dma::NT, 2) void assign_dma_kernel(
         const int linear = x_start + local;
         const int first_m = (linear / group_span) * kGroupM;
         const int gsize = min(tiles_m - first_m, kGroupM);
-        const int64_t m0 = (int64_t)(first_m + (linear % group_span) % gsize) * dma::BM;
-        const int64_t n0 = (int64_t)((linear % group_span) / gsize) * dma::BN;
+        // (the division by gsize runs on the vector unit: the tile indices
+        // go back to scalar registers, where the descriptors need them)
+        const int64_t m0 =
+            (int64_t)__builtin_amdgcn_readfirstlane(first_m + (linear % group_span) % gsize) * dma::BM;
+        const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane((linear % group_span) / gsize) * dma::BN;
         // This wave's DMA source: waves 0-3 copy centroid rows, 4-7 sample
         // rows, 64 rows each. Slot s of the wave's block is row s / 8 of it,
         // stored chunk s % 8, which holds logical chunk (s % 8) ^ swz(row);
         // with the (row / 2) % 8 swizzle that is (lane % 8) ^ (lane / 16),
         // flipped by 4 on odd instructions.
+        // In ragged tiles the buffer holds only the block's rows below k (or
+        // n), none for a block wholly past them (its base then stays at row 0
+        // of the matrix): the rows beyond read as zeros, or leave stale LDS,
+        // and reach only accumulators of centroids and samples that the
+        // epilogue skips.
         const int half = wave / (dma::PER_WAVE / 2);  // 0: centroids, 1: samples
-        const float *blk = half == 0 ? C + (m0 + (wave % 4) * 64) * d : X + (n0 + (wave % 4) * 64) * d;
+        const int64_t b0 = (half == 0 ? m0 : n0) + (wave % 4) * 64;
+        int blk_rows = 64;
+        if (kRagged) {
+            // (clamped in 64 bits, which only the vector unit compares; the
+            // result goes back to a scalar register, where the descriptor
+            // must live)
+            const int64_t left = (half == 0 ? k : n) - b0;
+            blk_rows = __builtin_amdgcn_readfirstlane((int)(left < 0 ? 0 : left < 64 ? left : 64));
+        }
+        const float *blk = (half == 0 ? C : X) + (blk_rows > 0 ? b0 : 0) * d;
         const __amdgpu_buffer_rsrc_t rsrc =
-            __builtin_amdgcn_make_buffer_rsrc((void *)blk, 0, (int)(64 * d * 4), 0x00020000);
+            __builtin_amdgcn_make_buffer_rsrc((void *)blk, 0, (int)(blk_rows * d * 4), 0x00020000);
         const int c0 = (lane & 7) ^ (lane >> 4);
         const int voff[2] = {(int)((lane >> 3) * d * 4 + c0 * 16),
                              (int)((lane >> 3) * d * 4 + (c0 ^ 4) * 16)};
@@ -615,7 +641,7 @@ __global__ __launch_bounds__(dma::NT, 2) void assign_dma_kernel(
 #pragma unroll
         for (int nb = 0; nb < dma::NB; ++nb) bL[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        dma_stage(rsrc, voff, row_bytes8, 0, buf0, wave);
+        dma_stage<kRagged>(rsrc, voff, row_bytes8, 0, buf0, wave);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         // Two stages per iteration: stage s from buf0 while s + 1 lands in
@@ -623,12 +649,12 @@ __global__ __launch_bounds__(dma::NT, 2) void assign_dma_kernel(
         // last iteration that load repeats stage s + 1 into buf0, which no one
         // reads any more; it completes before the tile's final barrier).
         for (int64_t s = 0; s < nk; s += 2) {
-            dma_compute(buf0, buf1, rsrc, voff, row_bytes8, (int)((s + 1) * dma::BK * 4), wave,
+            dma_compute<kRagged>(buf0, buf1, rsrc, voff, row_bytes8, (int)((s + 1) * dma::BK * 4), wave,
                         a_base, b_base, lane, aL, bL, acc);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             const int64_t s2 = s + 2 < nk ? s + 2 : s + 1;
-            dma_compute(buf1, buf0, rsrc, voff, row_bytes8, (int)(s2 * dma::BK * 4), wave,
+            dma_compute<kRagged>(buf1, buf0, rsrc, voff, row_bytes8, (int)(s2 * dma::BK * 4), wave,
                         a_base, b_base, lane, aL, bL, acc);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
@@ -643,28 +669,69 @@ __global__ __launch_bounds__(dma::NT, 2) void assign_dma_kernel(
         // index, the lowest one).
         float best[dma::NB];
         uint32_t bidx[dma::NB];
+        if constexpr (!kRagged) {
 #pragma unroll
-        for (int nb = 0; nb < dma::NB; ++nb) {
-            best[nb] = __builtin_inff();
-            bidx[nb] = (uint32_t)(m0 + wm * dma::MB * 32 + 4 * (lane >> 5));
-        }
+            for (int nb = 0; nb < dma::NB; ++nb) {
+                best[nb] = __builtin_inff();
+                bidx[nb] = (uint32_t)(m0 + wm * dma::MB * 32 + 4 * (lane >> 5));
+            }
 #pragma unroll
-        for (int mb = 0; mb < dma::MB; ++mb) {
-            float cnv[16];
+            for (int mb = 0; mb < dma::MB; ++mb) {
+                float cnv[16];
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                cnv[e] = cn[m0 + (wm * dma::MB + mb) * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)];
+                for (int e = 0; e < 16; ++e)
+                    cnv[e] = cn[m0 + (wm * dma::MB + mb) * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)];
 #pragma unroll
-            for (int nb = 0; nb < dma::NB; ++nb)
+                for (int nb = 0; nb < dma::NB; ++nb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int64_t m = m0 + (wm * dma::MB + mb) * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                        const float v = cnv[e] - 2.0f * acc[mb][nb][e];
+                        if (v < best[nb]) {
+                            best[nb] = v;
+                            bidx[nb] = (uint32_t)m;
+                        }
+                    }
+            }
+        } else {
+            // Ragged tiles skip the centroids from k on: their norm is taken
+            // as NaN (read at a clamped index, so every load stays
+            // unconditional), which never wins a strict less-than. A lane with
+            // no centroid below k starts from an index that every real
+            // candidate beats. Rows are counted from the tile's first one,
+            // starting from an offset the compiler cannot see through, so it
+            // forms the 64 per-element rows here rather than hoisting them out
+            // of the tile loop (where they spill).
+            int r0 = wm * dma::MB * 32 + 4 * (lane >> 5);
+            asm volatile("" : "+v"(r0));
+            const int lim = __builtin_amdgcn_readfirstlane(
+                (int)(k - m0 < dma::BM ? k - m0 : dma::BM));  // rows of this tile below k
+#pragma unroll
+            for (int nb = 0; nb < dma::NB; ++nb) {
+                best[nb] = __builtin_inff();
+                bidx[nb] = r0 < lim ? (uint32_t)(m0 + r0) : 0xffffffffu;
+            }
+#pragma unroll
+            for (int mb = 0; mb < dma::MB; ++mb) {
+                float cnv[16];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int64_t m = m0 + (wm * dma::MB + mb) * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                    const float v = cnv[e] - 2.0f * acc[mb][nb][e];
-                    if (v < best[nb]) {
-                        best[nb] = v;
-                        bidx[nb] = (uint32_t)m;
-                    }
+                    const int r = r0 + mb * 32 + 8 * (e >> 2) + (e & 3);
+                    const float c = cn[m0 + (r < lim ? r : lim - 1)];
+                    cnv[e] = r < lim ? c : __builtin_nanf("");
                 }
+#pragma unroll
+                for (int nb = 0; nb < dma::NB; ++nb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int r = r0 + mb * 32 + 8 * (e >> 2) + (e & 3);
+                        const float v = cnv[e] - 2.0f * acc[mb][nb][e];
+                        if (v < best[nb]) {
+                            best[nb] = v;
+                            bidx[nb] = (uint32_t)(m0 + r);
+                        }
+                    }
+            }
         }
 #pragma unroll
         for (int nb = 0; nb < dma::NB; ++nb) {
@@ -672,7 +739,7 @@ __global__ __launch_bounds__(dma::NT, 2) void assign_dma_kernel(
             const unsigned long long other = __shfl_xor(key, 32);
             key = other < key ? other : key;
             const int64_t smp = n0 + (wn * dma::NB + nb) * 32 + (lane & 31);
-            if (lane < 32) atomicMin(keys + smp, key);
+            if (lane < 32 && (!kRagged || smp < n)) atomicMin(keys + smp, key);
         }
         __syncthreads();  // the next tile's first DMA follows this tile's reads
     }
@@ -795,11 +862,18 @@ int64_t tile_blocks(int64_t n, int64_t k) {
 
 }  // namespace
 
-// Whether a shape's tiles are all full 256 x 256 ones with two 32-feature
-// stages per pass (the DMA-staged kernel's shapes; 32-bit buffer offsets
-// need 64 * d * 4 < 2^31).
-static bool dma_shape(int64_t n, int64_t k, int64_t d) {
-    return n % dma::BN == 0 && k % dma::BM == 0 && d % (2 * dma::BK) == 0 && d < (1 << 22);
+// Whether the DMA-staged kernel takes a shape: whole pairs of 32-feature
+// stages (32-bit buffer offsets need 64 * d * 4 < 2^31); any n and k, the
+// edge tiles cut short where n or k is not a multiple of 256.
+static bool dma_shape(int64_t d) { return d % (2 * dma::BK) == 0 && d < (1 << 22); }
+
+static bool dma_full(int64_t n, int64_t k) { return n % dma::BN == 0 && k % dma::BM == 0; }
+
+// Rounds of one tile per CU that `tiles` one-block-per-CU tiles take when
+// each XCD (an eighth of the CUs) runs an eighth of them.
+static int64_t tile_rounds(int64_t tiles, int64_t cus) {
+    const int64_t per_xcd = cus >= 8 ? cus / 8 : 1;
+    return cdiv(cdiv(tiles, 8), per_xcd);
 }
 
 static const char *assign_tile_name(int64_t n, int64_t k, int64_t d) {
@@ -810,13 +884,24 @@ static const char *assign_tile_name(int64_t n, int64_t k, int64_t d) {
                    !strcmp(forced, "64x64") || !strcmp(forced, "128x256") ||
                    !strcmp(forced, "256x256")))
         return forced;
-    // The DMA-staged 256 x 256 tile where every tile is full and there are
-    // enough to give each CU one; else the largest register-staged tile
-    // (fewest operand bytes per flop) when it gives at least two blocks per
-    // CU; otherwise 128 x 128 with short stages (3 blocks per CU), unless
-    // that leaves CUs idle, then 64 x 64.
-    if (dma_shape(n, k, d) && (n / dma::BN) * (k / dma::BM) >= 256) return "256x256";
-    if (tile_blocks<Tile128x256>(n, k) >= 512) return "128x256";
+    // The DMA-staged 256 x 256 tile where there are enough tiles to give each
+    // CU one and either every tile is full or, with edge tiles cut short, it
+    // still beats 128 x 256: a round of 256 x 256 tiles costs 1.8 rounds of
+    // 128 x 256 ones (measured at d = 1024 ... 4096: 1.79-1.82), so it loses
+    // where its coarser edge or last round wastes more (k = 300: 512 rows
+    // computed against 384). Else the largest register-staged tile (fewest
+    // operand bytes per flop) when it gives at least two blocks per CU;
+    // otherwise 128 x 128 with short stages (3 blocks per CU), unless that
+    // leaves CUs idle, then 64 x 64.
+    const int64_t big = cdiv(n, dma::BN) * cdiv(k, dma::BM);
+    const int64_t mid = tile_blocks<Tile128x256>(n, k);
+    if (dma_shape(d) && big >= 256) {
+        if (dma_full(n, k)) return "256x256";
+        const int cus = device_cus();
+        const int64_t c = cus > 0 ? cus : 256;
+        if (mid >= 512 && 9 * tile_rounds(big, c) < 5 * tile_rounds(mid, c)) return "256x256";
+    }
+    if (mid >= 512) return "128x256";
     if (tile_blocks<Tile128x128>(n, k) >= 256) return "128x128";
     return "64x64";
 }
@@ -842,12 +927,16 @@ hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, 
         // One persistent block per CU (128 KiB of LDS: one fits), each walking
         // its XCD's tiles; the walk needs at least 8 blocks or one per tile.
         const int cus = device_cus();
-        if (dma_shape(n, k, d) && vec_ok(X, d) && vec_ok(C, d) && cus >= 8) {
-            const int tm = (int)(k / dma::BM), tn = (int)(n / dma::BN);
+        if (dma_shape(d) && vec_ok(X, d) && vec_ok(C, d) && cus >= 8) {
+            const int tm = (int)cdiv(k, dma::BM), tn = (int)cdiv(n, dma::BN);
             const int64_t tiles = (int64_t)tm * tn;
             const unsigned blocks = (unsigned)(tiles < cus ? tiles : cus);
-            assign_dma_kernel<<<blocks, dma::NT, 0, stream>>>(X, C, cn, n, k, d, tm, tn, keys,
-                                                              stop);
+            if (dma_full(n, k))
+                assign_dma_kernel<false><<<blocks, dma::NT, 0, stream>>>(X, C, cn, n, k, d, tm, tn,
+                                                                         keys, stop);
+            else
+                assign_dma_kernel<true><<<blocks, dma::NT, 0, stream>>>(X, C, cn, n, k, d, tm, tn,
+                                                                        keys, stop);
             return hipGetLastError();
         }
         return launch_tiles_cfg<Tile128x256, 2>(X, C, cn, n, k, d, keys, stop, stream);

@@ -377,6 +377,27 @@ def test_dma_tile_walk(monkeypatch, n, k, d):
     assert np.array_equal(g_md.astype(np.float64), best)
 
 
+@pytest.mark.parametrize("n,k,d", [(9000, 2100, 128), (1000, 300, 64), (70, 17, 64),
+                                   (16385, 4095, 64), (5000, 1000, 1024), (300, 1, 64),
+                                   (2048, 700, 192), (700, 2048, 64)])
+def test_dma_tile_ragged(monkeypatch, n, k, d):
+    """The DMA-staged 256 x 256 kernel on shapes whose n or k is not a
+    multiple of 256: edge tiles where part of a wave's 64 rows, or all of
+    them, lie past n or k (9000 x 2100: the last tiles keep 40 samples and 52
+    centroids), 324 tiles down to one (70 x 17: fewer rows than one wave
+    loads), a single centroid, and ragged n or k alone. Integer data: labels
+    and distances bit-exact."""
+    monkeypatch.setenv("KMEANS_ASSIGN_TILE", "256x256")
+    gu.announce(f"dma ragged {n}x{k}x{d}")
+    X, C = datagen.make_integer(n, k, d, seed=n + 2 * k + d)
+    if k > 6:
+        C[k - 1] = C[5]
+    g_labels, g_md = gu.gpu_assign(X, C)
+    o_labels, best, _ = oracle.assign(X, C)
+    assert np.array_equal(g_labels, o_labels)
+    assert np.array_equal(g_md.astype(np.float64), best)
+
+
 def test_dma_tile_unaligned_falls_back(monkeypatch):
     """A 256 x 256 shape whose samples are not 16-byte aligned runs on the
     register-staged kernel instead (scalar loads), with the same results."""
@@ -459,7 +480,7 @@ def test_update_skewed_clusters(n, k, d, skew):
 
 
 @pytest.mark.parametrize("n,k,d,tile", [(1000, 37, 64, None), (4096, 32, 64, None),
-                                        (65536, 256, 256, "256x256")])
+                                        (65536, 256, 256, "256x256"), (1000, 37, 64, "256x256")])
 def test_overflowing_centroid_norms_keep_labels_in_range(monkeypatch, n, k, d, tile):
     """Finite centroids whose float32 squared norm overflows: every candidate
     distance of a row is +inf, so the lowest index wins the +inf tie, as for
