@@ -94,6 +94,10 @@ __global__ __launch_bounds__(256) void pp_norm_kernel(const float *__restrict__ 
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
+__device__ __forceinline__ float f4_at(const float4 &v, int e) {
+    return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+}
+
 // Every sample against up to 16 candidates with float64 matrix cores
 // (v_mfma_f64_16x16x4_f64: D(16 x 16) += A(16 x 4) B(4 x 16)). A block holds
 // 64 samples, 16 per wave; a wave's tile is its 16 samples x the 16 candidate
@@ -116,13 +120,19 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 // v_mfma_f64_4x4x4_4b_f64 instead: four independent 4 x 4 x 4 blocks per
 // instruction, a quarter of the 16 x 16 x 4 work. Its layout (probed on the
 // chip): lane 16k + 4b + i holds A[b][i][k], lane 16k + 4b + j holds
-// B[b][k][j], and lane 16i + 4b + j receives D[b][i][j]. Block b takes samples
-// 4b .. 4b+3 of the wave: the A operand is sample l % 16, feature k-group
-// l / 16 -- the same lane layout as the 16 x 16 x 4 product, so the sample
-// staging is unchanged -- and B is candidate 4h + l % 4 in the two
-// instructions h = 0, 1 of each feature step. Each lane then ends with two
-// values: sample 4 ((l / 4) % 4) + l / 16 against candidates l % 4 and
-// 4 + l % 4.
+// B[b][k][j], and lane 16i + 4b + j receives D[b][i][j]. The four blocks take
+// the same 4 samples and 4 candidates over four different feature
+// sub-ranges: a stage's 128 features are split into 16 runs of 8, lane
+// 16k + 4b + i taking run sigma(b, k) for both operands, and block b's
+// partial products are summed over the blocks at the end. Per feature step a
+// wave issues 8 instructions: sample group g = 0 .. 3 (samples 4g + i) x
+// candidate group h = 0, 1 (candidates 4h + j). Every lane thus reads from
+// LDS only the operands it uses: its 8 features of 4 samples and 2
+// candidates per stage (had the blocks taken four sample groups against the
+// same candidates, each lane would read the candidates four times over:
+// measured 4 % slower per seeding at 65536 x 8192, k = 1024, same centres).
+// After the sum, lane l keeps sample 4 ((l / 4) % 4) + l / 16 against
+// candidates l % 4 and 4 + l % 4.
 constexpr int kMfF = 128;           // features per stage
 constexpr int kMfRun = kMfF / 4;    // contiguous features per lane per stage
 constexpr int kMfLdk = kMfF + 4;    // padded LDS row of a candidate
@@ -196,16 +206,38 @@ __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
     __syncthreads();
 
     f64x4 acc = {0.0, 0.0, 0.0, 0.0};  // kSlots == 16
-    double acc8[2] = {0.0, 0.0};       // kSlots == 8: candidates l % 4 and 4 + l % 4
+    // kSlots == 8: with l = 16 i + 4 b + j (the output layout), block b's
+    // partial product of sample 4 g + i against candidate 4 h + j.
+    double acc8[4][2] = {{0.0, 0.0}, {0.0, 0.0}, {0.0, 0.0}, {0.0, 0.0}};
+    // Its operands (l = 16 k + 4 b + i): the 8 features 8 sigma(b, k) .. + 7
+    // of the stage, sigma(b, k) = 2 b + k % 2 + 8 (k / 2), a permutation of
+    // 0 .. 15 that puts the 16-byte reads of 16 consecutive lanes on
+    // distinct banks (rows 132 floats apart: a row shifts the banks by 4).
+    const int sig8 = 8 * (2 * ((lane >> 2) & 3) + (grp & 1) + 8 * (grp >> 1));
     for (int64_t c = 0; c < chunks; ++c) {
         const int cur = (int)(c & 1);
-        // This lane's A operands of the stage (its own wave's slice: the
-        // wave's LDS operations run in order, so the slice can be rewritten
-        // below without a barrier).
+        // This lane's operands of the stage: samples from its own wave's
+        // slice (the wave's LDS operations run in order, so the slice can be
+        // rewritten below without a barrier), candidates (8-slot instance)
+        // from the shared buffer the last barrier published.
         float4 xa[kMfRun / 4];
-        const float *arow = &xw[wave][lane & 15][grp * kMfRun];
+        float4 xa8[4][2], cb8[2][2];
+        if constexpr (kSlots == 16) {
+            const float *arow = &xw[wave][lane & 15][grp * kMfRun];
 #pragma unroll
-        for (int q = 0; q < kMfRun / 4; ++q) xa[q] = *reinterpret_cast<const float4 *>(arow + 4 * q);
+            for (int q = 0; q < kMfRun / 4; ++q) xa[q] = *reinterpret_cast<const float4 *>(arow + 4 * q);
+        } else {
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    xa8[g][hh] = *reinterpret_cast<const float4 *>(&xw[wave][4 * g + (lane & 3)][sig8 + 4 * hh]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    cb8[h][hh] = *reinterpret_cast<const float4 *>(&cs[cur][4 * h + (lane & 3)][sig8 + 4 * hh]);
+        }
         if (c + 1 < chunks) {
             const int64_t next = (c + 1 + rot) % chunks;
             load_x(next, xn);
@@ -223,20 +255,15 @@ __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
                 acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[q].w, (double)bv.w, acc, 0, 0, 0);
             }
         } else {
-            const float *b0 = &cs[cur][lane & 3][grp * kMfRun];
-            const float *b1 = &cs[cur][4 + (lane & 3)][grp * kMfRun];
 #pragma unroll
-            for (int q = 0; q < kMfRun / 4; ++q) {
-                const float4 v0 = *reinterpret_cast<const float4 *>(b0 + 4 * q);
-                const float4 v1 = *reinterpret_cast<const float4 *>(b1 + 4 * q);
-                acc8[0] = __builtin_amdgcn_mfma_f64_4x4x4f64((double)xa[q].x, (double)v0.x, acc8[0], 0, 0, 0);
-                acc8[1] = __builtin_amdgcn_mfma_f64_4x4x4f64((double)xa[q].x, (double)v1.x, acc8[1], 0, 0, 0);
-                acc8[0] = __builtin_amdgcn_mfma_f64_4x4x4f64((double)xa[q].y, (double)v0.y, acc8[0], 0, 0, 0);
-                acc8[1] = __builtin_amdgcn_mfma_f64_4x4x4f64((double)xa[q].y, (double)v1.y, acc8[1], 0, 0, 0);
-                acc8[0] = __builtin_amdgcn_mfma_f64_4x4x4f64((double)xa[q].z, (double)v0.z, acc8[0], 0, 0, 0);
-                acc8[1] = __builtin_amdgcn_mfma_f64_4x4x4f64((double)xa[q].z, (double)v1.z, acc8[1], 0, 0, 0);
-                acc8[0] = __builtin_amdgcn_mfma_f64_4x4x4f64((double)xa[q].w, (double)v0.w, acc8[0], 0, 0, 0);
-                acc8[1] = __builtin_amdgcn_mfma_f64_4x4x4f64((double)xa[q].w, (double)v1.w, acc8[1], 0, 0, 0);
+            for (int st = 0; st < 8; ++st) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        acc8[g][h] = __builtin_amdgcn_mfma_f64_4x4x4f64(
+                            (double)f4_at(xa8[g][st >> 2], st & 3), (double)f4_at(cb8[h][st >> 2], st & 3),
+                            acc8[g][h], 0, 0, 0);
             }
         }
         if (c + 1 < chunks) {
@@ -274,12 +301,24 @@ __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
     } else {
         // Lane l: sample 4 ((l / 4) % 4) + l / 16 against slots l % 4 and
         // 4 + l % 4; the 16 lanes of a slot differ in bits 2 .. 5.
-        const int64_t gi = row0 + 4 * ((lane >> 2) & 3) + grp;
+        const int gsel = (lane >> 2) & 3;
+        const int64_t gi = row0 + 4 * gsel + grp;
         double part[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+            // Sum over the blocks (lanes differing in bits 2 and 3): every lane
+            // adds (b0 + b1) + (b2 + b3), so all four hold the same bits.
+            double red[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                double v = acc8[g][h];
+                v += __shfl_xor(v, 4);
+                v += __shfl_xor(v, 8);
+                red[g] = v;
+            }
+            const double dot = gsel == 0 ? red[0] : gsel == 1 ? red[1] : gsel == 2 ? red[2] : red[3];
             const int t = 4 * h + (lane & 3);
-            part[h] = (t < trials && gi < n) ? dist_of(gi, t, acc8[h]) : 0.0;
+            part[h] = (t < trials && gi < n) ? dist_of(gi, t, dot) : 0.0;
 #pragma unroll
             for (int o = 4; o < 64; o <<= 1) part[h] += __shfl_xor(part[h], o);
         }
