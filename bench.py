@@ -84,9 +84,9 @@ def parse_args():
 def assign_kernel_name(n: int, k: int, d: int, cus: int = 256) -> str:
     """The product kernel kmeans_assign runs for 16-byte aligned inputs of
     this shape on a device with `cus` compute units (the launcher's rule:
-    DMA-staged 256 x 256 tiles when d is a multiple of 64, there are at least
-    256 of them and either every tile is full or 1.8 rounds of 128 x 256
-    tiles per round of them still come out ahead)."""
+    DMA-staged 256 x 256 tiles when d is a multiple of 4, there are at least
+    256 of them and either every tile is full (d a multiple of 64) or 1.8
+    rounds of 128 x 256 tiles per round of them still come out ahead)."""
     def cdiv(a, b):
         return -(-a // b)
 
@@ -95,8 +95,8 @@ def assign_kernel_name(n: int, k: int, d: int, cus: int = 256) -> str:
 
     big = cdiv(n, 256) * cdiv(k, 256)
     mid = cdiv(n, 256) * cdiv(k, 128)
-    if d % 64 == 0 and big >= 256:
-        if n % 256 == 0 and k % 256 == 0:
+    if d % 4 == 0 and big >= 256:
+        if n % 256 == 0 and k % 256 == 0 and d % 64 == 0:
             return "assign_dma_kernel"
         if mid >= 512 and 9 * rounds(big) < 5 * rounds(mid):
             return "assign_dma_kernel"

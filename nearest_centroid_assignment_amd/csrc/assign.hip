@@ -10,7 +10,7 @@
 //   row_sqnorms_kernel  ||c_j||^2 (and ||x_i||^2 for min_dist outside a Lloyd step)
 //   fill_keys_kernel    packed-key identity
 //   assign_dma_kernel   float32 MFMA product X_tile . C_tile^T in 256 x 256
-//                       tiles (d a multiple of 64; edge tiles cut short where
+//                       tiles (d a multiple of 4; edge tiles cut short where
 //                       n or k is not a multiple of 256), the operands moved
 //                       from global memory straight into LDS by buffer loads,
 //                       with the distance, the argmin and the merge across
@@ -450,8 +450,9 @@ __global__ __launch_bounds__(Cfg::kThreads, MinWaves) void assign_tile_kernel(
 
 // ------------------------------------------------ DMA-staged 256 x 256 tiles
 //
-// d % 64 == 0 and 16-byte aligned rows; any n and k (the ragged instance
-// reads only the rows below n and k and skips the rest). 8 waves in 2 x 4; each wave owns 128 centroids x 64 samples (4 x 2
+// 16-byte aligned rows of d % 4 == 0 floats, any n and k (the ragged
+// instances read only the rows below n and k and skip the rest, and the
+// any-d one also zeroes a partial last stage past d). 8 waves in 2 x 4; each wave owns 128 centroids x 64 samples (4 x 2
 // blocks of 32 x 32), so a fragment read from LDS feeds more MFMAs than in
 // the 128 x 256 tile (6 reads per 32 MFMAs instead of 4 per 16), a stage
 // holds twice the MFMAs per barrier, and the 128 accumulators per lane fit
@@ -495,6 +496,16 @@ __device__ __forceinline__ void dma_stage(__amdgpu_buffer_rsrc_t rsrc, const int
             rsrc, (__attribute__((address_space(3))) void *)(buf + (wave * dma::PER_WAVE + j) * 64 * 4),
             16, kRagged ? voff[j & 1] + j * row_bytes8 : voff[j & 1],
             kRagged ? kbytes : j * row_bytes8 + kbytes, 0, 0);
+}
+
+// Zeros the 16-byte chunks from `valid` on of every row of a stage buffer
+// (thread t: row t), so that a stage that ends inside the rows contributes
+// nothing past the last feature, whatever its DMA left there.
+__device__ __forceinline__ void dma_zero_tail(float *buf, int valid, int tid) {
+    static_assert(dma::NT == dma::ROWS, "one thread per stage row");
+    for (int c = valid; c < dma::BK / 4; ++c)
+        *reinterpret_cast<f32x4 *>(buf + tid * dma::BK + ((c ^ dma::swz(tid)) << 2)) =
+            f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // Fragments of group g (features 8g .. 8g + 7) for this lane: A rows
@@ -570,7 +581,12 @@ __device__ __forceinline__ void dma_compute(const float *buf, float *dst, __amdg
     for (int nb = 0; nb < dma::NB; ++nb) bL[nb] = b[1][nb];
 }
 
-template <bool kRagged>
+// The kernel's instances: whole tiles and pairs of stages; edge tiles cut
+// short, still pairs of stages; anything else (edge tiles, any number of
+// stages, a partial last one).
+enum DmaMode { kDmaFull = 0, kDmaRagged = 1, kDmaAnyD = 2 };
+
+template <int kMode>
 __global__ __launch_bounds__(dma::NT, 2) void assign_dma_kernel(
     const float *__restrict__ X, const float *__restrict__ C, const float *__restrict__ cn,
     int64_t n, int64_t k, int64_t d, int tiles_m, int tiles_n,
@@ -583,7 +599,11 @@ __global__ __launch_bounds__(dma::NT, 2) void assign_dma_kernel(
     const int wm = wave % dma::WM, wn = wave / dma::WM;
     const int a_base = wm * dma::MB * 32 + (lane & 31);
     const int b_base = dma::BM + wn * dma::NB * 32 + (lane & 31);
-    const int64_t nk = d / dma::BK;  // even
+    constexpr bool kRagged = kMode != kDmaFull;
+    constexpr bool kAnyD = kMode == kDmaAnyD;
+    const int64_t nk = kAnyD ? (d + dma::BK - 1) / dma::BK : d / dma::BK;  // stages (even unless kAnyD)
+    // 16-byte chunks of features in the last stage (8: a whole stage).
+    const int tail_chunks = (int)(d - (nk - 1) * dma::BK) / 4;
     // Tile counts fit an int: the library rejects shapes whose launch grid
     // would exceed 2^32 - 1 work-items, far fewer than 2^31 tiles.
     const int T = tiles_m * tiles_n;
@@ -628,6 +648,17 @@ __global__ __launch_bounds__(dma::NT, 2) void assign_dma_kernel(
         const int voff[2] = {(int)((lane >> 3) * d * 4 + c0 * 16),
                              (int)((lane >> 3) * d * 4 + (c0 ^ 4) * 16)};
         const int row_bytes8 = (int)(8 * d * 4);
+        // The last stage of a ragged tile may end inside the rows: there the
+        // lanes whose chunk lies past d take an offset of 2^31, beyond any
+        // buffer's records, so they touch no memory (also where the uniform
+        // offset is left out of the range check: the row's end can be the
+        // matrix's). Their LDS slots are zeroed once the stage has landed.
+        int voff_t[2] = {voff[0], voff[1]};
+        if (kAnyD) {
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+                if ((c0 ^ (4 * p)) >= tail_chunks) voff_t[p] = (int)0x80000000u;
+        }
         f32x16 acc[dma::MB][dma::NB];
 #pragma unroll
         for (int i = 0; i < dma::MB; ++i)
@@ -641,23 +672,56 @@ __global__ __launch_bounds__(dma::NT, 2) void assign_dma_kernel(
 #pragma unroll
         for (int nb = 0; nb < dma::NB; ++nb) bL[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        dma_stage<kRagged>(rsrc, voff, row_bytes8, 0, buf0, wave);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        // Two stages per iteration: stage s from buf0 while s + 1 lands in
-        // buf1, then stage s + 1 from buf1 while s + 2 lands in buf0 (on the
-        // last iteration that load repeats stage s + 1 into buf0, which no one
-        // reads any more; it completes before the tile's final barrier).
-        for (int64_t s = 0; s < nk; s += 2) {
-            dma_compute<kRagged>(buf0, buf1, rsrc, voff, row_bytes8, (int)((s + 1) * dma::BK * 4), wave,
-                        a_base, b_base, lane, aL, bL, acc);
+        if constexpr (!kAnyD) {
+            dma_stage<kRagged>(rsrc, voff, row_bytes8, 0, buf0, wave);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            const int64_t s2 = s + 2 < nk ? s + 2 : s + 1;
-            dma_compute<kRagged>(buf1, buf0, rsrc, voff, row_bytes8, (int)(s2 * dma::BK * 4), wave,
-                        a_base, b_base, lane, aL, bL, acc);
+            // Two stages per iteration: stage s from buf0 while s + 1 lands in
+            // buf1, then stage s + 1 from buf1 while s + 2 lands in buf0 (on
+            // the last iteration that load repeats stage s + 1 into buf0,
+            // which no one reads any more; it completes before the tile's
+            // final barrier).
+            for (int64_t s = 0; s < nk; s += 2) {
+                dma_compute<kRagged>(buf0, buf1, rsrc, voff, row_bytes8, (int)((s + 1) * dma::BK * 4),
+                                     wave, a_base, b_base, lane, aL, bL, acc);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                const int64_t s2 = s + 2 < nk ? s + 2 : s + 1;
+                dma_compute<kRagged>(buf1, buf0, rsrc, voff, row_bytes8, (int)(s2 * dma::BK * 4), wave,
+                                     a_base, b_base, lane, aL, bL, acc);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+            }
+        } else {
+            // One stage per iteration (any number of them), the buffers
+            // alternating: stage s from one while stage s + 1 lands in the
+            // other (the last iteration repeats stage s, which no one reads).
+            // A partial last stage loads with the tail offsets and is zeroed
+            // past d before anyone reads it. (Two stages per iteration with
+            // the odd and partial cases around them ran 1-5 % slower: the
+            // extra branches pushed the kernel past its registers.)
+            const bool partial = tail_chunks < dma::BK / 4;
+            dma_stage<true>(rsrc, partial && nk == 1 ? voff_t : voff, row_bytes8, 0, buf0, wave);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
+            if (partial && nk == 1) {
+                dma_zero_tail(buf0, tail_chunks, tid);
+                __syncthreads();
+            }
+            for (int64_t s = 0; s < nk; ++s) {
+                float *cur = (s & 1) ? buf1 : buf0;
+                float *nxt = (s & 1) ? buf0 : buf1;
+                const int64_t sn = s + 1 < nk ? s + 1 : s;
+                const bool tail_next = partial && sn == nk - 1;
+                dma_compute<true>(cur, nxt, rsrc, tail_next ? voff_t : voff, row_bytes8,
+                                  (int)(sn * dma::BK * 4), wave, a_base, b_base, lane, aL, bL, acc);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                if (tail_next && s + 1 < nk) {
+                    dma_zero_tail(nxt, tail_chunks, tid);
+                    __syncthreads();
+                }
+            }
         }
         dma_mma(aL, bL, acc);
 
@@ -862,12 +926,16 @@ int64_t tile_blocks(int64_t n, int64_t k) {
 
 }  // namespace
 
-// Whether the DMA-staged kernel takes a shape: whole pairs of 32-feature
-// stages (32-bit buffer offsets need 64 * d * 4 < 2^31); any n and k, the
-// edge tiles cut short where n or k is not a multiple of 256.
-static bool dma_shape(int64_t d) { return d % (2 * dma::BK) == 0 && d < (1 << 22); }
+// Whether the DMA-staged kernel takes a shape: rows of whole 16-byte chunks
+// (32-bit buffer offsets need 64 * d * 4 < 2^31); any n and k. Its full-tile
+// instance takes whole 256 x 256 tiles and pairs of 32-feature stages, the
+// ragged one everything else (edge tiles cut short where n or k is not a
+// multiple of 256, any number of stages, the last one partial).
+static bool dma_shape(int64_t d) { return d % 4 == 0 && d < (1 << 22); }
 
-static bool dma_full(int64_t n, int64_t k) { return n % dma::BN == 0 && k % dma::BM == 0; }
+static bool dma_full(int64_t n, int64_t k, int64_t d) {
+    return n % dma::BN == 0 && k % dma::BM == 0 && d % (2 * dma::BK) == 0;
+}
 
 // Rounds of one tile per CU that `tiles` one-block-per-CU tiles take when
 // each XCD (an eighth of the CUs) runs an eighth of them.
@@ -896,7 +964,7 @@ static const char *assign_tile_name(int64_t n, int64_t k, int64_t d) {
     const int64_t big = cdiv(n, dma::BN) * cdiv(k, dma::BM);
     const int64_t mid = tile_blocks<Tile128x256>(n, k);
     if (dma_shape(d) && big >= 256) {
-        if (dma_full(n, k)) return "256x256";
+        if (dma_full(n, k, d)) return "256x256";
         const int cus = device_cus();
         const int64_t c = cus > 0 ? cus : 256;
         if (mid >= 512 && 9 * tile_rounds(big, c) < 5 * tile_rounds(mid, c)) return "256x256";
@@ -931,12 +999,15 @@ hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, 
             const int tm = (int)cdiv(k, dma::BM), tn = (int)cdiv(n, dma::BN);
             const int64_t tiles = (int64_t)tm * tn;
             const unsigned blocks = (unsigned)(tiles < cus ? tiles : cus);
-            if (dma_full(n, k))
-                assign_dma_kernel<false><<<blocks, dma::NT, 0, stream>>>(X, C, cn, n, k, d, tm, tn,
-                                                                         keys, stop);
+            if (dma_full(n, k, d))
+                assign_dma_kernel<kDmaFull><<<blocks, dma::NT, 0, stream>>>(X, C, cn, n, k, d, tm,
+                                                                            tn, keys, stop);
+            else if (d % (2 * dma::BK) == 0)
+                assign_dma_kernel<kDmaRagged><<<blocks, dma::NT, 0, stream>>>(X, C, cn, n, k, d, tm,
+                                                                              tn, keys, stop);
             else
-                assign_dma_kernel<true><<<blocks, dma::NT, 0, stream>>>(X, C, cn, n, k, d, tm, tn,
-                                                                        keys, stop);
+                assign_dma_kernel<kDmaAnyD><<<blocks, dma::NT, 0, stream>>>(X, C, cn, n, k, d, tm,
+                                                                            tn, keys, stop);
             return hipGetLastError();
         }
         return launch_tiles_cfg<Tile128x256, 2>(X, C, cn, n, k, d, keys, stop, stream);

@@ -73,14 +73,16 @@ def test_assign_kernel_name_follows_the_tile_rule():
     for the aligned benchmark shapes and for the ragged shapes where they
     were measured faster than 128 x 256 ones on 256 CUs; the register-staged
     kernel where the 256-row edge or last round wastes more (k = 300,
-    50000 x 700), for fewer than 256 tiles, and for d not a multiple of 64."""
+    50000 x 700), for fewer than 256 tiles, and for rows that are not whole
+    16-byte chunks (d not a multiple of 4)."""
     dma, reg = "assign_dma_kernel", "assign_tile_kernel"
     for name in ("mid", "feature_heavy", "centroid_heavy", "sample_heavy"):
         cfg = datagen.CONFIGS[name]
         assert bench.assign_kernel_name(cfg.n, cfg.k, cfg.d) == dma
     for shape in [(65000, 1000, 2048), (100000, 1500, 1024), (65536, 4000, 4096),
-                  (131000, 8100, 1024), (20000, 5000, 512), (65000, 1024, 2048)]:
+                  (131000, 8100, 1024), (20000, 5000, 512), (65000, 1024, 2048),
+                  (65536, 1024, 96), (65536, 4096, 300), (65536, 4096, 992), (131072, 8192, 96)]:
         assert bench.assign_kernel_name(*shape) == dma, shape
     for shape in [(60000, 300, 2048), (50000, 700, 1024), (4000, 1000, 1024),
-                  (65536, 1024, 2050), (4096, 256, 512)]:
+                  (65536, 1024, 2050), (65536, 1024, 99), (4096, 256, 512)]:
         assert bench.assign_kernel_name(*shape) == reg, shape

@@ -379,14 +379,20 @@ def test_dma_tile_walk(monkeypatch, n, k, d):
 
 @pytest.mark.parametrize("n,k,d", [(9000, 2100, 128), (1000, 300, 64), (70, 17, 64),
                                    (16385, 4095, 64), (5000, 1000, 1024), (300, 1, 64),
-                                   (2048, 700, 192), (700, 2048, 64)])
+                                   (2048, 700, 192), (700, 2048, 64),
+                                   (9000, 2100, 96), (4096, 1024, 160), (2048, 512, 784),
+                                   (1000, 300, 100), (5000, 1000, 300), (777, 260, 28),
+                                   (70, 17, 4), (4096, 512, 20)])
 def test_dma_tile_ragged(monkeypatch, n, k, d):
-    """The DMA-staged 256 x 256 kernel on shapes whose n or k is not a
-    multiple of 256: edge tiles where part of a wave's 64 rows, or all of
-    them, lie past n or k (9000 x 2100: the last tiles keep 40 samples and 52
-    centroids), 324 tiles down to one (70 x 17: fewer rows than one wave
-    loads), a single centroid, and ragged n or k alone. Integer data: labels
-    and distances bit-exact."""
+    """The DMA-staged 256 x 256 kernel's ragged instance: edge tiles where
+    part of a wave's 64 rows, or all of them, lie past n or k (9000 x 2100:
+    the last tiles keep 40 samples and 52 centroids), 324 tiles down to one
+    (70 x 17: fewer rows than one wave loads), a single centroid, ragged n or
+    k alone; and feature counts that are not a multiple of 64: an odd number
+    of 32-feature stages (96, 160, 784), a last stage that ends inside the
+    rows (100, 300, 784: 1, 3 and 4 of its 8 chunks), a single partial
+    stage (28, 20, 4 features), with whole tiles (4096 x 1024, 2048 x 512)
+    or ragged ones. Integer data: labels and distances bit-exact."""
     monkeypatch.setenv("KMEANS_ASSIGN_TILE", "256x256")
     gu.announce(f"dma ragged {n}x{k}x{d}")
     X, C = datagen.make_integer(n, k, d, seed=n + 2 * k + d)
