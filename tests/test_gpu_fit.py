@@ -176,3 +176,26 @@ def test_fit_large_k_relocation():
     gu.check_min_dist(X, Cf, g["labels"], g["min_dist"], o_labels=o_labels, best=best)
     assert np.array_equal(g["counts"], np.bincount(g["labels"], minlength=len(C)))
     assert abs(g["inertia"] - float(np.sum(g["min_dist"].astype(np.float64)))) <= 1e-9 * g["inertia"]
+
+
+def test_fit_dma_any_d():
+    """20000 x 3000 x 100: the assignment runs on the DMA-staged kernel's
+    any-d instance (edge tiles on n and k, a last feature stage of one
+    16-byte chunk). Integer data: the first iteration matches the oracle's
+    driver outright; after three, the labels are the nearest-centroid labels
+    of the returned centres (near-tie rule) and counts, min_dist and inertia
+    agree with them."""
+    gu.announce("fit 20000x3000x100 (DMA any-d)")
+    X, C = datagen.make_integer(20000, 3000, 100, seed=31)
+    g = gpu_fit(X, C, 1, 0.0, True)
+    o = oracle.fit(X, C, 1, 0.0, True)
+    compare(g, o, X)
+    g = gpu_fit(X, C, 3, 0.0, True)
+    assert g["n_iter"] == 3
+    Cf = g["centres"]
+    o_labels, best, second = oracle.assign(X, Cf)
+    ties, mism = gu.check_labels(X, Cf, g["labels"], o_labels, best, second)
+    gu.announce(f"fit 20000x3000x100, 3 iterations: near-ties {ties}, label mismatches {mism}")
+    gu.check_min_dist(X, Cf, g["labels"], g["min_dist"], o_labels=o_labels, best=best)
+    assert np.array_equal(g["counts"], np.bincount(g["labels"], minlength=len(C)))
+    assert abs(g["inertia"] - float(np.sum(g["min_dist"].astype(np.float64)))) <= 1e-9 * g["inertia"]

@@ -130,6 +130,33 @@ def test_lloyd_min_dist_paths(n, k, d, what):
     assert np.all(np.abs(l_md.astype(np.float64) - a_md) <= 4e-6 * xn + 1e-6)
 
 
+# Shapes where the launcher's own rule (no forced tile) takes the DMA-staged
+# kernel's ragged instances: n not a multiple of 256 with d a multiple of 64,
+# and d a multiple of 4 only (a partial last stage).
+DMA_DEFAULT = [(65000, 1024, 128), (20000, 3000, 100), (40000, 2000, 300)]
+
+
+@pytest.mark.parametrize("n,k,d", DMA_DEFAULT, ids=[f"{n}x{k}x{d}" for n, k, d in DMA_DEFAULT])
+def test_lloyd_dma_ragged_default(n, k, d):
+    """The whole Lloyd step, every row against the oracle, on shapes that the
+    default selection sends to the ragged DMA instances (the host-side mirror
+    of the rule confirms the choice for a 256-CU device)."""
+    import os
+    import sys
+
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+
+    assert bench.assign_kernel_name(n, k, d) == "assign_dma_kernel"
+    gu.announce(f"lloyd dma ragged default {n}x{k}x{d}")
+    rng = np.random.default_rng(n + k + d)
+    centres = 2.0 * rng.standard_normal((k, d))
+    X = (centres[rng.integers(0, k, n)] + rng.standard_normal((n, d))).astype(np.float32)
+    C = X[rng.choice(n, k, replace=False)].copy()
+    res = gu.full_parity(X, C)
+    assert res["mismatches"] <= res["near_ties"]
+
+
 # The counting sort's paths by k: the cluster scan holds 1, 2, 4, 8 or 16
 # clusters per thread in registers up to k = 16384 and takes 1024-cluster
 # chunks above; the per-tile label table sits in LDS up to k = 16384 and in the
