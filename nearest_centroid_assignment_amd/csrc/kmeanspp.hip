@@ -115,29 +115,31 @@ __device__ __forceinline__ float f4_at(const float4 &v, int e) {
 // Output layout (probed on the chip): lane l, value i is sample (l / 16) +
 // 4 i of the wave's 16, candidate slot l % 16.
 //
-// With at most 8 trials (kSlots = 8; 8 at the pages' k = 1024) half of those
-// 16 slots would multiply zeros, so the product runs on
-// v_mfma_f64_4x4x4_4b_f64 instead: four independent 4 x 4 x 4 blocks per
-// instruction, a quarter of the 16 x 16 x 4 work. Its layout (probed on the
+// With at most 12 trials (kQuad, kSlots = 8 or 12; 8 at the pages' k = 1024)
+// a quarter to a half of those 16 slots would multiply zeros, so the product
+// runs on v_mfma_f64_4x4x4_4b_f64 instead: four independent 4 x 4 x 4 blocks
+// per instruction, a quarter of the 16 x 16 x 4 work. Its layout (probed on the
 // chip): lane 16k + 4b + i holds A[b][i][k], lane 16k + 4b + j holds
 // B[b][k][j], and lane 16i + 4b + j receives D[b][i][j]. The four blocks take
 // the same 4 samples and 4 candidates over four different feature
 // sub-ranges: a stage's 128 features are split into 16 runs of 8, lane
 // 16k + 4b + i taking run sigma(b, k) for both operands, and block b's
 // partial products are summed over the blocks at the end. Per feature step a
-// wave issues 8 instructions: sample group g = 0 .. 3 (samples 4g + i) x
-// candidate group h = 0, 1 (candidates 4h + j). Every lane thus reads from
-// LDS only the operands it uses: its 8 features of 4 samples and 2
-// candidates per stage (had the blocks taken four sample groups against the
-// same candidates, each lane would read the candidates four times over:
+// wave issues 4 H instructions: sample group g = 0 .. 3 (samples 4g + i) x
+// candidate group h < H = kSlots / 4 (candidates 4h + j). Every lane thus
+// reads from LDS only the operands it uses: its 8 features of 4 samples and
+// H candidates per stage (had the blocks taken four sample groups against
+// the same candidates, each lane would read the candidates four times over:
 // measured 4 % slower per seeding at 65536 x 8192, k = 1024, same centres).
 // After the sum, lane l keeps sample 4 ((l / 4) % 4) + l / 16 against
-// candidates l % 4 and 4 + l % 4.
+// candidates 4h + l % 4. At 9 to 11 trials the 12-slot instance takes
+// 367-373 us per centre at 65536 x 8192 against 391-397 for the 16 x 16
+// product, with the same chosen centres.
 constexpr int kMfF = 128;           // features per stage
 constexpr int kMfRun = kMfF / 4;    // contiguous features per lane per stage
 constexpr int kMfLdk = kMfF + 4;    // padded LDS row of a candidate
 
-template <bool kVec, int kSlots>
+template <bool kVec, int kSlots, bool kQuad>
 __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
     const float *__restrict__ X, const double *__restrict__ xnorm, int64_t n, int64_t d,
     int trials, const long long *__restrict__ cand, const PPState *__restrict__ st,
@@ -205,10 +207,15 @@ __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
     store_c(0, cv);
     __syncthreads();
 
-    f64x4 acc = {0.0, 0.0, 0.0, 0.0};  // kSlots == 16
-    // kSlots == 8: with l = 16 i + 4 b + j (the output layout), block b's
-    // partial product of sample 4 g + i against candidate 4 h + j.
-    double acc8[4][2] = {{0.0, 0.0}, {0.0, 0.0}, {0.0, 0.0}, {0.0, 0.0}};
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};  // !kQuad (16 slots)
+    // kQuad: with l = 16 i + 4 b + j (the output layout), block b's partial
+    // product of sample 4 g + i against candidate 4 h + j.
+    constexpr int H = kQuad ? kSlots / 4 : 1;
+    double acc8[4][H];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int h = 0; h < H; ++h) acc8[g][h] = 0.0;
     // Its operands (l = 16 k + 4 b + i): the 8 features 8 sigma(b, k) .. + 7
     // of the stage, sigma(b, k) = 2 b + k % 2 + 8 (k / 2), a permutation of
     // 0 .. 15 that puts the 16-byte reads of 16 consecutive lanes on
@@ -218,11 +225,11 @@ __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
         const int cur = (int)(c & 1);
         // This lane's operands of the stage: samples from its own wave's
         // slice (the wave's LDS operations run in order, so the slice can be
-        // rewritten below without a barrier), candidates (8-slot instance)
-        // from the shared buffer the last barrier published.
+        // rewritten below without a barrier), candidates (kQuad) from the
+        // shared buffer the last barrier published.
         float4 xa[kMfRun / 4];
-        float4 xa8[4][2], cb8[2][2];
-        if constexpr (kSlots == 16) {
+        float4 xa8[4][2], cb8[H][2];
+        if constexpr (!kQuad) {
             const float *arow = &xw[wave][lane & 15][grp * kMfRun];
 #pragma unroll
             for (int q = 0; q < kMfRun / 4; ++q) xa[q] = *reinterpret_cast<const float4 *>(arow + 4 * q);
@@ -233,7 +240,7 @@ __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
                 for (int hh = 0; hh < 2; ++hh)
                     xa8[g][hh] = *reinterpret_cast<const float4 *>(&xw[wave][4 * g + (lane & 3)][sig8 + 4 * hh]);
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < H; ++h)
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
                     cb8[h][hh] = *reinterpret_cast<const float4 *>(&cs[cur][4 * h + (lane & 3)][sig8 + 4 * hh]);
@@ -244,7 +251,7 @@ __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
             load_c(next, cv);
         }
         // Features beyond d were loaded as 0 for samples and candidates alike.
-        if constexpr (kSlots == 16) {
+        if constexpr (!kQuad) {
             const float *brow = &cs[cur][lane & 15][grp * kMfRun];
 #pragma unroll
             for (int q = 0; q < kMfRun / 4; ++q) {
@@ -260,7 +267,7 @@ __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
 #pragma unroll
-                    for (int h = 0; h < 2; ++h)
+                    for (int h = 0; h < H; ++h)
                         acc8[g][h] = __builtin_amdgcn_mfma_f64_4x4x4f64(
                             (double)f4_at(xa8[g][st >> 2], st & 3), (double)f4_at(cb8[h][st >> 2], st & 3),
                             acc8[g][h], 0, 0, 0);
@@ -284,7 +291,7 @@ __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
         out_buf[(int64_t)t * n + gi] = nd;
         return nd;
     };
-    if constexpr (kSlots == 16) {
+    if constexpr (!kQuad) {
         // Lane l: samples l / 16 + 4 i against slot l % 16.
         const int t = lane & 15;
         double part = 0.0;
@@ -299,13 +306,13 @@ __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
         part += __shfl_xor(part, 32);
         if (lane < 16) wpart[wave][lane] = part;
     } else {
-        // Lane l: sample 4 ((l / 4) % 4) + l / 16 against slots l % 4 and
-        // 4 + l % 4; the 16 lanes of a slot differ in bits 2 .. 5.
+        // Lane l: sample 4 ((l / 4) % 4) + l / 16 against slots 4h + l % 4;
+        // the 16 lanes of a slot differ in bits 2 .. 5.
         const int gsel = (lane >> 2) & 3;
         const int64_t gi = row0 + 4 * gsel + grp;
-        double part[2];
+        double part[H];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < H; ++h) {
             // Sum over the blocks (lanes differing in bits 2 and 3): every lane
             // adds (b0 + b1) + (b2 + b3), so all four hold the same bits.
             double red[4];
@@ -323,8 +330,8 @@ __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
             for (int o = 4; o < 64; o <<= 1) part[h] += __shfl_xor(part[h], o);
         }
         if (lane < 4) {
-            wpart[wave][lane] = part[0];
-            wpart[wave][4 + lane] = part[1];
+#pragma unroll
+            for (int h = 0; h < H; ++h) wpart[wave][4 * h + lane] = part[h];
         }
     }
     __syncthreads();
@@ -332,26 +339,31 @@ __global__ __launch_bounds__(256, 3) void pp_dist_kernel(
         out_parts[(int64_t)tid * nb + b] = ((wpart[0][tid] + wpart[1][tid]) + wpart[2][tid]) + wpart[3][tid];
 }
 
-template <int kSlots>
+template <int kSlots, bool kQuad>
 void launch_dist_slots(bool vec, int trials, unsigned nb, hipStream_t stream, const float *X,
                        const double *xnorm, int64_t n, int64_t d, const long long *cand,
                        const PPState *st, const double *prev, double *out, double *parts) {
     if (vec)
-        pp_dist_kernel<true, kSlots><<<nb, 256, 0, stream>>>(X, xnorm, n, d, trials, cand, st,
+        pp_dist_kernel<true, kSlots, kQuad><<<nb, 256, 0, stream>>>(X, xnorm, n, d, trials, cand, st,
                                                              prev, out, parts, nb);
     else
-        pp_dist_kernel<false, kSlots><<<nb, 256, 0, stream>>>(X, xnorm, n, d, trials, cand, st,
+        pp_dist_kernel<false, kSlots, kQuad><<<nb, 256, 0, stream>>>(X, xnorm, n, d, trials, cand, st,
                                                               prev, out, parts, nb);
 }
 
 void launch_dist(int trials, bool vec, unsigned nb, hipStream_t stream, const float *X,
                  const double *xnorm, int64_t n, int64_t d, const long long *cand,
                  const PPState *st, const double *prev, double *out, double *parts) {
+    // Up to 12 trials: 4 x 4 blocks, 2 or 3 candidate groups. 13 to 16: the
+    // 16 x 16 product (16 candidate slots on the 4 x 4 blocks take more
+    // registers than three blocks per CU allow, and spill: 50 % slower).
     if (trials <= 8)
-        launch_dist_slots<8>(vec, trials, nb, stream, X, xnorm, n, d, cand, st, prev, out, parts);
+        launch_dist_slots<8, true>(vec, trials, nb, stream, X, xnorm, n, d, cand, st, prev, out, parts);
+    else if (trials <= 12)
+        launch_dist_slots<12, true>(vec, trials, nb, stream, X, xnorm, n, d, cand, st, prev, out, parts);
     else
-        launch_dist_slots<16>(vec, trials, nb, stream, X, xnorm, n, d, cand, st, prev, out,
-                              parts);
+        launch_dist_slots<16, false>(vec, trials, nb, stream, X, xnorm, n, d, cand, st, prev, out,
+                                     parts);
 }
 
 constexpr int kSelWaves = 16;  // pp_select_kernel: one 1024-thread block

@@ -47,7 +47,7 @@ def test_pp_hand_example():
 @pytest.mark.parametrize("n,k,d,trials", [(500, 40, 7, 5), (3000, 64, 33, 6), (257, 257, 3, 1),
                                           (2048, 100, 1030, 16), (70, 1, 5, 3),
                                           (1500, 50, 260, 12), (600, 30, 64, 2),
-                                          (1100, 20, 516, 9)])
+                                          (1100, 20, 516, 9), (2000, 40, 130, 11)])
 def test_pp_integer_exact(n, k, d, trials):
     gu.announce(f"kmeans++ integer {n}x{k}x{d} trials {trials}")
     X, _ = datagen.make_integer(n, 1, d, seed=n + d)
