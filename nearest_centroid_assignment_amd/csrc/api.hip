@@ -184,7 +184,8 @@ int run_assign(const float *X, const float *C, int64_t n, int64_t k, int64_t d, 
                float *min_dist, bool add_norm, float *cn, const km::UpdateScratch *count_ws,
                km::Gate gate, hipStream_t s) {
     hipError_t e = km::launch_row_sqnorms(C, k, d, cn, s, gate);
-    if (e == hipSuccess) e = km::launch_fill_keys((unsigned long long *)labels, n, s, gate);
+    if (e == hipSuccess && !km::assign_stores_keys(X, C, n, k, d))
+        e = km::launch_fill_keys((unsigned long long *)labels, n, s, gate);
     if (e == hipSuccess && min_dist && add_norm)
         e = km::launch_row_sqnorms(X, n, d, min_dist, s, gate);
     if (e == hipSuccess)

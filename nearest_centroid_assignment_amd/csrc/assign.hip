@@ -16,12 +16,16 @@
 //                       with the distance, the argmin and the merge across
 //                       centroid tiles done on the accumulators: the (n, k)
 //                       distance matrix never exists in memory
+//   assign_smallk_kernel  the same for k <= 64: C resident in LDS, X read
+//                       once, straight into 16 x 16 x 4 MFMAs, one key store
+//                       per sample
 //   assign_tile_kernel  the same for any shape, operands staged through
 //                       registers into LDS, several tile sizes
 //   finalize_kernel     packed key -> int64 label, full squared distance
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "kernels.h"
@@ -809,6 +813,137 @@ __global__ __launch_bounds__(dma::NT, 2) void assign_dma_kernel(
     }
 }
 
+// ------------------------------------------------ small k: C resident in LDS
+//
+// k <= 64: the whole of C sits in LDS for the life of a block (rows rounded
+// up to 16, features to 64, zero-padded), and each wave streams groups of 16
+// samples of X from global memory straight into the B operand of
+// v_mfma_f32_16x16x4f32, so the kernel reads X once, at HBM speed, where a
+// 128- or 256-row centroid tile would repeat mostly-padding MFMAs for every
+// sample tile. Operand layout (probed on the chip): lane l holds A[l % 16]
+// [l / 16] and B[l / 16][l % 16], and value i of lane l receives D[4 (l / 16)
+// + i][l % 16]. With A = 16 centroid rows and B = 16 samples, lane (g = l /
+// 16, r = l % 16) feeds feature 16 q + 4 g + e of step (q, e) for both, so
+// one 16-byte load of row r gives four steps, and ends with sample r against
+// rows 4 g .. 4 g + 3 of each 16-row block. Every sample's key is stored once
+// (one pass covers all centroids): no atomics, no identity fill.
+namespace sk {
+constexpr int kWaves = 8;          // waves per block
+constexpr int kLdsFloats = 16384;  // C's LDS budget: 64 KiB (two blocks per CU)
+constexpr int kChunk = 64;         // features per load: four 16-byte loads per lane
+}  // namespace sk
+
+// Floats per LDS row of C: d rounded up to 64 plus 4, so that the 16-byte
+// reads of 16 consecutive rows (one per lane) fall on distinct banks.
+__host__ __device__ inline int64_t sk_ld(int64_t d) { return (d + sk::kChunk - 1) / sk::kChunk * sk::kChunk + 4; }
+
+template <int KB, int NCB>
+__global__ __launch_bounds__(sk::kWaves * 64) void assign_smallk_kernel(
+    const float *__restrict__ X, const float *__restrict__ C, const float *__restrict__ cn,
+    int64_t n, int64_t k, int64_t d, unsigned long long *__restrict__ keys,
+    const int *__restrict__ stop) {
+    extern __shared__ __align__(16) float cs[];  // 16 KB rows of sk_ld(d) floats
+    if (stop != nullptr && *stop != 0) return;  // kmeans_fit: converged
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, r = lane & 15;
+    const int64_t ld = sk_ld(d), q4 = (ld - 4) / 4;  // 16-byte chunks per padded row
+    // C into LDS: rows from k on and features from d on are zeros.
+    for (int64_t e = tid; e < 16 * KB * q4; e += sk::kWaves * 64) {
+        const int64_t row = e / q4, c = 4 * (e % q4);
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (row < k && c < d) v = *reinterpret_cast<const f32x4 *>(C + row * d + c);
+        *reinterpret_cast<f32x4 *>(cs + row * ld + c) = v;
+    }
+    // Norms of this lane's rows 16 kb + 4 g + i; NaN from k on, which never
+    // wins a strict less-than.
+    float cnv[KB][4];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t j = 16 * kb + 4 * g + i;
+            const float t = cn[j < k ? j : k - 1];
+            cnv[kb][i] = j < k ? t : __builtin_nanf("");
+        }
+    __syncthreads();  // the last barrier: waves run on their own from here
+
+    // C's rows as 16-byte units (ld is a multiple of 4), so that the A
+    // operands are read 16 bytes at a time.
+    const f32x4 *cs4 = reinterpret_cast<const f32x4 *>(cs);
+    const int64_t ld4 = ld / 4;
+    const int64_t groups = (n + 15) / 16;
+    const int64_t stride = (int64_t)gridDim.x * sk::kWaves;
+    const int64_t nc = (d + sk::kChunk - 1) / sk::kChunk;  // 64-feature chunks
+    // Each group's loads are issued together, NCB chunks (up to 256
+    // features) at a time, and used in the same iteration: the latency is
+    // covered by the other waves of the CU (up to 32), not by a prefetch
+    // carried from one iteration to the next (the compiler then waits for
+    // the prefetched loads at the top of each iteration).
+    for (int64_t grp = (int64_t)blockIdx.x * sk::kWaves + wave; grp < groups; grp += stride) {
+        const int64_t s = grp * 16 + r;
+        const float *row = X + (s < n ? s : n - 1) * d;
+        f32x4 acc[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) acc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int64_t c0 = 0; c0 < nc; c0 += NCB) {
+            // Chunk c: features 64 c + 16 q + 4 g; past d zeros, read at a
+            // clamped address so that every load is unconditional. Ordinary
+            // loads, not non-temporal ones: an instruction reads half of
+            // each row's 128-byte line (4 lanes x 16 bytes) and the next one
+            // the other half, which then comes from the cache (measured:
+            // 45.8 against 54.4 us at 1M x 16 x 64).
+            f32x4 x[NCB][4];
+#pragma unroll
+            for (int b = 0; b < NCB; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t f = (c0 + b) * sk::kChunk + 16 * q + 4 * g;
+                    const f32x4 t = *reinterpret_cast<const f32x4 *>(row + (f < d ? f : 0));
+                    x[b][q] = f < d ? t : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            // All of the batch's loads first (left alone, the scheduler
+            // moves each next to its products and the loads run one by one).
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int b = 0; b < NCB; ++b) {
+                // (chunks past the last one read column 0 of C: their x is 0)
+                const int64_t cc = c0 + b < nc ? c0 + b : 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        const f32x4 a = cs4[(16 * kb + r) * ld4 + cc * (sk::kChunk / 4) + 4 * q + g];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], x[b][q][e], acc[kb], 0, 0, 0);
+                    }
+            }
+        }
+        // Rows in increasing index per lane, strict less-than: the lowest
+        // index on ties, then the packed-key minimum over the four lane
+        // groups (which also prefers the lower index).
+        float best = __builtin_inff();
+        uint32_t bidx = 4 * g < k ? (uint32_t)(4 * g) : 0xffffffffu;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float v = cnv[kb][i] - 2.0f * acc[kb][i];
+                if (v < best) {
+                    best = v;
+                    bidx = (uint32_t)(16 * kb + 4 * g + i);
+                }
+            }
+        unsigned long long key = pack_key(best, bidx);
+        unsigned long long other = __shfl_xor(key, 16);
+        key = other < key ? other : key;
+        other = __shfl_xor(key, 32);
+        key = other < key ? other : key;
+        if (g == 0 && s < n) keys[s] = key;
+    }
+}
+
 // Tile shapes (centroids x samples; the launcher picks one by problem shape).
 using Tile128x256 = TileCfg<2, 4, 2, 2, 32>;  // 512 threads, 108 KiB LDS, 1 block per CU
 using Tile256x128 = TileCfg<4, 2, 2, 2, 32>;  // 512 threads, 108 KiB LDS, 1 block per CU
@@ -944,14 +1079,31 @@ static int64_t tile_rounds(int64_t tiles, int64_t cus) {
     return cdiv(cdiv(tiles, 8), per_xcd);
 }
 
+// 16-row blocks of C for the small-k kernel, 0 where it does not take the
+// shape (k above 64, rows not whole 16-byte chunks, or C past its LDS budget).
+static int smallk_blocks(int64_t k, int64_t d) {
+    if (k > 64 || d % 4 != 0 || d >= (1 << 22)) return 0;
+    const int kb = (int)((k + 15) / 16);
+    return 16 * kb * sk_ld(d) <= sk::kLdsFloats ? kb : 0;
+}
+
+static const char *regular_tile_name(int64_t n, int64_t k, int64_t d);
+
 static const char *assign_tile_name(int64_t n, int64_t k, int64_t d) {
-    // KMEANS_ASSIGN_TILE=256x256 | 128x256 | 256x128 | 128x128 | 64x64 forces
-    // a tile (tuning); 256x256 falls back to 128x256 where it does not apply.
+    // KMEANS_ASSIGN_TILE=smallk | 256x256 | 128x256 | 256x128 | 128x128 |
+    // 64x64 forces a tile (tuning); smallk and 256x256 fall back where they
+    // do not apply (smallk to the rule below, 256x256 to 128x256).
     const char *forced = getenv("KMEANS_ASSIGN_TILE");
     if (forced && (!strcmp(forced, "256x128") || !strcmp(forced, "128x128") ||
                    !strcmp(forced, "64x64") || !strcmp(forced, "128x256") ||
-                   !strcmp(forced, "256x256")))
+                   !strcmp(forced, "256x256") || !strcmp(forced, "smallk")))
         return forced;
+    // k <= 64: C resident in LDS and X streamed once.
+    if (smallk_blocks(k, d) > 0) return "smallk";
+    return regular_tile_name(n, k, d);
+}
+
+static const char *regular_tile_name(int64_t n, int64_t k, int64_t d) {
     // The DMA-staged 256 x 256 tile where there are enough tiles to give each
     // CU one and either every tile is full or, with edge tiles cut short, it
     // still beats 128 x 256: a round of 256 x 256 tiles costs 1.8 rounds of
@@ -977,6 +1129,9 @@ static const char *assign_tile_name(int64_t n, int64_t k, int64_t d) {
 int64_t assign_grid_threads(int64_t n, int64_t k, int64_t d) {
     if (n <= 0) return 0;
     const char *tile = assign_tile_name(n, k, d);
+    // The small-k grid is at most two blocks per CU, but unaligned rows fall
+    // back to the rule's tile: bound both by the latter.
+    if (!strcmp(tile, "smallk")) tile = regular_tile_name(n, k, d);
     if (!strcmp(tile, "256x128")) return tile_blocks<Tile256x128>(n, k) * Tile256x128::kThreads;
     if (!strcmp(tile, "128x128")) return tile_blocks<Tile128x128>(n, k) * Tile128x128::kThreads;
     // 256x256 launches at most one block per CU, but falls back to the
@@ -986,11 +1141,104 @@ int64_t assign_grid_threads(int64_t n, int64_t k, int64_t d) {
     return tile_blocks<Tile64x64>(n, k) * Tile64x64::kThreads;
 }
 
+template <int KB>
+static void launch_smallk_kb(int ncb, unsigned nb, unsigned nt, size_t lds, hipStream_t stream,
+                             const float *X, const float *C, const float *cn, int64_t n, int64_t k,
+                             int64_t d, unsigned long long *keys, const int *stop) {
+    switch (ncb) {
+    case 1: assign_smallk_kernel<KB, 1><<<nb, nt, lds, stream>>>(X, C, cn, n, k, d, keys, stop); break;
+    case 2: assign_smallk_kernel<KB, 2><<<nb, nt, lds, stream>>>(X, C, cn, n, k, d, keys, stop); break;
+    case 3: assign_smallk_kernel<KB, 3><<<nb, nt, lds, stream>>>(X, C, cn, n, k, d, keys, stop); break;
+    default: assign_smallk_kernel<KB, 4><<<nb, nt, lds, stream>>>(X, C, cn, n, k, d, keys, stop); break;
+    }
+}
+
+// Blocks of the (KB, NCB) instance a CU holds at once by its registers and
+// waves (the runtime's occupancy query without LDS; 0 if it fails). Cached
+// per device and instance in atomics: racing threads store the same value.
+template <int KB, int NCB>
+static int smallk_occupancy() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, assign_smallk_kernel<KB, NCB>,
+                                                         sk::kWaves * 64, 0) != hipSuccess)
+            return 0;
+        cached[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+template <int KB>
+static int smallk_blocks_per_cu_kb(int ncb) {
+    switch (ncb) {
+    case 1: return smallk_occupancy<KB, 1>();
+    case 2: return smallk_occupancy<KB, 2>();
+    case 3: return smallk_occupancy<KB, 3>();
+    default: return smallk_occupancy<KB, 4>();
+    }
+}
+
+static int smallk_blocks_per_cu(int kb, int ncb) {
+    switch (kb) {
+    case 1: return smallk_blocks_per_cu_kb<1>(ncb);
+    case 2: return smallk_blocks_per_cu_kb<2>(ncb);
+    case 3: return smallk_blocks_per_cu_kb<3>(ncb);
+    default: return smallk_blocks_per_cu_kb<4>(ncb);
+    }
+}
+
+static void launch_smallk(int kb, int ncb, unsigned nb, unsigned nt, size_t lds, hipStream_t stream,
+                          const float *X, const float *C, const float *cn, int64_t n, int64_t k,
+                          int64_t d, unsigned long long *keys, const int *stop) {
+    switch (kb) {
+    case 1: launch_smallk_kb<1>(ncb, nb, nt, lds, stream, X, C, cn, n, k, d, keys, stop); break;
+    case 2: launch_smallk_kb<2>(ncb, nb, nt, lds, stream, X, C, cn, n, k, d, keys, stop); break;
+    case 3: launch_smallk_kb<3>(ncb, nb, nt, lds, stream, X, C, cn, n, k, d, keys, stop); break;
+    default: launch_smallk_kb<4>(ncb, nb, nt, lds, stream, X, C, cn, n, k, d, keys, stop); break;
+    }
+}
+
+// Whether the small-k kernel runs for these arguments (it stores every key).
+static bool takes_smallk(const float *X, const float *C, int64_t n, int64_t k, int64_t d) {
+    return n > 0 && !strcmp(assign_tile_name(n, k, d), "smallk") && smallk_blocks(k, d) > 0 &&
+           vec_ok(X, d) && vec_ok(C, d);
+}
+
+bool assign_stores_keys(const float *X, const float *C, int64_t n, int64_t k, int64_t d) {
+    return takes_smallk(X, C, n, k, d);
+}
+
 hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, int64_t n,
                                int64_t k, int64_t d, unsigned long long *keys,
                                hipStream_t stream, const int *stop) {
     if (n <= 0) return hipSuccess;
     const char *tile = assign_tile_name(n, k, d);
+    if (!strcmp(tile, "smallk")) {
+        if (takes_smallk(X, C, n, k, d)) {
+            // Persistent waves over the 16-sample groups: as many blocks as
+            // the CUs hold at once, fewer where there are fewer groups.
+            const int kb = smallk_blocks(k, d);
+            const int ncb = (int)std::min<int64_t>(cdiv(d, sk::kChunk), 4);
+            const int cus = device_cus();
+            const size_t lds = (size_t)16 * kb * sk_ld(d) * sizeof(float);
+            // As many blocks as the CUs hold at once (by LDS, 160 KiB per CU,
+            // and by registers), so that no block waits for another to end.
+            int64_t per_cu = (int64_t)((160 << 10) / lds);
+            const int by_regs = smallk_blocks_per_cu(kb, ncb);
+            if (by_regs > 0 && per_cu > by_regs) per_cu = by_regs;
+            if (per_cu < 1) per_cu = 1;
+            int64_t blocks = cdiv(cdiv(n, 16), sk::kWaves);
+            const int64_t cap = per_cu * (int64_t)(cus > 0 ? cus : 256);
+            if (blocks > cap) blocks = cap;
+            const unsigned nb = (unsigned)blocks, nt = sk::kWaves * 64;
+            launch_smallk(kb, ncb, nb, nt, lds, stream, X, C, cn, n, k, d, keys, stop);
+            return hipGetLastError();
+        }
+        tile = regular_tile_name(n, k, d);
+    }
     if (!strcmp(tile, "256x256")) {
         // One persistent block per CU (128 KiB of LDS: one fits), each walking
         // its XCD's tiles; the walk needs at least 8 blocks or one per tile.

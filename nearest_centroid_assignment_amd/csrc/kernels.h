@@ -56,11 +56,16 @@ hipError_t launch_fill_keys(unsigned long long *keys, int64_t n, hipStream_t str
                             Gate gate = Gate{});
 
 // Fused Gram product + argmin epilogue: for every sample, atomically lowers
-// keys[i] to the packed (distance', index) of its best centroid per tile.
+// keys[i] to the packed (distance', index) of its best centroid per tile,
+// or, at k <= 64 (one pass over all centroids), stores it outright.
 // With stop != NULL every block returns at once if *stop is non-zero.
 hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, int64_t n,
                                int64_t k, int64_t d, unsigned long long *keys,
                                hipStream_t stream, const int *stop = nullptr);
+
+// Whether launch_assign_tiles with these arguments stores every sample's key
+// outright (then the identity fill before it is not needed).
+bool assign_stores_keys(const float *X, const float *C, int64_t n, int64_t k, int64_t d);
 
 // Turns packed keys into int64 labels in place. min_dist (nullable): with
 // add_norm it holds ||x_i||^2 on entry and the clamped full squared distance

@@ -45,8 +45,8 @@ ASSIGN_SOURCE = os.path.join(HERE, "csrc", "assign.hip")
 COPY_BYTES = 1 << 30
 COPY_KERNEL = "copy_kernel"
 # The assignment's product kernel: the DMA-staged 256 x 256 one on the full
-# large shapes, the register-staged one elsewhere.
-ASSIGN_KERNELS = ("assign_dma_kernel", "assign_tile_kernel")
+# large shapes, the small-k one for k <= 64, the register-staged one elsewhere.
+ASSIGN_KERNELS = ("assign_dma_kernel", "assign_smallk_kernel", "assign_tile_kernel")
 
 
 def kernel_digest() -> str:

@@ -75,7 +75,14 @@ def test_assign_kernel_name_follows_the_tile_rule():
     kernel where the 256-row edge or last round wastes more (k = 300,
     50000 x 700), for fewer than 256 tiles, and for rows that are not whole
     16-byte chunks (d not a multiple of 4)."""
-    dma, reg = "assign_dma_kernel", "assign_tile_kernel"
+    dma, reg, small = "assign_dma_kernel", "assign_tile_kernel", "assign_smallk_kernel"
+    for shape in [(512, 17, 64), (1 << 20, 16, 64), (1000, 1, 4), (2000, 64, 192),
+                  (513, 16, 960)]:
+        assert bench.assign_kernel_name(*shape) == small, shape
+    # k above 64, or C past 64 KiB of LDS (64 rows of 256 + 4 floats), or d not
+    # a multiple of 4: not the small-k kernel.
+    for shape in [(1 << 20, 65, 64), (262144, 64, 256), (513, 16, 1024), (4096, 16, 98)]:
+        assert bench.assign_kernel_name(*shape) != small, shape
     for name in ("mid", "feature_heavy", "centroid_heavy", "sample_heavy"):
         cfg = datagen.CONFIGS[name]
         assert bench.assign_kernel_name(cfg.n, cfg.k, cfg.d) == dma

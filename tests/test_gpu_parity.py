@@ -134,6 +134,20 @@ def test_lloyd_min_dist_paths(n, k, d, what):
 # kernel's ragged instances: n not a multiple of 256 with d a multiple of 64,
 # and d a multiple of 4 only (a partial last stage).
 DMA_DEFAULT = [(65000, 1024, 128), (20000, 3000, 100), (40000, 2000, 300)]
+# The small-k kernel in a whole Lloyd step (labels, min_dist, update).
+SMALLK_LLOYD = [(20000, 10, 64), (65536, 50, 96), (3001, 64, 192)]
+
+
+@pytest.mark.parametrize("n,k,d", SMALLK_LLOYD, ids=[f"{n}x{k}x{d}" for n, k, d in SMALLK_LLOYD])
+def test_lloyd_smallk(n, k, d):
+    """The whole Lloyd step, every row against the oracle, at k <= 64."""
+    gu.announce(f"lloyd smallk {n}x{k}x{d}")
+    rng = np.random.default_rng(n + k + d)
+    centres = 2.0 * rng.standard_normal((k, d))
+    X = (centres[rng.integers(0, k, n)] + rng.standard_normal((n, d))).astype(np.float32)
+    C = X[rng.choice(n, k, replace=False)].copy()
+    res = gu.full_parity(X, C)
+    assert res["mismatches"] <= res["near_ties"]
 
 
 @pytest.mark.parametrize("n,k,d", DMA_DEFAULT, ids=[f"{n}x{k}x{d}" for n, k, d in DMA_DEFAULT])
@@ -429,6 +443,55 @@ def test_dma_tile_ragged(monkeypatch, n, k, d):
     o_labels, best, _ = oracle.assign(X, C)
     assert np.array_equal(g_labels, o_labels)
     assert np.array_equal(g_md.astype(np.float64), best)
+
+
+SMALLK = [(1000, 1, 4), (1000, 5, 60), (4097, 16, 64), (3000, 17, 100), (5000, 33, 128),
+          (2000, 64, 192), (777, 48, 320), (513, 16, 960), (70, 3, 36), (40000, 20, 32)]
+
+
+@pytest.mark.parametrize("n,k,d", SMALLK, ids=[f"{n}x{k}x{d}" for n, k, d in SMALLK])
+def test_smallk_kernel(n, k, d):
+    """The small-k kernel (C resident in LDS, X streamed into 16 x 16 x 4
+    MFMAs), which the launcher takes for these shapes: one to four 16-row
+    blocks of C with rows past k, a last 16-sample group past n (1000, 4097,
+    777, 513, 70 samples), features past d in the last 64-feature load (4 to
+    960 features), many groups per wave (40000). Integer data with duplicate
+    centroids: labels (lowest index on ties) and distances bit-exact."""
+    import os
+    import sys
+
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+
+    assert bench.assign_kernel_name(n, k, d) == "assign_smallk_kernel"
+    gu.announce(f"smallk {n}x{k}x{d}")
+    X, C = datagen.make_integer(n, k, d, seed=n + 3 * k + d)
+    if k > 2:
+        C[k - 1] = C[1]
+    g_labels, g_md = gu.gpu_assign(X, C)
+    o_labels, best, _ = oracle.assign(X, C)
+    assert np.array_equal(g_labels, o_labels)
+    assert np.array_equal(g_md.astype(np.float64), best)
+
+
+def test_smallk_unaligned_falls_back():
+    """Samples that are not 16-byte aligned: the small-k shape runs on the
+    register-staged kernel instead (scalar loads), with the same results."""
+    import torch
+    from nearest_centroid_assignment_amd import binding
+
+    n, k, d = 3000, 16, 64
+    gu.announce(f"smallk fallback unaligned {n}x{k}x{d}")
+    X, C = datagen.make_integer(n, k, d, seed=78)
+    flat = torch.zeros(n * d + 1, dtype=torch.float32, device="cuda:0")
+    Xg = flat[1:].view(n, d)
+    Xg.copy_(torch.from_numpy(X))
+    assert Xg.data_ptr() % 16 != 0
+    labels, md = binding.assign(Xg, gu.to_gpu(C))
+    torch.cuda.synchronize()
+    o_labels, best, _ = oracle.assign(X, C)
+    assert np.array_equal(labels.cpu().numpy(), o_labels)
+    assert np.array_equal(md.cpu().numpy().astype(np.float64), best)
 
 
 def test_dma_tile_unaligned_falls_back(monkeypatch):
