@@ -84,16 +84,18 @@ def parse_args():
 def assign_kernel_name(n: int, k: int, d: int, cus: int = 256) -> str:
     """The product kernel kmeans_assign runs for 16-byte aligned inputs of
     this shape on a device with `cus` compute units (the launcher's rule: the
-    small-k kernel with C resident in LDS for k <= 64 where C fits in 64 KiB;
+    small-k kernel with C resident in LDS for k <= 64, or k <= 128 from 2^17
+    samples, where C fits in 64 KiB;
     else DMA-staged 256 x 256 tiles when d is a multiple of 4, there are at least
     256 of them and either every tile is full (d a multiple of 64) or 1.8
     rounds of 128 x 256 tiles per round of them still come out ahead)."""
     def cdiv(a, b):
         return -(-a // b)
 
-    # k <= 64: C resident in LDS (16-row blocks, rows of d rounded up to 64
-    # plus 4 floats, at most 64 KiB).
-    if k <= 64 and d % 4 == 0 and 16 * cdiv(k, 16) * (cdiv(d, 64) * 64 + 4) <= 16384:
+    # Small k (up to 64, or 128 from 2^17 samples): C resident in LDS
+    # (16-row blocks, rows of d rounded up to 64 plus 4 floats, at most 64 KiB).
+    small = k <= 64 or (k <= 128 and n >= 1 << 17)
+    if small and d % 4 == 0 and 16 * cdiv(k, 16) * (cdiv(d, 64) * 64 + 4) <= 16384:
         return "assign_smallk_kernel"
 
     def rounds(tiles):

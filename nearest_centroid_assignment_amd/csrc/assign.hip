@@ -16,7 +16,7 @@
 //                       with the distance, the argmin and the merge across
 //                       centroid tiles done on the accumulators: the (n, k)
 //                       distance matrix never exists in memory
-//   assign_smallk_kernel  the same for k <= 64: C resident in LDS, X read
+//   assign_smallk_kernel  the same for small k: C resident in LDS, X read
 //                       once, straight into 16 x 16 x 4 MFMAs, one key store
 //                       per sample
 //   assign_tile_kernel  the same for any shape, operands staged through
@@ -815,7 +815,7 @@ __global__ __launch_bounds__(dma::NT, 2) void assign_dma_kernel(
 
 // ------------------------------------------------ small k: C resident in LDS
 //
-// k <= 64: the whole of C sits in LDS for the life of a block (rows rounded
+// k <= 128 (up to eight 16-row blocks): the whole of C sits in LDS for the life of a block (rows rounded
 // up to 16, features to 64, zero-padded), and each wave streams groups of 16
 // samples of X from global memory straight into the B operand of
 // v_mfma_f32_16x16x4f32, so the kernel reads X once, at HBM speed, where a
@@ -1080,9 +1080,12 @@ static int64_t tile_rounds(int64_t tiles, int64_t cus) {
 }
 
 // 16-row blocks of C for the small-k kernel, 0 where it does not take the
-// shape (k above 64, rows not whole 16-byte chunks, or C past its LDS budget).
-static int smallk_blocks(int64_t k, int64_t d) {
-    if (k > 64 || d % 4 != 0 || d >= (1 << 22)) return 0;
+// shape: k above 128, or above 64 with fewer than 2^17 samples (there the
+// tiles keep more CUs busy: 4096 x 100 x 128 was 19 % slower on this kernel,
+// 2^18 x 128 x 128 the same, 2^20 samples with k = 72 to 128 17-50 %
+// faster), rows not whole 16-byte chunks, or C past its LDS budget.
+static int smallk_blocks(int64_t n, int64_t k, int64_t d) {
+    if (k > 128 || (k > 64 && n < (1 << 17)) || d % 4 != 0 || d >= (1 << 22)) return 0;
     const int kb = (int)((k + 15) / 16);
     return 16 * kb * sk_ld(d) <= sk::kLdsFloats ? kb : 0;
 }
@@ -1098,8 +1101,8 @@ static const char *assign_tile_name(int64_t n, int64_t k, int64_t d) {
                    !strcmp(forced, "64x64") || !strcmp(forced, "128x256") ||
                    !strcmp(forced, "256x256") || !strcmp(forced, "smallk")))
         return forced;
-    // k <= 64: C resident in LDS and X streamed once.
-    if (smallk_blocks(k, d) > 0) return "smallk";
+    // Small k: C resident in LDS and X streamed once.
+    if (smallk_blocks(n, k, d) > 0) return "smallk";
     return regular_tile_name(n, k, d);
 }
 
@@ -1186,7 +1189,11 @@ static int smallk_blocks_per_cu(int kb, int ncb) {
     case 1: return smallk_blocks_per_cu_kb<1>(ncb);
     case 2: return smallk_blocks_per_cu_kb<2>(ncb);
     case 3: return smallk_blocks_per_cu_kb<3>(ncb);
-    default: return smallk_blocks_per_cu_kb<4>(ncb);
+    case 4: return smallk_blocks_per_cu_kb<4>(ncb);
+    case 5: return smallk_blocks_per_cu_kb<5>(ncb);
+    case 6: return smallk_blocks_per_cu_kb<6>(ncb);
+    case 7: return smallk_blocks_per_cu_kb<7>(ncb);
+    default: return smallk_blocks_per_cu_kb<8>(ncb);
     }
 }
 
@@ -1197,13 +1204,17 @@ static void launch_smallk(int kb, int ncb, unsigned nb, unsigned nt, size_t lds,
     case 1: launch_smallk_kb<1>(ncb, nb, nt, lds, stream, X, C, cn, n, k, d, keys, stop); break;
     case 2: launch_smallk_kb<2>(ncb, nb, nt, lds, stream, X, C, cn, n, k, d, keys, stop); break;
     case 3: launch_smallk_kb<3>(ncb, nb, nt, lds, stream, X, C, cn, n, k, d, keys, stop); break;
-    default: launch_smallk_kb<4>(ncb, nb, nt, lds, stream, X, C, cn, n, k, d, keys, stop); break;
+    case 4: launch_smallk_kb<4>(ncb, nb, nt, lds, stream, X, C, cn, n, k, d, keys, stop); break;
+    case 5: launch_smallk_kb<5>(ncb, nb, nt, lds, stream, X, C, cn, n, k, d, keys, stop); break;
+    case 6: launch_smallk_kb<6>(ncb, nb, nt, lds, stream, X, C, cn, n, k, d, keys, stop); break;
+    case 7: launch_smallk_kb<7>(ncb, nb, nt, lds, stream, X, C, cn, n, k, d, keys, stop); break;
+    default: launch_smallk_kb<8>(ncb, nb, nt, lds, stream, X, C, cn, n, k, d, keys, stop); break;
     }
 }
 
 // Whether the small-k kernel runs for these arguments (it stores every key).
 static bool takes_smallk(const float *X, const float *C, int64_t n, int64_t k, int64_t d) {
-    return n > 0 && !strcmp(assign_tile_name(n, k, d), "smallk") && smallk_blocks(k, d) > 0 &&
+    return n > 0 && !strcmp(assign_tile_name(n, k, d), "smallk") && smallk_blocks(n, k, d) > 0 &&
            vec_ok(X, d) && vec_ok(C, d);
 }
 
@@ -1220,7 +1231,7 @@ hipError_t launch_assign_tiles(const float *X, const float *C, const float *cn, 
         if (takes_smallk(X, C, n, k, d)) {
             // Persistent waves over the 16-sample groups: as many blocks as
             // the CUs hold at once, fewer where there are fewer groups.
-            const int kb = smallk_blocks(k, d);
+            const int kb = smallk_blocks(n, k, d);
             const int ncb = (int)std::min<int64_t>(cdiv(d, sk::kChunk), 4);
             const int cus = device_cus();
             const size_t lds = (size_t)16 * kb * sk_ld(d) * sizeof(float);

@@ -77,11 +77,13 @@ def test_assign_kernel_name_follows_the_tile_rule():
     16-byte chunks (d not a multiple of 4)."""
     dma, reg, small = "assign_dma_kernel", "assign_tile_kernel", "assign_smallk_kernel"
     for shape in [(512, 17, 64), (1 << 20, 16, 64), (1000, 1, 4), (2000, 64, 192),
-                  (513, 16, 960)]:
+                  (513, 16, 960), (1 << 20, 100, 128), (1 << 17, 128, 64)]:
         assert bench.assign_kernel_name(*shape) == small, shape
-    # k above 64, or C past 64 KiB of LDS (64 rows of 256 + 4 floats), or d not
-    # a multiple of 4: not the small-k kernel.
-    for shape in [(1 << 20, 65, 64), (262144, 64, 256), (513, 16, 1024), (4096, 16, 98)]:
+    # k above 128, above 64 with fewer than 2^17 samples, C past 64 KiB of LDS
+    # (64 rows of 256 + 4 floats; 128 rows of 128 + 4), or d not a multiple of
+    # 4: not the small-k kernel.
+    for shape in [(4096, 65, 64), (1 << 20, 129, 32), (262144, 64, 256), (513, 16, 1024),
+                  (4096, 16, 98), (1 << 20, 128, 96)]:
         assert bench.assign_kernel_name(*shape) != small, shape
     for name in ("mid", "feature_heavy", "centroid_heavy", "sample_heavy"):
         cfg = datagen.CONFIGS[name]

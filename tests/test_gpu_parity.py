@@ -446,14 +446,15 @@ def test_dma_tile_ragged(monkeypatch, n, k, d):
 
 
 SMALLK = [(1000, 1, 4), (1000, 5, 60), (4097, 16, 64), (3000, 17, 100), (5000, 33, 128),
-          (2000, 64, 192), (777, 48, 320), (513, 16, 960), (70, 3, 36), (40000, 20, 32)]
+          (2000, 64, 192), (777, 48, 320), (513, 16, 960), (70, 3, 36), (40000, 20, 32),
+          (131072, 65, 60), (140000, 96, 100), (131072, 100, 128), (131075, 128, 64)]
 
 
 @pytest.mark.parametrize("n,k,d", SMALLK, ids=[f"{n}x{k}x{d}" for n, k, d in SMALLK])
 def test_smallk_kernel(n, k, d):
     """The small-k kernel (C resident in LDS, X streamed into 16 x 16 x 4
-    MFMAs), which the launcher takes for these shapes: one to four 16-row
-    blocks of C with rows past k, a last 16-sample group past n (1000, 4097,
+    MFMAs), which the launcher takes for these shapes: one to eight 16-row
+    blocks of C (k above 64 from 2^17 samples) with rows past k, a last 16-sample group past n (1000, 4097,
     777, 513, 70 samples), features past d in the last 64-feature load (4 to
     960 features), many groups per wave (40000). Integer data with duplicate
     centroids: labels (lowest index on ties) and distances bit-exact."""
