@@ -64,11 +64,13 @@ GRAPH_SHAPES = [
     ("probe", None),                       # 64 x 64 tiles, the one-launch counting path
     ("blobs", (2048, 512, 256)),           # full 256 x 256 tiles (the DMA kernel)
     ("blobs", (3000, 1500, 96)),           # k > 1024: the four-launch counting path
+    ("blobs", (3000, 20, 64)),             # the small-k kernel (keys stored, no identity fill)
 ]
 
 
 @pytest.mark.parametrize("noalloc", [False, True], ids=["workspace", "noalloc"])
-@pytest.mark.parametrize("name,shape", GRAPH_SHAPES, ids=["probe", "2048x512x256", "3000x1500x96"])
+@pytest.mark.parametrize("name,shape", GRAPH_SHAPES,
+                         ids=["probe", "2048x512x256", "3000x1500x96", "3000x20x64"])
 def test_lloyd_step_graph_replays(name, shape, noalloc):
     """kmeans_lloyd_step (with a workspace) or kmeans_lloyd_step_noalloc (the
     static scratch) captured once; four replays alternate two centre sets,
