@@ -23,6 +23,19 @@ summarize:
   the MALL in front of it), so the figure is beyond-L2 traffic, an upper
   bound of the HBM bytes.
 
+trace:
+    python3 -m nearest_centroid_assignment_amd.profile_run trace \
+        --dir <run dir> --workload mid --bench-line <file> --out <file.md>
+  writes the kernel-trace summary of a run of
+  ``rocprofv3 --kernel-trace --stats --output-format csv -d <run dir> -o bench
+  -- python3 -u bench.py --config <workload> --steps 5 --warmup 1
+  --no-cpu-baseline`` (its stdout, the bench line, saved in <file>): every
+  kernel's calls, average and minimum duration and share of the time, the
+  assignment's product kernel as a fraction of the fp32 MFMA peak (over all
+  its calls and over the timed assignment calls alone, the last ones before
+  the final assignment), the plain update's mean kernel in bytes per second,
+  and bench.py's own figures.
+
 kernels:
     python3 -m nearest_centroid_assignment_amd.profile_run kernels \
         --dir <run dir> [--dir <run dir> ...]
@@ -190,18 +203,120 @@ def kernel_table(dirs) -> list:
     return rows
 
 
+MFMA_FP32_PEAK_TFLOPS = 157.3
+
+
+def short_kernel_name(name: str) -> str:
+    """`void km::(anonymous namespace)::foo<1, 2>(float const*, ...)` -> `foo<1, 2>`."""
+    name = name.replace("(anonymous namespace)::", "").replace("km::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    return name.split("(")[0]
+
+
+def trace_summary(run_dir: str, workload: str, bench_line_file: str) -> str:
+    """Markdown summary of one rocprofv3 kernel-trace run of bench.py (see the
+    module docstring)."""
+    from . import datagen
+
+    cfg = datagen.CONFIGS[workload]
+    n, k, d = cfg.n, cfg.k, cfg.d
+    flops = 2.0 * n * k * d
+    with open(os.path.join(run_dir, "bench_kernel_stats.csv"), newline="") as f:
+        stats = list(csv.DictReader(f))
+    with open(os.path.join(run_dir, "bench_kernel_trace.csv"), newline="") as f:
+        trace = list(csv.DictReader(f))
+    bench = None
+    with open(bench_line_file) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{") and '"metric"' in line:
+                bench = json.loads(line)
+    if bench is None:
+        raise ValueError(f"no bench.py line in {bench_line_file}")
+    total_ns = sum(float(r["TotalDurationNs"]) for r in stats)
+    rows = sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))
+    out = [f"# Kernel trace — one Lloyd step, {workload} (n={n}, k={k}, d={d}, fp32)", "",
+           "Command (on one MI355X; `<repo>` is the repository root):", "",
+           f"    cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d "
+           f"<repo>/gpurun_out/trace_{workload} -o bench -- python3 -u <repo>/bench.py "
+           f"--config {workload} --steps 5 --warmup 1 --no-cpu-baseline", "",
+           "Summary written by `python3 -m nearest_centroid_assignment_amd.profile_run trace "
+           f"--dir <repo>/gpurun_out/trace_{workload} --workload {workload} --bench-line <that "
+           "command's stdout>`.", "",
+           "bench.py in that mode runs Lloyd steps untimed for at least 300 ms (the GPU's clocks "
+           "ramp up over the first tens of ms), then 1 warmup + 5 timed Lloyd steps, then 1 + "
+           f"{bench['assign_calls']} assignment-only calls (no min_dist), then one more assignment "
+           "and 5 update-only calls back to back. Figures from `bench_kernel_stats.csv` (ns, shown "
+           "in µs), averaged over every call. A Lloyd step runs row_sqnorms (centroids), fill_keys "
+           "(not where the product kernel stores every key), the assignment's product kernel, "
+           "rank_hist fused with finalize (`<true, true>`), the rest of the counting sort (k <= 1024 "
+           "and n <= 65536: place, one launch; otherwise tile_prefix, cluster_scan and scatter), "
+           "segment_mean with the sample norms (`<..., true>`) and add_norms; a plain update runs "
+           "rank_hist on labels (`<true, false>`), the same counting kernels and segment_mean "
+           "without norms.", "",
+           "| kernel | calls | average (µs) | min (µs) | share |", "|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {short_kernel_name(r['Name'])} | {r['Calls']} | "
+                   f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                   f"{100.0 * float(r['TotalDurationNs']) / total_ns:.2f} % |")
+    out += ["", "Derived:"]
+    prod = [r for r in rows if short_kernel_name(r["Name"]).startswith(ASSIGN_KERNELS)]
+    if prod:
+        p = prod[0]
+        pname = short_kernel_name(p["Name"])
+        avg_ms = float(p["AverageNs"]) / 1e6
+        out.append(f"* {pname}: 2·n·k·d = {flops:.4e} flop / {avg_ms:.3f} ms = "
+                   f"{flops / avg_ms / 1e9:.1f} TFLOP/s = "
+                   f"{flops / avg_ms / 1e9 / MFMA_FP32_PEAK_TFLOPS:.3f} of the "
+                   f"{MFMA_FP32_PEAK_TFLOPS} TFLOP/s fp32 MFMA peak.")
+        disp = sorted((int(r["Dispatch_Id"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                      for r in trace if r["Kernel_Name"] == p["Name"])
+        calls = int(bench["assign_calls"])
+        timed = [t for _, t in disp[len(disp) - 1 - calls: len(disp) - 1]]
+        if len(timed) == calls and calls > 0:
+            t_ms = sum(timed) / len(timed) / 1e6
+            out.append(f"* {pname} in the {calls} timed kmeans_assign calls alone (the average "
+                       f"above also counts the untimed pre-warm steps): {t_ms * 1e3:.1f} µs = "
+                       f"{flops / t_ms / 1e9:.1f} TFLOP/s = "
+                       f"{flops / t_ms / 1e9 / MFMA_FP32_PEAK_TFLOPS:.3f} of peak; bench.py's "
+                       "assign_ms below also counts the call's small kernels.")
+    plain = [r for r in rows if short_kernel_name(r["Name"]).startswith("segment_mean_kernel<")
+             and short_kernel_name(r["Name"]).endswith("false>")]
+    if plain:
+        b = 4.0 * n * d + 4.0 * k * d + 4.0 * n
+        t = float(plain[0]["AverageNs"]) / 1e9
+        out.append(f"* segment_mean (plain update): {t * 1e6:.1f} µs for 4·n·d + 4·k·d + 4n = "
+                   f"{b:.4e} B → {b / t / 1e12:.2f} TB/s.")
+    ub = 4.0 * n * d + 8.0 * n + 4.0 * k * d
+    out.append(f"* bench.py's line from the same run: Lloyd step {bench['lloyd_ms']:.3f} ms, "
+               f"kmeans_assign {bench['assign_ms']:.3f} ms ({bench['assign_tflops']:.1f} TFLOP/s), "
+               f"kmeans_update {bench['update_ms']:.3f} ms ({bench['update_hbm_gbps']:.0f} GB/s of "
+               f"algorithmic bytes 4nd + 8n + 4kd = {ub:.4e} B).")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
-    ap.add_argument("mode", nargs="?", default="run", choices=["run", "summarize", "kernels"])
+    ap.add_argument("mode", nargs="?", default="run",
+                    choices=["run", "summarize", "kernels", "trace"])
     ap.add_argument("--workload", default="feature_heavy")
     ap.add_argument("--op", default="assign", choices=["assign", "update", "kmeanspp"])
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--out")
     ap.add_argument("--dir", action="append", default=[])
+    ap.add_argument("--bench-line")
     a = ap.parse_args(argv)
     if a.mode == "run":
         run(a.workload, a.op)
+    elif a.mode == "trace":
+        text = trace_summary(a.dir[0], a.workload, a.bench_line)
+        if a.out:
+            with open(a.out, "w") as f:
+                f.write(text)
+        else:
+            print(text, end="")
     elif a.mode == "summarize":
         print(json.dumps(summarize(a.fetch, a.write, a.out, a.workload), indent=1))
     else:
