@@ -1,12 +1,14 @@
-"""A seeded sweep of Lloyd steps over random shapes, every assignment tile the
-launcher can select (by its own rule, or forced through KMEANS_ASSIGN_TILE,
-which falls back where a tile does not apply), against the oracle on every
-row under the parity rules of gpu_util. Seven regimes: small k (C resident in
+"""Seeded sweeps over random shapes against the oracle. First, Lloyd steps
+with every assignment tile the launcher can select (by its own rule, or
+forced through KMEANS_ASSIGN_TILE, which falls back where a tile does not
+apply), against the oracle on every row under the parity rules of gpu_util. Seven regimes: small k (C resident in
 LDS), ragged shapes big enough for the DMA-staged 256 x 256 tiles, whole
 multiples of the tiles, tiny odd shapes, many small clusters, anything, and
 integer-valued data (exact arithmetic, frequent exact ties, which the lowest
 index must win). A quarter of the cases move one centroid far away, so its
-cluster is empty and keeps its centre."""
+cluster is empty and keeps its centre. Then the Lloyd driver (kmeans_fit)
+on well-separated data, with and without relocation, and k-means++ seeding
+with the oracle's draws."""
 import numpy as np
 import pytest
 
@@ -71,3 +73,78 @@ def test_shape_sweep(monkeypatch, case):
     if regime == 6:
         # Exact arithmetic on both sides: the labels, ties included, are equal.
         assert r["mismatches"] == 0
+
+
+def _fit_case(i: int, seed0: int = 9300):
+    """Well-separated blobs (centres 8 sigma apart per feature) with every
+    centroid starting near its own blob's centre: no near ties, so the GPU
+    driver and the oracle's take the same labels at every iteration. With
+    relocation, one to three centroids start far away (empty clusters) and
+    one or two iterations run (a relocated centre then splits a blob, whose
+    later iterations do have near ties)."""
+    rng = np.random.default_rng(seed0 + i)
+    n, k, d = int(rng.integers(50, 20000)), int(rng.integers(2, 600)), int(rng.integers(2, 300))
+    k = min(k, n)
+    relocate = bool(rng.random() < 0.6)
+    far = [int(rng.integers(0, k)) for _ in range(int(rng.integers(1, 4)))] \
+        if rng.random() < 0.3 else []
+    max_iter = int(rng.choice([1, 2])) if relocate else int(rng.choice([1, 2, 5, 20]))
+    tol = float(rng.choice([0.0, 1e-4]))
+    return n, k, d, relocate, tuple(far), max_iter, tol
+
+
+FIT_CASES = [_fit_case(i) for i in range(30)]
+
+
+@pytest.mark.parametrize("case", FIT_CASES,
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}-reloc{int(c[3])}-far{len(c[4])}-it{c[5]}"
+                              for c in FIT_CASES])
+def test_fit_sweep(case):
+    import oracle
+    from tests.test_gpu_fit import compare, gpu_fit
+
+    n, k, d, relocate, far, max_iter, tol = case
+    gu.announce(f"fit sweep {n}x{k}x{d} relocate={relocate} far={len(far)} max_iter={max_iter}")
+    rng = np.random.default_rng(n + 7 * k + 13 * d)
+    centres = (8.0 * rng.standard_normal((k, d))).astype(np.float32)
+    X = (centres[rng.permutation(np.arange(n) % k)] + rng.standard_normal((n, d))).astype(np.float32)
+    C = (centres + 0.3 * rng.standard_normal((k, d))).astype(np.float32)
+    for j in far:
+        C = datagen.with_far_centroid(X, C, j)
+    g = gpu_fit(X, C, max_iter, tol, relocate)
+    o = oracle.fit(X, C, max_iter, tol, relocate)
+    compare(g, o, X)
+
+
+def _pp_case(i: int, seed0: int = 9800):
+    rng = np.random.default_rng(seed0 + i)
+    n, d, k = int(rng.integers(1, 12000)), int(rng.integers(1, 600)), int(rng.integers(1, 200))
+    return min(k, n), n, d, int(rng.integers(1, 17)), i % 2 == 0
+
+
+PP_CASES = [_pp_case(i) for i in range(30)]
+
+
+@pytest.mark.parametrize("case", PP_CASES,
+                         ids=[f"{c[1]}x{c[2]}-k{c[0]}-t{c[3]}-{'int' if c[4] else 'blobs'}"
+                              for c in PP_CASES])
+def test_kmeanspp_sweep(case):
+    """k-means++ seeding with the same draws as the oracle: integer samples
+    (every distance and potential exact) and blobs (float64 sums in two
+    orders, equal unless a draw falls within rounding of a boundary): the
+    chosen indices are equal."""
+    import oracle
+    from tests.test_gpu_kmeanspp import gpu_pp
+
+    k, n, d, trials, integer = case
+    gu.announce(f"kmeans++ sweep {n}x{d} k={k} trials={trials} integer={integer}")
+    seed = n + 7 * k + 13 * d
+    if integer:
+        X, _ = datagen.make_integer(n, 1, min(d, 256), seed=seed)
+    else:
+        X, _ = datagen.make_blobs(n, 1, d, max(1, min(n, 1 + seed % 49)), 2.0, 1.0, seed=seed)
+    first, rand = datagen.make_seeding_draws(n, k, trials, seed=seed)
+    C, ch = gpu_pp(X, k, first, trials, rand)
+    want = oracle.kmeanspp(X, k, first, trials, rand)
+    assert np.array_equal(ch, want)
+    assert np.array_equal(C, X[want])
