@@ -7,8 +7,8 @@ multiples of the tiles, tiny odd shapes, many small clusters, anything, and
 integer-valued data (exact arithmetic, frequent exact ties, which the lowest
 index must win). A quarter of the cases move one centroid far away, so its
 cluster is empty and keeps its centre. Then the Lloyd driver (kmeans_fit)
-on well-separated data, with and without relocation, and k-means++ seeding
-with the oracle's draws."""
+on well-separated data, with and without relocation, k-means++ seeding
+with the oracle's draws, and the update on skewed label distributions."""
 import numpy as np
 import pytest
 
@@ -148,3 +148,54 @@ def test_kmeanspp_sweep(case):
     want = oracle.kmeanspp(X, k, first, trials, rand)
     assert np.array_equal(ch, want)
     assert np.array_equal(C, X[want])
+
+
+def _update_case(i: int, seed0: int = 10400):
+    rng = np.random.default_rng(seed0 + i)
+    n, k, d = int(rng.integers(0, 70000)), int(rng.integers(1, 20000)), int(rng.integers(1, 700))
+    if n * d > 3e7:
+        d = max(1, int(3e7 // max(n, 1)))
+    return n, k, d, i % 5
+
+
+UPDATE_CASES = [_update_case(i) for i in range(30)]
+LABEL_KINDS = ("uniform", "zipf", "giant", "few-used", "sorted")
+
+
+@pytest.mark.parametrize("case", UPDATE_CASES,
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}-{LABEL_KINDS[c[3]]}" for c in UPDATE_CASES])
+def test_update_sweep(case):
+    """kmeans_update on labels it did not compute: uniform, Zipf-skewed (a few
+    clusters far above the split size, summed in parts), one cluster holding
+    nine rows in ten, a fiftieth of the clusters used (the rest empty, keeping
+    their centres) and sorted (each cluster's rows contiguous in X). Counts
+    bit-exact, centres per the update rule, bit-exact up to the split size."""
+    import torch
+
+    from nearest_centroid_assignment_amd import binding
+
+    n, k, d, kind = case
+    gu.announce(f"update sweep {n}x{k}x{d} labels={LABEL_KINDS[kind]}")
+    rng = np.random.default_rng(n + 7 * k + 13 * d)
+    if n == 0:
+        lab = np.zeros(0, np.int64)
+    elif kind == 0:
+        lab = rng.integers(0, k, n)
+    elif kind == 1:
+        lab = (rng.zipf(1.3, n) - 1) % k
+    elif kind == 2:
+        lab = np.where(rng.random(n) < 0.9, int(rng.integers(0, k)), rng.integers(0, k, n))
+    elif kind == 3:
+        used = rng.choice(k, size=max(1, k // 50), replace=False)
+        lab = used[rng.integers(0, len(used), n)]
+    else:
+        lab = np.sort(rng.integers(0, k, n))
+    lab = lab.astype(np.int64)
+    X = rng.standard_normal((n, d), dtype=np.float32) + np.float32(rng.uniform(-5, 5))
+    C_old = rng.standard_normal((k, d), dtype=np.float32)
+    Cg = gu.to_gpu(C_old)
+    C_new = torch.empty_like(Cg)
+    counts = torch.empty(k, dtype=torch.int64, device=Cg.device)
+    binding.kmeans_update(gu.to_gpu(X), gu.to_gpu(lab), Cg, C_new, counts)
+    torch.cuda.synchronize()
+    gu.check_update(X, lab, C_old, C_new.cpu().numpy(), counts.cpu().numpy())
